@@ -1,0 +1,178 @@
+"""CPU oracle for C = A * B^T (bf16 in, fp64 sums, one bf16 rounding).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg import this package.  It shares no code with the
+HIP library (``tile_level_dense_amd``) and never imports it.
+
+The arithmetic lives in ``hkg_oracle.c`` (plain C, built by gcc); this module
+only marshals numpy arrays through ctypes.  The operation is the NT projection
+GEMM of the FlyDSL "Prebuilt kernels guide" (section 3.1, Preshuffle GEMM:
+C[M,N] = A[M,K] @ B[N,K]^T); the bf16 output rounding is nearest-even, as in
+that guide's section 1.1 (bf16 handling on gfx950: hardware cvt_pk_bf16_f32).
+
+Arrays of bf16 are numpy ``uint16`` holding the raw bit patterns.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_DIR, "hkg_oracle.c")
+LIB = os.path.join(_DIR, "libhkg_oracle.so")
+
+
+def build(force=False, src=SRC, out=LIB):
+    """Compile the oracle with gcc (no fast-math; k order is the loop order)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+             "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.hkg_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.hkg_oracle_bf16_value.restype = ctypes.c_double
+    lib.hkg_oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.hkg_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.hkg_oracle_gemm_rows.argtypes = [u16p, u16p, i64, i64, i64, i64, i64,
+                                         u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_gemm_rows.restype = None
+    lib.hkg_oracle_gemm_entries.argtypes = [u16p, u16p, i64, i64, i64, i64p, i64p, i64,
+                                            u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_gemm_entries.restype = None
+    lib.hkg_oracle_max_threads.argtypes = []
+    lib.hkg_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a, ctype):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _check_operands(A, B):
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A must be M x K and B N x K (bf16 bit patterns)")
+    return A, B
+
+
+class Oracle:
+    """One loaded build of the oracle: the default one, or a variant a test built."""
+
+    def __init__(self, path=None):
+        if path is None:
+            path = LIB
+            if not os.path.exists(path):
+                build()
+        self.path = path
+        self.lib = _bind(path)
+
+    def bf16_value(self, bits):
+        """f64 value of one bf16 bit pattern (from the format definition)."""
+        return self.lib.hkg_oracle_bf16_value(int(bits))
+
+    def bf16_rne(self, x):
+        """Nearest-even bf16 bit pattern of one double."""
+        return int(self.lib.hkg_oracle_bf16_rne(float(x)))
+
+    def bf16_rne_array(self, x):
+        x = np.asarray(x, dtype=np.float64)
+        out = np.empty(x.shape, dtype=np.uint16)
+        flat = out.reshape(-1)
+        f = self.lib.hkg_oracle_bf16_rne
+        for t, v in enumerate(x.reshape(-1).tolist()):
+            flat[t] = f(v)
+        return out
+
+    def max_threads(self):
+        return int(self.lib.hkg_oracle_max_threads())
+
+    def gemm(self, A, B, rows=None, nthreads=0, want_sums=True):
+        """C = A * B^T over rows [r0, r1) of C (all rows by default).
+
+        Returns (C bits uint16, S float64, absS float64); S and absS are None
+        when want_sums is False.
+        """
+        A, B = _check_operands(A, B)
+        M, K = A.shape
+        N = B.shape[0]
+        r0, r1 = (0, M) if rows is None else rows
+        if not (0 <= r0 <= r1 <= M):
+            raise ValueError("row range out of bounds")
+        C = np.zeros((r1 - r0, N), dtype=np.uint16)
+        S = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        absS = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        if r1 > r0 and N > 0:
+            self.lib.hkg_oracle_gemm_rows(
+                _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), M, N, K, r0, r1,
+                _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double),
+                _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+    def gemm_entries(self, A, B, ii, jj, nthreads=0):
+        """Selected elements C[ii[t], jj[t]] with their S and absS."""
+        A, B = _check_operands(A, B)
+        M, K = A.shape
+        N = B.shape[0]
+        ii = np.ascontiguousarray(ii, dtype=np.int64)
+        jj = np.ascontiguousarray(jj, dtype=np.int64)
+        if ii.shape != jj.shape:
+            raise ValueError("index arrays differ in shape")
+        if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+            raise ValueError("index out of bounds")
+        n = ii.size
+        C = np.zeros(n, dtype=np.uint16)
+        S = np.zeros(n, dtype=np.float64)
+        absS = np.zeros(n, dtype=np.float64)
+        if n:
+            self.lib.hkg_oracle_gemm_entries(
+                _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), M, N, K,
+                _ptr(ii, ctypes.c_int64), _ptr(jj, ctypes.c_int64), n,
+                _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double),
+                _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def bf16_value(bits):
+    return default().bf16_value(bits)
+
+
+def bf16_rne(x):
+    return default().bf16_rne(x)
+
+
+def bf16_rne_array(x):
+    return default().bf16_rne_array(x)
+
+
+def max_threads():
+    return default().max_threads()
+
+
+def gemm(A, B, rows=None, nthreads=0, want_sums=True):
+    return default().gemm(A, B, rows, nthreads, want_sums)
+
+
+def gemm_entries(A, B, ii, jj, nthreads=0):
+    return default().gemm_entries(A, B, ii, jj, nthreads)

@@ -1,0 +1,173 @@
+/*
+ * hkg_oracle.c -- CPU oracle for the dense BF16 GEMM  C = A * B^T.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP library: it is built by gcc from this one file.
+ *
+ * What it computes (the plain definition, written out):
+ *   The operation is the NT-layout projection GEMM described on the FlyDSL
+ *   "prebuilt_kernels_guide" page (section 3.1, Preshuffle GEMM:
+ *   C[M,N] = A[M,K] @ B[N,K]^T) and on the "FlyDSL in PyTorch" blog page
+ *   (section "Dense GEMM": BF16 NT shapes, projection and feed-forward
+ *   layers).  A is M x K row-major, B is N x K row-major (K contiguous in
+ *   both), C is M x N row-major.
+ *
+ *     S[i][j]    = sum over k = 0..K-1 (ascending) of  a(i,k) * b(j,k)   in fp64
+ *     absS[i][j] = sum over k of |a(i,k) * b(j,k)|                        in fp64
+ *     C[i][j]    = bf16 nearest-even rounding of S[i][j], applied once, f64 -> bf16
+ *
+ *   A bf16 x bf16 product has at most 16 significant bits, so every product
+ *   is exact in fp64; the only fp64 roundings are in the running sums.
+ *   Round-to-nearest-even as the bf16 output rounding follows the same
+ *   FlyDSL guide (section 1.1, LayerNorm, "bf16 handling": RNE pack in
+ *   software on gfx942, the hardware cvt_pk_bf16_f32 instruction on gfx950).
+ *
+ * Build:  gcc -O2 -fopenmp -shared -fPIC hkg_oracle.c -o libhkg_oracle.so -lm
+ * (no -ffast-math, no -ffp-contract games: the k order is the loop order).
+ *
+ * Pins (checked by the CPU test suite, independent of this code):
+ *   bf16 conversion: all 65536 bit patterns round-trip; nearest-even ties;
+ *   agreement with an integer float32->bf16 rounding on float32 inputs and
+ *   with torch's float32->bfloat16 conversion.
+ *   GEMM: all-ones (C = K), identity on either side (C = B^T, C = A),
+ *   small-integer inputs against exact int64 products, exact-rational brute
+ *   force on tiny shapes, and the fp64 summation error bound.
+ */
+#include <stdint.h>
+#include <math.h>
+#include <string.h>
+#include <stdlib.h>
+#include <omp.h>
+
+/* ---- bf16 <-> f64 from the format's definition ------------------------- */
+/* bf16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.          */
+
+double hkg_oracle_bf16_value(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int f = bits & 0x7F;
+    double mag;
+    if (e == 0xFF)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)                     /* subnormal: 0.f * 2^-126 */
+        mag = ldexp((double)f / 128.0, -126);
+    else                                 /* normal: 1.f * 2^(e-127) */
+        mag = ldexp(1.0 + (double)f / 128.0, e - 127);
+    return sign ? -mag : mag;
+}
+
+/* Round a finite or infinite double to the nearest bf16, ties to even. */
+uint16_t hkg_oracle_bf16_rne(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (isinf(ax))
+        return sign | 0x7F80;
+    if (ax == 0.0)
+        return sign;
+    int e;
+    frexp(ax, &e);                  /* ax = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                  /* ax = (2m) * 2^E, 2m in [1, 2) */
+    if (E < -126)
+        E = -126;                   /* bf16 subnormal range: fixed quantum */
+    double q = ldexp(1.0, E - 7);   /* spacing of bf16 values near ax */
+    double n = rint(ax / q);        /* ax/q is exact (power-of-two scale); rint = nearest, ties to even */
+    double y = n * q;               /* exact */
+    if (y >= ldexp(1.0, 128))       /* past the largest finite bf16 */
+        return sign | 0x7F80;
+    /* y is a bf16 value, hence exactly a float32 whose low 16 bits are 0 */
+    float yf = (float)y;
+    uint32_t u;
+    memcpy(&u, &yf, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* Table of the 65536 bf16 values, built from the definition above. */
+static double g_val[65536];
+static int g_val_ready = 0;
+
+static void build_table(void)
+{
+    if (g_val_ready)
+        return;
+#pragma omp critical(hkg_oracle_table)
+    {
+        if (!g_val_ready) {
+            for (int b = 0; b < 65536; ++b)
+                g_val[b] = hkg_oracle_bf16_value((uint16_t)b);
+            __atomic_store_n(&g_val_ready, 1, __ATOMIC_RELEASE);
+        }
+    }
+}
+
+/* One output element: the fp64 sum over k ascending, and the sum of |products|. */
+static void dot_one(const uint16_t* a_row, const uint16_t* b_row, int64_t K,
+                    double* s_out, double* abs_out)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = g_val[a_row[k]] * g_val[b_row[k]];
+        s += p;
+        sa += fabs(p);
+    }
+    *s_out = s;
+    *abs_out = sa;
+}
+
+/*
+ * Rows [row_begin, row_end) of C = A * B^T.  Outputs are (row_end-row_begin) x N,
+ * row-major.  S and absS may be NULL.  nthreads <= 0 uses the OpenMP default.
+ */
+void hkg_oracle_gemm_rows(const uint16_t* A, const uint16_t* B,
+                          int64_t M, int64_t N, int64_t K,
+                          int64_t row_begin, int64_t row_end,
+                          uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    build_table();
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s, sa;
+            dot_one(A + i * K, B + j * K, K, &s, &sa);
+            int64_t o = (i - row_begin) * N + j;
+            C[o] = hkg_oracle_bf16_rne(s);
+            if (S)
+                S[o] = s;
+            if (absS)
+                absS[o] = sa;
+        }
+    }
+}
+
+/* Selected elements (ii[t], jj[t]), t < count, of C = A * B^T. */
+void hkg_oracle_gemm_entries(const uint16_t* A, const uint16_t* B,
+                             int64_t M, int64_t N, int64_t K,
+                             const int64_t* ii, const int64_t* jj, int64_t count,
+                             uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    (void)N;
+    build_table();
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+    for (int64_t t = 0; t < count; ++t) {
+        double s, sa;
+        dot_one(A + ii[t] * K, B + jj[t] * K, K, &s, &sa);
+        C[t] = hkg_oracle_bf16_rne(s);
+        if (S)
+            S[t] = s;
+        if (absS)
+            absS[t] = sa;
+    }
+}
+
+int hkg_oracle_max_threads(void) { return omp_get_max_threads(); }

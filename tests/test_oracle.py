@@ -1,0 +1,259 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle computes C = A * B^T with fp64 sums and one nearest-even bf16
+rounding (FlyDSL "Prebuilt kernels guide", section 3.1 for the operation,
+section 1.1 for the bf16 rounding).  Every check here compares it with
+something other than itself: the bf16 format definition and IEEE ties-to-even
+(golden cases), numpy's and torch's conversions, exact integer and rational
+arithmetic, identities (all-ones, identity matrices) and the fp64 summation
+error bound.  The mutation test plants plausible mistakes in a copy of the
+oracle source and checks that these pins catch every one.
+"""
+import os
+import shutil
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import exact
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "bf16_rne_cases.txt")
+
+
+def _golden_cases():
+    cases = []
+    for ln in open(GOLDEN):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        x, e = ln.split()[:2]
+        cases.append((float.fromhex(x), int(e, 16)))
+    return cases
+
+
+# ---------------------------------------------------------------- pin checks
+# Each check takes an Oracle so the mutation test can run it on a variant.
+
+def check_value_exhaustive(O):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = exact.widen(bits)
+    got = np.array([O.bf16_value(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def check_roundtrip_exhaustive(O):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = exact.widen(bits)
+    fin = np.isfinite(vals)
+    back = O.bf16_rne_array(vals[fin])
+    assert np.array_equal(back, bits[fin])
+
+
+def check_golden_ties(O):
+    for x, e in _golden_cases():
+        assert O.bf16_rne(x) == e, (x.hex(), hex(e), hex(O.bf16_rne(x)))
+
+
+def check_rne_vs_float32_bit_rounding(O, n=100_000):
+    # For inputs that are exactly float32, f64 -> bf16 and f32 -> bf16 rounding
+    # agree; the latter is the integer bit recipe (and torch's conversion).
+    rng = np.random.default_rng(1234)
+    u = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    x32 = u.view(np.float32)
+    keep = np.isfinite(x32) & (np.abs(x32) < np.float32(3.0e38))
+    x32 = x32[keep]
+    ref = workloads.f32_to_bf16_bits(x32)
+    got = O.bf16_rne_array(x32.astype(np.float64))
+    assert np.array_equal(got, ref)
+    try:
+        import torch
+    except ImportError:
+        return
+    tref = torch.from_numpy(x32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, tref)
+
+
+def check_all_ones(O):
+    for K in (256, 4096, 8192, 12288):
+        A = np.full((3, K), 0x3F80, dtype=np.uint16)
+        B = np.full((5, K), 0x3F80, dtype=np.uint16)
+        C, S, absS = O.gemm(A, B)
+        assert np.all(S == K) and np.all(absS == K)
+        assert np.all(C == exact.round_exact(K))
+
+
+def check_identity(O):
+    rng = np.random.default_rng(7)
+    K = 64
+    I = np.zeros((K, K), dtype=np.uint16)
+    I[np.arange(K), np.arange(K)] = 0x3F80
+    Bm = workloads.draw(rng, (40, K), ("normal", 0.0, 1.0))
+    C, _, _ = O.gemm(I, Bm)                 # A = I  ->  C = B^T
+    assert np.array_equal(C, Bm.T)
+    Am = workloads.draw(rng, (33, K), ("uniform", -1.0, 1.0))
+    C, _, _ = O.gemm(Am, I)                 # B = I  ->  C = A
+    assert np.array_equal(C, Am)
+
+
+def check_small_integers(O):
+    # Integer entries in [-4, 4]: every partial sum is an exact integer, so the
+    # result must equal the exact int64 product A @ B^T, rounded once.
+    rng = np.random.default_rng(11)
+    M, N, K = 37, 29, 131
+    ai = rng.integers(-4, 5, size=(M, K))
+    bi = rng.integers(-4, 5, size=(N, K))
+    A = workloads.f32_to_bf16_bits(ai.astype(np.float32))
+    B = workloads.f32_to_bf16_bits(bi.astype(np.float32))
+    C, S, absS = O.gemm(A, B)
+    ref = ai.astype(np.int64) @ bi.astype(np.int64).T
+    assert np.array_equal(S, ref.astype(np.float64))
+    assert np.array_equal(absS, (np.abs(ai)[:, None, :] * np.abs(bi)[None, :, :]).sum(-1).astype(np.float64))
+    want = np.array([[exact.round_exact(int(v)) for v in row] for row in ref], dtype=np.uint16)
+    assert np.array_equal(C, want)
+
+
+def check_brute_force_tiny(O):
+    # Random bf16 over a wide exponent range, tiny shapes, exact rationals.
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        M, N, K = [int(v) for v in rng.integers(1, 9, size=3)]
+        mant = rng.uniform(-2.0, 2.0, size=(M + N, K))
+        scale = 2.0 ** rng.integers(-20, 21, size=(M + N, K))
+        bits = workloads.f32_to_bf16_bits((mant * scale).astype(np.float32))
+        A, B = bits[:M], bits[M:]
+        C, S, absS = O.gemm(A, B)
+        for i in range(M):
+            for j in range(N):
+                s, sa = exact.exact_dot(A[i], B[j])
+                assert abs(Fraction(S[i, j]) - s) <= K * Fraction(2) ** -53 * sa
+                assert abs(Fraction(absS[i, j]) - sa) <= K * Fraction(2) ** -53 * sa
+                assert C[i, j] == exact.round_exact(s), (trial, i, j)
+
+
+def check_fp64_bound_workload(O):
+    # tiny_256 inputs: sampled entries against the exact sum.
+    A, B = workloads.workload_inputs("tiny_256")
+    K = A.shape[1]
+    rng = np.random.default_rng(3)
+    ii = rng.integers(0, A.shape[0], size=120)
+    jj = rng.integers(0, B.shape[0], size=120)
+    C, S, absS = O.gemm_entries(A, B, ii, jj)
+    for t in range(ii.size):
+        s, sa = exact.exact_dot(A[ii[t]], B[jj[t]])
+        assert abs(Fraction(S[t]) - s) <= K * Fraction(2) ** -53 * sa
+        assert Fraction(absS[t]) == sa or abs(Fraction(absS[t]) - sa) <= K * Fraction(2) ** -53 * sa
+        assert C[t] == exact.round_exact(s)
+
+
+def check_transpose_symmetry(O):
+    # C(A, B) = C(B, A)^T element for element (same dot products, same k order);
+    # and (A, -B) negates every element.
+    A, B = workloads.make_inputs(19, 23, 77, seed=9)
+    C1, S1, _ = O.gemm(A, B)
+    C2, S2, _ = O.gemm(B, A)
+    assert np.array_equal(C1, C2.T) and np.array_equal(S1, S2.T)
+    C3, S3, _ = O.gemm(A, B ^ np.uint16(0x8000))
+    assert np.array_equal(S3, -S1)
+
+
+ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
+              check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
+              check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
+              check_transpose_symmetry]
+
+
+@pytest.fixture(scope="module")
+def O():
+    oracle.build()
+    return oracle.Oracle()
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(O, check):
+    check(O)
+
+
+def test_empty_and_degenerate(O):
+    A = np.zeros((4, 0), dtype=np.uint16)
+    B = np.zeros((3, 0), dtype=np.uint16)
+    C, S, absS = O.gemm(A, B)          # K = 0: the empty sum is +0
+    assert C.shape == (4, 3) and np.all(C == 0) and np.all(S == 0)
+    C, _, _ = O.gemm(np.zeros((0, 5), np.uint16), np.zeros((2, 5), np.uint16))
+    assert C.shape == (0, 2)
+
+
+def test_rows_and_entries_consistent(O):
+    A, B = workloads.make_inputs(70, 45, 96, seed=2)
+    C, S, absS = O.gemm(A, B)
+    Cr, Sr, _ = O.gemm(A, B, rows=(13, 51))
+    assert np.array_equal(Cr, C[13:51]) and np.array_equal(Sr, S[13:51])
+    ii = np.array([0, 69, 13, 40]); jj = np.array([44, 0, 7, 21])
+    Ce, Se, ae = O.gemm_entries(A, B, ii, jj)
+    assert np.array_equal(Ce, C[ii, jj]) and np.array_equal(Se, S[ii, jj])
+    assert np.array_equal(ae, absS[ii, jj])
+
+
+def test_thread_count_does_not_change_result(O):
+    A, B = workloads.make_inputs(64, 40, 300, seed=4)
+    C1, S1, _ = O.gemm(A, B, nthreads=1)
+    C4, S4, _ = O.gemm(A, B, nthreads=4)
+    assert np.array_equal(C1, C4) and np.array_equal(S1, S4)
+
+
+# ------------------------------------------------------------ mutation test
+# Plausible mistakes planted in a copy of the oracle source; each must be
+# caught by at least one pin above.
+MUTANTS = {
+    "sign_of_sum": ("s += p;", "s -= p;"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 0; k < K - 1; ++k) {"),
+    "reversed_b_index": ("g_val[b_row[k]]", "g_val[b_row[K - 1 - k]]"),
+    "transposed_operands": ("dot_one(A + i * K, B + j * K, K, &s, &sa);",
+                            "dot_one(A + j * K, B + i * K, K, &s, &sa);"),
+    "truncating_rounding": ("double n = rint(ax / q);", "double n = floor(ax / q);"),
+    "ties_away_from_zero": ("double n = rint(ax / q);", "double n = round(ax / q);"),
+    "one_bit_too_many": ("double q = ldexp(1.0, E - 7);", "double q = ldexp(1.0, E - 8);"),
+    "no_subnormal_clamp": ("        E = -126;                   /* bf16 subnormal range: fixed quantum */",
+                           "        E = E;"),
+    "abs_sum_signed": ("sa += fabs(p);", "sa += p;"),
+    "exponent_bias": ("mag = ldexp(1.0 + (double)f / 128.0, e - 127);",
+                      "mag = ldexp(1.0 + (double)f / 128.0, e - 126);"),
+    "negative_zero_sign": ("uint16_t sign = signbit(x) ? 0x8000 : 0;",
+                           "uint16_t sign = (x < 0) ? 0x8000 : 0;"),
+}
+
+
+def _mutant_caught(path):
+    O = oracle.Oracle(path)
+    for check in ALL_CHECKS:
+        try:
+            check(O)
+        except AssertionError:
+            return check.__name__
+    return None
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_pins_catch_planted_mistakes():
+    src = open(oracle.SRC).read()
+    tmp = tempfile.mkdtemp(prefix="hkg_mutants_")
+    try:
+        uncaught = []
+        for name, (old, new) in MUTANTS.items():
+            assert src.count(old) == 1, "mutation site not unique: " + name
+            msrc = os.path.join(tmp, name + ".c")
+            with open(msrc, "w") as f:
+                f.write(src.replace(old, new))
+            lib = os.path.join(tmp, "lib_" + name + ".so")
+            oracle.build(force=True, src=msrc, out=lib)
+            if _mutant_caught(lib) is None:
+                uncaught.append(name)
+        assert not uncaught, "mutants not caught by any pin: %s" % uncaught
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
