@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 dense BF16 GEMM C = A * B^T (libhkg.so).
+
+One step = one call of hkg_gemm_bf16 on the square workload
+(8192 x 8192 x 8192, A and B uniform in [-1, 1] rounded to bf16, seed 0),
+inputs resident in HBM.  Prints ONE JSON line on stdout:
+
+  value        TFLOP/s over the timed steps (2 M N K per step)
+  roofline     the tile kernel against the 2.5 PFLOP/s dense bf16 MFMA peak
+  decode       the M = 16 decode GEMM (16 x 4096 x 4096, N(0,1) activations,
+               N(0, 0.02) weights) as HBM GB/s against 8 TB/s, timed over
+               buffer sets rotated across 2x the 256 MB last-level cache so
+               every launch streams B from HBM
+  cpu_baseline the CPU oracle (fp64, OpenMP) on a bounded row sample of the
+               square workload, scaled to TFLOP/s
+
+Progress and diagnostics go to stderr.  Timing uses HIP events on the stream
+the kernels are launched on (torch's current stream), bracketed by device
+synchronisation.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BF16 GEMM TFLOP/s @8192³ (% of 2.5 PF) + HBM GB/s @M=16 decode (% of 8 TB/s)"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+LLC_BYTES = 256 * 2**20
+# HipKittens' best 8192^3 BF16 GEMM on MI355X (talk notes, Table 2).
+PAGES_8192_TFLOPS = 1610.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def source_digest(fname):
+    with open(os.path.join(ROOT, "tile_level_dense_amd", "csrc", fname), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a reference copy), if they were taken
+    on the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(kernel)
+    if not e or e.get("source_digest") != source_digest(e.get("source", "")):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_launches(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps          # ms per call
+
+
+def bench_square(torch, hkg, steps, warmup):
+    import workloads
+    name = "square_8192"
+    w = workloads.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    log("generating %s inputs" % name)
+    A, B = workloads.workload_inputs(name)
+    a, b = to_dev(A, torch), to_dev(B, torch)
+    del A, B
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    plan = hkg.plan(M, N, K)
+    log("plan", plan.kernel_name.decode(), plan.reason.decode())
+    ms = time_launches(torch, lambda: hkg.gemm(a, b, out=c), steps, warmup)
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    log("square: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
+    return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan)
+
+
+def bench_decode(torch, hkg, steps, warmup):
+    import workloads
+    name = "decode_16x4096x4096"
+    w = workloads.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    A, B = workloads.workload_inputs(name)
+    alg_bytes = 2.0 * (M * K + N * K + M * N)
+    per_set = 2 * (M * K + N * K + M * N)
+    sets = int(np.ceil(2 * LLC_BYTES / per_set))
+    a0, b0 = to_dev(A, torch), to_dev(B, torch)
+    bufs = [(a0.clone(), b0.clone(), torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+            for _ in range(sets)]
+    plan = hkg.plan(M, N, K)
+    log("decode plan", plan.kernel_name.decode(), "rotating over %d buffer sets (%.0f MiB)"
+        % (sets, sets * per_set / 2**20))
+    # Capture one pass over all sets in a graph so host launch cost does not
+    # pace the ~microsecond kernels; replays run the launches back to back.
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for a, b, c in bufs:                      # warm the code path outside capture
+            hkg.gemm(a, b, out=c)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for a, b, c in bufs:
+            hkg.gemm(a, b, out=c)
+    reps = max(1, steps // sets)
+    ms_rot = time_launches(torch, graph.replay, reps, max(1, warmup // sets)) / sets
+    # Hot buffers (B resident in the last-level cache) for context.
+    a, b, c = bufs[0]
+    graph_hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_hot, stream=stream):
+        for _ in range(sets):
+            hkg.gemm(a, b, out=c)
+    ms_hot = time_launches(torch, graph_hot.replay, reps, max(1, warmup // sets)) / sets
+    gbps = alg_bytes / (ms_rot * 1e-3) / 1e9
+    gbps_hot = alg_bytes / (ms_hot * 1e-3) / 1e9
+    log("decode: %.2f us/call rotating (%.0f GB/s), %.2f us hot (%.0f GB/s)"
+        % (ms_rot * 1e3, gbps, ms_hot * 1e3, gbps_hot))
+    return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
+                alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets)
+
+
+def calibration_copy(torch, mib=1024):
+    """One device-to-device copy of a known size (mib MiB read, mib MiB
+    written), the reference dispatch for scaling HBM byte counters."""
+    src = torch.empty(mib * 2**20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline(target_s=15.0):
+    """The oracle on the first rows of the square workload, timed on the host."""
+    import oracle
+    import workloads
+    w = workloads.WORKLOADS["square_8192"]
+    M, N, K = w["M"], w["N"], w["K"]
+    A, B = workloads.workload_inputs("square_8192")
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=(0, threads), want_sums=False)
+    t1 = time.perf_counter() - t0
+    rows = int(min(M, max(threads, threads * round(target_s / max(t1, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=(0, rows), want_sums=False)
+    dt = time.perf_counter() - t0
+    tflops = 2.0 * rows * N * K / dt / 1e12
+    log("cpu oracle: %d rows x %d x %d in %.1f s on %d threads: %.2e TFLOP/s" % (rows, N, K, dt, threads, tflops))
+    return dict(value=tflops, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="rows 0..%d of the 8192^3 workload (%d x 8192 outputs, K = 8192), %.1f s"
+                       % (rows - 1, rows, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=2000)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
+        return 1
+    import tile_level_dense_amd as hkg
+    hkg.lib()
+
+    calibration_copy(torch)
+    sq = bench_square(torch, hkg, args.steps, args.warmup)
+    dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    tile_kernel = sq["plan"].kernel_name.decode()
+    skinny_kernel = dec["plan"].kernel_name.decode()
+    tr = measured_traffic(tile_kernel)
+    tr_dec = measured_traffic(skinny_kernel)
+    line = {
+        "metric": METRIC,
+        "value": round(sq["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sq["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(sq["tflops"] / PAGES_8192_TFLOPS, 4),
+        "baseline_note": "HipKittens 8192^3 BF16 GEMM on MI355X, 1610 TFLOP/s (pages' best figure)",
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "square_8192: C = A B^T, M = N = K = 8192, bf16 in, fp32 accumulate, bf16 out",
+                   "M": sq["M"], "N": sq["N"], "K": sq["K"], "kernel": tile_kernel,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(sq["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(sq["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": tr, "kernel": tile_kernel,
+                     "per_launch": "2 M N K = %.4g flop per launch (one launch per step)" % sq["flops"]},
+        "decode": {"workload": "decode_16x4096x4096: M = 16, N = 4096, K = 4096",
+                   "value": round(dec["gbps"], 1), "unit": "GB/s",
+                   "frac_of_hbm": round(dec["gbps"] / PEAK_HBM_GBPS, 4),
+                   "us_per_call": round(dec["ms"] * 1e3, 3),
+                   "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 1), "peak": PEAK_HBM_GBPS,
+                                "unit": "GB/s", "frac": round(dec["gbps"] / PEAK_HBM_GBPS, 4),
+                                "traffic": tr_dec, "kernel": skinny_kernel,
+                                "per_launch": "2 (M K + N K + M N) = %d bytes per launch" % dec["alg_bytes"]},
+                   "rotating_sets": dec["sets"], "launches_timed": dec["launches"],
+                   "llc_resident_gbps": round(dec["gbps_hot"], 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

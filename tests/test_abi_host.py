@@ -1,0 +1,248 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load and export every function include/hkg.h declares,
+the ctypes mirror of hkg_plan_t must match the C layout, plans must follow
+the documented selection rules, and every argument error must come back as
+its status code before any device work.  The build must refuse kernels that
+spill registers to scratch.
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import tile_level_dense_amd as hkg
+from tile_level_dense_amd import build as hkg_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hkg.h")
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hkg.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**(hkg_[a-z0-9_]+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    assert names == sorted(hkg.EXPORTED_SYMBOLS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", hkg.library_path()], stdout=subprocess.PIPE,
+                             text=True, check=True).stdout
+        exported = set(re.findall(r"\bT (hkg_[a-z0-9_]+)", out))
+        assert set(_declared_functions()) <= exported
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_plan_struct_layout_matches_header():
+    fields = [f for f, _ in hkg.Plan._fields_]
+    prog = ['#include <stdio.h>', '#include <stddef.h>', '#include "hkg.h"', 'int main(void){',
+            'printf("size %zu\\n", sizeof(hkg_plan_t));']
+    for f in fields:
+        prog.append('printf("%s %%zu\\n", offsetof(hkg_plan_t, %s));' % (f, f))
+    prog.append("return 0;}")
+    tmp = tempfile.mkdtemp()
+    try:
+        src = os.path.join(tmp, "layout.c")
+        exe = os.path.join(tmp, "layout")
+        open(src, "w").write("\n".join(prog))
+        subprocess.check_call(["gcc", "-std=c11", "-I" + os.path.join(ROOT, "include"), src, "-o", exe])
+        out = subprocess.run([exe], stdout=subprocess.PIPE, text=True, check=True).stdout.split("\n")
+        got = dict(ln.split() for ln in out if ln.strip())
+        assert int(got["size"]) == ctypes.sizeof(hkg.Plan)
+        for f in fields:
+            assert int(got[f]) == getattr(hkg.Plan, f).offset, f
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_abi_version(lib):
+    assert lib.hkg_abi_version() == hkg.HKG_ABI_VERSION
+
+
+def test_status_strings(lib):
+    for code in list(hkg.STATUS) + [-99]:
+        s = hkg.hkg_status_string(code)
+        assert isinstance(s, str) and s
+
+
+WORKLOAD_PLANS = {
+    (256, 256, 256): ("TILE", "tile_128x128x64"),
+    (16, 4096, 4096): ("SKINNY", "skinny_m16"),
+    (128, 12288, 4096): ("SKINNY", "skinny_m128"),
+    (4096, 4096, 12288): ("TILE", "tile_256x256x64"),
+    (8192, 8192, 8192): ("TILE", "tile_256x256x64"),
+}
+
+
+@pytest.mark.parametrize("shape", list(WORKLOAD_PLANS))
+def test_plan_for_workloads(shape):
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    kind, name = WORKLOAD_PLANS[shape]
+    assert hkg.KERNEL_NAMES[p.kernel_id] == kind
+    assert p.kernel_name.decode() == name
+    assert p.flops == 2.0 * M * N * K
+    assert p.algorithmic_bytes == 2.0 * (M * K + N * K + M * N)
+    assert p.scratch_bytes == 0 and p.vgprs > 0
+    assert p.M == M and p.N == N and p.K == K
+    # deterministic
+    q = hkg.plan(M, N, K)
+    assert bytes(p) == bytes(q)
+
+
+def test_plan_square_8192_geometry():
+    p = hkg.plan(8192, 8192, 8192)
+    assert (p.tile_m, p.tile_n, p.tile_k, p.waves) == (256, 256, 64, 8)
+    assert p.grid_x == 1024 and p.block_x == 512
+    assert p.xcd_window_w == 8 and p.xcd_chunk_c == 32
+    assert p.lds_bytes == 2 * (256 + 256) * 64 * 2
+    assert p.workspace_bytes == 0 and p.split_k == 1
+
+
+def test_plan_decode_geometry():
+    p = hkg.plan(16, 4096, 4096)
+    assert p.grid_x == 256 and p.split_k == 1 and p.workspace_bytes == 0
+
+
+def test_plan_boundaries():
+    assert hkg.KERNEL_NAMES[hkg.plan(128, 4096, 4096).kernel_id] == "SKINNY"
+    assert hkg.KERNEL_NAMES[hkg.plan(129, 4096, 4096).kernel_id] == "TILE"
+    assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 100).kernel_id] == "GENERIC"     # K % 8
+    assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 0).kernel_id] == "ZERO"
+    assert hkg.KERNEL_NAMES[hkg.plan(0, 512, 64).kernel_id] == "NONE"
+    assert hkg.KERNEL_NAMES[hkg.plan(5, 0, 64).kernel_id] == "NONE"
+    assert hkg.KERNEL_NAMES[hkg.plan(1, 1, 8).kernel_id] == "SKINNY"
+    # small N at decode M: split-K across workgroups with a workspace
+    p = hkg.plan(16, 256, 8192)
+    assert p.split_k > 1 and p.workspace_bytes == p.split_k * 16 * 256 * 4
+    # tile ladder: a grid that would underfill at 256x256 steps down
+    assert hkg.plan(2048, 2048, 1024).kernel_name.decode() == "tile_128x128x64"
+    assert hkg.plan(4096, 2048, 1024).kernel_name.decode() == "tile_256x128x64"
+
+
+@pytest.mark.parametrize("shape", [(-1, 4, 8), (4, -1, 8), (4, 4, -8), (2**31, 4, 8), (4, 4, 2**31),
+                                   (2**31 - 1, 2**31 - 1, 2**31 - 1)])
+def test_plan_rejects_bad_dims(shape):
+    st, _ = hkg.hkg_gemm_bf16_plan(*shape)
+    assert st == hkg.HKG_ERR_INVALID_ARG
+
+
+def test_plan_null_out(lib):
+    assert lib.hkg_gemm_bf16_plan(4, 4, 8, None) == hkg.HKG_ERR_INVALID_ARG
+
+
+def test_argument_errors_precede_device_work():
+    M, N, K = 64, 64, 64
+    # null pointers with nonzero sizes
+    assert hkg.hkg_gemm_bf16(None, 4096, 8192, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_gemm_bf16(4096, None, 8192, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_gemm_bf16(4096, 1 << 20, None, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    # C overlapping A or B
+    base = 1 << 30
+    assert hkg.hkg_gemm_bf16(base, base + (1 << 20), base + 64, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_gemm_bf16(base, base + (1 << 20), base + (1 << 20) + 128, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    # negative dims
+    assert hkg.hkg_gemm_bf16(base, base, base, -1, N, K) == hkg.HKG_ERR_INVALID_ARG
+    # empty output: nothing to do, even with null pointers
+    assert hkg.hkg_gemm_bf16(None, None, None, 0, 0, 0) == hkg.HKG_OK
+    assert hkg.hkg_gemm_bf16(None, 4096, None, 0, 64, 64) == hkg.HKG_OK
+
+
+def test_run_plan_errors_precede_device_work():
+    M, N, K = 512, 512, 512
+    p = hkg.plan(M, N, K)
+    A, B, C = 1 << 30, (1 << 30) + (1 << 22), (1 << 30) + (1 << 23)
+    assert hkg.hkg_gemm_bf16_run_plan(p, A, B, C, M + 1, N, K) == hkg.HKG_ERR_INVALID_ARG
+    q = hkg.Plan.from_buffer_copy(p)
+    q.variant = 99
+    assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    q = hkg.Plan.from_buffer_copy(p)
+    q.split_k = 2
+    assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    q = hkg.Plan.from_buffer_copy(p)
+    q.abi_version = 7
+    assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    # a fast-kernel plan on 2-byte aligned pointers
+    assert hkg.hkg_gemm_bf16_run_plan(p, A + 2, B, C, M, N, K) == hkg.HKG_ERR_MISALIGNED
+    # skinny split range
+    s = hkg.plan(16, 4096, 4096)
+    s.split_k = 65
+    assert hkg.hkg_gemm_bf16_run_plan(s, 1 << 30, 1 << 32, 1 << 33, 16, 4096, 4096) == hkg.HKG_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device status; a GPU is present")
+def test_no_device_status():
+    M, N, K = 64, 64, 64
+    A, B, C = 1 << 30, (1 << 30) + (1 << 20), (1 << 30) + (1 << 21)
+    assert hkg.hkg_gemm_bf16(A, B, C, M, N, K) == hkg.HKG_ERR_NO_DEVICE
+    p = hkg.plan(M, N, K)
+    assert hkg.hkg_gemm_bf16_run_plan(p, A, B, C, M, N, K) == hkg.HKG_ERR_NO_DEVICE
+
+
+def test_build_resources_have_no_scratch():
+    import json
+    path = os.path.join(hkg_build.BUILD, "kernel_resources.json")
+    if not os.path.exists(path):
+        hkg_build.build()
+    res = json.load(open(path))
+    entries = res["tile"] + res["skinny"] + [res["generic"]]
+    for e in entries:
+        assert e["scratch"] == 0 and e["vgpr_spill"] <= 0, e
+
+
+@pytest.mark.skipif(not os.path.exists(hkg_build.HIPCC), reason="hipcc not available")
+def test_build_gate_refuses_a_spilling_kernel():
+    src = r'''
+#include <hip/hip_runtime.h>
+__global__ __launch_bounds__(1024) void spills(const float* in, float* out, int n) {
+  float v[512];
+#pragma unroll
+  for (int i = 0; i < 512; ++i) v[i] = in[threadIdx.x * 512 + i] * (float)i;
+  float s = 0.f;
+  for (int r = 0; r < n; ++r)
+#pragma unroll
+    for (int i = 0; i < 512; ++i) s += v[(i * 7 + r) & 511] * v[i];
+  out[threadIdx.x] = s;
+}
+'''
+    tmp = tempfile.mkdtemp()
+    try:
+        f = os.path.join(tmp, "spill.hip")
+        open(f, "w").write(src)
+        p = subprocess.run([hkg_build.HIPCC, "-O3", "--offload-arch=gfx950", "-c", f, "-o",
+                            os.path.join(tmp, "spill.o"), "-Rpass-analysis=kernel-resource-usage"],
+                           stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        assert p.returncode == 0
+        res = hkg_build._parse_resources(p.stderr)
+        (name, r), = res.items()
+        e = hkg_build._entry(name, r)
+        assert e["scratch"] > 0
+        with pytest.raises(hkg_build.BuildError):
+            hkg_build._gate([e])
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Every case runs libhkg.so on an MI355X and compares element by element with
+the oracle on the same seeded inputs (tests/gates.py states the tolerance).
+Special inputs whose fp32 sums are exact (all-ones, identity, small
+integers) must match bit for bit.  The full-size workloads are compared on
+sampled rows spread over tiles and on random elements, plus properties of
+the whole output (finite, bit-identical on a repeat run).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import gates
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def hkg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tile_level_dense_amd as lib
+    lib.lib()
+    return lib
+
+
+def dev(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to("cuda")
+
+
+def host(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(hkg, A, B, **kw):
+    a, b = dev(A), dev(B)
+    c = hkg.gemm(a, b, **kw)
+    torch.cuda.synchronize()
+    return host(c)
+
+
+def full_check(C, A, B, exact=False):
+    Cr, S, absS = oracle.gemm(A, B)
+    if exact:
+        assert np.array_equal(C, Cr), "not bit-exact: %d of %d differ" % (int((C != Cr).sum()), C.size)
+        return None
+    return gates.compare(C, Cr, S, absS)
+
+
+def oracle_rows(A, B, rows):
+    """Oracle (C_ref, S, absS) for the listed rows of C."""
+    parts = [oracle.gemm(A, B, rows=(r, r + 1)) for r in rows]
+    return tuple(np.concatenate([p[t] for p in parts]) for t in range(3))
+
+
+def sample_rows(M, tile=256, extra=8, seed=0):
+    rows = {0, 1, M - 1, M // 2}
+    for t in range(0, M, tile):
+        rows.update({t, min(M - 1, t + tile - 1), min(M - 1, t + 17)})
+    rng = np.random.default_rng(seed)
+    rows.update(int(r) for r in rng.integers(0, M, size=extra))
+    return sorted(r for r in rows if 0 <= r < M)
+
+
+# ------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_workload_parity(hkg, name):
+    w = workloads.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    _say("workload", name, (M, N, K), "seed 0", "plan", hkg.plan(M, N, K).kernel_name.decode())
+    A, B = workloads.workload_inputs(name)
+    a, b = dev(A), dev(B)
+    c = hkg.gemm(a, b)
+    c2 = hkg.gemm(a, b)
+    torch.cuda.synchronize()
+    C = host(c)
+    assert np.array_equal(C, host(c2)), "repeat run differs"
+    assert torch.isfinite(c.float()).all().item()
+    if M * N * K <= 8 * 10**9:
+        stats = full_check(C, A, B)
+    else:
+        rows = sample_rows(M)
+        stats = gates.compare(C[rows], *oracle_rows(A, B, rows))
+        rng = np.random.default_rng(1)
+        ii = rng.integers(0, M, size=20000)
+        jj = rng.integers(0, N, size=20000)
+        Ce, Se, ae = oracle.gemm_entries(A, B, ii, jj)
+        gates.compare(C[ii, jj], Ce, Se, ae)
+    _say(name, stats)
+
+
+# -------------------------------------------------------- exact inputs
+EXACT_SHAPES = [(512, 512, 512), (300, 260, 136), (16, 1024, 4096), (128, 640, 1024), (5, 48, 8192)]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES)
+def test_all_ones_is_K(hkg, shape):
+    M, N, K = shape
+    _say("all-ones", shape)
+    A = np.full((M, K), 0x3F80, np.uint16)
+    B = np.full((N, K), 0x3F80, np.uint16)
+    C = run(hkg, A, B)
+    want = oracle.bf16_rne(float(K))
+    assert np.all(C == want)
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES)
+def test_small_integers_bit_exact(hkg, shape):
+    # |entries| <= 4 and K * 16 < 2^24: every fp32 partial sum is exact.
+    M, N, K = shape
+    _say("small-int", shape)
+    rng = np.random.default_rng(21)
+    A = workloads.f32_to_bf16_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float32))
+    B = workloads.f32_to_bf16_bits(rng.integers(-4, 5, size=(N, K)).astype(np.float32))
+    C = run(hkg, A, B)
+    full_check(C, A, B, exact=True)
+
+
+@pytest.mark.parametrize("side", ["A", "B"])
+def test_identity_bit_exact(hkg, side):
+    K = 384
+    _say("identity", side)
+    I = np.zeros((K, K), np.uint16)
+    I[np.arange(K), np.arange(K)] = 0x3F80
+    rng = np.random.default_rng(3)
+    X = workloads.draw(rng, (200, K), ("normal", 0.0, 1.0))
+    if side == "A":
+        C = run(hkg, I, X)          # C = X^T
+        assert np.array_equal(C, X.T)
+    else:
+        C = run(hkg, X, I)          # C = X
+        assert np.array_equal(C, X)
+
+
+def test_identity_skinny(hkg):
+    K = 1024
+    _say("identity skinny")
+    I = np.zeros((K, K), np.uint16)
+    I[np.arange(K), np.arange(K)] = 0x3F80
+    X = workloads.draw(np.random.default_rng(4), (40, K), ("uniform", -1.0, 1.0))
+    assert np.array_equal(run(hkg, X, I), X)
+
+
+# ------------------------------------------------------------ ragged
+RAGGED = [(1, 1, 8), (15, 17, 24), (17, 33, 40), (16, 4096, 64), (33, 100, 520), (127, 129, 136),
+          (128, 257, 72), (129, 127, 72), (255, 257, 264), (257, 255, 128), (300, 520, 200),
+          (513, 385, 1000), (1000, 36, 64), (64, 7, 4096), (7, 3000, 8),
+          (33, 47, 13), (130, 70, 99), (3, 5, 1), (200, 90, 1001)]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "%dx%dx%d" % s)
+def test_ragged_shapes(hkg, shape):
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    _say("ragged", shape, p.kernel_name.decode())
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=M * 7 + N)
+    full_check(run(hkg, A, B), A, B)
+
+
+# ---------------------------------------------------- forced plans
+def forced(hkg, A, B, edit):
+    M, K = A.shape
+    N = B.shape[0]
+    p = hkg.plan(M, N, K)
+    edit(p)
+    c = hkg.run_plan(p, dev(A), dev(B))
+    torch.cuda.synchronize()
+    return host(c)
+
+
+TILE_CASES = [(0, (300, 500, 136)), (1, (300, 500, 136)), (2, (300, 500, 136)),
+              (0, (256, 256, 64)), (1, (129, 1, 8)), (2, (700, 260, 520)), (0, (200, 1030, 72))]
+
+
+@pytest.mark.parametrize("variant,shape", TILE_CASES)
+def test_forced_tile_variants(hkg, variant, shape):
+    M, N, K = shape
+    _say("tile variant", variant, shape)
+    A, B = workloads.make_inputs(M, N, K, seed=variant + 10)
+    sizes = {0: (256, 256, 8), 1: (256, 128, 8), 2: (128, 128, 4)}[variant]
+
+    def edit(p):
+        p.kernel_id = hkg.HKG_KERNEL_TILE
+        p.variant = variant
+        p.tile_m, p.tile_n, p.waves = sizes
+        p.tile_k = 64
+        p.split_k = 1
+        p.workspace_bytes = 0
+    full_check(forced(hkg, A, B, edit), A, B)
+
+
+SKINNY_CASES = [(v, s, shape) for v, shape in [(0, (16, 512, 8192)), (1, (20, 300, 4096)),
+                                                 (2, (64, 1000, 2056)), (3, (128, 96, 8192)),
+                                                 (3, (100, 33, 1000))]
+                for s in (1, 3, 7)]
+
+
+@pytest.mark.parametrize("variant,split,shape", SKINNY_CASES)
+def test_forced_skinny_split(hkg, variant, split, shape):
+    M, N, K = shape
+    _say("skinny variant", variant, "split", split, shape)
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=split)
+
+    def edit(p):
+        p.kernel_id = hkg.HKG_KERNEL_SKINNY
+        p.variant = variant
+        p.split_k = split
+    C1 = forced(hkg, A, B, edit)
+    C2 = forced(hkg, A, B, edit)       # counters must be back at zero
+    assert np.array_equal(C1, C2)
+    full_check(C1, A, B)
+
+
+def test_forced_generic(hkg):
+    M, N, K = 150, 70, 264
+    _say("generic forced", (M, N, K))
+    A, B = workloads.make_inputs(M, N, K, seed=5)
+
+    def edit(p):
+        p.kernel_id = hkg.HKG_KERNEL_GENERIC
+    full_check(forced(hkg, A, B, edit), A, B)
+
+
+@pytest.mark.parametrize("w,c", [(0, 0), (1, 0), (3, 2), (8, 4), (5, 1), (9, 0), (8, 32), (2, 1)])
+def test_tile_orders(hkg, w, c):
+    M = N = 2304          # 9 x 9 tiles of 256: ragged against 8 XCDs and windows
+    K = 128
+    _say("tile order", w, c)
+    A, B = workloads.make_inputs(M, N, K, seed=w * 10 + c)
+
+    def edit(p):
+        p.kernel_id = hkg.HKG_KERNEL_TILE
+        p.variant = 0
+        p.tile_m = p.tile_n = 256
+        p.waves = 8
+        p.xcd_window_w = w
+        p.xcd_chunk_c = c
+    C = forced(hkg, A, B, edit)
+    rows = sample_rows(M, extra=16)
+    gates.compare(C[rows], *oracle_rows(A, B, rows))
+    # every tile written: compare a column sample over all rows
+    cols = np.arange(0, N, 97)
+    ii, jj = np.meshgrid(np.arange(M), cols, indexing="ij")
+    Ce, Se, ae = oracle.gemm_entries(A, B, ii.ravel(), jj.ravel())
+    gates.compare(C[ii.ravel(), jj.ravel()], Ce, Se, ae)
+
+
+# ----------------------------------------------------- edge handling
+def test_misaligned_pointers_take_generic(hkg):
+    M, N, K = 64, 48, 200
+    _say("misaligned", (M, N, K))
+    A, B = workloads.make_inputs(M, N, K, seed=6)
+    a_buf = torch.zeros(M * K + 1, dtype=torch.bfloat16, device="cuda")
+    b_buf = torch.zeros(N * K + 1, dtype=torch.bfloat16, device="cuda")
+    c_buf = torch.zeros(M * N + 1, dtype=torch.bfloat16, device="cuda")
+    a_buf[1:] = dev(A).reshape(-1)
+    b_buf[1:] = dev(B).reshape(-1)
+    st = hkg.hkg_gemm_bf16(a_buf.data_ptr() + 2, b_buf.data_ptr() + 2, c_buf.data_ptr() + 2, M, N, K,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == hkg.HKG_OK
+    torch.cuda.synchronize()
+    full_check(host(c_buf[1:]).reshape(M, N), A, B)
+    p = hkg.plan(M, N, K)
+    st = hkg.hkg_gemm_bf16_run_plan(p, a_buf.data_ptr() + 2, b_buf.data_ptr() + 2, c_buf.data_ptr() + 2,
+                                    M, N, K, None)
+    assert st == hkg.HKG_ERR_MISALIGNED
+
+
+def test_k_zero_fills_zero(hkg):
+    _say("K = 0")
+    a = torch.empty((37, 0), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((29, 0), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((37, 29), 3.0, dtype=torch.bfloat16, device="cuda")
+    hkg.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 0)
+
+
+def test_empty_output_is_noop(hkg):
+    _say("M = 0")
+    a = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.ones((8, 64), dtype=torch.bfloat16, device="cuda")
+    assert hkg.gemm(a, b).shape == (0, 8)
+
+
+def test_device_status_ok(hkg):
+    p = hkg.plan(256, 256, 256)
+    a = torch.zeros((256, 256), dtype=torch.bfloat16, device="cuda")
+    out = hkg.run_plan(p, a, a)
+    torch.cuda.synchronize()
+    assert out.shape == (256, 256)

@@ -1,0 +1,477 @@
+// C ABI of the dense BF16 GEMM library: argument checks, the shape-based
+// plan (kernel + tile + split + launch geometry), per-device state and
+// dispatch to the kernel launchers.  Declared in include/hkg.h.
+#include "hkg.h"
+#include "hkg_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+namespace hkg {
+namespace {
+
+// MI355X: 256 compute units in 8 XCDs of 32 (HipKittens talk notes, section
+// "compute hierarchy").  The plan is a pure function of (M, N, K) on this
+// device; a device that reports a different count still runs every plan
+// correctly.
+constexpr int kNumCUs = 256;
+
+// Skinny path for M up to this many rows (decode shapes).
+constexpr int64_t kSkinnyMaxM = 128;
+
+// Largest dimension the kernels index with 32-bit arithmetic.
+constexpr int64_t kMaxDim = INT32_MAX;
+
+thread_local std::string g_last_hip_error;
+
+void set_hip_error(hipError_t e, const char* where)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+    g_last_hip_error = buf;
+}
+
+void copy_str(char* dst, size_t cap, const char* src)
+{
+    std::snprintf(dst, cap, "%s", src);
+}
+
+// ---------------------------------------------------------------- per device
+struct DeviceState {
+    std::once_flag once;
+    hkg_status_t status = HKG_ERR_NO_DEVICE;
+    std::mutex ws_mutex;
+    float* ws = nullptr;          // split-K partials
+    size_t ws_bytes = 0;
+    int* counters = nullptr;      // split-K arrival counters (kept zero between calls)
+    size_t counter_count = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceState g_devices[kMaxDevices];
+
+hkg_status_t current_device(int* dev_out)
+{
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) {
+        if (e != hipSuccess)
+            set_hip_error(e, "hipGetDeviceCount");
+        return HKG_ERR_NO_DEVICE;
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_hip_error(e, "hipGetDevice");
+        return HKG_ERR_NO_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return HKG_ERR_UNSUPPORTED;
+    DeviceState& d = g_devices[dev];
+    std::call_once(d.once, [&]() {
+        hipDeviceProp_t prop;
+        hipError_t pe = hipGetDeviceProperties(&prop, dev);
+        if (pe != hipSuccess) {
+            set_hip_error(pe, "hipGetDeviceProperties");
+            d.status = HKG_ERR_HIP;
+            return;
+        }
+        d.status = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? HKG_OK : HKG_ERR_ARCH;
+    });
+    *dev_out = dev;
+    return d.status;
+}
+
+// Split-K scratch for `dev`: grown on demand, never shrunk, freed at exit.
+hkg_status_t get_workspace(int dev, size_t ws_bytes, size_t counters, float** ws, int** cnt)
+{
+    DeviceState& d = g_devices[dev];
+    std::lock_guard<std::mutex> lock(d.ws_mutex);
+    if (d.ws_bytes < ws_bytes) {
+        if (d.ws)
+            (void)hipFree(d.ws);
+        d.ws = nullptr;
+        d.ws_bytes = 0;
+        hipError_t e = hipMalloc((void**)&d.ws, ws_bytes);
+        if (e != hipSuccess) {
+            set_hip_error(e, "hipMalloc(split-K workspace)");
+            d.ws = nullptr;
+            return HKG_ERR_WORKSPACE;
+        }
+        d.ws_bytes = ws_bytes;
+    }
+    if (d.counter_count < counters) {
+        if (d.counters)
+            (void)hipFree(d.counters);
+        d.counters = nullptr;
+        d.counter_count = 0;
+        hipError_t e = hipMalloc((void**)&d.counters, counters * sizeof(int));
+        if (e == hipSuccess)
+            e = hipMemset(d.counters, 0, counters * sizeof(int));
+        if (e != hipSuccess) {
+            set_hip_error(e, "hipMalloc(split-K counters)");
+            return HKG_ERR_WORKSPACE;
+        }
+        d.counter_count = counters;
+    }
+    *ws = d.ws;
+    *cnt = d.counters;
+    return HKG_OK;
+}
+
+// --------------------------------------------------------------------- plan
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void fill_resources(hkg_plan_t* p, const KernelResources* r)
+{
+    if (!r)
+        return;
+    p->vgprs = r->vgprs;
+    p->agprs = r->agprs;
+    p->sgprs = r->sgprs;
+    p->scratch_bytes = r->scratch;
+}
+
+hkg_status_t check_dims(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return HKG_ERR_INVALID_ARG;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return HKG_ERR_INVALID_ARG;
+    // Each of A, B and C holds fewer than 2^40 elements (2 TiB of bf16).
+    const int64_t lim = (int64_t)1 << 40;
+    if ((M && K >= lim / M) || (N && K >= lim / N) || (M && N >= lim / M))
+        return HKG_ERR_INVALID_ARG;
+    return HKG_OK;
+}
+
+void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
+{
+    // Largest tile that still gives every compute unit a workgroup; the
+    // smallest rung otherwise (FlyDSL "Prebuilt kernels guide", section 3c,
+    // tile selection; 256 x 256 first: HipKittens talk notes, Table 2).
+    static const int ladder[] = {TILE_256x256, TILE_256x128, TILE_128x128};
+    int variant = TILE_128x128;
+    for (int v : ladder) {
+        const TileShape s = tile_shape(v);
+        if (cdiv(M, s.bm) * cdiv(N, s.bn) >= kNumCUs) {
+            variant = v;
+            break;
+        }
+    }
+    const TileShape s = tile_shape(variant);
+    const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
+    p->kernel_id = HKG_KERNEL_TILE;
+    p->variant = variant;
+    p->tile_m = s.bm;
+    p->tile_n = s.bn;
+    p->tile_k = s.bk;
+    p->waves = s.waves;
+    p->split_k = 1;
+    p->grid_x = (int32_t)(tm * tn);
+    p->grid_y = 1;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    // Chiplet-aware order (talk notes, section 3): 8-tall windows, so one
+    // XCD's 32 concurrent workgroups cover an 8 x 4 block of tiles, and 32
+    // consecutive tiles per XCD; off when the grid is under one XCD round.
+    p->xcd_window_w = tm >= 8 ? 8 : (int32_t)tm;
+    p->xcd_chunk_c = (tm * tn >= 8 * 32) ? 32 : 0;
+    p->lds_bytes = tile_lds_bytes(variant);
+    fill_resources(p, tile_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "tile_%dx%dx%d", s.bm, s.bn, s.bk);
+    std::snprintf(p->reason, sizeof p->reason, "M > %d; %lldx%lld tiles of %dx%d (largest rung filling %d CUs)",
+                  (int)kSkinnyMaxM, (long long)tm, (long long)tn, s.bm, s.bn, kNumCUs);
+}
+
+void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
+{
+    int variant = M <= 16 ? SKINNY_M16 : M <= 32 ? SKINNY_M32 : M <= 64 ? SKINNY_M64 : SKINNY_M128;
+    const SkinnyShape s = skinny_shape(variant);
+    const int64_t col_blocks = cdiv(N, 16);
+    const int64_t steps = cdiv(K, 32);
+    // Split K across workgroups only when the column blocks underfill the
+    // device, keeping at least 8 steps (256 k) per wave.
+    int64_t split = 1;
+    if (col_blocks < kNumCUs) {
+        split = cdiv(kNumCUs, col_blocks);
+        const int64_t max_split = steps / (8 * s.waves);
+        if (split > max_split)
+            split = max_split;
+        if (split > 64)
+            split = 64;
+        if (split < 1)
+            split = 1;
+    }
+    p->kernel_id = HKG_KERNEL_SKINNY;
+    p->variant = variant;
+    p->tile_m = 16 * s.mblocks;
+    p->tile_n = 16;
+    p->tile_k = 32;
+    p->waves = s.waves;
+    p->split_k = (int32_t)split;
+    p->grid_x = (int32_t)col_blocks;
+    p->grid_y = (int32_t)split;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    p->lds_bytes = skinny_lds_bytes(variant);
+    fill_resources(p, skinny_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d", 16 * s.mblocks);
+    std::snprintf(p->reason, sizeof p->reason, "M <= %d; %lld column blocks of 16, split-K %lld",
+                  (int)kSkinnyMaxM, (long long)col_blocks, (long long)split);
+}
+
+void plan_generic(int64_t M, int64_t N, hkg_plan_t* p, const char* why)
+{
+    p->kernel_id = HKG_KERNEL_GENERIC;
+    p->variant = 0;
+    p->tile_m = 16;
+    p->tile_n = 16;
+    p->tile_k = 1;
+    p->waves = 4;
+    p->split_k = 1;
+    p->grid_x = (int32_t)cdiv(N, 16);
+    p->grid_y = (int32_t)std::min<int64_t>(cdiv(M, 16), 65535);
+    p->grid_z = 1;
+    p->block_x = 256;
+    p->xcd_window_w = 0;
+    p->xcd_chunk_c = 0;
+    p->workspace_bytes = 0;
+    p->lds_bytes = 0;
+    fill_resources(p, generic_resources());
+    copy_str(p->kernel_name, sizeof p->kernel_name, "generic");
+    copy_str(p->reason, sizeof p->reason, why);
+}
+
+hkg_status_t make_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
+{
+    std::memset(p, 0, sizeof *p);
+    p->abi_version = HKG_ABI_VERSION;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->split_k = 1;
+    p->vgprs = p->agprs = p->sgprs = p->scratch_bytes = -1;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    p->flops = 2.0 * (double)M * (double)N * (double)K;
+    p->algorithmic_bytes = 2.0 * ((double)M * K + (double)N * K + (double)M * N);
+    if (M == 0 || N == 0) {
+        p->kernel_id = HKG_KERNEL_NONE;
+        copy_str(p->kernel_name, sizeof p->kernel_name, "none");
+        copy_str(p->reason, sizeof p->reason, "empty output");
+        return HKG_OK;
+    }
+    if (K == 0) {
+        p->kernel_id = HKG_KERNEL_ZERO;
+        p->grid_x = 1;
+        p->block_x = 256;
+        copy_str(p->kernel_name, sizeof p->kernel_name, "zero");
+        copy_str(p->reason, sizeof p->reason, "K == 0: C is the empty sum, +0");
+        return HKG_OK;
+    }
+    if (K % 8 != 0) {
+        plan_generic(M, N, p, "K % 8 != 0: fast kernels load 8 k values per 16-byte access");
+        return HKG_OK;
+    }
+    // Buffer-resource ranges of one tile / of A must stay below 2^31 bytes.
+    if (K > (int64_t)(INT32_MAX / 2) / 256) {
+        plan_generic(M, N, p, "K too large for 32-bit buffer offsets of a tile");
+        return HKG_OK;
+    }
+    if (M <= kSkinnyMaxM) {
+        plan_skinny(M, N, K, p);
+        return HKG_OK;
+    }
+    plan_tile(M, N, K, p);
+    const int64_t grid = (int64_t)cdiv(M, p->tile_m) * cdiv(N, p->tile_n);
+    if (grid > INT32_MAX)
+        plan_generic(M, N, p, "tile grid beyond 2^31 workgroups");
+    return HKG_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a_bytes > 0 && b_bytes > 0 && a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+hkg_status_t check_pointers(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t a_bytes = 2 * M * K, b_bytes = 2 * N * K, c_bytes = 2 * M * N;
+    if ((a_bytes && !A) || (b_bytes && !B) || (c_bytes && !C))
+        return HKG_ERR_INVALID_ARG;
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
+        return HKG_ERR_INVALID_ARG;
+    return HKG_OK;
+}
+
+bool plan_matches_library(const hkg_plan_t* p)
+{
+    switch (p->kernel_id) {
+    case HKG_KERNEL_NONE:
+        return p->M == 0 || p->N == 0;
+    case HKG_KERNEL_ZERO:
+        return p->K == 0 && p->M > 0 && p->N > 0;
+    case HKG_KERNEL_GENERIC:
+        return true;
+    case HKG_KERNEL_TILE: {
+        if (p->variant < 0 || p->variant >= TILE_NUM_VARIANTS)
+            return false;
+        const TileShape s = tile_shape(p->variant);
+        return p->tile_m == s.bm && p->tile_n == s.bn && p->split_k == 1 && p->xcd_window_w >= 0 &&
+               p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
+               cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
+    }
+    case HKG_KERNEL_SKINNY: {
+        if (p->variant < 0 || p->variant >= SKINNY_NUM_VARIANTS)
+            return false;
+        const SkinnyShape s = skinny_shape(p->variant);
+        return p->M <= 16 * s.mblocks && p->split_k >= 1 && p->split_k <= 64 && p->K > 0 &&
+               p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256;
+    }
+    default:
+        return false;
+    }
+}
+
+hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hipStream_t stream)
+{
+    const int64_t M = p->M, N = p->N, K = p->K;
+    if (p->kernel_id == HKG_KERNEL_NONE)
+        return HKG_OK;
+    int dev = 0;
+    hkg_status_t st = current_device(&dev);
+    if (st != HKG_OK)
+        return st;
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* b = (const uint16_t*)B;
+    uint16_t* c = (uint16_t*)C;
+    hipError_t e = hipSuccess;
+    switch (p->kernel_id) {
+    case HKG_KERNEL_ZERO:
+        e = launch_zero(c, M * N, stream);
+        break;
+    case HKG_KERNEL_GENERIC:
+        e = launch_generic(a, b, c, M, N, K, stream);
+        break;
+    case HKG_KERNEL_TILE:
+        e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c, stream);
+        break;
+    case HKG_KERNEL_SKINNY: {
+        float* ws = nullptr;
+        int* counters = nullptr;
+        if (p->split_k > 1) {
+            st = get_workspace(dev, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+                               (size_t)cdiv(N, 16), &ws, &counters);
+            if (st != HKG_OK)
+                return st;
+        }
+        e = launch_skinny(p->variant, a, b, c, (int)M, (int)N, (int)K, p->split_k, ws, counters, stream);
+        break;
+    }
+    default:
+        return HKG_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) {
+        set_hip_error(e, "kernel launch");
+        return HKG_ERR_HIP;
+    }
+    return HKG_OK;
+}
+
+struct Cleanup {
+    ~Cleanup()
+    {
+        for (auto& d : g_devices) {
+            if (d.ws)
+                (void)hipFree(d.ws);
+            if (d.counters)
+                (void)hipFree(d.counters);
+            d.ws = nullptr;
+            d.counters = nullptr;
+        }
+    }
+} g_cleanup;
+
+}  // namespace
+}  // namespace hkg
+
+using namespace hkg;
+
+extern "C" {
+
+hkg_status_t hkg_gemm_bf16_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out)
+{
+    if (!out)
+        return HKG_ERR_INVALID_ARG;
+    return make_plan(M, N, K, out);
+}
+
+hkg_status_t hkg_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                           void* stream)
+{
+    hkg_plan_t p;
+    hkg_status_t st = make_plan(M, N, K, &p);
+    if (st != HKG_OK)
+        return st;
+    st = check_pointers(A, B, C, M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if ((p.kernel_id == HKG_KERNEL_TILE || p.kernel_id == HKG_KERNEL_SKINNY) &&
+        !(aligned16(A) && aligned16(B) && aligned16(C)))
+        plan_generic(M, N, &p, "pointers not 16-byte aligned");
+    return run(&p, A, B, C, (hipStream_t)stream);
+}
+
+hkg_status_t hkg_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B, void* C,
+                                    int64_t M, int64_t N, int64_t K, void* stream)
+{
+    if (!plan || plan->abi_version != HKG_ABI_VERSION)
+        return HKG_ERR_INVALID_ARG;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (plan->M != M || plan->N != N || plan->K != K)
+        return HKG_ERR_INVALID_ARG;
+    st = check_pointers(A, B, C, M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (!plan_matches_library(plan))
+        return HKG_ERR_UNSUPPORTED;
+    if ((plan->kernel_id == HKG_KERNEL_TILE || plan->kernel_id == HKG_KERNEL_SKINNY) &&
+        !(aligned16(A) && aligned16(B) && aligned16(C)))
+        return HKG_ERR_MISALIGNED;
+    return run(plan, A, B, C, (hipStream_t)stream);
+}
+
+const char* hkg_status_string(hkg_status_t s)
+{
+    switch (s) {
+    case HKG_OK: return "ok";
+    case HKG_ERR_INVALID_ARG: return "invalid argument";
+    case HKG_ERR_MISALIGNED: return "pointer or K alignment does not fit the plan's kernel";
+    case HKG_ERR_UNSUPPORTED: return "plan not supported by this library";
+    case HKG_ERR_NO_DEVICE: return "no HIP device";
+    case HKG_ERR_ARCH: return "device is not gfx950 (MI355X)";
+    case HKG_ERR_HIP: return "HIP runtime error";
+    case HKG_ERR_WORKSPACE: return "split-K workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+const char* hkg_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int32_t hkg_abi_version(void) { return HKG_ABI_VERSION; }
+
+}  // extern "C"
