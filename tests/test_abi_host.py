@@ -246,3 +246,43 @@ __global__ __launch_bounds__(1024) void spills(const float* in, float* out, int 
             hkg_build._gate([e])
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def _tile_order_fn(lib):
+    f = lib.hkg_internal_tile_order
+    f.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(ctypes.c_int32)] * 2
+    f.restype = ctypes.c_int32
+    return f
+
+
+def test_tile_order_is_a_bijection(lib):
+    """The kernel's workgroup -> tile order (same inline function, host build)
+    must visit every tile exactly once for any grid and (W, C)."""
+    f = _tile_order_fn(lib)
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    grids = [(tm_, tn_) for tm_ in range(1, 20) for tn_ in range(1, 20)] + [(32, 32), (16, 16), (57, 57), (9, 9)]
+    for gm, gn in grids:
+        for w in (0, 1, 2, 3, 5, 8, 16):
+            for c in (0, 1, 2, 4, 7, 32):
+                seen = set()
+                for b in range(gm * gn):
+                    assert f(b, gm, gn, w, c, ctypes.byref(tm), ctypes.byref(tn)) == 0
+                    assert 0 <= tm.value < gm and 0 <= tn.value < gn
+                    seen.add((tm.value, tn.value))
+                assert len(seen) == gm * gn, (gm, gn, w, c)
+
+
+def test_tile_order_chiplet_blocks(lib):
+    """At 32 x 32 tiles with W = 8, C = 32 the 32 workgroups that one XCD
+    receives first (ids x, x + 8, ..., x + 248) cover an 8 x 4 block of tiles."""
+    f = _tile_order_fn(lib)
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    for xcd in range(8):
+        tiles = set()
+        for r in range(32):
+            f(xcd + 8 * r, 32, 32, 8, 32, ctypes.byref(tm), ctypes.byref(tn))
+            tiles.add((tm.value, tn.value))
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        assert len(tiles) == 32 and len(rows) == 8 and len(cols) == 4
+        assert cols == set(range(4 * xcd, 4 * xcd + 4))

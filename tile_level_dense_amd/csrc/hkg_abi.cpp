@@ -3,6 +3,7 @@
 // dispatch to the kernel launchers.  Declared in include/hkg.h.
 #include "hkg.h"
 #include "hkg_internal.h"
+#include "hkg_tile_order.h"
 
 #include <hip/hip_runtime.h>
 
@@ -473,5 +474,20 @@ const char* hkg_status_string(hkg_status_t s)
 const char* hkg_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
 int32_t hkg_abi_version(void) { return HKG_ABI_VERSION; }
+
+// Test hook, not part of include/hkg.h: the tile kernel's workgroup -> tile
+// order evaluated on the host (the same inline function the kernel uses).
+int32_t hkg_internal_tile_order(int32_t b, int32_t tiles_m, int32_t tiles_n, int32_t win_w,
+                                int32_t chunk_c, int32_t* tm, int32_t* tn)
+{
+    if (!tm || !tn || tiles_m <= 0 || tiles_n <= 0 || b < 0 || b >= tiles_m * tiles_n || win_w < 0 ||
+        chunk_c < 0)
+        return HKG_ERR_INVALID_ARG;
+    int m = 0, n = 0;
+    tile_order(b, tiles_m, tiles_n, win_w, chunk_c, m, n);
+    *tm = m;
+    *tn = n;
+    return HKG_OK;
+}
 
 }  // extern "C"

@@ -29,6 +29,7 @@
 //  * Ragged M, N and K: rows past the matrix and k past K fall outside the
 //    buffer resource's range and read as zero; stores are masked.
 #include "hkg_internal.h"
+#include "hkg_tile_order.h"
 
 namespace hkg {
 namespace {
@@ -57,38 +58,6 @@ __device__ __forceinline__ uint16_t bf16_elem(uint2 w, int r)
 {
     const uint32_t word = (r >> 1) ? w.y : w.x;
     return (uint16_t)(word >> ((r & 1) * 16));
-}
-
-// Chiplet-aware tile order (talk notes, section 3, Algorithm 1).
-// Step 1: workgroups are dispatched to the 8 XCDs round-robin; renumber them
-// so that C consecutive logical ids run on one XCD.  Step 2: walk the tile
-// grid column-first inside windows W tile rows tall.
-__device__ __forceinline__ void tile_order(int b, int tiles_m, int tiles_n, int win_w, int chunk_c,
-                                           int& tm, int& tn)
-{
-    const int total = tiles_m * tiles_n;
-    int L = b;
-    if (chunk_c > 0) {
-        const int group = 8 * chunk_c;
-        const int full = (total / group) * group;
-        if (b < full) {
-            const int xcd = b & 7;
-            const int r = b >> 3;
-            L = ((r / chunk_c) * 8 + xcd) * chunk_c + (r % chunk_c);
-        }
-    }
-    if (win_w > 0) {
-        const int span = win_w * tiles_n;
-        const int g = L / span;
-        const int row0 = g * win_w;
-        const int h = min(win_w, tiles_m - row0);
-        const int within = L - g * span;
-        tm = row0 + within % h;
-        tn = within / h;
-    } else {
-        tm = L / tiles_n;
-        tn = L - tm * tiles_n;
-    }
 }
 
 template <int BM, int BN, int WM, int WN>
