@@ -185,6 +185,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
+    ap.add_argument("--only", choices=["square", "decode"], help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -198,7 +199,15 @@ def main():
     hkg.lib()
 
     calibration_copy(torch)
+    if args.only == "decode":
+        dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+        print(json.dumps({"decode_gbps": round(dec["gbps"], 1), "us_per_call": round(dec["ms"] * 1e3, 3),
+                          "llc_resident_gbps": round(dec["gbps_hot"], 1)}), flush=True)
+        return 0
     sq = bench_square(torch, hkg, args.steps, args.warmup)
+    if args.only == "square":
+        print(json.dumps({"square_tflops": round(sq["tflops"], 2), "ms_per_step": round(sq["ms"], 4)}), flush=True)
+        return 0
     dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 

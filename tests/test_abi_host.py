@@ -91,11 +91,11 @@ def test_status_strings(lib):
 
 
 WORKLOAD_PLANS = {
-    (256, 256, 256): ("TILE", "tile_128x128x64"),
+    (256, 256, 256): ("TILE", "tile_128x128x64_"),
     (16, 4096, 4096): ("SKINNY", "skinny_m16"),
     (128, 12288, 4096): ("SKINNY", "skinny_m128"),
-    (4096, 4096, 12288): ("TILE", "tile_256x256x64"),
-    (8192, 8192, 8192): ("TILE", "tile_256x256x64"),
+    (4096, 4096, 12288): ("TILE", "tile_256x256x64_"),
+    (8192, 8192, 8192): ("TILE", "tile_256x256x64_"),
 }
 
 
@@ -105,7 +105,7 @@ def test_plan_for_workloads(shape):
     p = hkg.plan(M, N, K)
     kind, name = WORKLOAD_PLANS[shape]
     assert hkg.KERNEL_NAMES[p.kernel_id] == kind
-    assert p.kernel_name.decode() == name
+    assert p.kernel_name.decode().startswith(name)
     assert p.flops == 2.0 * M * N * K
     assert p.algorithmic_bytes == 2.0 * (M * K + N * K + M * N)
     assert p.scratch_bytes == 0 and p.vgprs > 0
@@ -141,8 +141,11 @@ def test_plan_boundaries():
     p = hkg.plan(16, 256, 8192)
     assert p.split_k > 1 and p.workspace_bytes == p.split_k * 16 * 256 * 4
     # tile ladder: a grid that would underfill at 256x256 steps down
-    assert hkg.plan(2048, 2048, 1024).kernel_name.decode() == "tile_128x128x64"
-    assert hkg.plan(4096, 2048, 1024).kernel_name.decode() == "tile_256x128x64"
+    for shape in [(2048, 2048, 1024), (4096, 2048, 1024), (1024, 8192, 4096)]:
+        p = hkg.plan(*shape)
+        assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE"
+        assert p.grid_x >= 256 or p.tile_m * p.tile_n == 128 * 128, p
+        assert (p.tile_m, p.tile_n) != (256, 256), p
 
 
 @pytest.mark.parametrize("shape", [(-1, 4, 8), (4, -1, 8), (4, 4, -8), (2**31, 4, 8), (4, 4, 2**31),

@@ -177,31 +177,48 @@ def forced(hkg, A, B, edit):
     return host(c)
 
 
-TILE_CASES = [(0, (300, 500, 136)), (1, (300, 500, 136)), (2, (300, 500, 136)),
-              (0, (256, 256, 64)), (1, (129, 1, 8)), (2, (700, 260, 520)), (0, (200, 1030, 72))]
+def force_tile(hkg, p, variant, win_w=None, chunk_c=None):
+    """Edit plan p to run tile-kernel variant `variant` (hkg_tile_configs.h)."""
+    from tile_level_dense_amd import build as hkg_build
+    bm, bn, bk, stages, wm, wn, _ = hkg_build.tile_configs()[variant]
+    p.kernel_id = hkg.HKG_KERNEL_TILE
+    p.variant = variant
+    p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn
+    p.split_k = 1
+    p.workspace_bytes = 0
+    if win_w is not None:
+        p.xcd_window_w = win_w
+    if chunk_c is not None:
+        p.xcd_chunk_c = chunk_c
 
 
-@pytest.mark.parametrize("variant,shape", TILE_CASES)
+def _n_tile_variants():
+    from tile_level_dense_amd import build as hkg_build
+    return len(hkg_build.tile_configs())
+
+
+TILE_SHAPES = [(300, 500, 136), (256, 256, 64), (129, 1, 8), (700, 260, 520), (200, 1030, 72),
+               (520, 1000, 392)]
+
+
+@pytest.mark.parametrize("variant", range(_n_tile_variants()))
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "%dx%dx%d" % s)
 def test_forced_tile_variants(hkg, variant, shape):
     M, N, K = shape
     _say("tile variant", variant, shape)
     A, B = workloads.make_inputs(M, N, K, seed=variant + 10)
-    sizes = {0: (256, 256, 8), 1: (256, 128, 8), 2: (128, 128, 4)}[variant]
-
-    def edit(p):
-        p.kernel_id = hkg.HKG_KERNEL_TILE
-        p.variant = variant
-        p.tile_m, p.tile_n, p.waves = sizes
-        p.tile_k = 64
-        p.split_k = 1
-        p.workspace_bytes = 0
-    full_check(forced(hkg, A, B, edit), A, B)
+    full_check(forced(hkg, A, B, lambda p: force_tile(hkg, p, variant)), A, B)
 
 
-SKINNY_CASES = [(v, s, shape) for v, shape in [(0, (16, 512, 8192)), (1, (20, 300, 4096)),
-                                                 (2, (64, 1000, 2056)), (3, (128, 96, 8192)),
-                                                 (3, (100, 33, 1000))]
-                for s in (1, 3, 7)]
+def _skinny_configs():
+    from tile_level_dense_amd import build as hkg_build
+    return hkg_build.skinny_configs()
+
+
+SKINNY_SHAPES = [(16, 512, 8192), (20, 300, 4096), (64, 1000, 2056), (128, 96, 8192), (100, 33, 1000),
+                 (1, 4100, 1024), (9, 64, 264)]
+SKINNY_CASES = [(v, s, shape) for v, cfg in enumerate(_skinny_configs()) for shape in SKINNY_SHAPES
+                if shape[0] <= 16 * cfg[0] for s in (1, 3, 7)]
 
 
 @pytest.mark.parametrize("variant,split,shape", SKINNY_CASES)
@@ -238,12 +255,7 @@ def test_tile_orders(hkg, w, c):
     A, B = workloads.make_inputs(M, N, K, seed=w * 10 + c)
 
     def edit(p):
-        p.kernel_id = hkg.HKG_KERNEL_TILE
-        p.variant = 0
-        p.tile_m = p.tile_n = 256
-        p.waves = 8
-        p.xcd_window_w = w
-        p.xcd_chunk_c = c
+        force_tile(hkg, p, 0, win_w=w, chunk_c=c)
     C = forced(hkg, A, B, edit)
     rows = sample_rows(M, extra=16)
     gates.compare(C[rows], *oracle_rows(A, B, rows))

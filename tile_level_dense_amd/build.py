@@ -28,10 +28,26 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Wall", "-Wno-unused-function",
           "-I" + INCLUDE, "-I" + CSRC, "-I" + BUILD]
 
-# tile_kernel<BM, BN, WM, WN> -> variant index (order of hkg::TileVariant)
-TILE_VARIANTS = [(256, 256), (256, 128), (128, 128)]
-# skinny_kernel<MB, WK, U> -> variant index by MB
-SKINNY_VARIANTS = [1, 2, 4, 8]
+
+
+def tile_configs():
+    """(BM, BN, BK, STAGES, WM, WN, SCHED) per tile variant, from hkg_tile_configs.h."""
+    text = open(os.path.join(CSRC, "hkg_tile_configs.h")).read()
+    body = text[text.index("#define HKG_TILE_CONFIGS(X)"):]
+    return [tuple(int(v) for v in m) for m in re.findall(
+        r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", body)]
+
+
+TILE_VARIANTS = tile_configs()
+def skinny_configs():
+    """(MB, WK, U, CP, AL) per skinny variant, from hkg_skinny_configs.h."""
+    text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
+    body = text[text.index("#define HKG_SKINNY_CONFIGS(X)"):]
+    return [tuple(int(v) for v in m) for m in re.findall(
+        r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", body)]
+
+
+SKINNY_VARIANTS = skinny_configs()
 
 
 class BuildError(RuntimeError):
@@ -87,17 +103,17 @@ def _table(resources):
     skinny = [None] * len(SKINNY_VARIANTS)
     generic = None
     for mangled, r in resources.items():
-        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", mangled)
+        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", mangled)
         if m:
-            key = (int(m.group(1)), int(m.group(2)))
+            key = tuple(int(g) for g in m.groups())
             if key in TILE_VARIANTS:
-                tile[TILE_VARIANTS.index(key)] = _entry("tile_%dx%dx64" % key, r)
+                tile[TILE_VARIANTS.index(key)] = _entry("tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
-        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)E", mangled)
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", mangled)
         if m:
-            mb = int(m.group(1))
-            if mb in SKINNY_VARIANTS:
-                skinny[SKINNY_VARIANTS.index(mb)] = _entry("skinny_m%d" % (16 * mb), r)
+            key = tuple(int(g) for g in m.groups())
+            if key in SKINNY_VARIANTS:
+                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_w%d_u%d_c%d_a%d" % ((16 * key[0],) + key[1:]), r)
             continue
         if "generic_kernel" in mangled:
             generic = _entry("generic", r)

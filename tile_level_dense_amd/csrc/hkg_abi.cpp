@@ -157,9 +157,8 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     // Largest tile that still gives every compute unit a workgroup; the
     // smallest rung otherwise (FlyDSL "Prebuilt kernels guide", section 3c,
     // tile selection; 256 x 256 first: HipKittens talk notes, Table 2).
-    static const int ladder[] = {TILE_256x256, TILE_256x128, TILE_128x128};
-    int variant = TILE_128x128;
-    for (int v : ladder) {
+    int variant = TILE_LADDER[sizeof(TILE_LADDER) / sizeof(TILE_LADDER[0]) - 1];
+    for (int v : TILE_LADDER) {
         const TileShape s = tile_shape(v);
         if (cdiv(M, s.bm) * cdiv(N, s.bn) >= kNumCUs) {
             variant = v;
@@ -186,14 +185,15 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     p->xcd_chunk_c = (tm * tn >= 8 * 32) ? 32 : 0;
     p->lds_bytes = tile_lds_bytes(variant);
     fill_resources(p, tile_resources(variant));
-    std::snprintf(p->kernel_name, sizeof p->kernel_name, "tile_%dx%dx%d", s.bm, s.bn, s.bk);
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "tile_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
+                  s.stages, s.wm, s.wn, s.sched);
     std::snprintf(p->reason, sizeof p->reason, "M > %d; %lldx%lld tiles of %dx%d (largest rung filling %d CUs)",
                   (int)kSkinnyMaxM, (long long)tm, (long long)tn, s.bm, s.bn, kNumCUs);
 }
 
 void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
-    int variant = M <= 16 ? SKINNY_M16 : M <= 32 ? SKINNY_M32 : M <= 64 ? SKINNY_M64 : SKINNY_M128;
+    const int variant = skinny_default_variant(M);
     const SkinnyShape s = skinny_shape(variant);
     const int64_t col_blocks = cdiv(N, 16);
     const int64_t steps = cdiv(K, 32);
@@ -224,7 +224,8 @@ void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
     p->lds_bytes = skinny_lds_bytes(variant);
     fill_resources(p, skinny_resources(variant));
-    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d", 16 * s.mblocks);
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d_w%d_u%d_c%d_a%d", 16 * s.mblocks, s.waves,
+                  s.unroll, s.cache_policy, s.a_lds);
     std::snprintf(p->reason, sizeof p->reason, "M <= %d; %lld column blocks of 16, split-K %lld",
                   (int)kSkinnyMaxM, (long long)col_blocks, (long long)split);
 }
@@ -330,7 +331,8 @@ bool plan_matches_library(const hkg_plan_t* p)
         if (p->variant < 0 || p->variant >= TILE_NUM_VARIANTS)
             return false;
         const TileShape s = tile_shape(p->variant);
-        return p->tile_m == s.bm && p->tile_n == s.bn && p->split_k == 1 && p->xcd_window_w >= 0 &&
+        return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
+               p->split_k == 1 && p->xcd_window_w >= 0 &&
                p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
                cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
     }

@@ -5,31 +5,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hkg_skinny_configs.h"
+#include "hkg_tile_configs.h"
+
 namespace hkg {
 
-// Tile-kernel instantiations (plan.variant for HKG_KERNEL_TILE).
-enum TileVariant : int {
-    TILE_256x256 = 0,   // 8 waves, 2 x 4 wave grid, 128 x 64 per wave
-    TILE_256x128 = 1,   // 8 waves, 4 x 2 wave grid,  64 x 64 per wave
-    TILE_128x128 = 2,   // 4 waves, 2 x 2 wave grid,  64 x 64 per wave
-    TILE_NUM_VARIANTS = 3
-};
+// Tile-kernel instantiations (plan.variant for HKG_KERNEL_TILE): the rows
+// of HKG_TILE_CONFIGS in hkg_tile_configs.h, in order.
+constexpr int TILE_NUM_VARIANTS = 0
+#define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1
+    HKG_TILE_CONFIGS(HKG_COUNT_TILE)
+#undef HKG_COUNT_TILE
+    ;
+
+// Default tile ladder of the planner, largest first (variant indices).
+constexpr int TILE_LADDER[] = {0, 2, 3};
 
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
-// number of 16-row blocks of A the kernel covers (M <= 16 * mblocks).
-enum SkinnyVariant : int {
-    SKINNY_M16 = 0,     // M <= 16
-    SKINNY_M32 = 1,     // M <= 32
-    SKINNY_M64 = 2,     // M <= 64
-    SKINNY_M128 = 3,    // M <= 128
-    SKINNY_NUM_VARIANTS = 4
-};
+// rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.
+constexpr int SKINNY_NUM_VARIANTS = 0
+#define HKG_COUNT_SKINNY(mb, wk, u, cp, al) +1
+    HKG_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
+#undef HKG_COUNT_SKINNY
+    ;
 
-struct TileShape { int bm, bn, bk, waves; };
+struct TileShape { int bm, bn, bk, stages, waves, wm, wn, sched; };
 TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 
-struct SkinnyShape { int mblocks, rows_n, waves; };
+struct SkinnyShape { int mblocks, rows_n, waves, unroll, cache_policy, a_lds; };
+// Planner default for M rows: the first variant whose MB covers M.
+int skinny_default_variant(int64_t M);
 SkinnyShape skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 

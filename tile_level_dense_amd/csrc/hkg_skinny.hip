@@ -25,6 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -44,14 +45,30 @@ __device__ __forceinline__ uint16_t bf16_elem(uint2 w, int r)
     return (uint16_t)(word >> ((r & 1) * 16));
 }
 
-__device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// Loaded fragments stay int vectors until the MFMA: bf16 vectors carried
+// through loop phis get repacked element by element, which forces a wait on
+// the load right after it is issued.
+template <int CP>
+__device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+
+__device__ __forceinline__ f32x4 mfma16(i32x4 b, i32x4 a, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
+                                                   c, 0, 0, 0);
 }
 
 // MB: 16-row blocks of A (M <= 16 MB).  WK: waves per workgroup, splitting
-// K.  U: 32-k steps loaded ahead per wave.
-template <int MB, int WK, int U>
+// K.  U: 32-k steps per chunk of loads; two chunks are in flight per wave
+// (the next chunk's loads are issued before the current chunk's MFMAs).
+// CP: cache-policy bits of the B loads (B is streamed once).
+// AL: 1 = each wave copies its A chunks into its own LDS region with
+// contiguous full-line buffer->LDS copies and reads MFMA fragments from
+// there; 0 = A fragments are loaded straight from global memory (16 rows x
+// 64 bytes per instruction, half cache lines).
+template <int MB, int WK, int U, int CP, int AL>
 __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
@@ -59,6 +76,16 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 {
     __shared__ f32x4 red[WK][MB][64];
     __shared__ int last_flag;
+    // A staging (AL = 1): per wave two chunk buffers of 16 MB rows x U*64
+    // bytes; 16-byte chunk c of row r sits at position c ^ (r % 16), so a
+    // fragment read (16 rows, one chunk) hits 16 distinct bank groups.
+    constexpr int RS = U * 64;                    // bytes of one row of a chunk
+    constexpr int A_CHUNK = 16 * MB * RS;         // bytes of one wave's chunk
+    constexpr int RPI = 1024 / RS;                // rows per 1 KB copy
+    constexpr int CPRW = RS / 16;                 // 16-byte chunks per row
+    constexpr int NCOPY = AL ? 16 * MB / RPI : 0; // copies per chunk
+    static_assert(!AL || (RS <= 1024 && 1024 % RS == 0 && CPRW >= 16), "chunk rows must tile 1 KB copies");
+    __shared__ __attribute__((aligned(1024))) char a_lds[AL ? WK * 2 * A_CHUNK : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -71,8 +98,14 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     const int per_wg = (steps + split_k - 1) / split_k;
     const int wg_begin = min(steps, (int)blockIdx.y * per_wg);
     const int wg_end = min(steps, wg_begin + per_wg);
+    // Wave w takes K slice (w + workgroup) mod WK, so workgroups that run
+    // at the same time read different parts of A (which every workgroup
+    // reads) instead of all hitting the same L2 channels together.  Partial
+    // sums are combined in slice order, so the result does not depend on
+    // the rotation.
     const int per_wave = (wg_end - wg_begin + WK - 1) / WK;
-    const int s_begin = min(wg_end, wg_begin + wave * per_wave);
+    const int slice = (wave + (int)blockIdx.x) % WK;
+    const int s_begin = min(wg_end, wg_begin + slice * per_wave);
     const int s_end = min(wg_end, s_begin + per_wave);
 
     const uint32_t row_bytes = (uint32_t)K * 2u;
@@ -91,30 +124,126 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     for (int i = 0; i < MB; ++i)
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = s_begin; s < s_end; s += U) {
-        bf16x8 bv[U];
-        bf16x8 av[U][MB];
+    // Steps past s_end (or k past K) load from an out-of-range offset and
+    // read zero, which the MFMA adds exactly; so chunks need no tail code.
+    auto load_chunk = [&](int s, i32x4 (&bv)[U], i32x4 (&av)[U][MB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
             const bool ok = step < s_end && step * 32 + lgrp * 8 < K;
             const uint32_t kb = (uint32_t)step * 64u;
-            bv[u] = load16(rb, ok ? b_lane + kb : kOutOfRange);
+            bv[u] = load16<CP>(rb, ok ? b_lane + kb : kOutOfRange);
+            if constexpr (!AL) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                av[u][i] = load16(ra, ok ? a_lane + (uint32_t)i * a_block + kb : kOutOfRange);
+                for (int i = 0; i < MB; ++i)
+                    av[u][i] = load16<0>(ra, ok ? a_lane + (uint32_t)i * a_block + kb : kOutOfRange);
+            }
         }
+    };
+    auto mfma_chunk = [&](const i32x4 (&bv)[U], const i32x4 (&av)[U][MB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[u], av[u][i], acc[i], 0, 0, 0);
+                acc[i] = mfma16(bv[u], av[u][i], acc[i]);
+    };
+
+    i32x4 b0[U], a0[U][MB], b1[U], a1[U][MB];
+    // Empty asm statements keep the compiler from sinking the next chunk's
+    // loads below the current chunk's MFMAs (which would put one full memory
+    // round trip per chunk on the critical path).
+    auto fence = [] { asm volatile("" ::: "memory"); };
+    if constexpr (!AL) {
+        // Chunks c and c + 1 are in flight while chunk c is multiplied.
+        const int nch = (s_end - s_begin + U - 1) / U;
+        if (nch > 0) {
+            load_chunk(s_begin, b0, a0);
+            fence();
+            load_chunk(s_begin + U, b1, a1);
+            fence();
+            for (int c = 0; c < nch; c += 2) {
+                mfma_chunk(b0, a0);
+                fence();
+                if (c + 2 < nch)
+                    load_chunk(s_begin + (c + 2) * U, b0, a0);
+                fence();
+                if (c + 1 >= nch)      // odd chunk count: buffer 1 holds an old chunk
+                    break;
+                mfma_chunk(b1, a1);
+                fence();
+                if (c + 3 < nch)
+                    load_chunk(s_begin + (c + 3) * U, b1, a1);
+                fence();
+            }
+        }
+    } else {
+        char* my_lds = a_lds + wave * 2 * A_CHUNK;
+        const int cr = lane / CPRW;               // row within a copy
+        const int cp = lane % CPRW;               // LDS position within the row
+        // Copy of A chunk (steps s .. s + U - 1) into buffer `buf`: copy j
+        // fills rows j RPI .. j RPI + RPI - 1; lane -> row j RPI + cr,
+        // position cp, which holds k-chunk cp ^ (row % 16).
+        auto copy_a = [&](int s, int buf) {
+            char* dst = my_lds + buf * A_CHUNK;
+            const bool live = s < s_end;
+#pragma unroll
+            for (int j = 0; j < NCOPY; ++j) {
+                const int row = j * RPI + cr;
+                const int c = cp ^ (row & 15);
+                const bool ok = live && s * 32 + c * 8 < K;
+                const uint32_t off = (uint32_t)row * row_bytes + (uint32_t)s * 64u + (uint32_t)c * 16u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + j * 1024), 16,
+                                                         ok ? off : kOutOfRange, 0, 0, 0);
+            }
+        };
+        // This wave's copy of `buf` has landed once at most 2 U + NCOPY of
+        // its later memory operations are in flight (loads complete in
+        // order): the chunk's own B loads and the next chunk's copies and
+        // B loads.
+        auto read_a = [&](int buf, i32x4 (&av)[U][MB]) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * U + NCOPY) : "memory");
+            const char* src = my_lds + buf * A_CHUNK;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int row = i * 16 + lrow;
+                    const int c = (u * 4 + lgrp) ^ lrow;
+                    av[u][i] = *(const i32x4*)(src + row * RS + c * 16);
+                }
+        };
+        // The wait counts in read_a rely on this issue order (copy, then B
+        // loads, chunk after chunk); the fences keep it.
+        if (s_begin < s_end) {
+            copy_a(s_begin, 0);
+            fence();
+            load_chunk(s_begin, b0, a0);
+            fence();
+            for (int s = s_begin; s < s_end; s += 2 * U) {
+                copy_a(s + U, 1);
+                fence();
+                load_chunk(s + U, b1, a1);
+                fence();
+                read_a(0, a0);
+                mfma_chunk(b0, a0);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // buffer 0 read before refilled
+                copy_a(s + 2 * U, 0);
+                fence();
+                load_chunk(s + 2 * U, b0, a0);
+                fence();
+                read_a(1, a1);
+                mfma_chunk(b1, a1);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // buffer 1 read before refilled
+            }
+            // no copy into LDS may be in flight past this point
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
     }
 
     // acc[i] lane: C[16 i + lane % 16][n0 + 4 (lane / 16) + r], r = 0..3.
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-        red[wave][i][lane] = acc[i];
+        red[slice][i][lane] = acc[i];
     __syncthreads();
 
     const bool vec_ok = (N & 3) == 0;
@@ -176,12 +305,12 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         counters[blockIdx.x] = 0;
 }
 
-template <int MB, int WK, int U>
+template <int MB, int WK, int U, int CP, int AL>
 hipError_t launch_skinny_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
                            int split_k, float* ws, int* counters, hipStream_t stream)
 {
     const int col_blocks = (N + 15) / 16;
-    hipLaunchKernelGGL((skinny_kernel<MB, WK, U>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
+    hipLaunchKernelGGL((skinny_kernel<MB, WK, U, CP, AL>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
                        A, B, C, M, N, K, split_k, ws, counters);
     return hipGetLastError();
 }
@@ -190,32 +319,46 @@ hipError_t launch_skinny_t(const uint16_t* A, const uint16_t* B, uint16_t* C, in
 
 SkinnyShape skinny_shape(int variant)
 {
-    switch (variant) {
-    case SKINNY_M16: return {1, 16, 8};
-    case SKINNY_M32: return {2, 16, 8};
-    case SKINNY_M64: return {4, 16, 8};
-    case SKINNY_M128: return {8, 16, 8};
-    default: return {0, 0, 0};
+    int v = 0;
+#define HKG_SHAPE(mb, wk, u, cp, al) \
+    if (v++ == variant)          \
+        return SkinnyShape{mb, 16, wk, u, cp, al};
+    HKG_SKINNY_CONFIGS(HKG_SHAPE)
+#undef HKG_SHAPE
+    return SkinnyShape{0, 0, 0, 0, 0, 0};
+}
+
+int skinny_default_variant(int64_t M)
+{
+    // smallest MB that covers M; among equal MB the first listed
+    int best = -1, best_mb = 1 << 30;
+    for (int v = 0; v < SKINNY_NUM_VARIANTS; ++v) {
+        const SkinnyShape s = skinny_shape(v);
+        if (16 * (int64_t)s.mblocks >= M && s.mblocks < best_mb) {
+            best = v;
+            best_mb = s.mblocks;
+        }
     }
+    return best;
 }
 
 int skinny_lds_bytes(int variant)
 {
     const SkinnyShape s = skinny_shape(variant);
-    return s.waves * s.mblocks * 64 * 16 + 4;
+    return s.waves * s.mblocks * 64 * 16 + 4 + (s.a_lds ? s.waves * 2 * 16 * s.mblocks * s.unroll * 64 : 0);
 }
 
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                          int M, int N, int K, int split_k, float* ws, int* counters,
                          hipStream_t stream)
 {
-    switch (variant) {
-    case SKINNY_M16: return launch_skinny_t<1, 8, 8>(A, B, C, M, N, K, split_k, ws, counters, stream);
-    case SKINNY_M32: return launch_skinny_t<2, 8, 4>(A, B, C, M, N, K, split_k, ws, counters, stream);
-    case SKINNY_M64: return launch_skinny_t<4, 8, 2>(A, B, C, M, N, K, split_k, ws, counters, stream);
-    case SKINNY_M128: return launch_skinny_t<8, 8, 2>(A, B, C, M, N, K, split_k, ws, counters, stream);
-    default: return hipErrorInvalidValue;
-    }
+    int v = 0;
+#define HKG_LAUNCH(mb, wk, u, cp, al) \
+    if (v++ == variant)               \
+        return launch_skinny_t<mb, wk, u, cp, al>(A, B, C, M, N, K, split_k, ws, counters, stream);
+    HKG_SKINNY_CONFIGS(HKG_LAUNCH)
+#undef HKG_LAUNCH
+    return hipErrorInvalidValue;
 }
 
 }  // namespace hkg

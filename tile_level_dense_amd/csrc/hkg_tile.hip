@@ -60,27 +60,69 @@ __device__ __forceinline__ uint16_t bf16_elem(uint2 w, int r)
     return (uint16_t)(word >> ((r & 1) * 16));
 }
 
-template <int BM, int BN, int WM, int WN>
+// Wait until at most N of this wave's buffer->LDS copies are in flight and
+// its LDS reads are done, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// `ahead` = stages issued after the one about to be read (0 .. MAXA).
+template <int L, int MAXA>
+__device__ __forceinline__ void sync_stage(int ahead)
+{
+    if constexpr (MAXA >= 3) {
+        if (ahead >= 3) {
+            wait_and_barrier<3 * L>();
+            return;
+        }
+    }
+    if constexpr (MAXA >= 2) {
+        if (ahead == 2) {
+            wait_and_barrier<2 * L>();
+            return;
+        }
+    }
+    if constexpr (MAXA >= 1) {
+        if (ahead == 1) {
+            wait_and_barrier<L>();
+            return;
+        }
+    }
+    wait_and_barrier<0>();
+}
+
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
 __global__ __launch_bounds__(WM * WN * 64, 1)
 void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                  uint16_t* __restrict__ C, int M, int N, int K,
                  int tiles_m, int tiles_n, int win_w, int chunk_c)
 {
-    constexpr int BK = 64;                 // k per stage: 128 bytes per row
     constexpr int NW = WM * WN;
+    constexpr int RB = BK * 2;             // bytes of one row of a stage
+    constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    constexpr int RPW = 1024 / RB;         // rows filled by one wave instruction (1 KB)
+    constexpr int RPL = 256 / RB;          // rows sharing one 256-byte sweep of the 64 banks
+    constexpr int KS = BK / 32;            // 32-k MFMA steps per stage
     constexpr int WTM = BM / WM;           // rows of C per wave
     constexpr int WTN = BN / WN;           // columns of C per wave
     constexpr int FM = WTM / 16;
     constexpr int FN = WTN / 16;
-    constexpr int A_BYTES = BM * BK * 2;
-    constexpr int B_BYTES = BN * BK * 2;
+    constexpr int A_BYTES = BM * RB;
+    constexpr int B_BYTES = BN * RB;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int A_LOADS = BM / (8 * NW);  // 1 KB = 8 rows per wave instruction
-    constexpr int B_LOADS = BN / (8 * NW);
-    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split over waves");
+    constexpr int A_LOADS = BM / (RPW * NW);
+    constexpr int B_LOADS = BN / (RPW * NW);
+    constexpr int L = A_LOADS + B_LOADS;   // copies per wave per stage
+    static_assert(BK == 32 || BK == 64, "stage k must be 32 or 64");
+    static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
+    static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
+    static_assert(STAGES * STAGE <= 160 * 1024, "LDS is 160 KiB per CU");
+    static_assert((STAGES - 2) * L <= 63, "vmcnt holds at most 63");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -102,58 +144,53 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + (size_t)n0 * (size_t)K), 0, (int)(rows_b * row_bytes), kBufferWord3);
 
+    // LDS layout of a stage: row r holds its logical 16-byte chunk c at
+    // position c ^ ((r / RPL) % CPR).  Sixteen consecutive rows read at one
+    // logical chunk then hit sixteen distinct 16-byte bank groups.
+    //
     // DMA sources of this lane.  Wave instruction i of the A copy fills LDS
-    // rows 8 g .. 8 g + 7 (g = wave + i NW); lane -> LDS row 8 g + lane / 8,
-    // position lane % 8, which holds logical chunk (lane % 8) ^ swizzle(row).
-    uint32_t a_off[A_LOADS], b_off[B_LOADS];
-    int a_k[A_LOADS], b_k[B_LOADS];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-        const int row = (wave + i * NW) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        a_off[i] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        a_k[i] = c * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-        const int row = (wave + i * NW) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        b_off[i] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
-        b_k[i] = c * 8;
-    }
+    // rows RPW g .. RPW g + RPW - 1 (g = wave + i NW); lane -> row
+    // RPW g + lane / CPR, position lane % CPR, which holds logical chunk
+    // (lane % CPR) ^ swizzle(row): the swizzle is applied to the source.
+    // Consecutive copies of a wave are NW * RPW rows apart, a multiple of
+    // RPL * CPR, so the swizzle (and the lane's chunk) is the same for all
+    // of them: one base offset per operand, plus a uniform row step.
+    static_assert((NW * RPW / RPL) % CPR == 0, "swizzle must repeat across a wave's copies");
+    constexpr int COPY_ROWS = NW * RPW;
+    const int lrow0 = wave * RPW + lane / CPR;
+    const int lchunk = (lane % CPR) ^ ((lrow0 / RPL) % CPR);
+    const uint32_t src_off = (uint32_t)lrow0 * row_bytes + (uint32_t)lchunk * 16u;
+    const int src_k = lchunk * 8;
+    const uint32_t copy_step = (uint32_t)COPY_ROWS * row_bytes;
 
     auto issue = [&](int stage, int k0) {
         char* base = smem + stage * STAGE;
-        const uint32_t kb = (uint32_t)k0 * 2u;
-        const bool tail = k0 + BK > K;
+        const bool k_out = k0 + src_k >= K;     // this lane's 8 k past the end
+        const uint32_t off0 = k_out ? kOutOfRange : src_off + (uint32_t)k0 * 2u;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            uint32_t off = a_off[i] + kb;
-            if (tail && k0 + a_k[i] >= K)
-                off = kOutOfRange;
+        for (int i = 0; i < A_LOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16, off, 0, 0, 0);
-        }
+                rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16,
+                k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            uint32_t off = b_off[i] + kb;
-            if (tail && k0 + b_k[i] >= K)
-                off = kOutOfRange;
+        for (int i = 0; i < B_LOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16, off, 0, 0, 0);
-        }
+                rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16,
+                k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
     };
 
     // Fragment reads: lane -> row (lane % 16) of a 16-row block, 8 k values
-    // at logical chunk 4 s + lane / 16 of the 32-k step s.  The row's swizzle
-    // depends only on lane % 16 because every block starts at a multiple of 16.
+    // at logical chunk 4 s + lane / 16 of the 32-k step s.  Every block
+    // starts at a multiple of 16 rows, so the swizzle depends on lane only.
     const int lrow = lane & 15;
     const int lgrp = lane >> 4;
-    const int swz = (lane >> 1) & 7;
-    const int chunk0 = ((0 + lgrp) ^ swz) * 16;
-    const int chunk1 = ((4 + lgrp) ^ swz) * 16;
-    const int a_frag = (wm * WTM + lrow) * 128;
-    const int b_frag = A_BYTES + (wn * WTN + lrow) * 128;
+    const int swz = (lrow / RPL) % CPR;
+    int chunk_off[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        chunk_off[s] = ((4 * s + lgrp) ^ swz) * 16;
+    const int a_frag = (wm * WTM + lrow) * RB;
+    const int b_frag = A_BYTES + (wn * WTN + lrow) * RB;
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -162,35 +199,142 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int stage) {
-        const char* base = smem + stage * STAGE;
+    auto read_frags = [&](const char* base, int s, bf16x8 (&af)[FM], bf16x8 (&bf)[FN]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int ch = s ? chunk1 : chunk0;
-            bf16x8 af[FM], bf[FN];
+        for (int i = 0; i < FM; ++i)
+            af[i] = *(const bf16x8*)(base + a_frag + i * 16 * RB + chunk_off[s]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *(const bf16x8*)(base + a_frag + i * 16 * 128 + ch);
+        for (int j = 0; j < FN; ++j)
+            bf[j] = *(const bf16x8*)(base + b_frag + j * 16 * RB + chunk_off[s]);
+    };
+    auto mfmas = [&](const bf16x8 (&af)[FM], const bf16x8 (&bf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bf[j] = *(const bf16x8*)(base + b_frag + j * 16 * 128 + ch);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    };
+
+    auto compute = [&](int stage) {
+        const char* base = smem + stage * STAGE;
+        if constexpr (SCHED == 0) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 af[FM], bf[FN];
+                read_frags(base, s, af, bf);
+                mfmas(af, bf);
+            }
+        } else {
+            // Fragments of step s + 1 are read while the MFMAs of step s run:
+            // one LDS read between every few MFMAs, so each read has many
+            // MFMA cycles to land before its first use.
+            bf16x8 af[2][FM], bf[2][FN];
+            read_frags(base, 0, af[0], bf[0]);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+            for (int s = 0; s < KS; ++s) {
+                const int cur = s & 1;
+                if (s + 1 < KS)
+                    read_frags(base, s + 1, af[cur ^ 1], bf[cur ^ 1]);
+                mfmas(af[cur], bf[cur]);
+            }
+            if constexpr (KS > 1) {
+                constexpr int READS = FM + FN;
+                constexpr int MF = FM * FN;
+                constexpr int PER = MF / READS > 0 ? MF / READS : 1;
+                // first step: its reads were issued above the loop
+                __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+                for (int r = 0; r < READS; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MF - PER * READS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+            }
         }
     };
 
     const int nk = (K + BK - 1) / BK;
-    issue(0, 0);
-    for (int t = 0; t < nk; ++t) {
-        // This wave's copy of step t has landed and its reads of step t - 1
-        // are done; the barrier extends both to the whole workgroup.
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (t + 1 < nk)
-            issue((t + 1) & 1, (t + 1) * BK);
-        compute(t & 1);
+    if constexpr (SCHED < 2) {
+        // K loop over a ring of STAGES buffers, prefetch distance STAGES - 1.
+        // At step t: this wave's copy of stage t has landed (vmcnt allows the
+        // later stages still in flight), all waves finished reading step t - 1
+        // (lgkmcnt + barrier), so buffer (t - 1) % STAGES is refilled with step
+        // t + STAGES - 1 while step t is computed.
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk)
+                issue(s, s * BK);
+        int read_stage = 0;
+        int write_stage = STAGES - 1;
+        for (int t = 0; t < nk; ++t) {
+            sync_stage<L, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+            if (t + STAGES - 1 < nk)
+                issue(write_stage, (t + STAGES - 1) * BK);
+            compute(read_stage);
+            read_stage = read_stage + 1 == STAGES ? 0 : read_stage + 1;
+            write_stage = write_stage + 1 == STAGES ? 0 : write_stage + 1;
+        }
+    } else {
+        // Register-pipelined loop.  Work proceeds in 32-k steps; the
+        // fragments of step u + 1 are read from LDS while the MFMAs of step u
+        // run.  Before the first read of a new stage every wave waits for its
+        // own reads of the previous stage (now in registers) and for its copy
+        // of the new stage, then joins the barrier: the previous stage's
+        // buffer is then free and is refilled right away with the stage
+        // STAGES ahead.  Copies past the end of K are issued with
+        // out-of-range offsets (they fill a buffer nobody reads), so the
+        // number of copies in flight, and with it every wait count, is the
+        // same on every step: the loop body has no branch around LDS reads,
+        // copies or waits.
+        constexpr int READS = FM + FN;
+        constexpr int MF = FM * FN;
+        static_assert(MF >= READS, "one MFMA per fragment read at least");
+        auto interleave = [&]() {
+#pragma unroll
+            for (int r = 0; r < READS; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MF - READS, 0);
+        };
+        auto stage_base = [&](int t) { return smem + (t % STAGES) * STAGE; };
+        auto new_stage = [&](int t) {      // about to read stage t + 1
+            wait_and_barrier<(STAGES - 2) * L>();
+            issue(t % STAGES, (t + STAGES) * BK);
+        };
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s)
+            issue(s, s * BK);
+        wait_and_barrier<(STAGES - 1) * L>();
+        bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
+        read_frags(smem, 0, af0, bf0);
+        if constexpr (KS == 2) {
+            for (int t = 0; t < nk; ++t) {
+                mfmas(af0, bf0);
+                read_frags(stage_base(t), 1, af1, bf1);
+                interleave();
+                new_stage(t);
+                mfmas(af1, bf1);
+                read_frags(stage_base(t + 1), 0, af0, bf0);
+                interleave();
+            }
+        } else {
+            for (int t = 0; t < nk; t += 2) {
+                new_stage(t);
+                mfmas(af0, bf0);
+                read_frags(stage_base(t + 1), 0, af1, bf1);
+                interleave();
+                if (t + 1 == nk)
+                    break;
+                new_stage(t + 1);
+                mfmas(af1, bf1);
+                read_frags(stage_base(t + 2), 0, af0, bf0);
+                interleave();
+            }
+        }
+        // Leave no copy in flight into LDS that is about to be released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
@@ -204,6 +348,9 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
+            // One block at a time: keeps the compiler from moving every
+            // accumulator into VGPRs at once (256 of them in 4-wave tiles).
+            __builtin_amdgcn_sched_barrier(0);
             const uint2 h = pack_bf16x4(acc[i][j]);
             if (vec_ok && n + 3 < N) {
                 *(uint2*)(crow + n) = h;
@@ -217,14 +364,14 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
 hipError_t launch_tile_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
                          int win_w, int chunk_c, hipStream_t stream)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((tile_kernel<BM, BN, WM, WN>), dim3(tiles_m * tiles_n), dim3(WM * WN * 64),
-                       0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c);
+    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED>), dim3(tiles_m * tiles_n),
+                       dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c);
     return hipGetLastError();
 }
 
@@ -232,29 +379,31 @@ hipError_t launch_tile_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
 
 TileShape tile_shape(int variant)
 {
-    switch (variant) {
-    case TILE_256x256: return {256, 256, 64, 8};
-    case TILE_256x128: return {256, 128, 64, 8};
-    case TILE_128x128: return {128, 128, 64, 4};
-    default: return {0, 0, 0, 0};
-    }
+    int v = 0;
+#define HKG_SHAPE(bm, bn, bk, st, wm, wn, sc) \
+    if (v++ == variant)                   \
+        return TileShape{bm, bn, bk, st, (wm) * (wn), wm, wn, sc};
+    HKG_TILE_CONFIGS(HKG_SHAPE)
+#undef HKG_SHAPE
+    return TileShape{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
 int tile_lds_bytes(int variant)
 {
     const TileShape s = tile_shape(variant);
-    return 2 * (s.bm + s.bn) * s.bk * 2;
+    return s.stages * (s.bm + s.bn) * s.bk * 2;
 }
 
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int chunk_c, hipStream_t stream)
 {
-    switch (variant) {
-    case TILE_256x256: return launch_tile_t<256, 256, 2, 4>(A, B, C, M, N, K, win_w, chunk_c, stream);
-    case TILE_256x128: return launch_tile_t<256, 128, 4, 2>(A, B, C, M, N, K, win_w, chunk_c, stream);
-    case TILE_128x128: return launch_tile_t<128, 128, 2, 2>(A, B, C, M, N, K, win_w, chunk_c, stream);
-    default: return hipErrorInvalidValue;
-    }
+    int v = 0;
+#define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc) \
+    if (v++ == variant)                        \
+        return launch_tile_t<bm, bn, bk, st, wm, wn, sc>(A, B, C, M, N, K, win_w, chunk_c, stream);
+    HKG_TILE_CONFIGS(HKG_LAUNCH)
+#undef HKG_LAUNCH
+    return hipErrorInvalidValue;
 }
 
 }  // namespace hkg

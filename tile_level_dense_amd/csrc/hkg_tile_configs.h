@@ -1,0 +1,23 @@
+// Instantiated configurations of the tile kernel, one X(...) per variant,
+// in variant order: X(BM, BN, BK, STAGES, WM, WN, SCHED)
+//   BM x BN   output tile of one workgroup
+//   BK        k per LDS stage (32 or 64)
+//   STAGES    LDS stages in the ring (prefetch distance STAGES - 1)
+//   WM x WN   wave grid (WM * WN waves; each wave owns BM/WM x BN/WN of C)
+//   SCHED     0: compiler-scheduled fragment reads; 1: reads of the next
+//             32-k step interleaved with the MFMAs of the current one;
+//             2: fragment reads of the next 32-k step (also across stages)
+//             overlap the current MFMAs; branch-free ring with STAGES - 1
+//             copies ahead
+// The build script reads this list to map code objects to variants.
+#pragma once
+
+#define HKG_TILE_CONFIGS(X)       \
+    X(256, 256, 64, 2, 2, 4, 2)   \
+    X(256, 256, 64, 2, 4, 2, 2)   \
+    X(256, 128, 64, 2, 4, 2, 2)   \
+    X(128, 128, 64, 2, 2, 2, 2)   \
+    X(128, 128, 64, 2, 2, 2, 0)   \
+    X(256, 256, 64, 2, 2, 4, 0)   \
+    X(256, 256, 64, 2, 4, 2, 1)   \
+    X(256, 256, 32, 4, 2, 4, 2)
