@@ -65,7 +65,7 @@ typedef enum {
 typedef enum {
     HKG_KERNEL_NONE = 0,        /* M == 0 or N == 0: nothing to do */
     HKG_KERNEL_TILE = 1,        /* large-tile MFMA kernel (compute-bound shapes) */
-    HKG_KERNEL_SKINNY = 2,      /* M <= 128: streams B once, split-K over waves / workgroups */
+    HKG_KERNEL_SKINNY = 2,      /* small M: streams B once, split-K over waves / workgroups */
     HKG_KERNEL_GENERIC = 3,     /* any alignment, any K: correctness fallback */
     HKG_KERNEL_ZERO = 4         /* K == 0: C is filled with +0 (the empty sum) */
 } hkg_kernel_t;

@@ -93,7 +93,7 @@ def test_status_strings(lib):
 WORKLOAD_PLANS = {
     (256, 256, 256): ("TILE", "tile_128x128x64_"),
     (16, 4096, 4096): ("SKINNY", "skinny_m16"),
-    (128, 12288, 4096): ("SKINNY", "skinny_m128"),
+    (128, 12288, 4096): ("TILE", "tile_128x128x64_"),
     (4096, 4096, 12288): ("TILE", "tile_256x256x64_"),
     (8192, 8192, 8192): ("TILE", "tile_256x256x64_"),
 }
@@ -130,8 +130,10 @@ def test_plan_decode_geometry():
 
 
 def test_plan_boundaries():
-    assert hkg.KERNEL_NAMES[hkg.plan(128, 4096, 4096).kernel_id] == "SKINNY"
-    assert hkg.KERNEL_NAMES[hkg.plan(129, 4096, 4096).kernel_id] == "TILE"
+    assert hkg.KERNEL_NAMES[hkg.plan(32, 4096, 4096).kernel_id] == "SKINNY"
+    assert hkg.KERNEL_NAMES[hkg.plan(33, 4096, 4096).kernel_id] == "TILE"
+    p = hkg.plan(128, 12288, 4096)       # one 128-row tile band, split-K 3
+    assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.split_k) == (128, 3)
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 100).kernel_id] == "GENERIC"     # K % 8
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 0).kernel_id] == "ZERO"
     assert hkg.KERNEL_NAMES[hkg.plan(0, 512, 64).kernel_id] == "NONE"
@@ -140,6 +142,15 @@ def test_plan_boundaries():
     # small N at decode M: split-K across workgroups with a workspace
     p = hkg.plan(16, 256, 8192)
     assert p.split_k > 1 and p.workspace_bytes == p.split_k * 16 * 256 * 4
+    # tile grid under one workgroup per CU: split-K across workgroups,
+    # at least 4 k-tiles per split
+    p = hkg.plan(256, 4096, 4096)
+    assert (p.tile_m, p.tile_n) == (128, 128) and p.grid_x == 64
+    assert p.split_k == 4 and p.grid_y == 4 and p.workspace_bytes == 4 * 256 * 4096 * 4
+    p = hkg.plan(256, 4096, 512)
+    assert p.split_k == 2
+    p = hkg.plan(256, 4096, 128)
+    assert p.split_k == 1 and p.workspace_bytes == 0
     # tile ladder: a grid that would underfill at 256x256 steps down
     for shape in [(2048, 2048, 1024), (4096, 2048, 1024), (1024, 8192, 4096)]:
         p = hkg.plan(*shape)
@@ -185,8 +196,16 @@ def test_run_plan_errors_precede_device_work():
     q.variant = 99
     assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
     q = hkg.Plan.from_buffer_copy(p)
-    q.split_k = 2
+    q.split_k = 17           # tile split range is 1..16
     assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    q.split_k = 0
+    assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    # split-K exists only in tile variants with at most 16 accumulator
+    # blocks per wave (256 x 256 over 8 waves has 32)
+    q = hkg.plan(8192, 8192, 8192)
+    assert (q.tile_m, q.tile_n, q.waves) == (256, 256, 8)
+    q.split_k = 2
+    assert hkg.hkg_gemm_bf16_run_plan(q, 1 << 40, 2 << 40, 3 << 40, 8192, 8192, 8192) == hkg.HKG_ERR_UNSUPPORTED
     q = hkg.Plan.from_buffer_copy(p)
     q.abi_version = 7
     assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_INVALID_ARG

@@ -177,15 +177,16 @@ def forced(hkg, A, B, edit):
     return host(c)
 
 
-def force_tile(hkg, p, variant, win_w=None, chunk_c=None):
+def force_tile(hkg, p, variant, win_w=None, chunk_c=None, split=1):
     """Edit plan p to run tile-kernel variant `variant` (hkg_tile_configs.h)."""
     from tile_level_dense_amd import build as hkg_build
     bm, bn, bk, stages, wm, wn, _ = hkg_build.tile_configs()[variant]
     p.kernel_id = hkg.HKG_KERNEL_TILE
     p.variant = variant
     p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn
-    p.split_k = 1
-    p.workspace_bytes = 0
+    p.split_k = split
+    p.grid_y = split
+    p.workspace_bytes = split * p.M * p.N * 4 if split > 1 else 0
     if win_w is not None:
         p.xcd_window_w = win_w
     if chunk_c is not None:
@@ -210,6 +211,31 @@ def test_forced_tile_variants(hkg, variant, shape):
     full_check(forced(hkg, A, B, lambda p: force_tile(hkg, p, variant)), A, B)
 
 
+TILE_SPLIT_SHAPES = [(300, 500, 136), (520, 1000, 392), (129, 40, 4104)]
+
+
+def _split_variants():
+    from tile_level_dense_amd import build as hkg_build
+    return [v for v, (bm, bn, bk, st, wm, wn, sc) in enumerate(hkg_build.tile_configs())
+            if (bm // wm // 16) * (bn // wn // 16) <= 16]
+
+
+@pytest.mark.parametrize("variant", _split_variants())
+@pytest.mark.parametrize("split", (2, 3, 5))
+@pytest.mark.parametrize("shape", TILE_SPLIT_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_forced_tile_split(hkg, variant, split, shape):
+    """Split-K tile runs, including splits whose K range is empty (K of 2
+    or 3 k-tiles over 5 splits); two runs agree bit for bit (the partials
+    are summed in split order)."""
+    M, N, K = shape
+    _say("tile variant", variant, "split", split, shape)
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.05), seed=split + 10)
+    C1 = forced(hkg, A, B, lambda p: force_tile(hkg, p, variant, split=split))
+    full_check(C1, A, B)
+    C2 = forced(hkg, A, B, lambda p: force_tile(hkg, p, variant, split=split))
+    assert np.array_equal(C1, C2)
+
+
 def _skinny_configs():
     from tile_level_dense_amd import build as hkg_build
     return hkg_build.skinny_configs()
@@ -227,9 +253,12 @@ def test_forced_skinny_split(hkg, variant, split, shape):
     _say("skinny variant", variant, "split", split, shape)
     A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=split)
 
+    mb, nb, wk, u, cp = _skinny_configs()[variant]
+
     def edit(p):
         p.kernel_id = hkg.HKG_KERNEL_SKINNY
         p.variant = variant
+        p.tile_m, p.tile_n, p.waves = 16 * mb, 16 * nb, wk
         p.split_k = split
     C1 = forced(hkg, A, B, edit)
     C2 = forced(hkg, A, B, edit)       # counters must be back at zero

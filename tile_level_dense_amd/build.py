@@ -40,7 +40,7 @@ def tile_configs():
 
 TILE_VARIANTS = tile_configs()
 def skinny_configs():
-    """(MB, WK, U, CP, AL) per skinny variant, from hkg_skinny_configs.h."""
+    """(MB, NB, WK, U, CP) per skinny variant, from hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
     body = text[text.index("#define HKG_SKINNY_CONFIGS(X)"):]
     return [tuple(int(v) for v in m) for m in re.findall(
@@ -113,7 +113,7 @@ def _table(resources):
         if m:
             key = tuple(int(g) for g in m.groups())
             if key in SKINNY_VARIANTS:
-                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_w%d_u%d_c%d_a%d" % ((16 * key[0],) + key[1:]), r)
+                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_n%d_w%d_u%d_c%d" % ((16 * key[0], 16 * key[1]) + key[2:]), r)
             continue
         if "generic_kernel" in mangled:
             generic = _entry("generic", r)

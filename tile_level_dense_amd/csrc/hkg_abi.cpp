@@ -23,8 +23,13 @@ namespace {
 // correctly.
 constexpr int kNumCUs = 256;
 
-// Skinny path for M up to this many rows (decode shapes).
-constexpr int64_t kSkinnyMaxM = 128;
+// Skinny path for M up to this many rows (decode shapes).  Above it the
+// tile kernel with a 128-row tile (B still read once) and split-K measured
+// faster on MI355X at N = 4096 .. 12288, K = 4096 .. 12288 (M = 64: 1.1-1.7x
+// except at N = K = 4096; M = 128: 1.0-2.2x).
+constexpr int64_t kSkinnyMaxM = 32;
+// Largest split-K factor of the tile kernel.
+constexpr int64_t kMaxTileSplit = 16;
 
 // Largest dimension the kernels index with 32-bit arithmetic.
 constexpr int64_t kMaxDim = INT32_MAX;
@@ -152,6 +157,8 @@ hkg_status_t check_dims(int64_t M, int64_t N, int64_t K)
     return HKG_OK;
 }
 
+void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N);
+
 void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
     // Largest tile that still gives every compute unit a workgroup; the
@@ -167,17 +174,33 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     }
     const TileShape s = tile_shape(variant);
     const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
+    // Split K across workgroups when even the smallest rung leaves compute
+    // units idle, keeping at least 4 k-tiles per split (the pipeline depth).
+    int64_t split = 1;
+    if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {   // fp32 partials addressed in 32 bits
+        split = std::min<int64_t>(cdiv(kNumCUs, tm * tn), cdiv(K, s.bk) / 4);
+        split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
+    }
+    fill_tile(p, variant, split, M, N);
+}
+
+// Fill the tile-kernel fields of p for (variant, split).
+void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
+{
+    const TileShape s = tile_shape(variant);
+    const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
     p->kernel_id = HKG_KERNEL_TILE;
     p->variant = variant;
     p->tile_m = s.bm;
     p->tile_n = s.bn;
     p->tile_k = s.bk;
     p->waves = s.waves;
-    p->split_k = 1;
+    p->split_k = (int32_t)split;
     p->grid_x = (int32_t)(tm * tn);
-    p->grid_y = 1;
+    p->grid_y = (int32_t)split;
     p->grid_z = 1;
     p->block_x = s.waves * 64;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
     // Chiplet-aware order (talk notes, section 3): 8-tall windows, so one
     // XCD's 32 concurrent workgroups cover an 8 x 4 block of tiles, and 32
     // consecutive tiles per XCD; off when the grid is under one XCD round.
@@ -187,18 +210,54 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     fill_resources(p, tile_resources(variant));
     std::snprintf(p->kernel_name, sizeof p->kernel_name, "tile_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
                   s.stages, s.wm, s.wn, s.sched);
-    std::snprintf(p->reason, sizeof p->reason, "M > %d; %lldx%lld tiles of %dx%d (largest rung filling %d CUs)",
-                  (int)kSkinnyMaxM, (long long)tm, (long long)tn, s.bm, s.bn, kNumCUs);
+    std::snprintf(p->reason, sizeof p->reason, "%lldx%lld tiles of %dx%d, split-K %lld (largest rung filling %d CUs)",
+                  (long long)tm, (long long)tn, s.bm, s.bn, (long long)split, kNumCUs);
+}
+
+// Fill the skinny-kernel fields of p for (variant, split).
+void fill_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N, const char* why)
+{
+    const SkinnyShape s = skinny_shape(variant);
+    const int64_t col_blocks = cdiv(N, 16 * s.nblocks);
+    p->kernel_id = HKG_KERNEL_SKINNY;
+    p->variant = variant;
+    p->tile_m = 16 * s.mblocks;
+    p->tile_n = 16 * s.nblocks;
+    p->tile_k = 32;
+    p->waves = s.waves;
+    p->split_k = (int32_t)split;
+    p->grid_x = (int32_t)col_blocks;
+    p->grid_y = (int32_t)split;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->xcd_window_w = 0;
+    p->xcd_chunk_c = 0;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    p->lds_bytes = skinny_lds_bytes(variant);
+    fill_resources(p, skinny_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d_n%d_w%d_u%d_c%d", 16 * s.mblocks,
+                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy);
+    std::snprintf(p->reason, sizeof p->reason, "M <= %d; %lld column blocks of %d, split-K %lld%s%s",
+                  (int)kSkinnyMaxM, (long long)col_blocks, 16 * s.nblocks, (long long)split, why ? "; " : "",
+                  why ? why : "");
 }
 
 void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
-    const int variant = skinny_default_variant(M);
+    // Smallest A coverage (16-row blocks) that holds M; one B block per
+    // workgroup; split K across workgroups only when the column blocks
+    // underfill the device, keeping at least 8 steps (256 k) per wave.
+    int variant = -1, best_mb = 1 << 30;
+    for (int v = 0; v < SKINNY_NUM_VARIANTS; ++v) {
+        const SkinnyShape s = skinny_shape(v);
+        if (s.nblocks == 1 && 16 * (int64_t)s.mblocks >= M && s.mblocks < best_mb) {
+            variant = v;
+            best_mb = s.mblocks;
+        }
+    }
     const SkinnyShape s = skinny_shape(variant);
-    const int64_t col_blocks = cdiv(N, 16);
+    const int64_t col_blocks = cdiv(N, 16 * s.nblocks);
     const int64_t steps = cdiv(K, 32);
-    // Split K across workgroups only when the column blocks underfill the
-    // device, keeping at least 8 steps (256 k) per wave.
     int64_t split = 1;
     if (col_blocks < kNumCUs) {
         split = cdiv(kNumCUs, col_blocks);
@@ -210,24 +269,7 @@ void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
         if (split < 1)
             split = 1;
     }
-    p->kernel_id = HKG_KERNEL_SKINNY;
-    p->variant = variant;
-    p->tile_m = 16 * s.mblocks;
-    p->tile_n = 16;
-    p->tile_k = 32;
-    p->waves = s.waves;
-    p->split_k = (int32_t)split;
-    p->grid_x = (int32_t)col_blocks;
-    p->grid_y = (int32_t)split;
-    p->grid_z = 1;
-    p->block_x = s.waves * 64;
-    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
-    p->lds_bytes = skinny_lds_bytes(variant);
-    fill_resources(p, skinny_resources(variant));
-    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d_w%d_u%d_c%d_a%d", 16 * s.mblocks, s.waves,
-                  s.unroll, s.cache_policy, s.a_lds);
-    std::snprintf(p->reason, sizeof p->reason, "M <= %d; %lld column blocks of 16, split-K %lld",
-                  (int)kSkinnyMaxM, (long long)col_blocks, (long long)split);
+    fill_skinny(p, variant, split, M, N, nullptr);
 }
 
 void plan_generic(int64_t M, int64_t N, hkg_plan_t* p, const char* why)
@@ -332,7 +374,9 @@ bool plan_matches_library(const hkg_plan_t* p)
             return false;
         const TileShape s = tile_shape(p->variant);
         return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
-               p->split_k == 1 && p->xcd_window_w >= 0 &&
+               p->split_k >= 1 && p->split_k <= kMaxTileSplit &&
+               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn)) &&
+               (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
                p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
                cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
     }
@@ -340,8 +384,8 @@ bool plan_matches_library(const hkg_plan_t* p)
         if (p->variant < 0 || p->variant >= SKINNY_NUM_VARIANTS)
             return false;
         const SkinnyShape s = skinny_shape(p->variant);
-        return p->M <= 16 * s.mblocks && p->split_k >= 1 && p->split_k <= 64 && p->K > 0 &&
-               p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256;
+        return p->M <= 16 * s.mblocks && p->tile_n == 16 * s.nblocks && p->split_k >= 1 && p->split_k <= 64 &&
+               p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256;
     }
     default:
         return false;
@@ -368,9 +412,19 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hip
     case HKG_KERNEL_GENERIC:
         e = launch_generic(a, b, c, M, N, K, stream);
         break;
-    case HKG_KERNEL_TILE:
-        e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c, stream);
+    case HKG_KERNEL_TILE: {
+        float* ws = nullptr;
+        int* counters = nullptr;
+        if (p->split_k > 1) {
+            st = get_workspace(dev, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+                               (size_t)(cdiv(M, p->tile_m) * cdiv(N, p->tile_n)), &ws, &counters);
+            if (st != HKG_OK)
+                return st;
+        }
+        e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c,
+                        p->split_k, ws, counters, stream);
         break;
+    }
     case HKG_KERNEL_SKINNY: {
         float* ws = nullptr;
         int* counters = nullptr;

@@ -24,24 +24,29 @@ constexpr int TILE_LADDER[] = {0, 2, 3};
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
 // rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.
 constexpr int SKINNY_NUM_VARIANTS = 0
-#define HKG_COUNT_SKINNY(mb, wk, u, cp, al) +1
+#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp) +1
     HKG_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
 #undef HKG_COUNT_SKINNY
     ;
 
 struct TileShape { int bm, bn, bk, stages, waves, wm, wn, sched; };
+// Split-K is built into tile variants whose waves hold at most 16 blocks
+// of 16 x 16 accumulators (the split sums need as many registers again).
+constexpr bool tile_split_capable(int bm, int bn, int wm, int wn) { return (bm / wm / 16) * (bn / wn / 16) <= 16; }
 TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 
-struct SkinnyShape { int mblocks, rows_n, waves, unroll, cache_policy, a_lds; };
-// Planner default for M rows: the first variant whose MB covers M.
-int skinny_default_variant(int64_t M);
+struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy; };
 SkinnyShape skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 
 // Launchers: enqueue one kernel on `stream`; return the launch error.
+// split_k == 1: plain launch.  split_k > 1: K divided across workgroups,
+// fp32 partials in `ws` (split_k * M * N floats) and per-tile arrival
+// counters in `counters` (one per output tile, zero on entry and on exit).
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
-                       int M, int N, int K, int win_w, int xcd_chunk, hipStream_t stream);
+                       int M, int N, int K, int win_w, int xcd_chunk, int split_k, float* ws,
+                       int* counters, hipStream_t stream);
 
 // split_k == 1: plain launch.  split_k > 1: fp32 partials in `ws`
 // (split_k * M * N floats) and per-column-block arrival counters in `counters`

@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // gfx9 buffer descriptor word 3 for a raw (unswizzled, stride 0) buffer of
@@ -44,6 +45,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufferWord3 = 0x00020000;
 // An offset past every range this file creates (ranges are < 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of buffer loads/stores: sc1, device scope (the
+// access is coherent across the XCDs' L2 caches).
+constexpr int kDeviceScope = 16;
 
 // Four fp32 values -> four bf16 (nearest-even, v_cvt_pk_bf16_f32) packed in
 // two 32-bit words, element r in bits 16 (r % 2) of word r / 2.  Single
@@ -94,10 +98,11 @@ __device__ __forceinline__ void sync_stage(int ahead)
 }
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
-__global__ __launch_bounds__(WM * WN * 64, 1)
+__global__ __launch_bounds__(WM * WN * 64, 2)
 void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                  uint16_t* __restrict__ C, int M, int N, int K,
-                 int tiles_m, int tiles_n, int win_w, int chunk_c)
+                 int tiles_m, int tiles_n, int win_w, int chunk_c,
+                 int split_k, float* __restrict__ ws, int* __restrict__ counters)
 {
     constexpr int NW = WM * WN;
     constexpr int RB = BK * 2;             // bytes of one row of a stage
@@ -163,9 +168,19 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int src_k = lchunk * 8;
     const uint32_t copy_step = (uint32_t)COPY_ROWS * row_bytes;
 
-    auto issue = [&](int stage, int k0) {
+    // K range of this workgroup: stages [kt0, kt0 + nk) of 64 (or 32) k;
+    // split_k > 1 divides K across workgroups (blockIdx.y).
+    const int nk_all = (K + BK - 1) / BK;
+    const int per_split = (nk_all + split_k - 1) / split_k;
+    const int kt0 = min(nk_all, (int)blockIdx.y * per_split);
+    const int nk = min(nk_all, kt0 + per_split) - kt0;
+    const int kbase = kt0 * BK;
+    const int k_lim = min(K, (kt0 + nk) * BK);
+
+    auto issue = [&](int stage, int kl) {
         char* base = smem + stage * STAGE;
-        const bool k_out = k0 + src_k >= K;     // this lane's 8 k past the end
+        const int k0 = kbase + kl;
+        const bool k_out = k0 + src_k >= k_lim;  // this lane's 8 k past the range
         const uint32_t off0 = k_out ? kOutOfRange : src_off + (uint32_t)k0 * 2u;
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i)
@@ -254,7 +269,6 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
         }
     };
 
-    const int nk = (K + BK - 1) / BK;
     if constexpr (SCHED < 2) {
         // K loop over a ring of STAGES buffers, prefetch distance STAGES - 1.
         // At step t: this wave's copy of stage t has landed (vmcnt allows the
@@ -337,6 +351,98 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
+    if constexpr (tile_split_capable(BM, BN, WM, WN)) if (split_k > 1) {
+        // Split-K: each workgroup writes its fp32 partial tile; the last one
+        // of the tile to arrive adds the partials in split order 0, 1, ...
+        // (the same order whichever split arrives last, so results are
+        // deterministic) and goes on to the rounding store below.  Partials
+        // are written and read with device-scope (sc1) accesses, which are
+        // coherent across the XCDs' L2 caches without flushing them; every
+        // store has completed (vmcnt) before the arrival is counted.
+        __shared__ int last_flag;
+        const int me = blockIdx.y;
+        const bool vec4 = (N & 3) == 0;
+        const int part_bytes = M * N * 4;          // below 2^31: checked by the planner
+        auto part = [&](int sp) { return ws + (size_t)sp * (size_t)M * (size_t)N; };
+        {
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(part(me), 0, part_bytes, kBufferWord3);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m0 + wm * WTM + i * 16 + lrow;
+                if (m >= M)
+                    continue;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
+                    if (vec4 && n + 3 < N) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r,
+                                                               (m * N + n) * 4, 0, kDeviceScope);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < N)
+                                __hip_atomic_store(part(me) + (size_t)m * N + n + q, acc[i][j][q], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int tile = tm * tiles_n + tn;
+        if (threadIdx.x == 0) {
+            const int prev = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = (prev == split_k - 1);
+        }
+        __syncthreads();
+        if (!last_flag)
+            return;
+        // Sums are formed GR block rows at a time (at most 64 registers of
+        // running totals beside the accumulators).
+        constexpr int GR = FN >= 16 ? 1 : 16 / FN;
+#pragma unroll
+        for (int g = 0; g < FM; g += GR) {
+            f32x4 tot[GR][FN];
+            for (int sp = 0; sp < split_k; ++sp) {
+                const __amdgpu_buffer_rsrc_t r =
+                    __builtin_amdgcn_make_buffer_rsrc(part(sp), 0, part_bytes, kBufferWord3);
+#pragma unroll
+                for (int ii = 0; ii < GR; ++ii) {
+                    const int i = g + ii;
+                    if (i >= FM)
+                        break;
+                    const int m = m0 + wm * WTM + i * 16 + lrow;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
+                        f32x4 v = acc[i][j];           // this split's own partial
+                        if (sp != me && m < M) {
+                            if (vec4 && n + 3 < N) {
+                                v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  r, (m * N + n) * 4, 0, kDeviceScope));
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    v[q] = n + q < N ? __hip_atomic_load(part(sp) + (size_t)m * N + n + q,
+                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                     : 0.f;
+                            }
+                        }
+                        tot[ii][j] = sp == 0 ? v : tot[ii][j] + v;
+                    }
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < GR; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    if (g + ii < FM)
+                        acc[g + ii][j] = tot[ii][j];
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -366,12 +472,13 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
 hipError_t launch_tile_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                         int win_w, int chunk_c, hipStream_t stream)
+                         int win_w, int chunk_c, int split_k, float* ws, int* counters, hipStream_t stream)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED>), dim3(tiles_m * tiles_n),
-                       dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c);
+    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED>), dim3(tiles_m * tiles_n, split_k),
+                       dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c,
+                       split_k, ws, counters);
     return hipGetLastError();
 }
 
@@ -395,12 +502,14 @@ int tile_lds_bytes(int variant)
 }
 
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
-                       int M, int N, int K, int win_w, int chunk_c, hipStream_t stream)
+                       int M, int N, int K, int win_w, int chunk_c, int split_k, float* ws, int* counters,
+                       hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc) \
     if (v++ == variant)                        \
-        return launch_tile_t<bm, bn, bk, st, wm, wn, sc>(A, B, C, M, N, K, win_w, chunk_c, stream);
+        return launch_tile_t<bm, bn, bk, st, wm, wn, sc>(A, B, C, M, N, K, win_w, chunk_c, split_k, ws, counters, \
+                                                         stream);
     HKG_TILE_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
