@@ -13,6 +13,8 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                every launch streams B from HBM
   cpu_baseline the CPU oracle (fp64, OpenMP) on a bounded row sample of the
                square workload, scaled to TFLOP/s
+  vendor_context  torch.mm (hipBLASLt) on the same inputs with the same
+               timing, for comparison across machines whose clocks differ
 
 Progress and diagnostics go to stderr.  Timing uses HIP events on the stream
 the kernels are launched on (torch's current stream), bracketed by device
@@ -97,7 +99,11 @@ def bench_square(torch, hkg, steps, warmup):
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     log("square: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
-    return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan)
+    # Context only: the vendor library on the same inputs, same protocol.
+    ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup)
+    tflops_v = flops / (ms_v * 1e-3) / 1e12
+    log("square, torch.mm (hipBLASLt) for context: %.3f ms/step, %.1f TFLOP/s" % (ms_v, tflops_v))
+    return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v)
 
 
 def bench_decode(torch, hkg, steps, warmup):
@@ -140,8 +146,20 @@ def bench_decode(torch, hkg, steps, warmup):
     gbps_hot = alg_bytes / (ms_hot * 1e-3) / 1e9
     log("decode: %.2f us/call rotating (%.0f GB/s), %.2f us hot (%.0f GB/s)"
         % (ms_rot * 1e3, gbps, ms_hot * 1e3, gbps_hot))
+    # Context only: the vendor library over the same rotating buffers.
+    with torch.cuda.stream(stream):
+        for a, b, c in bufs:
+            torch.mm(a, b.t(), out=c)
+    torch.cuda.synchronize()
+    graph_v = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_v, stream=stream):
+        for a, b, c in bufs:
+            torch.mm(a, b.t(), out=c)
+    ms_v = time_launches(torch, graph_v.replay, reps, max(1, warmup // sets)) / sets
+    gbps_v = alg_bytes / (ms_v * 1e-3) / 1e9
+    log("decode, torch.mm (hipBLASLt) for context: %.2f us/call rotating (%.0f GB/s)" % (ms_v * 1e3, gbps_v))
     return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
-                alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets)
+                alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets, vendor_gbps=gbps_v)
 
 
 def calibration_copy(torch, mib=1024):
@@ -247,6 +265,9 @@ def main():
                    "rotating_sets": dec["sets"], "launches_timed": dec["launches"],
                    "llc_resident_gbps": round(dec["gbps_hot"], 1)},
         "cpu_baseline": cpu,
+        "vendor_context": {"library": "torch.mm (hipBLASLt), same inputs and timing in the same run",
+                           "square_tflops": round(sq["vendor_tflops"], 2),
+                           "decode_gbps": round(dec["vendor_gbps"], 1)},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -120,7 +120,8 @@ def test_plan_square_8192_geometry():
     assert (p.tile_m, p.tile_n, p.tile_k, p.waves) == (256, 256, 64, 8)
     assert p.grid_x == 1024 and p.block_x == 512
     assert p.xcd_window_w == 8 and p.xcd_chunk_c == 32
-    assert p.lds_bytes == 2 * (256 + 256) * 64 * 2
+    # ping-pong schedule: A halves double-, B triple-buffered
+    assert p.lds_bytes == (4 * 128 + 3 * 256) * 64 * 2
     assert p.workspace_bytes == 0 and p.split_k == 1
 
 

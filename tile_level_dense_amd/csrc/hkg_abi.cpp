@@ -142,6 +142,8 @@ void fill_resources(hkg_plan_t* p, const KernelResources* r)
     p->agprs = r->agprs;
     p->sgprs = r->sgprs;
     p->scratch_bytes = r->scratch;
+    if (r->lds >= 0)
+        p->lds_bytes = r->lds;          // the code object's figure (static LDS of the kernel)
 }
 
 hkg_status_t check_dims(int64_t M, int64_t N, int64_t K)

@@ -19,7 +19,7 @@ constexpr int TILE_NUM_VARIANTS = 0
     ;
 
 // Default tile ladder of the planner, largest first (variant indices).
-constexpr int TILE_LADDER[] = {0, 2, 3};
+constexpr int TILE_LADDER[] = {0, 1, 2};
 
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
 // rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.

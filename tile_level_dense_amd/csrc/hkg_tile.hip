@@ -124,10 +124,12 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
-    static_assert(STAGES * STAGE <= 160 * 1024, "LDS is 160 KiB per CU");
+    // SCHED 5 keeps A halves double-buffered and B triple-buffered.
+    constexpr int SMEM = SCHED == 5 ? 4 * (BM / 2) * RB + 3 * B_BYTES : STAGES * STAGE;
+    static_assert(SMEM <= 160 * 1024, "LDS is 160 KiB per CU");
     static_assert((STAGES - 2) * L <= 63, "vmcnt holds at most 63");
 
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -289,7 +291,7 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
             read_stage = read_stage + 1 == STAGES ? 0 : read_stage + 1;
             write_stage = write_stage + 1 == STAGES ? 0 : write_stage + 1;
         }
-    } else {
+    } else if constexpr (SCHED == 2) {
         // Register-pipelined loop.  Work proceeds in 32-k steps; the
         // fragments of step u + 1 are read from LDS while the MFMAs of step u
         // run.  Before the first read of a new stage every wave waits for its
@@ -348,6 +350,131 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
             }
         }
         // Leave no copy in flight into LDS that is about to be released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        // Ping-pong (HipKittens talk notes, section 2, 8-wave schedule).
+        // Waves 0-3 (group 0) and 4-7 (group 1) put one wave on each SIMD
+        // and alternate a memory phase (LDS fragment reads of a whole
+        // stage, plus copies) with a compute phase (the stage's MFMAs),
+        // phases separated by workgroup barriers.  Group 1 joins one extra
+        // barrier at the start, so the groups run half a stage apart and
+        // each SIMD's matrix unit is fed by one wave while the other reads.
+        // Every copy is issued in a memory phase: a copy that the vector
+        // memory path cannot take yet stalls its wave, and in a compute
+        // phase that would stall the MFMAs too.  That needs these buffer
+        // lifetimes: group g alone reads A rows 128 g .. 128 g + 127
+        // (double-buffered per group), both groups read B (triple-
+        // buffered); 160 KiB of LDS in all.
+        // Phase j lies between barriers j and j + 1; group 0 reads stage t
+        // in phase 2t and computes it in 2t + 1, group 1 reads it in
+        // 2t + 1 and computes it in 2t + 2.  Copies, A first:
+        //   group 0, phase 2t:     A rows 0-127 of stage t + 1, B rows
+        //                          0-127 of stage t + 2
+        //   group 1, phase 2t + 1: A rows 128-255 of stage t + 1, B rows
+        //                          128-255 of stage t + 2
+        // Each lands in a buffer whose last reader finished before the
+        // phase began.  A wave waits for its A copies at the end of its
+        // next compute phase and for its B copies one memory phase later
+        // (group 1) or one compute phase later (group 0): in every case
+        // before the first phase that reads them.
+        static_assert(SCHED == 5, "schedules 0, 1, 2 and 5");
+        static_assert(BM == 256 && BN == 256 && BK == 64 && NW == 8 && WM <= 4,
+                      "split-buffer ping-pong: 256 x 256 x 64 tile, 8 waves");
+        constexpr int HALF = 128 * RB;                  // 128 rows of one stage
+        constexpr int CPW = 128 / (RPW * 4);            // copies per half per wave
+        char* const a_buf = smem;                       // [group][stage % 2]
+        char* const b_buf = smem + 4 * HALF;            // [stage % 3]: rows 0-255
+        const int g = wave >> 2;
+        const int w4 = wave & 3;
+        // DMA source of this lane within a 128-row half (same swizzle rule
+        // as the copies above; a group's 4 waves fill 32 rows per round).
+        const int prow = w4 * RPW + lane / CPR;
+        const int pchunk = (lane % CPR) ^ ((prow / RPL) % CPR);
+        const uint32_t p_off = (uint32_t)(128 * g + prow) * row_bytes + (uint32_t)pchunk * 16u;
+        const int p_k = pchunk * 8;
+        const uint32_t p_step = (uint32_t)(4 * RPW) * row_bytes;
+        static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a group's copies");
+        auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t) {
+            const int k0 = kbase + t * BK;
+            const bool k_out = k0 + p_k >= k_lim;
+            const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * 2u;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (w4 + 4 * i) * 1024), 16,
+                                                         k_out ? kOutOfRange : off0 + (uint32_t)i * p_step, 0,
+                                                         0, 0);
+        };
+        auto copy_a = [&](int t) { copy_half(rsrc_a, a_buf + (2 * g + (t & 1)) * HALF, t); };
+        auto copy_b = [&](int t) { copy_half(rsrc_b, b_buf + (t % 3) * 2 * HALF + g * HALF, t); };
+        const int a_row = wm * WTM - 128 * g + lrow;    // row within the group's A half
+        const int b_row = wn * WTN + lrow;
+        bf16x8 af[KS][FM], bf[KS][FN];
+        auto read_stage = [&](int t) {
+            const char* ab = a_buf + (2 * g + (t & 1)) * HALF + a_row * RB;
+            const char* bb = b_buf + (t % 3) * 2 * HALF + b_row * RB;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    af[s][i] = *(const bf16x8*)(ab + i * 16 * RB + chunk_off[s]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + chunk_off[s]);
+            }
+        };
+        auto mfma_stage = [&]() {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                mfmas(af[s], bf[s]);
+        };
+        auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+        auto phase_barrier = [&]() {
+            fence();
+            asm volatile("s_barrier" ::: "memory");
+            fence();
+        };
+        const bool g1 = g == 1;
+        // Prologue: stage 0, and this group's B rows of stage 1.
+        copy_a(0);
+        copy_b(0);
+        copy_b(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+        phase_barrier();
+        if (!g1) {
+            for (int t = 0; t < nk; ++t) {
+                read_stage(t);                 // phase 2t: memory
+                fence();
+                copy_a(t + 1);
+                copy_b(t + 2);
+                fence();
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                phase_barrier();
+                mfma_stage();                  // phase 2t + 1: compute
+                fence();
+                // all but this phase's B copies: A of stage t + 1 and the
+                // B rows of stage t + 1 copied a memory phase earlier
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+                phase_barrier();
+            }
+        } else {
+            phase_barrier();                   // phase 0: group 0 reads stage 0
+            for (int t = 0; t < nk; ++t) {
+                read_stage(t);                 // phase 2t + 1: memory
+                fence();
+                copy_a(t + 1);
+                copy_b(t + 2);
+                fence();
+                // B rows of stage t + 1 (copied a memory phase earlier)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * CPW) : "memory");
+                phase_barrier();
+                mfma_stage();                  // phase 2t + 2: compute
+                fence();
+                // A of stage t + 1
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+                if (t + 1 < nk)
+                    phase_barrier();
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
@@ -498,6 +625,8 @@ TileShape tile_shape(int variant)
 int tile_lds_bytes(int variant)
 {
     const TileShape s = tile_shape(variant);
+    if (s.sched == 5)                   // A halves double-, B triple-buffered
+        return (4 * (s.bm / 2) + 3 * s.bn) * s.bk * 2;
     return s.stages * (s.bm + s.bn) * s.bk * 2;
 }
 

@@ -8,16 +8,18 @@
 //             32-k step interleaved with the MFMAs of the current one;
 //             2: fragment reads of the next 32-k step (also across stages)
 //             overlap the current MFMAs; branch-free ring with STAGES - 1
-//             copies ahead
+//             copies ahead; 5: ping-pong of two 4-wave groups (256 x 256 x
+//             64 tile, 8 waves; STAGES is not used), copies issued only in
+//             memory phases, A halves double- and B triple-buffered
 // The build script reads this list to map code objects to variants.
 #pragma once
 
 #define HKG_TILE_CONFIGS(X)       \
-    X(256, 256, 64, 2, 2, 4, 2)   \
-    X(256, 256, 64, 2, 4, 2, 2)   \
+    X(256, 256, 64, 2, 4, 2, 5)   \
     X(256, 128, 64, 2, 4, 2, 2)   \
     X(128, 128, 64, 2, 2, 2, 2)   \
     X(128, 128, 64, 2, 2, 2, 0)   \
+    X(256, 256, 64, 2, 2, 4, 2)   \
+    X(256, 256, 64, 2, 2, 4, 5)   \
     X(256, 256, 64, 2, 2, 4, 0)   \
-    X(256, 256, 64, 2, 4, 2, 1)   \
     X(256, 256, 32, 4, 2, 4, 2)
