@@ -52,6 +52,10 @@ def _bind(path):
     lib.hkg_oracle_gemm_entries.restype = None
     lib.hkg_oracle_max_threads.argtypes = []
     lib.hkg_oracle_max_threads.restype = ctypes.c_int
+    lib.hkg_oracle_activation.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.hkg_oracle_activation.restype = ctypes.c_double
+    lib.hkg_oracle_epilogue.argtypes = [f64p, u16p, i64, i64, i64p, ctypes.c_int, f64p, u16p]
+    lib.hkg_oracle_epilogue.restype = ctypes.c_int
     return lib
 
 
@@ -144,6 +148,42 @@ class Oracle:
         return C, S, absS
 
 
+    def activation(self, x, epilogue):
+        """act(x) in fp64 for one epilogue (x already includes the bias)."""
+        return float(self.lib.hkg_oracle_activation(float(x), EPILOGUES[epilogue]))
+
+    def epilogue(self, S, bias, epilogue, cols=None):
+        """Fused epilogue on unrounded sums (FlyDSL prebuilt kernels guide,
+        section 3.1): Y = act(S + bias[column]) in fp64 and its bf16 rounding.
+
+        S: sums, any shape; whole rows of an N-column C unless `cols` gives
+        each element's column.  bias: uint16 bf16 bits, one per column.
+        Returns (C bits uint16, Y float64), both shaped like S.
+        """
+        S = np.ascontiguousarray(S, dtype=np.float64)
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+        epi = EPILOGUES[epilogue]
+        N = bias.size
+        if cols is not None:
+            cols = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+            if cols.size != S.size or (cols.size and (cols.min() < 0 or cols.max() >= N)):
+                raise ValueError("column indices do not match S or bias")
+        elif epi != 0 and S.size and (S.ndim < 1 or S.shape[-1] != N):
+            raise ValueError("bias must hold one value per column")
+        C = np.zeros(S.shape, dtype=np.uint16)
+        Y = np.zeros(S.shape, dtype=np.float64)
+        if S.size:
+            rc = self.lib.hkg_oracle_epilogue(_ptr(S, ctypes.c_double), _ptr(bias, ctypes.c_uint16) if N else None,
+                                              S.size, max(N, 1), _ptr(cols, ctypes.c_int64),
+                                              epi, _ptr(Y, ctypes.c_double), _ptr(C, ctypes.c_uint16))
+            if rc != 0:
+                raise ValueError("unknown epilogue")
+        return C, Y
+
+
+# Fused epilogues by name (FlyDSL prebuilt kernels guide, section 3.1).
+EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
+
 _default = None
 
 
@@ -176,3 +216,11 @@ def gemm(A, B, rows=None, nthreads=0, want_sums=True):
 
 def gemm_entries(A, B, ii, jj, nthreads=0):
     return default().gemm_entries(A, B, ii, jj, nthreads)
+
+
+def activation(x, epilogue):
+    return default().activation(x, epilogue)
+
+
+def epilogue(S, bias, epilogue, cols=None):
+    return default().epilogue(S, bias, epilogue, cols)

@@ -34,7 +34,12 @@
  *   GEMM: all-ones (C = K), identity on either side (C = B^T, C = A),
  *   small-integer inputs against exact int64 products, exact-rational brute
  *   force on tiny shapes, and the fp64 summation error bound.
+ *   Epilogue: bias through all-ones products (C = K + b, exact), ReLU's
+ *   definition, the odd parts SiLU(x) - SiLU(-x) = x and GELU(x) - GELU(-x) = x,
+ *   the closed form sigmoid(ln 3) = 3/4, the normal quantile Phi(1.959963985)
+ *   = 0.975, and slopes 1/2 at 0.
  */
+#define _DEFAULT_SOURCE  /* M_SQRT1_2 under -std=c11 */
 #include <stdint.h>
 #include <math.h>
 #include <string.h>
@@ -171,3 +176,61 @@ void hkg_oracle_gemm_entries(const uint16_t* A, const uint16_t* B,
 }
 
 int hkg_oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* ---- fused epilogue ------------------------------------------------------
+ * The FlyDSL "prebuilt_kernels_guide" page (section 3.1, Preshuffle GEMM,
+ * parameter `epilogue`) lists the fused epilogues "none", "bias",
+ * "bias_relu", "bias_silu" and "bias_gelu", with the bias one value per
+ * output column in the output dtype.  Read plainly, on the unrounded sum S:
+ *
+ *   x = S[i][j] + bias[j]                   (bf16 bias, widened exactly)
+ *   y = x                                   bias
+ *       x if x > 0, else +0                 bias_relu
+ *       x * sigmoid(x) = x / (1 + e^-x)     bias_silu
+ *       x * Phi(x) = x * erfc(-x/sqrt 2)/2  bias_gelu (Phi: standard normal
+ *                                            CDF; erfc keeps the left tail
+ *                                            accurate)
+ *   C[i][j] = bf16 nearest-even rounding of y, once.
+ *
+ * "none" is the plain GEMM: y = S, bias unused.  All in fp64.
+ */
+enum { HKG_ORACLE_EPI_NONE = 0, HKG_ORACLE_EPI_BIAS = 1, HKG_ORACLE_EPI_BIAS_RELU = 2,
+       HKG_ORACLE_EPI_BIAS_SILU = 3, HKG_ORACLE_EPI_BIAS_GELU = 4 };
+
+double hkg_oracle_activation(double x, int epi)
+{
+    switch (epi) {
+    case HKG_ORACLE_EPI_BIAS_RELU:
+        return x > 0.0 ? x : 0.0;
+    case HKG_ORACLE_EPI_BIAS_SILU:
+        return x / (1.0 + exp(-x));
+    case HKG_ORACLE_EPI_BIAS_GELU:
+        return 0.5 * x * erfc(-x * M_SQRT1_2);
+    default:
+        return x;
+    }
+}
+
+/*
+ * count results with sums S[t]; element t belongs to output column cols[t]
+ * (cols NULL: column t mod N, i.e. whole rows of an N-column C).  Writes the
+ * unrounded epilogue value Y[t] (may be NULL) and its bf16 rounding C[t].
+ * Returns -1 for an unknown epilogue, else 0.
+ */
+int hkg_oracle_epilogue(const double* S, const uint16_t* bias, int64_t count, int64_t N,
+                        const int64_t* cols, int epi, double* Y, uint16_t* C)
+{
+    if (epi < HKG_ORACLE_EPI_NONE || epi > HKG_ORACLE_EPI_BIAS_GELU)
+        return -1;
+    for (int64_t t = 0; t < count; ++t) {
+        double y = S[t];
+        if (epi != HKG_ORACLE_EPI_NONE) {
+            const int64_t j = cols ? cols[t] : t % N;
+            y = hkg_oracle_activation(S[t] + hkg_oracle_bf16_value(bias[j]), epi);
+        }
+        if (Y)
+            Y[t] = y;
+        C[t] = hkg_oracle_bf16_rne(y);
+    }
+    return 0;
+}

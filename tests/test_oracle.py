@@ -14,6 +14,8 @@ import shutil
 import tempfile
 from fractions import Fraction
 
+import math
+
 import numpy as np
 import pytest
 
@@ -163,10 +165,85 @@ def check_transpose_symmetry(O):
     assert np.array_equal(S3, -S1)
 
 
+# ---------------------------------------------------------------- epilogue
+# Fused epilogues of the FlyDSL prebuilt kernels guide (section 3.1): bias
+# per column, then ReLU, SiLU or GELU, on the unrounded sum, rounded once.
+
+def check_epilogue_bias_exact(O):
+    # All-ones operands make S = K exactly; x = K + b is then known exactly
+    # in rationals (fp64 holds it to one rounding) and the results are known
+    # in closed form for bias and ReLU: C = round(K + b), round(max(K + b, 0)).
+    K = 256
+    A = np.full((3, K), 0x3F80, dtype=np.uint16)
+    B = np.full((7, K), 0x3F80, dtype=np.uint16)
+    bvals = [-300.0, -256.0, -0.5, 0.0, 1.0, 3.5, 2.0 ** -130]
+    bias = workloads.f32_to_bf16_bits(np.array(bvals, dtype=np.float32))
+    bias[3] = 0x8000                                  # -0 adds nothing
+    _, S, _ = O.gemm(A, B)
+    xs = [Fraction(K) + Fraction(float(v)) for v in exact.widen(bias).tolist()]
+    C, Y = O.epilogue(S, bias, "bias")
+    ulp = Fraction(2) ** -52
+    for j, x in enumerate(xs):
+        assert abs(Fraction(Y[0, j]) - x) <= ulp * abs(x) and C[1, j] == exact.round_exact(x), j
+    C, Y = O.epilogue(S, bias, "bias_relu")
+    for j, x in enumerate(xs):
+        want = x if x > 0 else Fraction(0)
+        assert abs(Fraction(Y[2, j]) - want) <= ulp * want and C[2, j] == exact.round_exact(want), j
+    assert C[0, 1] == 0x0000                          # relu(0) is +0
+    C0, Y0 = O.epilogue(S, bias, "none")              # plain GEMM: bias unused
+    assert np.all(Y0 == K) and np.all(C0 == exact.round_exact(K))
+
+
+def check_epilogue_closed_forms(O):
+    # sigmoid(ln 3) = 3/4 exactly, so SiLU(ln 3) = (3/4) ln 3; the 0.975
+    # quantile of the standard normal, 1.959963984540054, gives
+    # GELU(q) = 0.975 q; both activations have slope 1/2 at 0.
+    l3 = math.log(3.0)
+    assert abs(O.activation(l3, "bias_silu") - 0.75 * l3) <= 1e-15
+    q = 1.959963984540054
+    assert abs(O.activation(q, "bias_gelu") - 0.975 * q) <= 1e-14
+    assert abs(O.activation(-q, "bias_gelu") + 0.025 * q) <= 1e-14
+    for name in ("bias_silu", "bias_gelu"):
+        h = 1e-9
+        assert abs(O.activation(h, name) / h - 0.5) <= 1e-8, name
+        assert O.activation(0.0, name) == 0.0
+    assert O.activation(-2.5, "bias_relu") == 0.0 and O.activation(2.5, "bias_relu") == 2.5
+    assert O.activation(-2.5, "bias") == -2.5
+
+
+def check_epilogue_odd_parts(O):
+    # x sigmoid(x) - (-x) sigmoid(-x) = x and x Phi(x) - (-x) Phi(-x) = x.
+    for x in (0.125, 0.5, 1.0, 2.5, 7.0, 20.0, 40.0):
+        for name in ("bias_silu", "bias_gelu"):
+            d = O.activation(x, name) - O.activation(-x, name)
+            assert abs(d - x) <= 4e-16 * x, (name, x, d)
+    # the far left tail stays a tiny negative number, not a cancellation zero
+    g = O.activation(-10.0, "bias_gelu")
+    assert -1e-21 < g < -1e-24
+
+
+def check_epilogue_columns(O):
+    # One bias value per column: row layout and explicit column indices agree,
+    # and a column shift is visible.
+    rng = np.random.default_rng(21)
+    S = rng.normal(0.0, 3.0, size=(5, 9))
+    bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 1.0, size=9).astype(np.float32))
+    for name in ("bias", "bias_relu", "bias_silu", "bias_gelu"):
+        C, Y = O.epilogue(S, bias, name)
+        jj = np.tile(np.arange(9), 5)
+        Ce, Ye = O.epilogue(S.ravel(), bias, name, cols=jj)
+        assert np.array_equal(Ce, C.ravel()) and np.array_equal(Ye, Y.ravel())
+        for j in (0, 4, 8):
+            x = S[2, j] + float(exact.widen(bias[j]))
+            assert Y[2, j] == O.activation(x, name)
+            assert C[2, j] == O.bf16_rne(Y[2, j])
+
+
 ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
               check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
               check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
-              check_transpose_symmetry]
+              check_transpose_symmetry, check_epilogue_bias_exact, check_epilogue_closed_forms,
+              check_epilogue_odd_parts, check_epilogue_columns]
 
 
 @pytest.fixture(scope="module")
@@ -226,6 +303,18 @@ MUTANTS = {
                       "mag = ldexp(1.0 + (double)f / 128.0, e - 126);"),
     "negative_zero_sign": ("uint16_t sign = signbit(x) ? 0x8000 : 0;",
                            "uint16_t sign = (x < 0) ? 0x8000 : 0;"),
+    "relu_as_abs": ("return x > 0.0 ? x : 0.0;", "return fabs(x);"),
+    "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    "gelu_tanh_form": ("return 0.5 * x * erfc(-x * M_SQRT1_2);",
+                       "return 0.5 * x * (1.0 + tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)));"),
+    "gelu_wrong_tail": ("return 0.5 * x * erfc(-x * M_SQRT1_2);", "return 0.5 * x * erfc(x * M_SQRT1_2);"),
+    "gelu_no_half": ("return 0.5 * x * erfc(-x * M_SQRT1_2);", "return x * erfc(-x * M_SQRT1_2);"),
+    "gelu_cancelling_tail": ("return 0.5 * x * erfc(-x * M_SQRT1_2);",
+                             "return 0.5 * x * (1.0 + erf(x * M_SQRT1_2));"),
+    "bias_after_activation": ("y = hkg_oracle_activation(S[t] + hkg_oracle_bf16_value(bias[j]), epi);",
+                              "y = hkg_oracle_activation(S[t], epi) + hkg_oracle_bf16_value(bias[j]);"),
+    "bias_shifted_column": ("const int64_t j = cols ? cols[t] : t % N;",
+                            "const int64_t j = cols ? cols[t] : (t + 1) % N;"),
 }
 
 
