@@ -13,6 +13,8 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                every launch streams B from HBM
   cpu_baseline the CPU oracle (fp64, OpenMP) on a bounded row sample of the
                square workload, scaled to TFLOP/s
+  epilogue     the same two workloads with a fused bias + GELU (square) and
+               bias + SiLU (decode) epilogue
   vendor_context  torch.mm (hipBLASLt) on the same inputs with the same
                timing, for comparison across machines whose clocks differ
 
@@ -99,11 +101,17 @@ def bench_square(torch, hkg, steps, warmup):
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     log("square: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
+    # Fused epilogue (bias + GELU, one bias value per column) on the same
+    # inputs: its cost over the plain GEMM.
+    bias = torch.linspace(-1.0, 1.0, N, device="cuda").to(torch.bfloat16)
+    ms_e = time_launches(torch, lambda: hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_gelu"), steps, warmup)
+    log("square with bias+GELU epilogue: %.3f ms/step, %.1f TFLOP/s" % (ms_e, flops / (ms_e * 1e-3) / 1e12))
     # Context only: the vendor library on the same inputs, same protocol.
     ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup)
     tflops_v = flops / (ms_v * 1e-3) / 1e12
     log("square, torch.mm (hipBLASLt) for context: %.3f ms/step, %.1f TFLOP/s" % (ms_v, tflops_v))
-    return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v)
+    return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v,
+                epi_ms=ms_e, epi_tflops=flops / (ms_e * 1e-3) / 1e12)
 
 
 def bench_decode(torch, hkg, steps, warmup):
@@ -144,6 +152,19 @@ def bench_decode(torch, hkg, steps, warmup):
     ms_hot = time_launches(torch, graph_hot.replay, reps, max(1, warmup // sets)) / sets
     gbps = alg_bytes / (ms_rot * 1e-3) / 1e9
     gbps_hot = alg_bytes / (ms_hot * 1e-3) / 1e9
+    # Fused bias + SiLU epilogue over the same rotating buffers.
+    bias = torch.linspace(-1.0, 1.0, N, device="cuda").to(torch.bfloat16)
+    with torch.cuda.stream(stream):
+        for a, b, c in bufs:
+            hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_silu")
+    torch.cuda.synchronize()
+    graph_e = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_e, stream=stream):
+        for a, b, c in bufs:
+            hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_silu")
+    ms_e = time_launches(torch, graph_e.replay, reps, max(1, warmup // sets)) / sets
+    log("decode with bias+SiLU epilogue: %.2f us/call rotating (%.0f GB/s)"
+        % (ms_e * 1e3, (alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9))
     log("decode: %.2f us/call rotating (%.0f GB/s), %.2f us hot (%.0f GB/s)"
         % (ms_rot * 1e3, gbps, ms_hot * 1e3, gbps_hot))
     # Context only: the vendor library over the same rotating buffers.
@@ -159,7 +180,8 @@ def bench_decode(torch, hkg, steps, warmup):
     gbps_v = alg_bytes / (ms_v * 1e-3) / 1e9
     log("decode, torch.mm (hipBLASLt) for context: %.2f us/call rotating (%.0f GB/s)" % (ms_v * 1e3, gbps_v))
     return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
-                alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets, vendor_gbps=gbps_v)
+                alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets, vendor_gbps=gbps_v,
+                epi_ms=ms_e, epi_gbps=(alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9)
 
 
 def calibration_copy(torch, mib=1024):
@@ -200,7 +222,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~75 ms of warm-up at 8192^3: the engine clock settles under sustained
+    # MFMA load within a few tens of launches; shorter warm-ups time the ramp.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
     ap.add_argument("--only", choices=["square", "decode"], help="time one leg only (profiler runs)")
@@ -265,6 +289,11 @@ def main():
                    "rotating_sets": dec["sets"], "launches_timed": dec["launches"],
                    "llc_resident_gbps": round(dec["gbps_hot"], 1)},
         "cpu_baseline": cpu,
+        "epilogue": {"square_bias_gelu_tflops": round(sq["epi_tflops"], 2),
+                     "square_bias_gelu_ms": round(sq["epi_ms"], 4),
+                     "decode_bias_silu_gbps": round(dec["epi_gbps"], 1),
+                     "decode_bias_silu_us": round(dec["epi_ms"] * 1e3, 3),
+                     "note": "fused bias + activation (FlyDSL guide epilogues); decode bytes include the bias"},
         "vendor_context": {"library": "torch.mm (hipBLASLt), same inputs and timing in the same run",
                            "square_tflops": round(sq["vendor_tflops"], 2),
                            "decode_gbps": round(dec["vendor_gbps"], 1)},

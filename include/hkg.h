@@ -67,8 +67,28 @@ typedef enum {
     HKG_KERNEL_TILE = 1,        /* large-tile MFMA kernel (compute-bound shapes) */
     HKG_KERNEL_SKINNY = 2,      /* small M: streams B once, split-K over waves / workgroups */
     HKG_KERNEL_GENERIC = 3,     /* any alignment, any K: correctness fallback */
-    HKG_KERNEL_ZERO = 4         /* K == 0: C is filled with +0 (the empty sum) */
+    HKG_KERNEL_ZERO = 4         /* K == 0: C is the empty sum, +0 (then the epilogue) */
 } hkg_kernel_t;
+
+/*
+ * Fused epilogues, applied to the fp32 sum before the one rounding to bf16
+ * (the list of the FlyDSL "Prebuilt kernels guide", section 3.1, Preshuffle
+ * GEMM, parameter `epilogue`; its bias holds one value per output column in
+ * the output dtype):  x = sum + bias[n] and
+ *   BIAS       y = x
+ *   BIAS_RELU  y = x if x > 0, else +0
+ *   BIAS_SILU  y = x / (1 + exp(-x))
+ *   BIAS_GELU  y = x * Phi(x), Phi the standard normal CDF (exact GELU,
+ *              evaluated as x/2 * erfc(-x / sqrt 2))
+ * then C[m][n] = bf16 nearest-even rounding of y.  NONE is the plain GEMM.
+ */
+typedef enum {
+    HKG_EPILOGUE_NONE = 0,
+    HKG_EPILOGUE_BIAS = 1,
+    HKG_EPILOGUE_BIAS_RELU = 2,
+    HKG_EPILOGUE_BIAS_SILU = 3,
+    HKG_EPILOGUE_BIAS_GELU = 4
+} hkg_epilogue_t;
 
 /*
  * A launch plan.  Plain data owned by the caller.  hkg_gemm_bf16_plan fills
@@ -117,13 +137,34 @@ hkg_status_t hkg_gemm_bf16_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out
 /*
  * Runs `plan` on (A, B, C).  M, N, K must equal plan->M, N, K.  A fast-kernel
  * plan on unaligned pointers or K % 8 != 0 returns HKG_ERR_MISALIGNED; an
- * edited plan outside the ranges hkg_gemm_bf16_plan produces returns
+ * edited plan outside the ranges the library supports returns
  * HKG_ERR_UNSUPPORTED.  Edits that are accepted: xcd_window_w >= 0,
- * xcd_chunk_c >= 0, kernel_id GENERIC for any shape, split_k for SKINNY
- * within [1, 64].
+ * xcd_chunk_c >= 0; kernel_id GENERIC for any shape; kernel_id TILE with any
+ * tile variant (tile_m/tile_n/tile_k/waves matching it) and split_k in
+ * [1, 16] (above 1 only for variants of at most 16 accumulator blocks per
+ * wave and M * N < 2^29); kernel_id SKINNY with a variant whose rows cover M
+ * and split_k in [1, 64].
  */
 hkg_status_t hkg_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B,
                                     void* C, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * C = epilogue(A * B^T + bias) (hkg_epilogue_t above), on `stream`, with the
+ * plan and fallbacks of hkg_gemm_bf16; HKG_EPILOGUE_NONE is exactly
+ * hkg_gemm_bf16.  bias: device pointer to N bf16 values (one per column of
+ * C), caller-owned, 2-byte aligned, not overlapping C; unused (may be NULL)
+ * for HKG_EPILOGUE_NONE.  K == 0 gives C = epilogue(bias).
+ * Errors, before any device work: an unknown epilogue code, a NULL bias
+ * with another code, or bias overlapping C -> HKG_ERR_INVALID_ARG; bias at
+ * an odd address -> HKG_ERR_MISALIGNED.
+ */
+hkg_status_t hkg_gemm_bf16_epilogue(const void* A, const void* B, const void* bias, void* C,
+                                    int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream);
+
+/* hkg_gemm_bf16_run_plan with a fused epilogue (arguments as above). */
+hkg_status_t hkg_gemm_bf16_run_plan_epilogue(const hkg_plan_t* plan, const void* A, const void* B,
+                                             const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                                             int32_t epilogue, void* stream);
 
 /* Static description of a status code. */
 const char* hkg_status_string(hkg_status_t status);

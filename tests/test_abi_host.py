@@ -188,6 +188,37 @@ def test_argument_errors_precede_device_work():
     assert hkg.hkg_gemm_bf16(None, 4096, None, 0, 64, 64) == hkg.HKG_OK
 
 
+def test_epilogue_errors_precede_device_work():
+    M, N, K = 64, 64, 64
+    A, B, C = 1 << 30, (1 << 30) + (1 << 22), (1 << 30) + (1 << 23)
+    bias = (1 << 30) + (1 << 24)
+    # unknown codes
+    for code in (-1, 5, 99):
+        assert hkg.hkg_gemm_bf16_epilogue(A, B, bias, C, M, N, K, code) == hkg.HKG_ERR_INVALID_ARG
+    # a bias is needed for every code but none
+    for code in (1, 2, 3, 4):
+        assert hkg.hkg_gemm_bf16_epilogue(A, B, None, C, M, N, K, code) == hkg.HKG_ERR_INVALID_ARG
+    # bias overlapping C, bias at an odd address
+    assert hkg.hkg_gemm_bf16_epilogue(A, B, C + 128, C, M, N, K, 1) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_gemm_bf16_epilogue(A, B, bias + 1, C, M, N, K, 1) == hkg.HKG_ERR_MISALIGNED
+    # empty output: nothing to do, any bias
+    assert hkg.hkg_gemm_bf16_epilogue(None, 4096, None, None, 0, 8, 8, 4) == hkg.HKG_OK
+    # the same checks on the plan path
+    p = hkg.plan(M, N, K)
+    assert hkg.hkg_gemm_bf16_run_plan_epilogue(p, A, B, None, C, M, N, K, 2) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_gemm_bf16_run_plan_epilogue(p, A, B, bias, C, M, N, K, 7) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.EPILOGUES == {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="a GPU is present")
+def test_epilogue_calls_report_no_device():
+    M, N, K = 64, 64, 64
+    A, B, C = 1 << 30, (1 << 30) + (1 << 22), (1 << 30) + (1 << 23)
+    bias = (1 << 30) + (1 << 24)
+    assert hkg.hkg_gemm_bf16_epilogue(A, B, bias, C, M, N, K, 3) == hkg.HKG_ERR_NO_DEVICE
+    assert hkg.hkg_gemm_bf16_epilogue(A, B, None, C, M, N, K, 0) == hkg.HKG_ERR_NO_DEVICE
+
+
 def test_run_plan_errors_precede_device_work():
     M, N, K = 512, 512, 512
     p = hkg.plan(M, N, K)

@@ -2,9 +2,11 @@
 
 Argument marshalling only: every step of the GEMM runs in the library's HIP
 kernels.  The binding uses ctypes and mirrors the C ABI of include/hkg.h with
-the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_plan``,
-``hkg_gemm_bf16_run_plan``, ``hkg_status_string``); ``gemm`` is the
-torch-facing convenience wrapper.  torch supplies device memory and streams.
+the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_epilogue``,
+``hkg_gemm_bf16_plan``, ``hkg_gemm_bf16_run_plan``,
+``hkg_gemm_bf16_run_plan_epilogue``, ``hkg_status_string``); ``gemm`` is the
+torch-facing convenience wrapper (with ``bias=`` and ``epilogue=`` for the
+fused epilogues).  torch supplies device memory and streams.
 
 There is no fallback: if the library is not built and cannot be built, or a
 call fails, an exception is raised.
@@ -12,9 +14,10 @@ call fails, an exception is raised.
 import ctypes
 import os
 
-__all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_plan", "hkg_gemm_bf16_run_plan",
-           "hkg_status_string", "hkg_last_hip_error", "gemm", "plan", "run_plan", "library_path",
-           "EXPORTED_SYMBOLS", "KERNEL_NAMES"]
+__all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_plan",
+           "hkg_gemm_bf16_run_plan", "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string",
+           "hkg_last_hip_error", "gemm", "plan", "run_plan", "library_path", "EXPORTED_SYMBOLS",
+           "KERNEL_NAMES", "EPILOGUES"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -33,8 +36,12 @@ HKG_ERR_WORKSPACE = -7
 KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO"}
 HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO = range(5)
 
-EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_plan", "hkg_gemm_bf16_run_plan",
-                    "hkg_status_string", "hkg_last_hip_error", "hkg_abi_version"]
+# hkg_epilogue_t codes by the FlyDSL guide's names
+EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
+
+EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_plan", "hkg_gemm_bf16_run_plan",
+                    "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string", "hkg_last_hip_error",
+                    "hkg_abi_version"]
 
 
 class Plan(ctypes.Structure):
@@ -100,6 +107,11 @@ def _load():
     lib.hkg_gemm_bf16_plan.restype = ctypes.c_int
     lib.hkg_gemm_bf16_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, i64, i64, i64, vp]
     lib.hkg_gemm_bf16_run_plan.restype = ctypes.c_int
+    lib.hkg_gemm_bf16_epilogue.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, vp]
+    lib.hkg_gemm_bf16_epilogue.restype = ctypes.c_int
+    lib.hkg_gemm_bf16_run_plan_epilogue.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, i64, i64, i64,
+                                                    ctypes.c_int32, vp]
+    lib.hkg_gemm_bf16_run_plan_epilogue.restype = ctypes.c_int
     lib.hkg_status_string.argtypes = [ctypes.c_int]
     lib.hkg_status_string.restype = ctypes.c_char_p
     lib.hkg_last_hip_error.argtypes = []
@@ -131,6 +143,16 @@ def hkg_gemm_bf16_plan(M, N, K):
 
 def hkg_gemm_bf16_run_plan(plan_, A, B, C, M, N, K, stream=None):
     return _load().hkg_gemm_bf16_run_plan(ctypes.byref(plan_), A, B, C, M, N, K, stream)
+
+
+def hkg_gemm_bf16_epilogue(A, B, bias, C, M, N, K, epilogue, stream=None):
+    """C-ABI call with raw device addresses (ints) and an epilogue code."""
+    return _load().hkg_gemm_bf16_epilogue(A, B, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_bf16_run_plan_epilogue(plan_, A, B, bias, C, M, N, K, epilogue, stream=None):
+    return _load().hkg_gemm_bf16_run_plan_epilogue(ctypes.byref(plan_), A, B, bias, C, M, N, K, epilogue,
+                                                   stream)
 
 
 def hkg_status_string(status):
@@ -170,17 +192,34 @@ def _check(a, b, out):
     return M, N, K
 
 
-def gemm(a, b, out=None, stream=None):
-    """C = a @ b.T for bf16 device tensors a (M x K) and b (N x K)."""
+def _epilogue_args(a, N, bias, epilogue):
+    import torch
+    code = EPILOGUES[epilogue]
+    if code == 0:
+        return 0, 0
+    if bias is None or bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,) or not bias.is_contiguous() \
+            or bias.device != a.device:
+        raise ValueError("epilogue %r needs a contiguous bf16 bias of %d values on A's device" % (epilogue, N))
+    return bias.data_ptr(), code
+
+
+def gemm(a, b, out=None, stream=None, bias=None, epilogue="none"):
+    """C = epilogue(a @ b.T + bias) for bf16 device tensors a (M x K), b (N x K)
+    and bias (N); epilogue one of EPILOGUES ("none" ignores bias)."""
     import torch
     M, N, K = _check(a, b, out)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     with torch.cuda.device(a.device):
-        st = _load().hkg_gemm_bf16(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
-                                   _stream_handle(stream, a.device))
+        if code == 0:
+            st = _load().hkg_gemm_bf16(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                                       _stream_handle(stream, a.device))
+        else:
+            st = _load().hkg_gemm_bf16_epilogue(a.data_ptr(), b.data_ptr(), bias_ptr, out.data_ptr(), M, N, K,
+                                                code, _stream_handle(stream, a.device))
     if st != HKG_OK:
-        raise HkgError(st, "hkg_gemm_bf16")
+        raise HkgError(st, "hkg_gemm_bf16" if code == 0 else "hkg_gemm_bf16_epilogue")
     return out
 
 
@@ -191,14 +230,20 @@ def plan(M, N, K):
     return p
 
 
-def run_plan(plan_, a, b, out=None, stream=None):
+def run_plan(plan_, a, b, out=None, stream=None, bias=None, epilogue="none"):
     import torch
     M, N, K = _check(a, b, out)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     with torch.cuda.device(a.device):
-        st = _load().hkg_gemm_bf16_run_plan(ctypes.byref(plan_), a.data_ptr(), b.data_ptr(),
-                                            out.data_ptr(), M, N, K, _stream_handle(stream, a.device))
+        if code == 0:
+            st = _load().hkg_gemm_bf16_run_plan(ctypes.byref(plan_), a.data_ptr(), b.data_ptr(),
+                                                out.data_ptr(), M, N, K, _stream_handle(stream, a.device))
+        else:
+            st = _load().hkg_gemm_bf16_run_plan_epilogue(ctypes.byref(plan_), a.data_ptr(), b.data_ptr(), bias_ptr,
+                                                         out.data_ptr(), M, N, K, code,
+                                                         _stream_handle(stream, a.device))
     if st != HKG_OK:
-        raise HkgError(st, "hkg_gemm_bf16_run_plan")
+        raise HkgError(st, "hkg_gemm_bf16_run_plan" if code == 0 else "hkg_gemm_bf16_run_plan_epilogue")
     return out

@@ -103,16 +103,18 @@ def _table(resources):
     skinny = [None] * len(SKINNY_VARIANTS)
     generic = None
     for mangled, r in resources.items():
-        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", mangled)
+        # The table holds the plain instantiations (no fused epilogue); the
+        # gate below checks every kernel, epilogue instantiations included.
+        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", mangled)
         if m:
-            key = tuple(int(g) for g in m.groups())
-            if key in TILE_VARIANTS:
+            key = tuple(int(g) for g in m.groups()[:7])
+            if key in TILE_VARIANTS and m.group(8) == "0":
                 tile[TILE_VARIANTS.index(key)] = _entry("tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
-        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", mangled)
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", mangled)
         if m:
-            key = tuple(int(g) for g in m.groups())
-            if key in SKINNY_VARIANTS:
+            key = tuple(int(g) for g in m.groups()[:5])
+            if key in SKINNY_VARIANTS and m.group(6) == "0":
                 skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_n%d_w%d_u%d_c%d" % ((16 * key[0], 16 * key[1]) + key[2:]), r)
             continue
         if "generic_kernel" in mangled:
@@ -157,7 +159,7 @@ def build(verbose=False):
     for _, r in results:
         res.update(r)
     tile, skinny, generic = _table(res)
-    _gate(tile + skinny + [generic])
+    _gate([_entry(name, r) for name, r in res.items()])
     _write_inc(tile, skinny, generic)
     with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
         objs += [f.result()[0] for f in [ex.submit(_compile, s, False) for s in HOST_SOURCES]]

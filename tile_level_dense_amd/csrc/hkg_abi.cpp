@@ -394,7 +394,8 @@ bool plan_matches_library(const hkg_plan_t* p)
     }
 }
 
-hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hipStream_t stream)
+hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, const uint16_t* bias, int epi,
+                 hipStream_t stream)
 {
     const int64_t M = p->M, N = p->N, K = p->K;
     if (p->kernel_id == HKG_KERNEL_NONE)
@@ -409,10 +410,10 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hip
     hipError_t e = hipSuccess;
     switch (p->kernel_id) {
     case HKG_KERNEL_ZERO:
-        e = launch_zero(c, M * N, stream);
+        e = launch_zero(c, M, N, bias, epi, stream);
         break;
     case HKG_KERNEL_GENERIC:
-        e = launch_generic(a, b, c, M, N, K, stream);
+        e = launch_generic(a, b, c, M, N, K, bias, epi, stream);
         break;
     case HKG_KERNEL_TILE: {
         float* ws = nullptr;
@@ -424,7 +425,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hip
                 return st;
         }
         e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c,
-                        p->split_k, ws, counters, stream);
+                        p->split_k, ws, counters, bias, epi, stream);
         break;
     }
     case HKG_KERNEL_SKINNY: {
@@ -436,7 +437,8 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, hip
             if (st != HKG_OK)
                 return st;
         }
-        e = launch_skinny(p->variant, a, b, c, (int)M, (int)N, (int)K, p->split_k, ws, counters, stream);
+        e = launch_skinny(p->variant, a, b, c, (int)M, (int)N, (int)K, p->split_k, ws, counters, bias, epi,
+                          stream);
         break;
     }
     default:
@@ -463,6 +465,66 @@ struct Cleanup {
     }
 } g_cleanup;
 
+// Epilogue arguments: a known code, and for every code but NONE a bias of N
+// bf16 values that is 2-byte aligned and does not overlap C.
+hkg_status_t check_epilogue(const void* bias, const void* C, int64_t M, int64_t N, int32_t epi)
+{
+    if (epi < HKG_EPILOGUE_NONE || epi > HKG_EPILOGUE_BIAS_GELU)
+        return HKG_ERR_INVALID_ARG;
+    if (epi == HKG_EPILOGUE_NONE || M == 0 || N == 0)
+        return HKG_OK;
+    if (!bias)
+        return HKG_ERR_INVALID_ARG;
+    if (overlaps(C, 2 * M * N, bias, 2 * N))
+        return HKG_ERR_INVALID_ARG;
+    if (((uintptr_t)bias & 1u) != 0)
+        return HKG_ERR_MISALIGNED;
+    return HKG_OK;
+}
+
+hkg_status_t gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                  int32_t epi, void* stream)
+{
+    hkg_plan_t p;
+    hkg_status_t st = make_plan(M, N, K, &p);
+    if (st != HKG_OK)
+        return st;
+    st = check_pointers(A, B, C, M, N, K);
+    if (st != HKG_OK)
+        return st;
+    st = check_epilogue(bias, C, M, N, epi);
+    if (st != HKG_OK)
+        return st;
+    if ((p.kernel_id == HKG_KERNEL_TILE || p.kernel_id == HKG_KERNEL_SKINNY) &&
+        !(aligned16(A) && aligned16(B) && aligned16(C)))
+        plan_generic(M, N, &p, "pointers not 16-byte aligned");
+    return run(&p, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
+}
+
+hkg_status_t run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* bias, void* C,
+                      int64_t M, int64_t N, int64_t K, int32_t epi, void* stream)
+{
+    if (!plan || plan->abi_version != HKG_ABI_VERSION)
+        return HKG_ERR_INVALID_ARG;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (plan->M != M || plan->N != N || plan->K != K)
+        return HKG_ERR_INVALID_ARG;
+    st = check_pointers(A, B, C, M, N, K);
+    if (st != HKG_OK)
+        return st;
+    st = check_epilogue(bias, C, M, N, epi);
+    if (st != HKG_OK)
+        return st;
+    if (!plan_matches_library(plan))
+        return HKG_ERR_UNSUPPORTED;
+    if ((plan->kernel_id == HKG_KERNEL_TILE || plan->kernel_id == HKG_KERNEL_SKINNY) &&
+        !(aligned16(A) && aligned16(B) && aligned16(C)))
+        return HKG_ERR_MISALIGNED;
+    return run(plan, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
+}
+
 }  // namespace
 }  // namespace hkg
 
@@ -480,38 +542,26 @@ hkg_status_t hkg_gemm_bf16_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out
 hkg_status_t hkg_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                            void* stream)
 {
-    hkg_plan_t p;
-    hkg_status_t st = make_plan(M, N, K, &p);
-    if (st != HKG_OK)
-        return st;
-    st = check_pointers(A, B, C, M, N, K);
-    if (st != HKG_OK)
-        return st;
-    if ((p.kernel_id == HKG_KERNEL_TILE || p.kernel_id == HKG_KERNEL_SKINNY) &&
-        !(aligned16(A) && aligned16(B) && aligned16(C)))
-        plan_generic(M, N, &p, "pointers not 16-byte aligned");
-    return run(&p, A, B, C, (hipStream_t)stream);
+    return gemm(A, B, nullptr, C, M, N, K, HKG_EPILOGUE_NONE, stream);
+}
+
+hkg_status_t hkg_gemm_bf16_epilogue(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                                    int64_t N, int64_t K, int32_t epilogue, void* stream)
+{
+    return gemm(A, B, bias, C, M, N, K, epilogue, stream);
 }
 
 hkg_status_t hkg_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B, void* C,
                                     int64_t M, int64_t N, int64_t K, void* stream)
 {
-    if (!plan || plan->abi_version != HKG_ABI_VERSION)
-        return HKG_ERR_INVALID_ARG;
-    hkg_status_t st = check_dims(M, N, K);
-    if (st != HKG_OK)
-        return st;
-    if (plan->M != M || plan->N != N || plan->K != K)
-        return HKG_ERR_INVALID_ARG;
-    st = check_pointers(A, B, C, M, N, K);
-    if (st != HKG_OK)
-        return st;
-    if (!plan_matches_library(plan))
-        return HKG_ERR_UNSUPPORTED;
-    if ((plan->kernel_id == HKG_KERNEL_TILE || plan->kernel_id == HKG_KERNEL_SKINNY) &&
-        !(aligned16(A) && aligned16(B) && aligned16(C)))
-        return HKG_ERR_MISALIGNED;
-    return run(plan, A, B, C, (hipStream_t)stream);
+    return run_plan(plan, A, B, nullptr, C, M, N, K, HKG_EPILOGUE_NONE, stream);
+}
+
+hkg_status_t hkg_gemm_bf16_run_plan_epilogue(const hkg_plan_t* plan, const void* A, const void* B,
+                                             const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                                             int32_t epilogue, void* stream)
+{
+    return run_plan(plan, A, B, bias, C, M, N, K, epilogue, stream);
 }
 
 const char* hkg_status_string(hkg_status_t s)

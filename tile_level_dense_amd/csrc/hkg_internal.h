@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hkg_epilogue.h"
 #include "hkg_skinny_configs.h"
 #include "hkg_tile_configs.h"
 
@@ -41,24 +42,27 @@ SkinnyShape skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 
 // Launchers: enqueue one kernel on `stream`; return the launch error.
+// Every launcher takes the fused epilogue (`epi`, an EPI_* code, and `bias`,
+// N bf16 values; bias is not read when epi == EPI_NONE).
 // split_k == 1: plain launch.  split_k > 1: K divided across workgroups,
 // fp32 partials in `ws` (split_k * M * N floats) and per-tile arrival
 // counters in `counters` (one per output tile, zero on entry and on exit).
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int xcd_chunk, int split_k, float* ws,
-                       int* counters, hipStream_t stream);
+                       int* counters, const uint16_t* bias, int epi, hipStream_t stream);
 
 // split_k == 1: plain launch.  split_k > 1: fp32 partials in `ws`
 // (split_k * M * N floats) and per-column-block arrival counters in `counters`
 // (grid_x ints, zero on entry and left zero on exit).
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                          int M, int N, int K, int split_k, float* ws, int* counters,
-                         hipStream_t stream);
+                         const uint16_t* bias, int epi, hipStream_t stream);
 
 hipError_t launch_generic(const uint16_t* A, const uint16_t* B, uint16_t* C,
-                          int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                          int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epi, hipStream_t stream);
 
-hipError_t launch_zero(uint16_t* C, int64_t count, hipStream_t stream);
+// K == 0: C[i][n] = epilogue(+0) (the empty sum).
+hipError_t launch_zero(uint16_t* C, int64_t M, int64_t N, const uint16_t* bias, int epi, hipStream_t stream);
 
 // Build-time resource figures of each kernel (filled by the generated
 // hkg_resources.inc; -1 where unknown).

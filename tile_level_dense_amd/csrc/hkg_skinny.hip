@@ -17,8 +17,9 @@
 //    followed by an LDS combine of the FlyDSL "Prebuilt kernels guide",
 //    section 1.1).  Workgroups that share a column block along K (split-K)
 //    write fp32 partials and the last one to arrive sums them in split
-//    order (split-K on fp32 partials: same guide, section 3c).  The result
-//    is rounded to bf16 once.
+//    order (split-K on fp32 partials: same guide, section 3c).  The fused
+//    epilogue (bias, activation) acts on the fp32 total, which is then
+//    rounded to bf16 once.
 #include "hkg_internal.h"
 
 namespace hkg {
@@ -65,11 +66,12 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 b, i32x4 a, f32x4 c)
 // MB: 16-row blocks of A (M <= 16 MB).  NB: 16-row blocks of B per
 // workgroup.  WK: waves per workgroup, splitting K.  U: 32-k steps per chunk
 // of loads.  CP: cache-policy bits of the B loads (B is streamed once).
-template <int MB, int NB, int WK, int U, int CP>
+template <int MB, int NB, int WK, int U, int CP, bool EPI>
 __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
-                   float* __restrict__ ws, int* __restrict__ counters)
+                   float* __restrict__ ws, int* __restrict__ counters,
+                   const uint16_t* __restrict__ bias, int epi)
 {
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
@@ -186,6 +188,12 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         if (m >= M)
             continue;
         if (split_k == 1) {
+            if (EPI) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        sum[r] = epi_apply(sum[r], bias, n + r, epi);
+            }
             const uint2 h = pack_bf16x4(sum);
             uint16_t* crow = C + (size_t)m * (size_t)N;
             if (vec_ok && n + 3 < N) {
@@ -232,19 +240,22 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         for (int sp = 0; sp < split_k; ++sp)
             sum += __hip_atomic_load(ws + ((size_t)sp * (size_t)M + (size_t)m) * (size_t)N + n0 + c,
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (EPI)
+            sum = epi_apply(sum, bias, n0 + c, epi);
         C[(size_t)m * (size_t)N + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int U, int CP>
+template <int MB, int NB, int WK, int U, int CP, bool EPI>
 hipError_t launch_skinny_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                           int split_k, float* ws, int* counters, hipStream_t stream)
+                           int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
+                           hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
-                       A, B, C, M, N, K, split_k, ws, counters);
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
+                       A, B, C, M, N, K, split_k, ws, counters, bias, epi);
     return hipGetLastError();
 }
 
@@ -269,12 +280,16 @@ int skinny_lds_bytes(int variant)
 
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                          int M, int N, int K, int split_k, float* ws, int* counters,
-                         hipStream_t stream)
+                         const uint16_t* bias, int epi, hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(mb, nb, wk, u, cp) \
     if (v++ == variant)               \
-        return launch_skinny_t<mb, nb, wk, u, cp>(A, B, C, M, N, K, split_k, ws, counters, stream);
+        return epi == EPI_NONE                                                                                \
+                   ? launch_skinny_t<mb, nb, wk, u, cp, false>(A, B, C, M, N, K, split_k, ws, counters, bias, epi, \
+                                                               stream)                                            \
+                   : launch_skinny_t<mb, nb, wk, u, cp, true>(A, B, C, M, N, K, split_k, ws, counters, bias, epi,  \
+                                                              stream);
     HKG_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;

@@ -97,12 +97,13 @@ __device__ __forceinline__ void sync_stage(int ahead)
     wait_and_barrier<0>();
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI>
 __global__ __launch_bounds__(WM * WN * 64, 2)
 void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                  uint16_t* __restrict__ C, int M, int N, int K,
                  int tiles_m, int tiles_n, int win_w, int chunk_c,
-                 int split_k, float* __restrict__ ws, int* __restrict__ counters)
+                 int split_k, float* __restrict__ ws, int* __restrict__ counters,
+                 const uint16_t* __restrict__ bias, int epi)
 {
     constexpr int NW = WM * WN;
     constexpr int RB = BK * 2;             // bytes of one row of a stage
@@ -325,29 +326,15 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
         wait_and_barrier<(STAGES - 1) * L>();
         bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
         read_frags(smem, 0, af0, bf0);
-        if constexpr (KS == 2) {
-            for (int t = 0; t < nk; ++t) {
-                mfmas(af0, bf0);
-                read_frags(stage_base(t), 1, af1, bf1);
-                interleave();
-                new_stage(t);
-                mfmas(af1, bf1);
-                read_frags(stage_base(t + 1), 0, af0, bf0);
-                interleave();
-            }
-        } else {
-            for (int t = 0; t < nk; t += 2) {
-                new_stage(t);
-                mfmas(af0, bf0);
-                read_frags(stage_base(t + 1), 0, af1, bf1);
-                interleave();
-                if (t + 1 == nk)
-                    break;
-                new_stage(t + 1);
-                mfmas(af1, bf1);
-                read_frags(stage_base(t + 2), 0, af0, bf0);
-                interleave();
-            }
+        static_assert(KS == 2, "the register-pipelined loop takes 64-k stages");
+        for (int t = 0; t < nk; ++t) {
+            mfmas(af0, bf0);
+            read_frags(stage_base(t), 1, af1, bf1);
+            interleave();
+            new_stage(t);
+            mfmas(af1, bf1);
+            read_frags(stage_base(t + 1), 0, af0, bf0);
+            interleave();
         }
         // Leave no copy in flight into LDS that is about to be released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -570,8 +557,67 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
             __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
     const bool vec_ok = (N & 3) == 0;
+    if constexpr (EPI) {
+        // Fused epilogue (bias, activation) through LDS: each wave writes
+        // its fp32 accumulators, CH block rows at a time, into its own LDS
+        // region (rows padded by 16 bytes so the 16 rows of a block land on
+        // distinct banks), then walks the region four columns per lane in
+        // row order, applying bias and activation once per element (one
+        // copy of the activation code instead of one per accumulator
+        // register) and storing bf16 rows.
+        constexpr int REGION = SMEM / NW;               // bytes per wave
+        constexpr int ROWB = WTN * 4 + 16;              // padded fp32 row of a wave tile
+        constexpr int CH0 = REGION / (16 * ROWB);       // block rows that fit
+        constexpr int CH = CH0 >= FM ? FM : (CH0 >= 8 ? 8 : (CH0 >= 4 ? 4 : (CH0 >= 2 ? 2 : 1)));
+        constexpr int QPR = WTN / 4;                    // four-column groups per row
+        static_assert(CH0 >= 1 && FM % CH == 0, "epilogue staging needs a block row of LDS per wave");
+        static_assert(64 % QPR == 0, "a lane keeps its four columns across the walk");
+        // This lane's four columns are the same on every row of the walk:
+        // read their bias values once, before the barrier.
+        const int ncol = n0 + wn * WTN + (lane % QPR) * 4;
+        float bv[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            bv[rr] = ncol + rr < N ? __uint_as_float((uint32_t)bias[ncol + rr] << 16) : 0.f;
+        __syncthreads();                                // every wave is done with the stages
+        char* const wbuf = smem + wave * REGION;
+#pragma unroll
+        for (int c = 0; c < FM; c += CH) {
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    *(f32x4*)(wbuf + (ii * 16 + lrow) * ROWB + (j * 16 + lgrp * 4) * 4) = acc[c + ii][j];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            for (int q = lane; q < CH * 16 * QPR; q += 64) {
+                const int r = q / QPR;
+                const int col = (q - r * QPR) * 4;
+                const int m = m0 + wm * WTM + c * 16 + r;
+                const int n = n0 + wn * WTN + col;
+                if (m >= M)
+                    continue;
+                f32x4 v = *(const f32x4*)(wbuf + r * ROWB + col * 4);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    v[rr] = epi_activation(v[rr] + bv[rr], epi);
+                const uint2 h = pack_bf16x4(v);
+                uint16_t* crow = C + (size_t)m * (size_t)N;
+                if (vec_ok && n + 3 < N) {
+                    *(uint2*)(crow + n) = h;
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (n + rr < N)
+                            crow[n + rr] = bf16_elem(h, rr);
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // region reads done before the next chunk
+        }
+        return;
+    }
+
+    // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * WTM + i * 16 + lrow;
@@ -597,15 +643,16 @@ void tile_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI>
 hipError_t launch_tile_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                         int win_w, int chunk_c, int split_k, float* ws, int* counters, hipStream_t stream)
+                         int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
+                         int epi, hipStream_t stream)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED>), dim3(tiles_m * tiles_n, split_k),
+    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI>), dim3(tiles_m * tiles_n, split_k),
                        dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c,
-                       split_k, ws, counters);
+                       split_k, ws, counters, bias, epi);
     return hipGetLastError();
 }
 
@@ -632,13 +679,16 @@ int tile_lds_bytes(int variant)
 
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int chunk_c, int split_k, float* ws, int* counters,
-                       hipStream_t stream)
+                       const uint16_t* bias, int epi, hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc) \
     if (v++ == variant)                        \
-        return launch_tile_t<bm, bn, bk, st, wm, wn, sc>(A, B, C, M, N, K, win_w, chunk_c, split_k, ws, counters, \
-                                                         stream);
+        return epi == EPI_NONE                                                                               \
+                   ? launch_tile_t<bm, bn, bk, st, wm, wn, sc, false>(A, B, C, M, N, K, win_w, chunk_c, split_k,   \
+                                                                      ws, counters, bias, epi, stream)            \
+                   : launch_tile_t<bm, bn, bk, st, wm, wn, sc, true>(A, B, C, M, N, K, win_w, chunk_c, split_k,    \
+                                                                     ws, counters, bias, epi, stream);
     HKG_TILE_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;

@@ -21,5 +21,4 @@
     X(128, 128, 64, 2, 2, 2, 0)   \
     X(256, 256, 64, 2, 2, 4, 2)   \
     X(256, 256, 64, 2, 2, 4, 5)   \
-    X(256, 256, 64, 2, 2, 4, 0)   \
-    X(256, 256, 32, 4, 2, 4, 2)
+    X(256, 256, 64, 2, 2, 4, 0)
