@@ -52,6 +52,17 @@ def _bind(path):
     lib.hkg_oracle_gemm_entries.restype = None
     lib.hkg_oracle_max_threads.argtypes = []
     lib.hkg_oracle_max_threads.restype = ctypes.c_int
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.hkg_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.hkg_oracle_e4m3_value.restype = ctypes.c_double
+    lib.hkg_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.hkg_oracle_e8m0_value.restype = ctypes.c_double
+    lib.hkg_oracle_mx_gemm_rows.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, i64, i64,
+                                            u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_mx_gemm_rows.restype = None
+    lib.hkg_oracle_mx_gemm_entries.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, i64p, i64p, i64,
+                                               u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_mx_gemm_entries.restype = None
     lib.hkg_oracle_activation.argtypes = [ctypes.c_double, ctypes.c_int]
     lib.hkg_oracle_activation.restype = ctypes.c_double
     lib.hkg_oracle_epilogue.argtypes = [f64p, u16p, i64, i64, i64p, ctypes.c_int, f64p, u16p]
@@ -148,6 +159,68 @@ class Oracle:
         return C, S, absS
 
 
+    def e4m3_value(self, bits):
+        """f64 value of one E4M3 (OCP e4m3fn) code, from the format definition."""
+        return self.lib.hkg_oracle_e4m3_value(int(bits))
+
+    def e8m0_value(self, bits):
+        """f64 value 2^(e - 127) of one E8M0 scale code (0xFF: NaN)."""
+        return self.lib.hkg_oracle_e8m0_value(int(bits))
+
+    def _mx_operands(self, A, SA, B, SB):
+        A = np.ascontiguousarray(A, dtype=np.uint8)
+        B = np.ascontiguousarray(B, dtype=np.uint8)
+        SA = np.ascontiguousarray(SA, dtype=np.uint8)
+        SB = np.ascontiguousarray(SB, dtype=np.uint8)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[1] or A.shape[1] % 32:
+            raise ValueError("A must be M x K and B N x K E4M3 codes, K a multiple of 32")
+        K = A.shape[1]
+        if SA.shape != (A.shape[0], K // 32) or SB.shape != (B.shape[0], K // 32):
+            raise ValueError("scales must be M x K/32 and N x K/32 E8M0 codes")
+        return A, SA, B, SB
+
+    def mx_gemm(self, A, SA, B, SB, rows=None, nthreads=0, want_sums=True):
+        """MXFP8 C = (A * 2^SA) (B * 2^SB)^T over rows [r0, r1) (FlyDSL blog, MXFP
+        section): (C bits uint16, S, absS) like gemm()."""
+        A, SA, B, SB = self._mx_operands(A, SA, B, SB)
+        M, K = A.shape
+        N = B.shape[0]
+        r0, r1 = (0, M) if rows is None else rows
+        if not (0 <= r0 <= r1 <= M):
+            raise ValueError("row range out of bounds")
+        C = np.zeros((r1 - r0, N), dtype=np.uint16)
+        S = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        absS = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        if r1 > r0 and N > 0:
+            self.lib.hkg_oracle_mx_gemm_rows(
+                _ptr(A, ctypes.c_uint8), _ptr(SA, ctypes.c_uint8), _ptr(B, ctypes.c_uint8),
+                _ptr(SB, ctypes.c_uint8), M, N, K, r0, r1, _ptr(C, ctypes.c_uint16),
+                _ptr(S, ctypes.c_double), _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+    def mx_gemm_entries(self, A, SA, B, SB, ii, jj, nthreads=0):
+        """Selected elements of the MXFP8 product with their S and absS."""
+        A, SA, B, SB = self._mx_operands(A, SA, B, SB)
+        M, K = A.shape
+        N = B.shape[0]
+        ii = np.ascontiguousarray(ii, dtype=np.int64)
+        jj = np.ascontiguousarray(jj, dtype=np.int64)
+        if ii.shape != jj.shape:
+            raise ValueError("index arrays differ in shape")
+        if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+            raise ValueError("index out of bounds")
+        n = ii.size
+        C = np.zeros(n, dtype=np.uint16)
+        S = np.zeros(n, dtype=np.float64)
+        absS = np.zeros(n, dtype=np.float64)
+        if n:
+            self.lib.hkg_oracle_mx_gemm_entries(
+                _ptr(A, ctypes.c_uint8), _ptr(SA, ctypes.c_uint8), _ptr(B, ctypes.c_uint8),
+                _ptr(SB, ctypes.c_uint8), M, N, K, _ptr(ii, ctypes.c_int64), _ptr(jj, ctypes.c_int64), n,
+                _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double), _ptr(absS, ctypes.c_double),
+                int(nthreads))
+        return C, S, absS
+
     def activation(self, x, epilogue):
         """act(x) in fp64 for one epilogue (x already includes the bias)."""
         return float(self.lib.hkg_oracle_activation(float(x), EPILOGUES[epilogue]))
@@ -220,6 +293,14 @@ def gemm_entries(A, B, ii, jj, nthreads=0):
 
 def activation(x, epilogue):
     return default().activation(x, epilogue)
+
+
+def mx_gemm(A, SA, B, SB, rows=None, nthreads=0, want_sums=True):
+    return default().mx_gemm(A, SA, B, SB, rows, nthreads, want_sums)
+
+
+def mx_gemm_entries(A, SA, B, SB, ii, jj, nthreads=0):
+    return default().mx_gemm_entries(A, SA, B, SB, ii, jj, nthreads)
 
 
 def epilogue(S, bias, epilogue, cols=None):

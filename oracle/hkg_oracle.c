@@ -34,6 +34,9 @@
  *   GEMM: all-ones (C = K), identity on either side (C = B^T, C = A),
  *   small-integer inputs against exact int64 products, exact-rational brute
  *   force on tiny shapes, and the fp64 summation error bound.
+ *   MXFP8: every E4M3 and E8M0 code against torch's float8_e4m3fn and
+ *   float8_e8m0fnu conversions; all-ones with unit scales (C = K); scale
+ *   changes multiply exactly by powers of two; exact rationals on tiny shapes.
  *   Epilogue: bias through all-ones products (C = K + b, exact), ReLU's
  *   definition, the odd parts SiLU(x) - SiLU(-x) = x and GELU(x) - GELU(-x) = x,
  *   the closed form sigmoid(ln 3) = 3/4, the normal quantile Phi(1.959963985)
@@ -233,4 +236,125 @@ int hkg_oracle_epilogue(const double* S, const uint16_t* bias, int64_t count, in
         C[t] = hkg_oracle_bf16_rne(y);
     }
     return 0;
+}
+
+
+/* ---- MXFP8 GEMM ----------------------------------------------------------
+ * The "FlyDSL in PyTorch" blog page (section on MXFP) describes the block-
+ * scaled GEMM: operands FP8 E4M3, one E8M0 scale per 32 values along the
+ * reduction axis (BlockWise1x32), fp32 accumulation, bf16 output, K a
+ * multiple of 128.  Written out:
+ *
+ *   a(i,k) = e4m3(A[i][k]) * e8m0(SA[i][k / 32]),  b(j,k) likewise with SB
+ *   S[i][j] = sum over k ascending of a(i,k) * b(j,k)   (fp64)
+ *   C[i][j] = bf16 nearest-even rounding of S[i][j], once
+ *
+ * Layouts: A is M x K bytes and B N x K bytes (K contiguous), SA is M x K/32
+ * and SB N x K/32 bytes (one row of scales per operand row).
+ * E4M3 (OCP "e4m3fn"): 1 sign, 4 exponent bits (bias 7), 3 fraction bits;
+ * exponent field 0 holds subnormals 0.f * 2^-6; no infinities; S.1111.111
+ * is NaN; the largest finite value is 448.  E8M0: an unsigned exponent,
+ * value 2^(e - 127); 0xFF is NaN.
+ * A product of two E4M3 values has at most 8 significant bits and the
+ * scales are powers of two in [2^-127, 2^127], so every scaled product is
+ * exact in fp64; only the running sums round.
+ */
+double hkg_oracle_e4m3_value(uint8_t bits)
+{
+    int sign = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xF;
+    int f = bits & 0x7;
+    double mag;
+    if (e == 0xF && f == 0x7)
+        mag = NAN;
+    else if (e == 0)                     /* subnormal: 0.f * 2^-6 */
+        mag = ldexp((double)f / 8.0, -6);
+    else                                 /* normal: 1.f * 2^(e-7) */
+        mag = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+double hkg_oracle_e8m0_value(uint8_t bits)
+{
+    return bits == 0xFF ? NAN : ldexp(1.0, (int)bits - 127);
+}
+
+static double g_e4m3[256];
+static int g_e4m3_ready = 0;
+
+static void build_e4m3_table(void)
+{
+    if (g_e4m3_ready)
+        return;
+#pragma omp critical(hkg_oracle_e4m3_table)
+    {
+        if (!g_e4m3_ready) {
+            for (int b = 0; b < 256; ++b)
+                g_e4m3[b] = hkg_oracle_e4m3_value((uint8_t)b);
+            __atomic_store_n(&g_e4m3_ready, 1, __ATOMIC_RELEASE);
+        }
+    }
+}
+
+static void mx_dot_one(const uint8_t* a_row, const uint8_t* sa_row, const uint8_t* b_row,
+                       const uint8_t* sb_row, int64_t K, double* s_out, double* abs_out)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = (g_e4m3[a_row[k]] * hkg_oracle_e8m0_value(sa_row[k / 32])) *
+                   (g_e4m3[b_row[k]] * hkg_oracle_e8m0_value(sb_row[k / 32]));
+        s += p;
+        sa += fabs(p);
+    }
+    *s_out = s;
+    *abs_out = sa;
+}
+
+/* Rows [row_begin, row_end) of the MXFP8 product; outputs as in
+ * hkg_oracle_gemm_rows.  K must be a multiple of 32. */
+void hkg_oracle_mx_gemm_rows(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                             int64_t M, int64_t N, int64_t K, int64_t row_begin, int64_t row_end,
+                             uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    build_e4m3_table();
+    const int64_t KB = K / 32;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s, sa;
+            mx_dot_one(A + i * K, SA + i * KB, B + j * K, SB + j * KB, K, &s, &sa);
+            int64_t o = (i - row_begin) * N + j;
+            C[o] = hkg_oracle_bf16_rne(s);
+            if (S)
+                S[o] = s;
+            if (absS)
+                absS[o] = sa;
+        }
+    }
+}
+
+/* Selected elements (ii[t], jj[t]) of the MXFP8 product. */
+void hkg_oracle_mx_gemm_entries(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                                int64_t M, int64_t N, int64_t K, const int64_t* ii, const int64_t* jj,
+                                int64_t count, uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    (void)N;
+    build_e4m3_table();
+    const int64_t KB = K / 32;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+    for (int64_t t = 0; t < count; ++t) {
+        double s, sa;
+        mx_dot_one(A + ii[t] * K, SA + ii[t] * KB, B + jj[t] * K, SB + jj[t] * KB, K, &s, &sa);
+        C[t] = hkg_oracle_bf16_rne(s);
+        if (S)
+            S[t] = s;
+        if (absS)
+            absS[t] = sa;
+    }
 }

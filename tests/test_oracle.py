@@ -239,11 +239,108 @@ def check_epilogue_columns(O):
             assert C[2, j] == O.bf16_rne(Y[2, j])
 
 
+# ------------------------------------------------------------------ MXFP8
+# Block-scaled FP8 GEMM (FlyDSL-in-PyTorch blog, MXFP section): E4M3 values,
+# one E8M0 scale per 32 along K.
+
+def _torch_e4m3(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def check_e4m3_exhaustive(O):
+    # Every E4M3 code against torch's float8_e4m3fn (an independent decoder).
+    ref = _torch_e4m3(np.arange(256, dtype=np.uint8))
+    got = np.array([O.e4m3_value(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert O.e4m3_value(0x7E) == 448.0 and nan.sum() == 2
+
+
+def check_e8m0_exhaustive(O):
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([O.e8m0_value(b) for b in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert all(got[e] == 2.0 ** (e - 127) for e in range(255))
+
+
+def check_mx_all_ones(O):
+    # E4M3 0x38 is 1.0; unit scales (code 127): C = K exactly.
+    for K in (128, 4096):
+        A = np.full((3, K), 0x38, dtype=np.uint8)
+        B = np.full((5, K), 0x38, dtype=np.uint8)
+        s = np.full((3, K // 32), 127, dtype=np.uint8)
+        t = np.full((5, K // 32), 127, dtype=np.uint8)
+        C, S, absS = O.mx_gemm(A, s, B, t)
+        assert np.all(S == K) and np.all(absS == K) and np.all(C == exact.round_exact(K))
+
+
+def check_mx_unit_scales_equal_bf16_gemm(O):
+    # With unit scales the MX product is the bf16 product of the same values
+    # (every E4M3 value is a bf16 value): pinned to the bf16 oracle.
+    A, SA, B, SB = workloads.make_mx_inputs(9, 7, 96, seed=3)
+    SA[:] = 127
+    SB[:] = 127
+    ab = workloads.f32_to_bf16_bits(_torch_e4m3(A).astype(np.float32))
+    bb = workloads.f32_to_bf16_bits(_torch_e4m3(B).astype(np.float32))
+    C1, S1, a1 = O.mx_gemm(A, SA, B, SB)
+    C2, S2, a2 = O.gemm(ab, bb)
+    assert np.array_equal(S1, S2) and np.array_equal(a1, a2) and np.array_equal(C1, C2)
+
+
+def check_mx_scales_are_powers_of_two(O):
+    # Raising row i's scales by d multiplies row i of S by 2^d exactly; a
+    # column's scales likewise; and a block's scale reaches only its block:
+    # with all codes zero outside block b, the row equals block b's product.
+    A, SA, B, SB = workloads.make_mx_inputs(6, 5, 128, seed=4)
+    _, S, _ = O.mx_gemm(A, SA, B, SB)
+    SA2 = SA.copy(); SA2[2] += 3
+    SB2 = SB.copy(); SB2[4] -= 2
+    _, S2, _ = O.mx_gemm(A, SA2, B, SB2)
+    want = S.copy(); want[2] *= 8.0; want[:, 4] *= 0.25
+    assert np.array_equal(S2, want)
+    Az = A.copy(); Az[:, :64] = 0; Az[:, 96:] = 0          # keep block 2 only
+    _, Sz, _ = O.mx_gemm(Az, SA, B, SB)
+    SA3 = SA.copy(); SA3[:, 0] += 5; SA3[:, 1] -= 4; SA3[:, 3] += 1
+    _, Sz3, _ = O.mx_gemm(Az, SA3, B, SB)
+    assert np.array_equal(Sz, Sz3)
+
+
+def check_mx_brute_force_tiny(O):
+    # Exact rationals from torch's decode and the scale definition.
+    rng = np.random.default_rng(17)
+    for trial in range(4):
+        M, N = [int(v) for v in rng.integers(1, 5, size=2)]
+        K = 64
+        A = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+        B = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+        A[(A & 0x7F) == 0x7F] = 0x11                      # no NaN codes
+        B[(B & 0x7F) == 0x7F] = 0x22
+        SA = rng.integers(100, 150, size=(M, 2)).astype(np.uint8)
+        SB = rng.integers(100, 150, size=(N, 2)).astype(np.uint8)
+        av, bv = _torch_e4m3(A), _torch_e4m3(B)
+        C, S, absS = O.mx_gemm(A, SA, B, SB)
+        for i in range(M):
+            for j in range(N):
+                s = sum(Fraction(float(av[i, k])) * Fraction(2) ** (int(SA[i, k // 32]) - 127) *
+                        Fraction(float(bv[j, k])) * Fraction(2) ** (int(SB[j, k // 32]) - 127) for k in range(K))
+                sa = sum(abs(Fraction(float(av[i, k])) * Fraction(float(bv[j, k]))) *
+                         Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254) for k in range(K))
+                assert abs(Fraction(S[i, j]) - s) <= K * Fraction(2) ** -53 * sa, (trial, i, j)
+                assert C[i, j] == exact.round_exact(s), (trial, i, j)
+
+
 ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
               check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
               check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
               check_transpose_symmetry, check_epilogue_bias_exact, check_epilogue_closed_forms,
-              check_epilogue_odd_parts, check_epilogue_columns]
+              check_epilogue_odd_parts, check_epilogue_columns, check_e4m3_exhaustive,
+              check_e8m0_exhaustive, check_mx_all_ones, check_mx_unit_scales_equal_bf16_gemm,
+              check_mx_scales_are_powers_of_two, check_mx_brute_force_tiny]
 
 
 @pytest.fixture(scope="module")
@@ -277,6 +374,36 @@ def test_rows_and_entries_consistent(O):
     assert np.array_equal(ae, absS[ii, jj])
 
 
+def test_mx_rows_and_entries_consistent(O):
+    A, SA, B, SB = workloads.make_mx_inputs(40, 33, 160, seed=6)
+    C, S, absS = O.mx_gemm(A, SA, B, SB)
+    Cr, Sr, _ = O.mx_gemm(A, SA, B, SB, rows=(7, 29))
+    assert np.array_equal(Cr, C[7:29]) and np.array_equal(Sr, S[7:29])
+    ii = np.array([0, 39, 7, 20]); jj = np.array([32, 0, 5, 17])
+    Ce, Se, ae = O.mx_gemm_entries(A, SA, B, SB, ii, jj)
+    assert np.array_equal(Ce, C[ii, jj]) and np.array_equal(Se, S[ii, jj])
+    assert np.array_equal(ae, absS[ii, jj])
+    C1, S1, _ = O.mx_gemm(A, SA, B, SB, nthreads=1)
+    assert np.array_equal(C1, C) and np.array_equal(S1, S)
+
+
+def test_mx_quantizer_round_trips(O):
+    # The input generator's MX quantisation: every block's largest magnitude
+    # lands in [224, 448] after scaling and rounding (or the block is zero), and the decoded
+    # values stay within one E4M3 rounding (2^-4 relative, or the subnormal
+    # spacing 2^-9 of the scaled value) of the drawn ones.
+    rng = np.random.default_rng(5)
+    x = rng.normal(0.0, 1.0, size=(8, 256))
+    x[3, 32:64] = 0.0
+    A, SA = workloads.mx_quantize(x)
+    dec = np.array([[O.e4m3_value(c) for c in row] for row in A])
+    scale = np.repeat(np.array([[O.e8m0_value(e) for e in row] for row in SA]), 32, axis=1)
+    amax = np.abs(dec).reshape(8, 8, 32).max(axis=2)
+    assert np.all((amax >= 224) | (amax == 0)) and amax.max() <= 448
+    assert amax[3, 1] == 0
+    assert np.all(np.abs(dec * scale - x) <= (2.0 ** -4 * np.abs(x) + 2.0 ** -10 * scale))
+
+
 def test_thread_count_does_not_change_result(O):
     A, B = workloads.make_inputs(64, 40, 300, seed=4)
     C1, S1, _ = O.gemm(A, B, nthreads=1)
@@ -288,8 +415,14 @@ def test_thread_count_does_not_change_result(O):
 # Plausible mistakes planted in a copy of the oracle source; each must be
 # caught by at least one pin above.
 MUTANTS = {
-    "sign_of_sum": ("s += p;", "s -= p;"),
-    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 0; k < K - 1; ++k) {"),
+    "sign_of_sum": ("double p = g_val[a_row[k]] * g_val[b_row[k]];\n        s += p;",
+                    "double p = g_val[a_row[k]] * g_val[b_row[k]];\n        s -= p;"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double p = g_val",
+                          "for (int64_t k = 0; k < K - 1; ++k) {\n        double p = g_val"),
+    "mx_dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double p = (g_e4m3",
+                             "for (int64_t k = 0; k < K - 1; ++k) {\n        double p = (g_e4m3"),
+    "mx_transposed_operands": ("mx_dot_one(A + i * K, SA + i * KB, B + j * K, SB + j * KB, K, &s, &sa);",
+                               "mx_dot_one(A + j * K, SA + j * KB, B + i * K, SB + i * KB, K, &s, &sa);"),
     "reversed_b_index": ("g_val[b_row[k]]", "g_val[b_row[K - 1 - k]]"),
     "transposed_operands": ("dot_one(A + i * K, B + j * K, K, &s, &sa);",
                             "dot_one(A + j * K, B + i * K, K, &s, &sa);"),
@@ -298,7 +431,8 @@ MUTANTS = {
     "one_bit_too_many": ("double q = ldexp(1.0, E - 7);", "double q = ldexp(1.0, E - 8);"),
     "no_subnormal_clamp": ("        E = -126;                   /* bf16 subnormal range: fixed quantum */",
                            "        E = E;"),
-    "abs_sum_signed": ("sa += fabs(p);", "sa += p;"),
+    "abs_sum_signed": ("s += p;\n        sa += fabs(p);\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/*\n * Rows",
+                       "s += p;\n        sa += p;\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/*\n * Rows"),
     "exponent_bias": ("mag = ldexp(1.0 + (double)f / 128.0, e - 127);",
                       "mag = ldexp(1.0 + (double)f / 128.0, e - 126);"),
     "negative_zero_sign": ("uint16_t sign = signbit(x) ? 0x8000 : 0;",
@@ -315,6 +449,16 @@ MUTANTS = {
                               "y = hkg_oracle_activation(S[t], epi) + hkg_oracle_bf16_value(bias[j]);"),
     "bias_shifted_column": ("const int64_t j = cols ? cols[t] : t % N;",
                             "const int64_t j = cols ? cols[t] : (t + 1) % N;"),
+    "mx_one_scale_per_row": ("(g_e4m3[a_row[k]] * hkg_oracle_e8m0_value(sa_row[k / 32]))",
+                             "(g_e4m3[a_row[k]] * hkg_oracle_e8m0_value(sa_row[0]))"),
+    "mx_b_scaled_by_a": ("(g_e4m3[b_row[k]] * hkg_oracle_e8m0_value(sb_row[k / 32]))",
+                         "(g_e4m3[b_row[k]] * hkg_oracle_e8m0_value(sa_row[k / 32]))"),
+    "e8m0_bias": ("ldexp(1.0, (int)bits - 127)", "ldexp(1.0, (int)bits - 128)"),
+    "e4m3_bias": ("mag = ldexp(1.0 + (double)f / 8.0, e - 7);", "mag = ldexp(1.0 + (double)f / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("mag = ldexp((double)f / 8.0, -6);", "mag = ldexp((double)f / 8.0, -7);"),
+    "e4m3_ieee_style_nan": ("if (e == 0xF && f == 0x7)", "if (e == 0xF)"),
+    "mx_abs_sum_signed": ("s += p;\n        sa += fabs(p);\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/* Rows [row_begin, row_end) of the MXFP8",
+                          "s += p;\n        sa += p;\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/* Rows [row_begin, row_end) of the MXFP8"),
 }
 
 

@@ -1,7 +1,9 @@
-"""Seeded synthetic inputs for the dense BF16 GEMM C = A * B^T.
+"""Seeded synthetic inputs for the dense BF16 GEMM C = A * B^T and its
+block-scaled FP8 (MXFP8) variant.
 
 This module is shared by the tests, the benchmark and the smoke check.  It
-holds no GEMM arithmetic: it only draws input matrices and names the five
+holds no GEMM arithmetic: it only draws input matrices (and, for MXFP8,
+encodes them as E4M3 codes with per-block E8M0 scales) and names the
 workload shapes.  Neither the oracle nor the HIP library imports it; the
 callers hand its arrays to both.
 
@@ -48,15 +50,19 @@ def bf16_bits_to_f32(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def draw(rng, shape, dist):
+def draw_values(rng, shape, dist):
+    """float64 draws of one distribution."""
     kind = dist[0]
     if kind == "uniform":
-        x = rng.uniform(dist[1], dist[2], size=shape)
-    elif kind == "normal":
-        x = rng.normal(dist[1], dist[2], size=shape)
-    else:
-        raise ValueError("unknown distribution %r" % (kind,))
-    return f32_to_bf16_bits(x.astype(np.float32))
+        return rng.uniform(dist[1], dist[2], size=shape)
+    if kind == "normal":
+        return rng.normal(dist[1], dist[2], size=shape)
+    raise ValueError("unknown distribution %r" % (kind,))
+
+
+def draw(rng, shape, dist):
+    """bf16 bit patterns of one distribution (float64 -> float32 -> bf16)."""
+    return f32_to_bf16_bits(draw_values(rng, shape, dist).astype(np.float32))
 
 
 def make_inputs(M, N, K, a=("uniform", -1.0, 1.0), b=("uniform", -1.0, 1.0), seed=0):
@@ -70,3 +76,48 @@ def make_inputs(M, N, K, a=("uniform", -1.0, 1.0), b=("uniform", -1.0, 1.0), see
 def workload_inputs(name, seed=0):
     w = WORKLOADS[name]
     return make_inputs(w["M"], w["N"], w["K"], w["a"], w["b"], seed)
+
+
+# ------------------------------------------------------------ MXFP8 inputs
+# Block-scaled FP8 operands (FlyDSL-in-PyTorch blog, MXFP section: E4M3
+# values, one E8M0 scale per 32 values along K).  Recipe: draw float64
+# values as above (A first, then B, one stream), then for every block of 32
+# along K pick the scale 2^e with e = ceil(log2(max|x| / 448)) (so the
+# block's largest magnitude fits E4M3's 448; all-zero blocks get e = 0),
+# store e + 127 as the E8M0 code, and the E4M3 codes of x / 2^e rounded to
+# nearest-even (torch's float8_e4m3fn conversion).  Returns uint8 arrays
+# (A, SA, B, SB) with SA M x K/32 and SB N x K/32.
+MX_WORKLOADS = {
+    "mx_tiny_256": dict(M=256, N=256, K=256, a=("normal", 0.0, 1.0), b=("normal", 0.0, 1.0)),
+    "mx_decode_32x4096x4096": dict(M=32, N=4096, K=4096, a=("normal", 0.0, 1.0), b=("normal", 0.0, 0.02)),
+    "mx_square_8192": dict(M=8192, N=8192, K=8192, a=("normal", 0.0, 1.0), b=("normal", 0.0, 1.0)),
+}
+
+
+def mx_quantize(x):
+    """float64 rows (R x K, K % 32 == 0) -> (E4M3 codes R x K, E8M0 codes R x K/32)."""
+    import torch
+    x = np.asarray(x, dtype=np.float64)
+    R, K = x.shape
+    blocks = x.reshape(R, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.ceil(np.log2(amax / 448.0)), 0.0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    scaled = blocks / np.ldexp(1.0, e)[:, :, None]
+    codes = torch.from_numpy(scaled.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.reshape(R, K).copy(), (e + 127).astype(np.uint8)
+
+
+def make_mx_inputs(M, N, K, a=("normal", 0.0, 1.0), b=("normal", 0.0, 1.0), seed=0):
+    rng = np.random.default_rng(seed)
+    xa = draw_values(rng, (M, K), a)
+    xb = draw_values(rng, (N, K), b)
+    A, SA = mx_quantize(xa)
+    B, SB = mx_quantize(xb)
+    return A, SA, B, SB
+
+
+def mx_workload_inputs(name, seed=0):
+    w = MX_WORKLOADS[name]
+    return make_mx_inputs(w["M"], w["N"], w["K"], w["a"], w["b"], seed)
