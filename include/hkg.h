@@ -59,7 +59,7 @@ typedef enum {
     HKG_ERR_NO_DEVICE = -4,     /* no HIP device is visible */
     HKG_ERR_ARCH = -5,          /* the current device is not gfx950 */
     HKG_ERR_HIP = -6,           /* a HIP runtime call or launch failed; see hkg_last_hip_error */
-    HKG_ERR_WORKSPACE = -7      /* the split-K workspace could not be allocated */
+    HKG_ERR_WORKSPACE = -7      /* a library workspace (split-K partials, packed MXFP8 scales) could not be allocated */
 } hkg_status_t;
 
 typedef enum {
@@ -67,7 +67,8 @@ typedef enum {
     HKG_KERNEL_TILE = 1,        /* large-tile MFMA kernel (compute-bound shapes) */
     HKG_KERNEL_SKINNY = 2,      /* small M: streams B once, split-K over waves / workgroups */
     HKG_KERNEL_GENERIC = 3,     /* any alignment, any K: correctness fallback */
-    HKG_KERNEL_ZERO = 4         /* K == 0: C is the empty sum, +0 (then the epilogue) */
+    HKG_KERNEL_ZERO = 4,        /* K == 0: C is the empty sum, +0 (then the epilogue) */
+    HKG_KERNEL_MX_TILE = 5      /* MXFP8 large-tile kernel (scaled MFMA) */
 } hkg_kernel_t;
 
 /*
@@ -165,6 +166,81 @@ hkg_status_t hkg_gemm_bf16_epilogue(const void* A, const void* B, const void* bi
 hkg_status_t hkg_gemm_bf16_run_plan_epilogue(const hkg_plan_t* plan, const void* A, const void* B,
                                              const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                                              int32_t epilogue, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM (MXFP8), the block-scaled format of the
+ * FlyDSL-in-PyTorch blog post (MXFP section: E4M3 values with one E8M0
+ * scale per 32 values along K, K a multiple of 128 for the scaled MFMA):
+ *
+ *   C[i][j] = bf16( sum over k of  a(i,k) 2^(SA[i][k/32] - 127) * b(j,k) 2^(SB[j][k/32] - 127) )
+ *
+ *   A: M x K bytes, OCP FP8 E4M3 codes ("e4m3fn": bias 7, no infinities,
+ *      S.1111.111 is NaN, largest finite 448), row-major; B: N x K likewise.
+ *   SA: M x K/32 bytes, E8M0 codes (value 2^(e - 127), 0xFF is NaN),
+ *      row-major (one code per row per 32 consecutive k); SB: N x K/32.
+ *   C: M x N bf16, row-major, nearest-even.  K must be a multiple of 128
+ *   (else HKG_ERR_INVALID_ARG); M and N are free.  NaN codes give results
+ *   that are not specified here.
+ *
+ * Accuracy.  Each output is a float sum of scaled products formed by the
+ * matrix cores; on gfx950 the scaled FP8 instruction adds the products of
+ * each group of 8 consecutive k (one scale block) at a fixed point aligned
+ * to the group's largest product, truncating smaller products toward zero
+ * to 2^-13 of that product's power of two, and combines groups and the
+ * running sum in fp32.  So |C - exact| <= 2^-8 |C| + (truncation of each
+ * group: below 7 * 2^-13 of its largest product) + fp32 accumulation.
+ *
+ * Scale packing.  The kernel consumes scales in a packed layout: for each
+ * 64-row group of an operand and each 128-k stage, 256 bytes (see
+ * hkg_mx_pack_scales).  hkg_gemm_mxfp8 packs SA and SB itself into a
+ * library-owned device buffer on every call; callers with fixed weights
+ * pack once with hkg_mx_pack_scales and call hkg_gemm_mxfp8_prepacked.
+ *
+ * Pointers: A, B, C 16-byte aligned, packed scales 4-byte aligned (else
+ * HKG_ERR_MISALIGNED), all device memory owned by the caller; C overlaps
+ * no input.  bias / epilogue as in hkg_gemm_bf16_epilogue.  Shapes whose
+ * packed scales reach 2^31 bytes, or K above 8388480, give
+ * HKG_ERR_UNSUPPORTED.  The library's packed-scale buffer (like the split-K
+ * workspace) is shared by all calls on a device: calls on different streams
+ * of one device must not overlap in time.
+ */
+
+/* The plan an MXFP8 call of this shape uses (host only, no device). */
+hkg_status_t hkg_gemm_mxfp8_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out);
+
+/* C = epilogue(MXFP8 A * B^T + bias) with natural-layout scales SA, SB. */
+hkg_status_t hkg_gemm_mxfp8(const void* A, const void* SA, const void* B, const void* SB, const void* bias,
+                            void* C, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream);
+
+/*
+ * Bytes of the packed form of `rows` x K/32 scales: ceil(rows / 64) * 64 *
+ * K / 32.  -1 for negative sizes or K % 128 != 0.
+ */
+int64_t hkg_mx_packed_scales_bytes(int64_t rows, int64_t K);
+
+/*
+ * Packs S (rows x K/32 E8M0 codes, row-major, device memory) into P
+ * (hkg_mx_packed_scales_bytes(rows, K) bytes, 4-byte aligned, device
+ * memory, not overlapping S) on `stream`.  Layout: for 64-row group R, stage
+ * t (128 k) and lane l in 0..63, the 4 bytes at offset ((R * K/128 + t) * 64
+ * + l) * 4 hold, in byte f, the code of row 64 R + 16 f + l % 16, block
+ * 4 t + l / 16 (0 past the last row).
+ */
+hkg_status_t hkg_mx_pack_scales(const void* S, void* P, int64_t rows, int64_t K, void* stream);
+
+/* hkg_gemm_mxfp8 with packed scales PA (of A, M rows) and PB (of B, N rows). */
+hkg_status_t hkg_gemm_mxfp8_prepacked(const void* A, const void* PA, const void* B, const void* PB,
+                                      const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                                      int32_t epilogue, void* stream);
+
+/*
+ * Runs an MXFP8 plan (from hkg_gemm_mxfp8_plan, possibly edited: variant
+ * with matching tile fields, split_k in [1, 16] for split-capable variants,
+ * xcd fields >= 0) on packed scales; other plans give HKG_ERR_UNSUPPORTED.
+ */
+hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
+                                     const void* PB, const void* bias, void* C, int64_t M, int64_t N,
+                                     int64_t K, int32_t epilogue, void* stream);
 
 /* Static description of a status code. */
 const char* hkg_status_string(hkg_status_t status);

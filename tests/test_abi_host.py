@@ -264,7 +264,7 @@ def test_build_resources_have_no_scratch():
     if not os.path.exists(path):
         hkg_build.build()
     res = json.load(open(path))
-    entries = res["tile"] + res["skinny"] + [res["generic"]]
+    entries = res["tile"] + res["mx_tile"] + res["skinny"] + [res["generic"]]
     for e in entries:
         assert e["scratch"] == 0 and e["vgpr_spill"] <= 0, e
 
@@ -340,3 +340,91 @@ def test_tile_order_chiplet_blocks(lib):
         cols = {t[1] for t in tiles}
         assert len(tiles) == 32 and len(rows) == 8 and len(cols) == 4
         assert cols == set(range(4 * xcd, 4 * xcd + 4))
+
+
+# ------------------------------------------------------------------ MXFP8
+@pytest.mark.parametrize("shape,variant,split", [
+    ((8192, 8192, 8192), 0, 1),          # 32 x 32 ping-pong tiles fill the device
+    ((4096, 4096, 12288), 0, 1),
+    ((32, 4096, 4096), 1, 8),            # decode: 32 tiles of 128, split to 256 workgroups
+    ((128, 12288, 4096), 1, 3),
+    ((256, 256, 256), 1, 1),             # 4 tiles; K / 128 / 4 = 0 splits -> 1
+    ((1000, 1000, 384), 1, 1),
+])
+def test_mx_plan_selection(shape, variant, split):
+    p = hkg.mx_plan(*shape)
+    M, N, K = shape
+    assert p.kernel_id == hkg.HKG_KERNEL_MX_TILE and p.variant == variant and p.split_k == split, p
+    assert p.tile_k == 128 and p.flops == 2.0 * M * N * K
+    assert p.algorithmic_bytes == M * K + N * K + (M + N) * (K // 32) + 2 * M * N
+    assert p.workspace_bytes == (split * M * N * 4 if split > 1 else 0)
+    assert p.vgprs > 0 and p.scratch_bytes == 0
+
+
+def test_mx_plan_edge_shapes():
+    assert hkg.hkg_gemm_mxfp8_plan(64, 64, 100)[0] == hkg.HKG_ERR_INVALID_ARG      # K % 128
+    assert hkg.hkg_gemm_mxfp8_plan(-1, 64, 128)[0] == hkg.HKG_ERR_INVALID_ARG
+    st, p = hkg.hkg_gemm_mxfp8_plan(0, 64, 128)
+    assert st == hkg.HKG_OK and p.kernel_id == hkg.HKG_KERNEL_NONE
+    st, p = hkg.hkg_gemm_mxfp8_plan(5, 7, 0)
+    assert st == hkg.HKG_OK and p.kernel_id == hkg.HKG_KERNEL_ZERO
+    # K beyond the 32-bit offsets of one 256-row tile
+    assert hkg.hkg_gemm_mxfp8_plan(64, 64, 8388608)[0] == hkg.HKG_ERR_UNSUPPORTED
+
+
+def test_mx_packed_scale_bytes():
+    assert hkg.hkg_mx_packed_scales_bytes(1, 128) == 64 * 4
+    assert hkg.hkg_mx_packed_scales_bytes(64, 128) == 64 * 4
+    assert hkg.hkg_mx_packed_scales_bytes(65, 256) == 128 * 8
+    assert hkg.hkg_mx_packed_scales_bytes(0, 256) == 0
+    assert hkg.hkg_mx_packed_scales_bytes(10, 96) == -1
+    assert hkg.hkg_mx_packed_scales_bytes(-1, 128) == -1
+
+
+def test_mx_argument_errors_precede_device_work():
+    M, N, K = 64, 64, 256
+    A, SA, B, SB, C = [(1 << 30) + i * (1 << 22) for i in range(5)]
+    bias = (1 << 30) + 5 * (1 << 22)
+    f = hkg.hkg_gemm_mxfp8
+    assert f(A, SA, B, SB, None, C, M, N, 200) == hkg.HKG_ERR_INVALID_ARG          # K % 128
+    assert f(None, SA, B, SB, None, C, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, None, B, SB, None, C, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, SA, B, None, None, C, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, SA, B, SB, None, SA + 16, M, N, K) == hkg.HKG_ERR_INVALID_ARG       # C overlaps SA
+    assert f(A, SA, B, SB, None, C, M, N, K, 3) == hkg.HKG_ERR_INVALID_ARG          # epilogue without bias
+    assert f(A, SA, B, SB, bias + 1, C, M, N, K, 1) == hkg.HKG_ERR_MISALIGNED
+    assert f(A + 8, SA, B, SB, None, C, M, N, K) == hkg.HKG_ERR_MISALIGNED
+    assert f(None, None, B, SB, None, None, 0, N, K) == hkg.HKG_OK                  # empty output
+    g = hkg.hkg_gemm_mxfp8_prepacked
+    assert g(A, SA + 2, B, SB, None, C, M, N, K) == hkg.HKG_ERR_MISALIGNED           # packed scales: 4 bytes
+    assert g(A, SA, B, SB, None, C + 8, M, N, K) == hkg.HKG_ERR_MISALIGNED
+    assert hkg.hkg_mx_pack_scales(SA, SB, M, 100) == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_mx_pack_scales(SA, SA + 64, M, K) == hkg.HKG_ERR_INVALID_ARG      # overlap
+    assert hkg.hkg_mx_pack_scales(SA, SB + 2, M, K) == hkg.HKG_ERR_MISALIGNED
+    assert hkg.hkg_mx_pack_scales(None, None, 0, K) == hkg.HKG_OK
+
+
+def test_mx_run_plan_checks():
+    M, N, K = 512, 512, 512
+    A, PA, B, PB, C = [(1 << 30) + i * (1 << 22) for i in range(5)]
+    p = hkg.mx_plan(M, N, K)
+    r = hkg.hkg_gemm_mxfp8_run_plan
+    assert r(p, A, PA, B, PB, None, C, M + 1, N, K) == hkg.HKG_ERR_INVALID_ARG
+    q = hkg.Plan.from_buffer_copy(p)
+    q.variant = 7
+    assert r(q, A, PA, B, PB, None, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    # a bf16 plan is not an MXFP8 plan, and the other way round
+    assert r(hkg.plan(M, N, K), A, PA, B, PB, None, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    assert hkg.hkg_gemm_bf16_run_plan(p, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    # split-K only in the 128 x 128 variant
+    q = hkg.mx_plan(8192, 8192, 8192)
+    q.split_k = 2
+    assert r(q, 1 << 40, 2 << 40, 3 << 40, 4 << 40, None, 5 << 40, 8192, 8192, 8192) == hkg.HKG_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device status; a GPU is present")
+def test_mx_no_device_status():
+    M, N, K = 64, 64, 256
+    A, SA, B, SB, C = [(1 << 30) + i * (1 << 22) for i in range(5)]
+    assert hkg.hkg_gemm_mxfp8(A, SA, B, SB, None, C, M, N, K) == hkg.HKG_ERR_NO_DEVICE
+    assert hkg.hkg_mx_pack_scales(SA, SB, M, K) == hkg.HKG_ERR_NO_DEVICE

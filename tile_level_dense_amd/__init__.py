@@ -1,11 +1,15 @@
-"""Python binding of libhkg.so, the gfx950 dense BF16 GEMM C = A * B^T.
+"""Python binding of libhkg.so, the gfx950 dense BF16 GEMM C = A * B^T (and
+its block-scaled FP8 form, MXFP8).
 
 Argument marshalling only: every step of the GEMM runs in the library's HIP
 kernels.  The binding uses ctypes and mirrors the C ABI of include/hkg.h with
 the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_epilogue``,
 ``hkg_gemm_bf16_plan``, ``hkg_gemm_bf16_run_plan``,
-``hkg_gemm_bf16_run_plan_epilogue``, ``hkg_status_string``); ``gemm`` is the
-torch-facing convenience wrapper (with ``bias=`` and ``epilogue=`` for the
+``hkg_gemm_bf16_run_plan_epilogue``, ``hkg_status_string``, and the MXFP8
+calls ``hkg_gemm_mxfp8``, ``hkg_gemm_mxfp8_plan``, ``hkg_mx_pack_scales``,
+``hkg_mx_packed_scales_bytes``, ``hkg_gemm_mxfp8_prepacked``,
+``hkg_gemm_mxfp8_run_plan``); ``gemm`` and ``gemm_mxfp8`` are the
+torch-facing convenience wrappers (with ``bias=`` and ``epilogue=`` for the
 fused epilogues).  torch supplies device memory and streams.
 
 There is no fallback: if the library is not built and cannot be built, or a
@@ -17,7 +21,9 @@ import os
 __all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_plan",
            "hkg_gemm_bf16_run_plan", "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string",
            "hkg_last_hip_error", "gemm", "plan", "run_plan", "library_path", "EXPORTED_SYMBOLS",
-           "KERNEL_NAMES", "EPILOGUES"]
+           "KERNEL_NAMES", "EPILOGUES", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
+           "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan", "gemm_mxfp8",
+           "mx_plan", "mx_pack_scales", "run_mx_plan"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -33,15 +39,16 @@ HKG_ERR_NO_DEVICE = -4
 HKG_ERR_ARCH = -5
 HKG_ERR_HIP = -6
 HKG_ERR_WORKSPACE = -7
-KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO"}
-HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO = range(5)
+KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE"}
+HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE = range(6)
 
 # hkg_epilogue_t codes by the FlyDSL guide's names
 EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
 
 EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_plan", "hkg_gemm_bf16_run_plan",
                     "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string", "hkg_last_hip_error",
-                    "hkg_abi_version"]
+                    "hkg_abi_version", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
+                    "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan"]
 
 
 class Plan(ctypes.Structure):
@@ -118,6 +125,19 @@ def _load():
     lib.hkg_last_hip_error.restype = ctypes.c_char_p
     lib.hkg_abi_version.argtypes = []
     lib.hkg_abi_version.restype = ctypes.c_int32
+    i32 = ctypes.c_int32
+    lib.hkg_gemm_mxfp8_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    lib.hkg_gemm_mxfp8_plan.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp8.restype = ctypes.c_int
+    lib.hkg_mx_packed_scales_bytes.argtypes = [i64, i64]
+    lib.hkg_mx_packed_scales_bytes.restype = i64
+    lib.hkg_mx_pack_scales.argtypes = [vp, vp, i64, i64, vp]
+    lib.hkg_mx_pack_scales.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp8_prepacked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp8_prepacked.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp8_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp8_run_plan.restype = ctypes.c_int
     if lib.hkg_abi_version() != HKG_ABI_VERSION:
         raise ImportError("libhkg.so ABI version %d, binding expects %d" % (lib.hkg_abi_version(), HKG_ABI_VERSION))
     _lib = lib
@@ -153,6 +173,33 @@ def hkg_gemm_bf16_epilogue(A, B, bias, C, M, N, K, epilogue, stream=None):
 def hkg_gemm_bf16_run_plan_epilogue(plan_, A, B, bias, C, M, N, K, epilogue, stream=None):
     return _load().hkg_gemm_bf16_run_plan_epilogue(ctypes.byref(plan_), A, B, bias, C, M, N, K, epilogue,
                                                    stream)
+
+
+def hkg_gemm_mxfp8(A, SA, B, SB, bias, C, M, N, K, epilogue=0, stream=None):
+    """C-ABI call with raw device addresses (ints); returns the status code."""
+    return _load().hkg_gemm_mxfp8(A, SA, B, SB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_mxfp8_plan(M, N, K):
+    p = Plan()
+    st = _load().hkg_gemm_mxfp8_plan(M, N, K, ctypes.byref(p))
+    return st, p
+
+
+def hkg_mx_packed_scales_bytes(rows, K):
+    return _load().hkg_mx_packed_scales_bytes(rows, K)
+
+
+def hkg_mx_pack_scales(S, P, rows, K, stream=None):
+    return _load().hkg_mx_pack_scales(S, P, rows, K, stream)
+
+
+def hkg_gemm_mxfp8_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
+    return _load().hkg_gemm_mxfp8_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_mxfp8_run_plan(plan_, A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
+    return _load().hkg_gemm_mxfp8_run_plan(ctypes.byref(plan_), A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
 
 
 def hkg_status_string(status):
@@ -246,4 +293,86 @@ def run_plan(plan_, a, b, out=None, stream=None, bias=None, epilogue="none"):
                                                          _stream_handle(stream, a.device))
     if st != HKG_OK:
         raise HkgError(st, "hkg_gemm_bf16_run_plan" if code == 0 else "hkg_gemm_bf16_run_plan_epilogue")
+    return out
+
+
+# ------------------------------------------------------------------ MXFP8
+def _check_mx(a, sa, b, sb, out, packed):
+    """Shapes of uint8 device tensors: a M x K and b N x K E4M3 codes; sa, sb the
+    E8M0 scales, M x K/32 and N x K/32 (or, packed, the packed byte counts)."""
+    import torch
+    for t, name in ((a, "A"), (b, "B"), (sa, "SA"), (sb, "SB")):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.device != a.device:
+            raise ValueError("%s must be a contiguous uint8 device tensor on A's device" % name)
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("A must be M x K and B N x K, got %s and %s" % (tuple(a.shape), tuple(b.shape)))
+    M, K = a.shape
+    N = b.shape[0]
+    if packed:
+        if sa.numel() != max(0, hkg_mx_packed_scales_bytes(M, K)) or \
+                sb.numel() != max(0, hkg_mx_packed_scales_bytes(N, K)):
+            raise ValueError("packed scales must hold hkg_mx_packed_scales_bytes(rows, K) bytes")
+    elif tuple(sa.shape) != (M, K // 32) or tuple(sb.shape) != (N, K // 32):
+        raise ValueError("SA must be M x K/32 and SB N x K/32")
+    if out is not None and (out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
+                            or out.device != a.device):
+        raise ValueError("out must be a contiguous bf16 %d x %d tensor on A's device" % (M, N))
+    return M, N, K
+
+
+def gemm_mxfp8(a, sa, b, sb, out=None, stream=None, bias=None, epilogue="none", packed=False):
+    """C = epilogue(MXFP8 a @ b.T + bias): a (M x K) and b (N x K) uint8 E4M3
+    codes, sa / sb their E8M0 scales (M x K/32, N x K/32; or packed by
+    mx_pack_scales when packed=True), K % 128 == 0."""
+    import torch
+    M, N, K = _check_mx(a, sa, b, sb, out, packed)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    fn = _load().hkg_gemm_mxfp8_prepacked if packed else _load().hkg_gemm_mxfp8
+    with torch.cuda.device(a.device):
+        st = fn(a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(), bias_ptr or None, out.data_ptr(), M, N, K,
+                code, _stream_handle(stream, a.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp8_prepacked" if packed else "hkg_gemm_mxfp8")
+    return out
+
+
+def mx_pack_scales(s, K, stream=None):
+    """Packed form (uint8 device tensor) of E8M0 scales s (rows x K/32)."""
+    import torch
+    if s.dtype != torch.uint8 or s.dim() != 2 or not s.is_cuda or not s.is_contiguous() or s.shape[1] * 32 != K:
+        raise ValueError("scales must be a contiguous uint8 rows x K/32 device tensor")
+    rows = s.shape[0]
+    n = hkg_mx_packed_scales_bytes(rows, K)
+    if n < 0:
+        raise HkgError(HKG_ERR_INVALID_ARG, "hkg_mx_packed_scales_bytes")
+    p = torch.empty(n, dtype=torch.uint8, device=s.device)
+    with torch.cuda.device(s.device):
+        st = _load().hkg_mx_pack_scales(s.data_ptr(), p.data_ptr(), rows, K, _stream_handle(stream, s.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_mx_pack_scales")
+    return p
+
+
+def mx_plan(M, N, K):
+    st, p = hkg_gemm_mxfp8_plan(M, N, K)
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp8_plan")
+    return p
+
+
+def run_mx_plan(plan_, a, pa, b, pb, out=None, stream=None, bias=None, epilogue="none"):
+    """Runs an MXFP8 plan on packed scales pa, pb."""
+    import torch
+    M, N, K = _check_mx(a, pa, b, pb, out, True)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    with torch.cuda.device(a.device):
+        st = _load().hkg_gemm_mxfp8_run_plan(ctypes.byref(plan_), a.data_ptr(), pa.data_ptr(), b.data_ptr(),
+                                             pb.data_ptr(), bias_ptr or None, out.data_ptr(), M, N, K, code,
+                                             _stream_handle(stream, a.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp8_run_plan")
     return out

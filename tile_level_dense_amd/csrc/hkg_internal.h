@@ -19,6 +19,14 @@ constexpr int TILE_NUM_VARIANTS = 0
 #undef HKG_COUNT_TILE
     ;
 
+// MXFP8 tile-kernel instantiations (plan.variant for HKG_KERNEL_MX_TILE):
+// the rows of HKG_MX_TILE_CONFIGS.
+constexpr int MX_TILE_NUM_VARIANTS = 0
+#define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1
+    HKG_MX_TILE_CONFIGS(HKG_COUNT_TILE)
+#undef HKG_COUNT_TILE
+    ;
+
 // Default tile ladder of the planner, largest first (variant indices).
 constexpr int TILE_LADDER[] = {0, 1, 2};
 
@@ -37,6 +45,11 @@ constexpr bool tile_split_capable(int bm, int bn, int wm, int wn) { return (bm /
 TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 
+TileShape mx_tile_shape(int variant);
+int mx_tile_lds_bytes(int variant);
+// Bytes of the packed scales of `rows` rows (rows rounded up to 64).
+int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
+
 struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy; };
 SkinnyShape skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
@@ -50,6 +63,16 @@ int skinny_lds_bytes(int variant);
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int xcd_chunk, int split_k, float* ws,
                        int* counters, const uint16_t* bias, int epi, hipStream_t stream);
+
+// MXFP8 tile kernel: A, B E4M3 codes, K % 128 == 0, psa / psb the packed
+// scales (launch_mx_pack) of A and B; other arguments as launch_tile.
+hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                          int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
+                          int epi, const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
+
+// Packs rows x (K / 32) E8M0 codes S into the tile kernel's layout P
+// (mx_packed_scale_bytes(rows, K) bytes, 4-byte aligned).
+hipError_t launch_mx_pack(const uint8_t* S, uint32_t* P, int64_t rows, int64_t K, hipStream_t stream);
 
 // split_k == 1: plain launch.  split_k > 1: fp32 partials in `ws`
 // (split_k * M * N floats) and per-column-block arrival counters in `counters`
@@ -68,6 +91,7 @@ hipError_t launch_zero(uint16_t* C, int64_t M, int64_t N, const uint16_t* bias, 
 // hkg_resources.inc; -1 where unknown).
 struct KernelResources { const char* name; int vgprs, agprs, sgprs, scratch, lds; };
 const KernelResources* tile_resources(int variant);
+const KernelResources* mx_tile_resources(int variant);
 const KernelResources* skinny_resources(int variant);
 const KernelResources* generic_resources();
 

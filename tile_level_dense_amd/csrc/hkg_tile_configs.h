@@ -22,3 +22,10 @@
     X(256, 256, 64, 2, 2, 4, 2)   \
     X(256, 256, 64, 2, 2, 4, 5)   \
     X(256, 256, 64, 2, 2, 4, 0)
+
+// MXFP8 instantiations (E4M3 operands, E8M0 scale per 32 k), same fields;
+// BK = 128 k (128 bytes per row, as the bf16 BK = 64), SCHED 5 or 0 (a
+// two-stage ring).  Wave tiles are whole 64-row scale groups.
+#define HKG_MX_TILE_CONFIGS(X)     \
+    X(256, 256, 128, 2, 4, 2, 5)   \
+    X(128, 128, 128, 2, 2, 2, 0)
