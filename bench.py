@@ -17,6 +17,12 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                bias + SiLU (decode) epilogue
   vendor_context  torch.mm (hipBLASLt) on the same inputs with the same
                timing, for comparison across machines whose clocks differ
+  mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
+               mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
+               MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
+               buffers), with scales packed once (the kernel) and per call
+               (hkg_gemm_mxfp8 with natural-layout scales); torch._scaled_mm
+               with one scale per tensor for context
 
 Progress and diagnostics go to stderr.  Timing uses HIP events on the stream
 the kernels are launched on (torch's current stream), bracketed by device
@@ -36,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BF16 GEMM TFLOP/s @8192³ (% of 2.5 PF) + HBM GB/s @M=16 decode (% of 8 TB/s)"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 LLC_BYTES = 256 * 2**20
 # HipKittens' best 8192^3 BF16 GEMM on MI355X (talk notes, Table 2).
@@ -184,6 +191,100 @@ def bench_decode(torch, hkg, steps, warmup):
                 epi_ms=ms_e, epi_gbps=(alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9)
 
 
+def mx_to_dev(x, torch):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda")
+
+
+def vendor_fp8(torch, a, b, out):
+    """torch._scaled_mm on the same E4M3 codes with unit per-tensor scales
+    (not block-scaled; context only), or None where unsupported."""
+    one = torch.ones((), device="cuda")
+    af, bf = a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn)
+    try:
+        torch._scaled_mm(af, bf.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    except Exception as ex:              # noqa: BLE001 - context figure only
+        log("torch._scaled_mm unavailable: %s" % str(ex)[:100])
+        return None
+    return lambda: torch._scaled_mm(af, bf.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+
+
+def bench_mx_square(torch, hkg, steps, warmup):
+    import workloads
+    name = "mx_square_8192"
+    w = workloads.MX_WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    log("generating %s inputs" % name)
+    A, SA, B, SB = workloads.mx_workload_inputs(name)
+    a, sa, b, sb = (mx_to_dev(x, torch) for x in (A, SA, B, SB))
+    del A, SA, B, SB
+    pa, pb = hkg.mx_pack_scales(sa, K), hkg.mx_pack_scales(sb, K)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    plan = hkg.mx_plan(M, N, K)
+    log("mx plan", plan.kernel_name.decode(), plan.reason.decode())
+    flops = 2.0 * M * N * K
+    ms = time_launches(torch, lambda: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True), steps, warmup)
+    ms_nat = time_launches(torch, lambda: hkg.gemm_mxfp8(a, sa, b, sb, out=c), steps, warmup)
+    log("mx square: %.3f ms/step (%.1f TFLOP/s) packed scales, %.3f ms with per-call packing"
+        % (ms, flops / ms / 1e9, ms_nat))
+    fn = vendor_fp8(torch, a, b, c)
+    ms_v = time_launches(torch, fn, steps, warmup) if fn else None
+    if ms_v:
+        log("mx square, torch._scaled_mm per-tensor fp8 for context: %.3f ms (%.1f TFLOP/s)" % (ms_v, flops / ms_v / 1e9))
+    return dict(M=M, N=N, K=K, ms=ms, tflops=flops / ms / 1e9, ms_nat=ms_nat, tflops_nat=flops / ms_nat / 1e9,
+                flops=flops, plan=plan, vendor_tflops=(flops / ms_v / 1e9) if ms_v else None)
+
+
+def bench_mx_decode(torch, hkg, steps, warmup):
+    import workloads
+    name = "mx_decode_32x4096x4096"
+    w = workloads.MX_WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    A, SA, B, SB = workloads.mx_workload_inputs(name)
+    alg_bytes = float(M * K + N * K + (M + N) * (K // 32) + 2 * M * N)
+    per_set = M * K + N * K + (M + N) * (K // 32) * 2 + 2 * M * N
+    sets = int(np.ceil(2 * LLC_BYTES / per_set))
+    a0, sa0, b0, sb0 = (mx_to_dev(x, torch) for x in (A, SA, B, SB))
+    bufs = []
+    for _ in range(sets):
+        a, sa, b, sb = a0.clone(), sa0.clone(), b0.clone(), sb0.clone()
+        bufs.append((a, sa, hkg.mx_pack_scales(sa, K), b, sb, hkg.mx_pack_scales(sb, K),
+                     torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    plan = hkg.mx_plan(M, N, K)
+    log("mx decode plan", plan.kernel_name.decode(), plan.reason.decode(), "over %d buffer sets" % sets)
+    stream = torch.cuda.Stream()
+    reps = max(1, steps // sets)
+
+    def graph_of(call):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for buf in bufs:
+                call(*buf)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for buf in bufs:
+                call(*buf)
+        return g
+
+    g_pk = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True))
+    ms = time_launches(torch, g_pk.replay, reps, max(1, warmup // sets)) / sets
+    g_nat = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, sa, b, sb, out=c))
+    ms_nat = time_launches(torch, g_nat.replay, reps, max(1, warmup // sets)) / sets
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    log("mx decode: %.2f us/call rotating (%.0f GB/s) packed scales, %.2f us with per-call packing"
+        % (ms * 1e3, gbps, ms_nat * 1e3))
+    ms_v = None
+    if vendor_fp8(torch, bufs[0][0], bufs[0][3], bufs[0][6]):
+        one = torch.ones((), device="cuda")
+        g_v = graph_of(lambda a, sa, pa, b, sb, pb, c: torch._scaled_mm(
+            a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn).t(), scale_a=one, scale_b=one,
+            out_dtype=torch.bfloat16))
+        ms_v = time_launches(torch, g_v.replay, reps, max(1, warmup // sets)) / sets
+        log("mx decode, torch._scaled_mm per-tensor fp8 for context: %.2f us" % (ms_v * 1e3))
+    return dict(M=M, N=N, K=K, ms=ms, gbps=gbps, ms_nat=ms_nat, alg_bytes=alg_bytes, sets=sets, plan=plan,
+                launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
+
+
 def calibration_copy(torch, mib=1024):
     """One device-to-device copy of a known size (mib MiB read, mib MiB
     written), the reference dispatch for scaling HBM byte counters."""
@@ -227,7 +328,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
-    ap.add_argument("--only", choices=["square", "decode"], help="time one leg only (profiler runs)")
+    ap.add_argument("--only", choices=["square", "decode", "mx"], help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -246,11 +347,19 @@ def main():
         print(json.dumps({"decode_gbps": round(dec["gbps"], 1), "us_per_call": round(dec["ms"] * 1e3, 3),
                           "llc_resident_gbps": round(dec["gbps_hot"], 1)}), flush=True)
         return 0
+    if args.only == "mx":
+        mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
+        mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+        print(json.dumps({"mx_square_tflops": round(mxs["tflops"], 2), "mx_decode_gbps": round(mxd["gbps"], 1)}),
+              flush=True)
+        return 0
     sq = bench_square(torch, hkg, args.steps, args.warmup)
     if args.only == "square":
         print(json.dumps({"square_tflops": round(sq["tflops"], 2), "ms_per_step": round(sq["ms"], 4)}), flush=True)
         return 0
     dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+    mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
+    mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
@@ -297,6 +406,27 @@ def main():
         "vendor_context": {"library": "torch.mm (hipBLASLt), same inputs and timing in the same run",
                            "square_tflops": round(sq["vendor_tflops"], 2),
                            "decode_gbps": round(dec["vendor_gbps"], 1)},
+        "mxfp8": {
+            "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",
+                       "tflops": round(mxs["tflops"], 2), "ms": round(mxs["ms"], 4),
+                       "per_call_packing_tflops": round(mxs["tflops_nat"], 2),
+                       "roofline": {"bound": "mfma", "achieved": round(mxs["tflops"], 2), "peak": PEAK_FP8_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(mxs["tflops"] / PEAK_FP8_TFLOPS, 4),
+                                    "traffic": measured_traffic(mxs["plan"].kernel_name.decode()),
+                                    "kernel": mxs["plan"].kernel_name.decode(),
+                                    "per_launch": "2 M N K = %.4g flop per launch" % mxs["flops"]},
+                       "vendor_fp8_per_tensor_tflops": round(mxs["vendor_tflops"], 2) if mxs["vendor_tflops"] else None},
+            "decode": {"workload": "mx_decode_32x4096x4096: M = 32, N = K = 4096, B N(0, 0.02)",
+                       "gbps": round(mxd["gbps"], 1), "us_per_call": round(mxd["ms"] * 1e3, 3),
+                       "per_call_packing_us": round(mxd["ms_nat"] * 1e3, 3),
+                       "roofline": {"bound": "hbm", "achieved": round(mxd["gbps"], 1), "peak": PEAK_HBM_GBPS,
+                                    "unit": "GB/s", "frac": round(mxd["gbps"] / PEAK_HBM_GBPS, 4),
+                                    "traffic": measured_traffic(mxd["plan"].kernel_name.decode()),
+                                    "kernel": mxd["plan"].kernel_name.decode(),
+                                    "per_launch": "M K + N K + (M + N) K / 32 + 2 M N = %d bytes" % mxd["alg_bytes"]},
+                       "rotating_sets": mxd["sets"], "launches_timed": mxd["launches"],
+                       "vendor_fp8_per_tensor_us": round(mxd["vendor_us"], 3) if mxd["vendor_us"] else None},
+        },
     }
     print(json.dumps(line), flush=True)
     return 0
