@@ -50,6 +50,10 @@ def _bind(path):
     lib.hkg_oracle_gemm_entries.argtypes = [u16p, u16p, i64, i64, i64, i64p, i64p, i64,
                                             u16p, f64p, f64p, ctypes.c_int]
     lib.hkg_oracle_gemm_entries.restype = None
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.hkg_oracle_grouped_gemm_rows.argtypes = [u16p, u16p, i32p, i64, i64, i64, i64, i64, i64,
+                                                 u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_grouped_gemm_rows.restype = ctypes.c_int
     lib.hkg_oracle_max_threads.argtypes = []
     lib.hkg_oracle_max_threads.restype = ctypes.c_int
     u8p = ctypes.POINTER(ctypes.c_uint8)
@@ -133,6 +137,33 @@ class Oracle:
                 _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), M, N, K, r0, r1,
                 _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double),
                 _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+    def grouped_gemm(self, A, B, offs, rows=None, nthreads=0):
+        """Grouped C: A (M x K bf16 bits), B (G x N x K), offs (G int, row ends
+        of each expert, non-decreasing, <= M).  Rows [r0, r1), default all rows
+        of experts [0, offs[-1]).  Returns (C, S, absS)."""
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        B = np.ascontiguousarray(B, dtype=np.uint16)
+        offs = np.ascontiguousarray(offs, dtype=np.int32)
+        if A.ndim != 2 or B.ndim != 3 or A.shape[1] != B.shape[2] or offs.shape != (B.shape[0],):
+            raise ValueError("A must be M x K, B G x N x K and offs G values")
+        M, K = A.shape
+        G, N = B.shape[0], B.shape[1]
+        if G and (np.any(np.diff(offs) < 0) or offs[0] < 0 or offs[-1] > M):
+            raise ValueError("offsets must be non-decreasing within [0, M]")
+        end = int(offs[-1]) if G else 0
+        r0, r1 = (0, end) if rows is None else rows
+        if not (0 <= r0 <= r1 <= M):
+            raise ValueError("row range out of bounds")
+        C = np.zeros((r1 - r0, N), dtype=np.uint16)
+        S = np.zeros((r1 - r0, N), dtype=np.float64)
+        absS = np.zeros((r1 - r0, N), dtype=np.float64)
+        if r1 > r0 and N > 0:
+            self.lib.hkg_oracle_grouped_gemm_rows(
+                _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), _ptr(offs, ctypes.c_int32), G, M, N, K,
+                r0, r1, _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double), _ptr(absS, ctypes.c_double),
+                int(nthreads))
         return C, S, absS
 
     def gemm_entries(self, A, B, ii, jj, nthreads=0):
@@ -285,6 +316,10 @@ def max_threads():
 
 def gemm(A, B, rows=None, nthreads=0, want_sums=True):
     return default().gemm(A, B, rows, nthreads, want_sums)
+
+
+def grouped_gemm(A, B, offs, rows=None, nthreads=0):
+    return default().grouped_gemm(A, B, offs, rows, nthreads)
 
 
 def gemm_entries(A, B, ii, jj, nthreads=0):

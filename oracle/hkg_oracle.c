@@ -37,6 +37,10 @@
  *   MXFP8: every E4M3 and E8M0 code against torch's float8_e4m3fn and
  *   float8_e8m0fnu conversions; all-ones with unit scales (C = K); scale
  *   changes multiply exactly by powers of two; exact rationals on tiny shapes.
+ *   Grouped GEMM: one expert equals the dense oracle; all-ones activations
+ *   against expert weights filled with (g + 1) give C = K (g + 1) exactly in
+ *   each expert's rows (boundaries, empty experts); permuting the experts
+ *   permutes the rows; exact rationals on tiny shapes.
  *   Epilogue: bias through all-ones products (C = K + b, exact), ReLU's
  *   definition, the odd parts SiLU(x) - SiLU(-x) = x and GELU(x) - GELU(-x) = x,
  *   the closed form sigmoid(ln 3) = 3/4, the normal quantile Phi(1.959963985)
@@ -179,6 +183,63 @@ void hkg_oracle_gemm_entries(const uint16_t* A, const uint16_t* B,
 }
 
 int hkg_oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* ---- grouped GEMM ----------------------------------------------------------
+ * The FlyDSL-in-PyTorch blog (grouped GEMM section, mixture of experts): the
+ * activations of all experts concatenated as A[sum of M_g, K], one weight per
+ * expert, and offsets marking where each expert's rows end.  Read with this
+ * library's NT convention (each expert's weight N x K, K contiguous, stacked
+ * as B[G][N][K]) and offs[g] the end (exclusive) of expert g's rows, expert g
+ * owns rows [offs[g-1], offs[g]) (offs[-1] = 0), and
+ *     C[i][j] = bf16( sum over k of A[i][k] * B[g][j][k] )   for i in group g,
+ * i.e. the dense definition above with the row's own expert weight.  Offsets
+ * are non-decreasing; rows at or past offs[G-1] belong to no expert.
+ */
+static int64_t group_of_row(const int32_t* offs, int64_t G, int64_t i)
+{
+    /* first g with offs[g] > i; G if none */
+    int64_t lo = 0, hi = G;
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if ((int64_t)offs[mid] > i)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+/* Rows [row_begin, row_end) of the grouped product; outputs as in
+ * hkg_oracle_gemm_rows.  Rows of no expert give C = 0, S = absS = 0 and
+ * return value 0 for the caller to know; 1 otherwise (all rows grouped). */
+int hkg_oracle_grouped_gemm_rows(const uint16_t* A, const uint16_t* B, const int32_t* offs, int64_t G,
+                                 int64_t M, int64_t N, int64_t K, int64_t row_begin, int64_t row_end,
+                                 uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    build_table();
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+    int all_grouped = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(&& : all_grouped)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        const int64_t g = group_of_row(offs, G, i);
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0, sa = 0.0;
+            if (g < G)
+                dot_one(A + i * K, B + (g * N + j) * K, K, &s, &sa);
+            int64_t o = (i - row_begin) * N + j;
+            C[o] = hkg_oracle_bf16_rne(s);
+            if (S)
+                S[o] = s;
+            if (absS)
+                absS[o] = sa;
+        }
+        if (g >= G)
+            all_grouped = 0;
+    }
+    return all_grouped;
+}
 
 /* ---- fused epilogue ------------------------------------------------------
  * The FlyDSL "prebuilt_kernels_guide" page (section 3.1, Preshuffle GEMM,

@@ -334,13 +334,71 @@ def check_mx_brute_force_tiny(O):
                 assert C[i, j] == exact.round_exact(s), (trial, i, j)
 
 
+# ------------------------------------------------------------ grouped GEMM
+# FlyDSL-in-PyTorch blog, grouped GEMM section: concatenated expert rows,
+# one weight per expert, cumulative row-end offsets.
+
+def check_grouped_one_expert_is_dense(O):
+    A, B = workloads.make_inputs(37, 21, 96, seed=11)
+    C1, S1, a1 = O.grouped_gemm(A, B[None], np.array([37], np.int32))
+    C2, S2, a2 = O.gemm(A, B)
+    assert np.array_equal(C1, C2) and np.array_equal(S1, S2) and np.array_equal(a1, a2)
+
+
+def check_grouped_expert_identity(O):
+    # All-ones activations; expert g's weight is all (g + 1) (exact bf16
+    # integers), so row i's outputs are K (g + 1) with g its expert: fixes
+    # every boundary, empty experts (repeated offsets) included.
+    K, N = 64, 5
+    offs = np.array([0, 3, 3, 9, 10, 10, 17], dtype=np.int32)       # experts 0, 2, 5 empty
+    G, M = offs.size, 20
+    A = np.full((M, K), 0x3F80, dtype=np.uint16)
+    vals = np.arange(1, G + 1, dtype=np.float32)
+    B = np.repeat(workloads.f32_to_bf16_bits(vals)[:, None, None], N, axis=1).repeat(K, axis=2)
+    C, S, _ = O.grouped_gemm(A, B, offs)
+    assert C.shape == (17, N)
+    want_g = np.searchsorted(offs, np.arange(17), side="right")
+    assert np.array_equal(S, np.repeat((K * (want_g + 1.0))[:, None], N, axis=1))
+
+
+def check_grouped_permutation(O):
+    # Reordering the experts (with their rows) reorders the output rows.
+    rng = np.random.default_rng(4)
+    sizes = np.array([5, 0, 9, 3])
+    A, _ = workloads.make_inputs(int(sizes.sum()), 1, 64, seed=5)
+    B = workloads.draw(rng, (4, 11, 64), ("uniform", -1.0, 1.0))
+    offs = np.cumsum(sizes).astype(np.int32)
+    C, S, _ = O.grouped_gemm(A, B, offs)
+    perm = [2, 0, 3, 1]
+    starts = np.concatenate([[0], offs[:-1]])
+    rows = np.concatenate([np.arange(starts[g], offs[g]) for g in perm]).astype(np.int64)
+    C2, S2, _ = O.grouped_gemm(A[rows], B[perm], np.cumsum(sizes[perm]).astype(np.int32))
+    assert np.array_equal(C2, C[rows]) and np.array_equal(S2, S[rows])
+
+
+def check_grouped_brute_force_tiny(O):
+    rng = np.random.default_rng(12)
+    A = workloads.draw(rng, (6, 16), ("normal", 0.0, 1.0))
+    B = workloads.draw(rng, (3, 4, 16), ("normal", 0.0, 1.0))
+    offs = np.array([2, 2, 6], dtype=np.int32)
+    C, S, absS = O.grouped_gemm(A, B, offs)
+    av, bv = exact.widen(A), exact.widen(B)
+    for i in range(6):
+        g = 0 if i < 2 else 2
+        for j in range(4):
+            s = sum(Fraction(float(av[i, k])) * Fraction(float(bv[g, j, k])) for k in range(16))
+            assert abs(Fraction(S[i, j]) - s) <= 16 * Fraction(2) ** -53 * Fraction(absS[i, j])
+            assert C[i, j] == exact.round_exact(s)
+
+
 ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
               check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
               check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
               check_transpose_symmetry, check_epilogue_bias_exact, check_epilogue_closed_forms,
               check_epilogue_odd_parts, check_epilogue_columns, check_e4m3_exhaustive,
               check_e8m0_exhaustive, check_mx_all_ones, check_mx_unit_scales_equal_bf16_gemm,
-              check_mx_scales_are_powers_of_two, check_mx_brute_force_tiny]
+              check_mx_scales_are_powers_of_two, check_mx_brute_force_tiny, check_grouped_one_expert_is_dense,
+              check_grouped_expert_identity, check_grouped_permutation, check_grouped_brute_force_tiny]
 
 
 @pytest.fixture(scope="module")
@@ -449,6 +507,11 @@ MUTANTS = {
                               "y = hkg_oracle_activation(S[t], epi) + hkg_oracle_bf16_value(bias[j]);"),
     "bias_shifted_column": ("const int64_t j = cols ? cols[t] : t % N;",
                             "const int64_t j = cols ? cols[t] : (t + 1) % N;"),
+    "group_boundary_inclusive": ("if ((int64_t)offs[mid] > i)", "if ((int64_t)offs[mid] >= i)"),
+    "group_next_expert": ("dot_one(A + i * K, B + (g * N + j) * K, K, &s, &sa);",
+                          "dot_one(A + i * K, B + (((g + 1) % G) * N + j) * K, K, &s, &sa);"),
+    "group_always_first": ("const int64_t g = group_of_row(offs, G, i);",
+                           "const int64_t g = group_of_row(offs, G, i) < G ? 0 : G;"),
     "mx_one_scale_per_row": ("(g_e4m3[a_row[k]] * hkg_oracle_e8m0_value(sa_row[k / 32]))",
                              "(g_e4m3[a_row[k]] * hkg_oracle_e8m0_value(sa_row[0]))"),
     "mx_b_scaled_by_a": ("(g_e4m3[b_row[k]] * hkg_oracle_e8m0_value(sb_row[k / 32]))",

@@ -121,3 +121,36 @@ def make_mx_inputs(M, N, K, a=("normal", 0.0, 1.0), b=("normal", 0.0, 1.0), seed
 def mx_workload_inputs(name, seed=0):
     w = MX_WORKLOADS[name]
     return make_mx_inputs(w["M"], w["N"], w["K"], w["a"], w["b"], seed)
+
+
+# ------------------------------------------------------------ grouped GEMM
+# Mixture-of-experts GEMMs (FlyDSL-in-PyTorch blog, grouped GEMM section):
+# the rows of all experts concatenated in A (sum of M_g rows), one N x K
+# weight per expert stacked in B (G x N x K), and int32 offsets holding each
+# expert's row end (cumulative sums of the sizes).  The blog measures uniform
+# expert loads and ragged ones with empty and heavily skewed experts; these
+# stand in for both.  Recipe: A drawn first, then B, from one seeded stream,
+# as for the dense workloads.
+GROUPED_WORKLOADS = {
+    "grouped_tiny": dict(sizes=[64, 0, 100, 92], N=256, K=256,
+                         a=("uniform", -1.0, 1.0), b=("uniform", -1.0, 1.0)),
+    "moe_uniform_8x1024_4096x4096": dict(sizes=[1024] * 8, N=4096, K=4096,
+                                         a=("normal", 0.0, 1.0), b=("normal", 0.0, 0.02)),
+    "moe_ragged_16_8192_4096x4096": dict(sizes=[0, 1500, 37, 0, 800, 3000, 1, 255, 256, 257, 0, 1024, 500, 62,
+                                                300, 200], N=4096, K=4096,
+                                         a=("normal", 0.0, 1.0), b=("normal", 0.0, 0.02)),
+}
+
+
+def make_grouped_inputs(sizes, N, K, a=("uniform", -1.0, 1.0), b=("uniform", -1.0, 1.0), seed=0):
+    """(A bits sum(sizes) x K, B bits G x N x K, offs int32 G) from one seeded stream."""
+    rng = np.random.default_rng(seed)
+    sizes = np.asarray(sizes, dtype=np.int64)
+    A = draw(rng, (int(sizes.sum()), K), a)
+    B = draw(rng, (sizes.size, N, K), b)
+    return A, B, np.cumsum(sizes).astype(np.int32)
+
+
+def grouped_workload_inputs(name, seed=0):
+    w = GROUPED_WORKLOADS[name]
+    return make_grouped_inputs(w["sizes"], w["N"], w["K"], w["a"], w["b"], seed)
