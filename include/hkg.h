@@ -68,7 +68,8 @@ typedef enum {
     HKG_KERNEL_SKINNY = 2,      /* small M: streams B once, split-K over waves / workgroups */
     HKG_KERNEL_GENERIC = 3,     /* any alignment, any K: correctness fallback */
     HKG_KERNEL_ZERO = 4,        /* K == 0: C is the empty sum, +0 (then the epilogue) */
-    HKG_KERNEL_MX_TILE = 5      /* MXFP8 large-tile kernel (scaled MFMA) */
+    HKG_KERNEL_MX_TILE = 5,     /* MXFP8 large-tile kernel (scaled MFMA) */
+    HKG_KERNEL_GROUPED = 6      /* grouped (mixture-of-experts) tile kernel, persistent grid */
 } hkg_kernel_t;
 
 /*
@@ -241,6 +242,38 @@ hkg_status_t hkg_gemm_mxfp8_prepacked(const void* A, const void* PA, const void*
 hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
                                      const void* PB, const void* bias, void* C, int64_t M, int64_t N,
                                      int64_t K, int32_t epilogue, void* stream);
+
+/*
+ * Grouped GEMM for mixture-of-experts layers (FlyDSL-in-PyTorch blog,
+ * grouped GEMM section: concatenated activations, one weight per expert,
+ * cumulative row offsets, one launch on a persistent grid):
+ *
+ *   C[i][j] = epilogue( sum over k of A[i][k] * B[g][j][k] + bias[g][j] ),
+ *             for offs[g-1] <= i < offs[g]  (offs[-1] = 0)
+ *
+ *   A: M x K bf16, the rows of all experts concatenated; B: G x N x K bf16,
+ *   expert g's weight N x K with K contiguous (the NT layout of
+ *   hkg_gemm_bf16; the blog's B[G, K, N] with unit stride along K); offs: G
+ *   int32 row ends, device memory, non-decreasing, at most M; C: M x N bf16.
+ *   Rows at or past offs[G-1] are not written.  bias: G x N bf16 (one row per
+ *   expert) for epilogues other than NONE.  Empty experts (equal offsets)
+ *   cost nothing.  Offsets are read on the device: values outside [0, M] are
+ *   clamped and a decreasing offset makes its expert empty, so no offsets
+ *   can make the kernel access memory outside A, B, C; the result for such
+ *   offsets is not specified.
+ *   A, B, C 16-byte aligned, offs 4-byte aligned, K % 8 == 0 (else
+ *   HKG_ERR_MISALIGNED / HKG_ERR_UNSUPPORTED; there is no general fallback).
+ *   M, N or G == 0 launches nothing.  Rounding as hkg_gemm_bf16.
+ */
+hkg_status_t hkg_grouped_gemm_bf16_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* out);
+
+hkg_status_t hkg_grouped_gemm_bf16(const void* A, const void* B, const void* offs, const void* bias, void* C,
+                                   int64_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream);
+
+/* Runs a grouped plan (variant, grid_x >= 1 and xcd_chunk_c may be edited). */
+hkg_status_t hkg_grouped_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* offs,
+                                            const void* bias, void* C, int64_t G, int64_t M, int64_t N, int64_t K,
+                                            int32_t epilogue, void* stream);
 
 /* Static description of a status code. */
 const char* hkg_status_string(hkg_status_t status);

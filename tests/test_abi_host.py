@@ -264,7 +264,7 @@ def test_build_resources_have_no_scratch():
     if not os.path.exists(path):
         hkg_build.build()
     res = json.load(open(path))
-    entries = res["tile"] + res["mx_tile"] + res["skinny"] + [res["generic"]]
+    entries = res["tile"] + res["mx_tile"] + res["grouped"] + res["skinny"] + [res["generic"]]
     for e in entries:
         assert e["scratch"] == 0 and e["vgpr_spill"] <= 0, e
 
@@ -428,3 +428,59 @@ def test_mx_no_device_status():
     A, SA, B, SB, C = [(1 << 30) + i * (1 << 22) for i in range(5)]
     assert hkg.hkg_gemm_mxfp8(A, SA, B, SB, None, C, M, N, K) == hkg.HKG_ERR_NO_DEVICE
     assert hkg.hkg_mx_pack_scales(SA, SB, M, K) == hkg.HKG_ERR_NO_DEVICE
+
+
+# ------------------------------------------------------------ grouped GEMM
+@pytest.mark.parametrize("shape,variant,grid", [
+    ((8, 8192, 4096, 4096), 0, 256),      # experts of 1024 rows: 256 x 256 tiles, one workgroup per CU
+    ((16, 8192, 4096, 4096), 0, 256),
+    ((64, 4096, 2048, 1024), 1, 512),     # 64 rows per expert: 128 x 128, two per CU
+    ((4, 256, 256, 256), 1, 12),          # grid capped at the most tiles the experts can have
+])
+def test_grouped_plan_selection(shape, variant, grid):
+    G, M, N, K = shape
+    p = hkg.grouped_plan(*shape)
+    assert p.kernel_id == hkg.HKG_KERNEL_GROUPED and p.variant == variant and p.grid_x == grid, p
+    assert p.split_k == 1 and p.workspace_bytes == 0 and p.xcd_chunk_c == 1
+    assert p.algorithmic_bytes == 2 * (M * K + G * N * K + M * N)
+    assert p.vgprs > 0 and p.scratch_bytes == 0
+
+
+def test_grouped_plan_edges():
+    for shape in ((0, 64, 64, 64), (4, 0, 64, 64), (4, 64, 0, 64)):
+        st, p = hkg.hkg_grouped_gemm_bf16_plan(*shape)
+        assert st == hkg.HKG_OK and p.kernel_id == hkg.HKG_KERNEL_NONE
+    assert hkg.hkg_grouped_gemm_bf16_plan(-1, 64, 64, 64)[0] == hkg.HKG_ERR_INVALID_ARG
+    assert hkg.hkg_grouped_gemm_bf16_plan(4, 64, 64, 100)[0] == hkg.HKG_ERR_UNSUPPORTED     # K % 8
+
+
+def test_grouped_argument_errors_precede_device_work():
+    G, M, N, K = 4, 256, 128, 64
+    A, B, offs, C, bias = [(1 << 30) + i * (1 << 24) for i in range(5)]
+    f = hkg.hkg_grouped_gemm_bf16
+    assert f(None, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, B, None, None, C, G, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, B, offs, None, offs, G, M, N, K) == hkg.HKG_ERR_INVALID_ARG          # C overlaps offs
+    assert f(A, B, offs, None, C, G, M, N, K, 2) == hkg.HKG_ERR_INVALID_ARG          # bias needed
+    assert f(A, B, offs, bias + 1, C, G, M, N, K, 1) == hkg.HKG_ERR_MISALIGNED
+    assert f(A + 8, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_MISALIGNED
+    assert f(A, B, offs + 2, None, C, G, M, N, K) == hkg.HKG_ERR_MISALIGNED
+    assert f(A, B, offs, None, C, G, M, N, K, 9) == hkg.HKG_ERR_INVALID_ARG
+    assert f(None, None, None, None, None, 0, 0, N, K) == hkg.HKG_OK
+    p = hkg.grouped_plan(G, M, N, K)
+    r = hkg.hkg_grouped_gemm_bf16_run_plan
+    assert r(p, A, B, offs, None, C, G, M + 1, N, K) == hkg.HKG_ERR_INVALID_ARG
+    q = hkg.Plan.from_buffer_copy(p)
+    q.variant = 5
+    assert r(q, A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    assert r(hkg.plan(M, N, K), A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    q = hkg.Plan.from_buffer_copy(p)
+    q.grid_x = 0
+    assert r(q, A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device status; a GPU is present")
+def test_grouped_no_device_status():
+    G, M, N, K = 4, 256, 128, 64
+    A, B, offs, C = [(1 << 30) + i * (1 << 24) for i in range(4)]
+    assert hkg.hkg_grouped_gemm_bf16(A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_NO_DEVICE

@@ -8,8 +8,9 @@ the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_epilogue``,
 ``hkg_gemm_bf16_run_plan_epilogue``, ``hkg_status_string``, and the MXFP8
 calls ``hkg_gemm_mxfp8``, ``hkg_gemm_mxfp8_plan``, ``hkg_mx_pack_scales``,
 ``hkg_mx_packed_scales_bytes``, ``hkg_gemm_mxfp8_prepacked``,
-``hkg_gemm_mxfp8_run_plan``); ``gemm`` and ``gemm_mxfp8`` are the
-torch-facing convenience wrappers (with ``bias=`` and ``epilogue=`` for the
+``hkg_gemm_mxfp8_run_plan``, and the grouped calls ``hkg_grouped_gemm_bf16``,
+``hkg_grouped_gemm_bf16_plan``, ``hkg_grouped_gemm_bf16_run_plan``); ``gemm``,
+``gemm_mxfp8`` and ``grouped_gemm`` are the torch-facing convenience wrappers (with ``bias=`` and ``epilogue=`` for the
 fused epilogues).  torch supplies device memory and streams.
 
 There is no fallback: if the library is not built and cannot be built, or a
@@ -23,7 +24,8 @@ __all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_g
            "hkg_last_hip_error", "gemm", "plan", "run_plan", "library_path", "EXPORTED_SYMBOLS",
            "KERNEL_NAMES", "EPILOGUES", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
            "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan", "gemm_mxfp8",
-           "mx_plan", "mx_pack_scales", "run_mx_plan"]
+           "mx_plan", "mx_pack_scales", "run_mx_plan", "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan",
+           "hkg_grouped_gemm_bf16_run_plan", "grouped_gemm", "grouped_plan"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -39,8 +41,9 @@ HKG_ERR_NO_DEVICE = -4
 HKG_ERR_ARCH = -5
 HKG_ERR_HIP = -6
 HKG_ERR_WORKSPACE = -7
-KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE"}
-HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE = range(6)
+KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE", 6: "GROUPED"}
+(HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE,
+ HKG_KERNEL_GROUPED) = range(7)
 
 # hkg_epilogue_t codes by the FlyDSL guide's names
 EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
@@ -48,7 +51,8 @@ EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 
 EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_plan", "hkg_gemm_bf16_run_plan",
                     "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string", "hkg_last_hip_error",
                     "hkg_abi_version", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
-                    "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan"]
+                    "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan",
+                    "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan", "hkg_grouped_gemm_bf16_run_plan"]
 
 
 class Plan(ctypes.Structure):
@@ -138,6 +142,13 @@ def _load():
     lib.hkg_gemm_mxfp8_prepacked.restype = ctypes.c_int
     lib.hkg_gemm_mxfp8_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.hkg_gemm_mxfp8_run_plan.restype = ctypes.c_int
+    lib.hkg_grouped_gemm_bf16_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(Plan)]
+    lib.hkg_grouped_gemm_bf16_plan.restype = ctypes.c_int
+    lib.hkg_grouped_gemm_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.hkg_grouped_gemm_bf16.restype = ctypes.c_int
+    lib.hkg_grouped_gemm_bf16_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                                   vp]
+    lib.hkg_grouped_gemm_bf16_run_plan.restype = ctypes.c_int
     if lib.hkg_abi_version() != HKG_ABI_VERSION:
         raise ImportError("libhkg.so ABI version %d, binding expects %d" % (lib.hkg_abi_version(), HKG_ABI_VERSION))
     _lib = lib
@@ -200,6 +211,22 @@ def hkg_gemm_mxfp8_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=
 
 def hkg_gemm_mxfp8_run_plan(plan_, A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
     return _load().hkg_gemm_mxfp8_run_plan(ctypes.byref(plan_), A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_grouped_gemm_bf16(A, B, offs, bias, C, G, M, N, K, epilogue=0, stream=None):
+    """C-ABI call with raw device addresses (ints); returns the status code."""
+    return _load().hkg_grouped_gemm_bf16(A, B, offs, bias, C, G, M, N, K, epilogue, stream)
+
+
+def hkg_grouped_gemm_bf16_plan(G, M, N, K):
+    p = Plan()
+    st = _load().hkg_grouped_gemm_bf16_plan(G, M, N, K, ctypes.byref(p))
+    return st, p
+
+
+def hkg_grouped_gemm_bf16_run_plan(plan_, A, B, offs, bias, C, G, M, N, K, epilogue=0, stream=None):
+    return _load().hkg_grouped_gemm_bf16_run_plan(ctypes.byref(plan_), A, B, offs, bias, C, G, M, N, K, epilogue,
+                                                  stream)
 
 
 def hkg_status_string(status):
@@ -375,4 +402,50 @@ def run_mx_plan(plan_, a, pa, b, pb, out=None, stream=None, bias=None, epilogue=
                                              _stream_handle(stream, a.device))
     if st != HKG_OK:
         raise HkgError(st, "hkg_gemm_mxfp8_run_plan")
+    return out
+
+
+# ----------------------------------------------------------- grouped GEMM
+def grouped_plan(G, M, N, K):
+    st, p = hkg_grouped_gemm_bf16_plan(G, M, N, K)
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_grouped_gemm_bf16_plan")
+    return p
+
+
+def grouped_gemm(a, b, offs, out=None, stream=None, bias=None, epilogue="none", plan=None):
+    """Mixture-of-experts GEMM: a (M x K bf16, experts' rows concatenated),
+    b (G x N x K bf16, one weight per expert), offs (G int32 row ends, device),
+    bias (G x N bf16) for epilogues.  Rows of no expert in `out` are left as
+    they are (zeros when out is None)."""
+    import torch
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or offs.dtype != torch.int32:
+        raise TypeError("A, B must be torch.bfloat16 and offs torch.int32")
+    if a.dim() != 2 or b.dim() != 3 or a.shape[1] != b.shape[2] or offs.dim() != 1 or offs.shape[0] != b.shape[0]:
+        raise ValueError("A must be M x K, B G x N x K and offs G values")
+    for t in (a, b, offs):
+        if not t.is_cuda or not t.is_contiguous() or t.device != a.device:
+            raise ValueError("operands must be contiguous device tensors on one device")
+    M, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    code = EPILOGUES[epilogue]
+    bias_ptr = None
+    if code:
+        if bias is None or bias.dtype != torch.bfloat16 or tuple(bias.shape) != (G, N) or not bias.is_contiguous() \
+                or bias.device != a.device:
+            raise ValueError("epilogue %r needs a contiguous bf16 G x N bias on A's device" % epilogue)
+        bias_ptr = bias.data_ptr()
+    if out is None:
+        out = torch.zeros((M, N), dtype=torch.bfloat16, device=a.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != a.device:
+        raise ValueError("out must be a contiguous bf16 %d x %d tensor on A's device" % (M, N))
+    with torch.cuda.device(a.device):
+        args = (a.data_ptr(), b.data_ptr(), offs.data_ptr(), bias_ptr, out.data_ptr(), G, M, N, K, code,
+                _stream_handle(stream, a.device))
+        if plan is None:
+            st = _load().hkg_grouped_gemm_bf16(*args)
+        else:
+            st = _load().hkg_grouped_gemm_bf16_run_plan(ctypes.byref(plan), *args)
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_grouped_gemm_bf16")
     return out

@@ -1,7 +1,7 @@
 """Build libhkg.so (gfx950) in-tree from csrc/ with hipcc.
 
 Every kernel file is compiled with the compiler's kernel-resource-usage
-report; the build parses it, refuses any kernel with scratch use or register
+report; the build parses it, refuses any kernel with scratch use or VGPR
 spills, and compiles the figures into the library (hkg_plan_t reports them).
 """
 import concurrent.futures
@@ -30,11 +30,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 
-def tile_configs(mx=False):
-    """(BM, BN, BK, STAGES, WM, WN, SCHED) per tile variant (bf16, or MXFP8 with mx=True),
-    from hkg_tile_configs.h."""
+def tile_configs(mx=False, grouped=False):
+    """(BM, BN, BK, STAGES, WM, WN, SCHED) per tile variant (bf16; MXFP8 with mx=True;
+    grouped with grouped=True), from hkg_tile_configs.h."""
     text = open(os.path.join(CSRC, "hkg_tile_configs.h")).read()
-    start = text.index("#define HKG_MX_TILE_CONFIGS(X)" if mx else "#define HKG_TILE_CONFIGS(X)")
+    start = text.index("#define HKG_MX_TILE_CONFIGS(X)" if mx else
+                       "#define HKG_GROUPED_CONFIGS(X)" if grouped else "#define HKG_TILE_CONFIGS(X)")
     body = text[start:]
     end = body.find("#define", 10)
     body = body if end < 0 else body[:end]
@@ -44,6 +45,7 @@ def tile_configs(mx=False):
 
 TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
+GROUPED_VARIANTS = tile_configs(grouped=True)
 def skinny_configs():
     """(MB, NB, WK, U, CP) per skinny variant, from hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
@@ -106,17 +108,20 @@ def _entry(name, r):
 def _table(resources):
     tile = [None] * len(TILE_VARIANTS)
     mx_tile = [None] * len(MX_TILE_VARIANTS)
+    grouped = [None] * len(GROUPED_VARIANTS)
     skinny = [None] * len(SKINNY_VARIANTS)
     generic = None
     for mangled, r in resources.items():
         # The table holds the plain instantiations (no fused epilogue); the
         # gate below checks every kernel, epilogue instantiations included.
-        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E",
-                      mangled)
+        m = re.search(r"tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)"
+                      r"ELb([01])ELb([01])ELb([01])E", mangled)
         if m:
             key = tuple(int(g) for g in m.groups()[:7])
-            plain, mx = m.group(8) == "0", m.group(9) == "1"
-            if plain and not mx and key in TILE_VARIANTS:
+            plain, mx, grp = m.group(8) == "0", m.group(9) == "1", m.group(10) == "1"
+            if plain and grp and key in GROUPED_VARIANTS:
+                grouped[GROUPED_VARIANTS.index(key)] = _entry("grouped_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
+            elif plain and not mx and not grp and key in TILE_VARIANTS:
                 tile[TILE_VARIANTS.index(key)] = _entry("tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             elif plain and mx and key in MX_TILE_VARIANTS:
                 mx_tile[MX_TILE_VARIANTS.index(key)] = _entry("mxtile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
@@ -133,31 +138,37 @@ def _table(resources):
             pass
     missing = [i for i, e in enumerate(tile) if e is None] + \
               [100 + i for i, e in enumerate(skinny) if e is None] + \
-              [200 + i for i, e in enumerate(mx_tile) if e is None] + ([-1] if generic is None else [])
+              [200 + i for i, e in enumerate(mx_tile) if e is None] + \
+              [300 + i for i, e in enumerate(grouped) if e is None] + ([-1] if generic is None else [])
     if missing:
         raise BuildError("resource report missing kernels: %s" % missing)
-    return tile, mx_tile, skinny, generic
+    return tile, mx_tile, grouped, skinny, generic
 
 
 def _gate(entries):
-    bad = [e for e in entries if e["scratch"] != 0 or e["vgpr_spill"] > 0 or e["sgpr_spill"] > 0]
+    # Refused: any scratch use, any VGPR spill (memory traffic that the
+    # hand-placed vmcnt waits do not account for).  SGPR spills with no
+    # scratch live in VGPR lanes (v_writelane / v_readlane, no memory access)
+    # and are allowed.
+    bad = [e for e in entries if e["scratch"] != 0 or e["vgpr_spill"] > 0]
     if bad:
         raise BuildError("kernels use scratch / spill registers (refused): %s" % bad)
 
 
-def _write_inc(tile, mx_tile, skinny, generic):
+def _write_inc(tile, mx_tile, grouped, skinny, generic):
     def row(e):
         return '{"%s", %d, %d, %d, %d, %d}' % (e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"])
     text = "// generated by tile_level_dense_amd/build.py -- do not edit\n"
     text += "const KernelResources kTileResources[] = {\n    " + ",\n    ".join(row(e) for e in tile) + "};\n"
     text += "const KernelResources kMxTileResources[] = {\n    " + ",\n    ".join(row(e) for e in mx_tile) + "};\n"
+    text += "const KernelResources kGroupedResources[] = {\n    " + ",\n    ".join(row(e) for e in grouped) + "};\n"
     text += "const KernelResources kSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in skinny) + "};\n"
     text += "const KernelResources kGenericResources = " + row(generic) + ";\n"
     path = os.path.join(BUILD, "hkg_resources.inc")
     with open(path, "w") as f:
         f.write(text)
     with open(os.path.join(BUILD, "kernel_resources.json"), "w") as f:
-        json.dump(dict(tile=tile, mx_tile=mx_tile, skinny=skinny, generic=generic), f, indent=1)
+        json.dump(dict(tile=tile, mx_tile=mx_tile, grouped=grouped, skinny=skinny, generic=generic), f, indent=1)
 
 
 def build(verbose=False):
@@ -170,16 +181,16 @@ def build(verbose=False):
     res = {}
     for _, r in results:
         res.update(r)
-    tile, mx_tile, skinny, generic = _table(res)
+    tile, mx_tile, grouped, skinny, generic = _table(res)
     _gate([_entry(name, r) for name, r in res.items()])
-    _write_inc(tile, mx_tile, skinny, generic)
+    _write_inc(tile, mx_tile, grouped, skinny, generic)
     with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
         objs += [f.result()[0] for f in [ex.submit(_compile, s, False) for s in HOST_SOURCES]]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if verbose:
-        for e in tile + mx_tile + skinny + [generic]:
+        for e in tile + mx_tile + grouped + skinny + [generic]:
             print("%-18s vgpr %3d agpr %3d sgpr %3d scratch %d lds %6d occ %d" % (
                 e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"], e["occupancy"]))
     return LIB

@@ -774,6 +774,144 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
                   (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------ grouped GEMM
+// Mixture-of-experts GEMM (FlyDSL-in-PyTorch blog, grouped GEMM section) on a
+// persistent grid: expert g owns rows [offs[g-1], offs[g]) of A and C.
+
+void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
+{
+    const TileShape s = grouped_shape(variant);
+    const int64_t tn = cdiv(N, s.bn);
+    // Workgroups resident at once: one per CU for the 128 KiB-LDS 256 x 256
+    // tile, two for the 64 KiB 128 x 128 tile; never more than the tiles
+    // the experts can have.
+    const int64_t per_cu = s.bm >= 256 ? 1 : 2;
+    const int64_t bound = (cdiv(M, s.bm) + G) * tn;
+    const int64_t grid = std::min<int64_t>(kNumCUs * per_cu, bound);
+    p->kernel_id = HKG_KERNEL_GROUPED;
+    p->variant = variant;
+    p->tile_m = s.bm;
+    p->tile_n = s.bn;
+    p->tile_k = s.bk;
+    p->waves = s.waves;
+    p->split_k = 1;
+    p->grid_x = (int32_t)std::max<int64_t>(grid, 1);
+    p->grid_y = 1;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->workspace_bytes = 0;
+    p->xcd_window_w = 0;
+    p->xcd_chunk_c = 1;                 // chiplet-contiguous walk when the grid is a multiple of 8
+    p->lds_bytes = s.stages * (s.bm + s.bn) * s.bk * 2;
+    fill_resources(p, grouped_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "grouped_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
+                  s.stages, s.wm, s.wn, s.sched);
+    std::snprintf(p->reason, sizeof p->reason, "grouped: %lld experts, %d x %d tiles on a persistent grid of %lld",
+                  (long long)G, s.bm, s.bn, (long long)grid);
+}
+
+hkg_status_t make_grouped_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
+{
+    std::memset(p, 0, sizeof *p);
+    p->abi_version = HKG_ABI_VERSION;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->split_k = 1;
+    p->vgprs = p->agprs = p->sgprs = p->scratch_bytes = -1;
+    if (G < 0 || G > kMaxDim)
+        return HKG_ERR_INVALID_ARG;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (G && K >= ((int64_t)1 << 40) / G / std::max<int64_t>(N, 1))     // B holds G N K < 2^40 elements
+        return HKG_ERR_INVALID_ARG;
+    p->flops = 2.0 * (double)M * (double)N * (double)K;                  // at most: every row in an expert
+    p->algorithmic_bytes = 2.0 * ((double)M * K + (double)G * N * K + (double)M * N);
+    if (M == 0 || N == 0 || G == 0) {
+        p->kernel_id = HKG_KERNEL_NONE;
+        copy_str(p->kernel_name, sizeof p->kernel_name, "none");
+        copy_str(p->reason, sizeof p->reason, "no rows in any expert");
+        return HKG_OK;
+    }
+    if (K % 8 != 0 || K > (int64_t)(INT32_MAX / 2) / 256)
+        return HKG_ERR_UNSUPPORTED;
+    // 256 x 256 tiles when the experts average at least 256 rows and those
+    // tiles fill the device; 128 x 128 otherwise.
+    const TileShape big = grouped_shape(0);
+    const int variant = (M / G >= big.bm && cdiv(M, big.bm) * cdiv(N, big.bn) >= kNumCUs) ? 0 : 1;
+    const TileShape s = grouped_shape(variant);
+    if ((cdiv(M, s.bm) + G) * cdiv(N, s.bn) > INT32_MAX)
+        return HKG_ERR_UNSUPPORTED;
+    fill_grouped(p, variant, G, M, N);
+    return HKG_OK;
+}
+
+bool grouped_plan_matches_library(const hkg_plan_t* p, int64_t G)
+{
+    if (p->kernel_id == HKG_KERNEL_NONE)
+        return p->M == 0 || p->N == 0 || G == 0;
+    if (p->kernel_id != HKG_KERNEL_GROUPED || p->variant < 0 || p->variant >= GROUPED_NUM_VARIANTS)
+        return false;
+    const TileShape s = grouped_shape(p->variant);
+    return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves && p->split_k == 1 &&
+           p->grid_x >= 1 && p->xcd_chunk_c >= 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
+           (cdiv(p->M, s.bm) + G) * cdiv(p->N, s.bn) <= INT32_MAX;
+}
+
+hkg_status_t grouped(const hkg_plan_t* plan, const void* A, const void* B, const void* offs, const void* bias,
+                     void* C, int64_t G, int64_t M, int64_t N, int64_t K, int32_t epi, void* stream)
+{
+    hkg_plan_t own;
+    const hkg_plan_t* p = plan;
+    if (!p) {
+        hkg_status_t st = make_grouped_plan(G, M, N, K, &own);
+        if (st != HKG_OK)
+            return st;
+        p = &own;
+    } else {
+        if (p->abi_version != HKG_ABI_VERSION || G < 0)
+            return HKG_ERR_INVALID_ARG;
+        hkg_status_t st = check_dims(M, N, K);
+        if (st != HKG_OK)
+            return st;
+        if (p->M != M || p->N != N || p->K != K)
+            return HKG_ERR_INVALID_ARG;
+    }
+    const int64_t a_bytes = 2 * M * K, b_bytes = 2 * G * N * K, c_bytes = 2 * M * N, o_bytes = 4 * G;
+    if ((a_bytes && !A) || (b_bytes && !B) || (c_bytes && !C) || (o_bytes && !offs))
+        return HKG_ERR_INVALID_ARG;
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes) || overlaps(C, c_bytes, offs, o_bytes))
+        return HKG_ERR_INVALID_ARG;
+    // bias: G x N values when an epilogue is asked for
+    if (epi < HKG_EPILOGUE_NONE || epi > HKG_EPILOGUE_BIAS_GELU)
+        return HKG_ERR_INVALID_ARG;
+    if (epi != HKG_EPILOGUE_NONE && M > 0 && N > 0 && G > 0) {
+        if (!bias || overlaps(C, c_bytes, bias, 2 * G * N))
+            return HKG_ERR_INVALID_ARG;
+        if (((uintptr_t)bias & 1u) != 0)
+            return HKG_ERR_MISALIGNED;
+    }
+    if (plan && !grouped_plan_matches_library(p, G))
+        return HKG_ERR_UNSUPPORTED;
+    if (p->kernel_id == HKG_KERNEL_NONE)
+        return HKG_OK;
+    if (!(aligned16(A) && aligned16(B) && aligned16(C)) || ((uintptr_t)offs & 3u) != 0)
+        return HKG_ERR_MISALIGNED;
+    int dev = 0;
+    hkg_status_t st = current_device(&dev);
+    if (st != HKG_OK)
+        return st;
+    hipError_t e = launch_grouped(p->variant, (const uint16_t*)A, (const uint16_t*)B, (const int*)offs, (int)G,
+                                  (uint16_t*)C, (int)M, (int)N, (int)K, p->grid_x, p->xcd_chunk_c,
+                                  (const uint16_t*)bias, epi, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, "kernel launch");
+        return HKG_ERR_HIP;
+    }
+    return HKG_OK;
+}
+
 }  // namespace
 }  // namespace hkg
 
@@ -887,6 +1025,28 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
         return HKG_ERR_MISALIGNED;
     return run_mx(plan, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epilogue,
                   (hipStream_t)stream);
+}
+
+hkg_status_t hkg_grouped_gemm_bf16_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* out)
+{
+    if (!out)
+        return HKG_ERR_INVALID_ARG;
+    return make_grouped_plan(G, M, N, K, out);
+}
+
+hkg_status_t hkg_grouped_gemm_bf16(const void* A, const void* B, const void* offs, const void* bias, void* C,
+                                   int64_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream)
+{
+    return grouped(nullptr, A, B, offs, bias, C, G, M, N, K, epilogue, stream);
+}
+
+hkg_status_t hkg_grouped_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* offs,
+                                            const void* bias, void* C, int64_t G, int64_t M, int64_t N, int64_t K,
+                                            int32_t epilogue, void* stream)
+{
+    if (!plan)
+        return HKG_ERR_INVALID_ARG;
+    return grouped(plan, A, B, offs, bias, C, G, M, N, K, epilogue, stream);
 }
 
 const char* hkg_status_string(hkg_status_t s)

@@ -27,6 +27,14 @@ constexpr int MX_TILE_NUM_VARIANTS = 0
 #undef HKG_COUNT_TILE
     ;
 
+// Grouped-GEMM instantiations (plan.variant for HKG_KERNEL_GROUPED): the
+// rows of HKG_GROUPED_CONFIGS.
+constexpr int GROUPED_NUM_VARIANTS = 0
+#define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1
+    HKG_GROUPED_CONFIGS(HKG_COUNT_TILE)
+#undef HKG_COUNT_TILE
+    ;
+
 // Default tile ladder of the planner, largest first (variant indices).
 constexpr int TILE_LADDER[] = {0, 1, 2};
 
@@ -46,6 +54,7 @@ TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 
 TileShape mx_tile_shape(int variant);
+TileShape grouped_shape(int variant);
 int mx_tile_lds_bytes(int variant);
 // Bytes of the packed scales of `rows` rows (rows rounded up to 64).
 int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
@@ -70,6 +79,13 @@ hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint1
                           int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
                           int epi, const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
 
+// Grouped GEMM: A (M x K), B (G x N x K), offs (G row ends, device int32),
+// C (M x N), bias G x N when epi != EPI_NONE; `grid` persistent workgroups,
+// xcd_chunks != 0 for the chiplet-contiguous tile walk.
+hipError_t launch_grouped(int variant, const uint16_t* A, const uint16_t* B, const int* offs, int G, uint16_t* C,
+                          int M, int N, int K, int grid, int xcd_chunks, const uint16_t* bias, int epi,
+                          hipStream_t stream);
+
 // Packs rows x (K / 32) E8M0 codes S into the tile kernel's layout P
 // (mx_packed_scale_bytes(rows, K) bytes, 4-byte aligned).
 hipError_t launch_mx_pack(const uint8_t* S, uint32_t* P, int64_t rows, int64_t K, hipStream_t stream);
@@ -92,6 +108,7 @@ hipError_t launch_zero(uint16_t* C, int64_t M, int64_t N, const uint16_t* bias, 
 struct KernelResources { const char* name; int vgprs, agprs, sgprs, scratch, lds; };
 const KernelResources* tile_resources(int variant);
 const KernelResources* mx_tile_resources(int variant);
+const KernelResources* grouped_resources(int variant);
 const KernelResources* skinny_resources(int variant);
 const KernelResources* generic_resources();
 

@@ -29,3 +29,9 @@
 #define HKG_MX_TILE_CONFIGS(X)     \
     X(256, 256, 128, 2, 4, 2, 5)   \
     X(128, 128, 128, 2, 2, 2, 0)
+
+// Grouped (mixture-of-experts) instantiations on a persistent grid, same
+// fields; bf16 only, no split-K.
+#define HKG_GROUPED_CONFIGS(X)     \
+    X(256, 256, 64, 2, 2, 4, 2)    \
+    X(128, 128, 64, 2, 2, 2, 2)

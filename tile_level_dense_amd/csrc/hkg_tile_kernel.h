@@ -138,14 +138,17 @@ __device__ __forceinline__ void sync_stage(int ahead)
 // MX = false: A, B bf16 (M x K, N x K), BK = 32 or 64.
 // MX = true: A, B E4M3 codes, BK = 128, K % 128 == 0; PSA, PSB the packed
 // E8M0 scales of A and B (mx_pack_kernel layout).
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI, bool MX>
+// GROUPED = true: the persistent grouped (mixture-of-experts) form, B the
+// G x N x K expert weights, offs the G row ends of the experts in A and C.
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI, bool MX, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * 64, 2)
 void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                  uint16_t* __restrict__ C, int M, int N, int K,
                  int tiles_m, int tiles_n, int win_w, int chunk_c,
                  int split_k, float* __restrict__ ws, int* __restrict__ counters,
                  const uint16_t* __restrict__ bias, int epi,
-                 const uint32_t* __restrict__ PSA, const uint32_t* __restrict__ PSB)
+                 const uint32_t* __restrict__ PSA, const uint32_t* __restrict__ PSB,
+                 const int* __restrict__ offs, int G)
 {
     constexpr int NW = WM * WN;
     constexpr int EB = MX ? 1 : 2;         // bytes per element
@@ -183,591 +186,696 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
-    int tm, tn;
-    tile_order(blockIdx.x, tiles_m, tiles_n, win_w, chunk_c, tm, tn);
-    if (tm >= tiles_m || tn >= tiles_n)    // uniform per workgroup; never taken for a valid order
-        return;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
     const uint32_t row_bytes = (uint32_t)K * (uint32_t)EB;
-    const int rows_a = min(BM, M - m0);
-    const int rows_b = min(BN, N - n0);
+    __shared__ int last_flag;               // split-K: this workgroup arrived last
 
-    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)Av + (size_t)m0 * row_bytes), 0, (int)(rows_a * row_bytes), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)Bv + (size_t)n0 * row_bytes), 0, (int)(rows_b * row_bytes), kBufferWord3);
+    // One output tile: C rows [m0, min(m0 + BM, m_lim)) by columns
+    // [tn BN, tn BN + BN), from A rows m0.. and rows tn BN.. of b_rows (the
+    // tile's N x K operand; an expert's weight in grouped mode), with bias_t
+    // the bias row of that operand.  tm, tn index split-K's arrival counters
+    // (dense mode only).
+    auto run_tile = [&](int tm, int tn, int m0, int m_lim, const char* b_rows, const uint16_t* bias_t) {
+        (void)tm;
+        // In the persistent loop the lane-derived offsets are recomputed per
+        // tile (an opaque copy of the lane id) rather than kept live across
+        // tiles beside the accumulators.
+        int lane = threadIdx.x & 63;
+        if constexpr (GROUPED)
+            asm volatile("" : "+v"(lane));
+        const int n0 = tn * BN;
+        const int rows_a = min(BM, m_lim - m0);
+        const int rows_b = min(BN, N - n0);
 
-    // LDS layout of a stage: row r holds its logical 16-byte chunk c at
-    // position c ^ ((r / RPL) % CPR).  Sixteen consecutive rows read at one
-    // logical chunk then hit sixteen distinct 16-byte bank groups.
-    //
-    // DMA sources of this lane.  Wave instruction i of the A copy fills LDS
-    // rows RPW g .. RPW g + RPW - 1 (g = wave + i NW); lane -> row
-    // RPW g + lane / CPR, position lane % CPR, which holds logical chunk
-    // (lane % CPR) ^ swizzle(row): the swizzle is applied to the source.
-    // Consecutive copies of a wave are NW * RPW rows apart, a multiple of
-    // RPL * CPR, so the swizzle (and the lane's chunk) is the same for all
-    // of them: one base offset per operand, plus a uniform row step.
-    static_assert((NW * RPW / RPL) % CPR == 0, "swizzle must repeat across a wave's copies");
-    constexpr int COPY_ROWS = NW * RPW;
-    const int lrow0 = wave * RPW + lane / CPR;
-    const int lchunk = (lane % CPR) ^ ((lrow0 / RPL) % CPR);
-    const uint32_t src_off = (uint32_t)lrow0 * row_bytes + (uint32_t)lchunk * 16u;
-    const int src_k = lchunk * KPC;
-    const uint32_t copy_step = (uint32_t)COPY_ROWS * row_bytes;
+        const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)Av + (size_t)m0 * row_bytes), 0, (int)(rows_a * row_bytes), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(b_rows + (size_t)n0 * row_bytes), 0, (int)(rows_b * row_bytes), kBufferWord3);
 
-    // K range of this workgroup: stages [kt0, kt0 + nk) of BK k;
-    // split_k > 1 divides K across workgroups (blockIdx.y).
-    const int nk_all = (K + BK - 1) / BK;
-    const int per_split = (nk_all + split_k - 1) / split_k;
-    const int kt0 = min(nk_all, (int)blockIdx.y * per_split);
-    const int nk = min(nk_all, kt0 + per_split) - kt0;
-    const int kbase = kt0 * BK;
-    const int k_lim = min(K, (kt0 + nk) * BK);
+        // LDS layout of a stage: row r holds its logical 16-byte chunk c at
+        // position c ^ ((r / RPL) % CPR).  Sixteen consecutive rows read at one
+        // logical chunk then hit sixteen distinct 16-byte bank groups.
+        //
+        // DMA sources of this lane.  Wave instruction i of the A copy fills LDS
+        // rows RPW g .. RPW g + RPW - 1 (g = wave + i NW); lane -> row
+        // RPW g + lane / CPR, position lane % CPR, which holds logical chunk
+        // (lane % CPR) ^ swizzle(row): the swizzle is applied to the source.
+        // Consecutive copies of a wave are NW * RPW rows apart, a multiple of
+        // RPL * CPR, so the swizzle (and the lane's chunk) is the same for all
+        // of them: one base offset per operand, plus a uniform row step.
+        static_assert((NW * RPW / RPL) % CPR == 0, "swizzle must repeat across a wave's copies");
+        constexpr int COPY_ROWS = NW * RPW;
+        const int lrow0 = wave * RPW + lane / CPR;
+        const int lchunk = (lane % CPR) ^ ((lrow0 / RPL) % CPR);
+        const uint32_t src_off = (uint32_t)lrow0 * row_bytes + (uint32_t)lchunk * 16u;
+        const int src_k = lchunk * KPC;
+        const uint32_t copy_step = (uint32_t)COPY_ROWS * row_bytes;
 
-    auto issue = [&](int stage, int kl) {
-        char* base = smem + stage * STAGE;
-        const int k0 = kbase + kl;
-        const bool k_out = k0 + src_k >= k_lim;  // this lane's chunk past the range
-        const uint32_t off0 = k_out ? kOutOfRange : src_off + (uint32_t)k0 * (uint32_t)EB;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16,
-                k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16,
-                k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
-    };
+        // K range of this workgroup: stages [kt0, kt0 + nk) of BK k;
+        // split_k > 1 divides K across workgroups (blockIdx.y).
+        const int nk_all = (K + BK - 1) / BK;
+        const int per_split = (nk_all + split_k - 1) / split_k;
+        const int kt0 = min(nk_all, (int)blockIdx.y * per_split);
+        const int nk = min(nk_all, kt0 + per_split) - kt0;
+        const int kbase = kt0 * BK;
+        const int k_lim = min(K, (kt0 + nk) * BK);
 
-    // Fragment reads: lane -> row (lane % 16) of a 16-row block, logical
-    // chunk 4 s + lane / 16 for read s (bf16: 8 k of the 32-k step s; MXFP8:
-    // the two 16-byte halves of the lane's operand).  Every block starts at
-    // a multiple of 16 rows, so the swizzle depends on lane only.
-    const int lrow = lane & 15;
-    const int lgrp = lane >> 4;
-    const int swz = (lrow / RPL) % CPR;
-    int chunk_off[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-        chunk_off[s] = ((4 * s + lgrp) ^ swz) * 16;
-    const int a_frag = (wm * WTM + lrow) * RB;
-    const int b_frag = A_BYTES + (wn * WTN + lrow) * RB;
+        auto issue = [&](int stage, int kl) {
+            char* base = smem + stage * STAGE;
+            const int k0 = kbase + kl;
+            const bool k_out = k0 + src_k >= k_lim;  // this lane's chunk past the range
+            const uint32_t off0 = k_out ? kOutOfRange : src_off + (uint32_t)k0 * (uint32_t)EB;
+    #pragma unroll
+            for (int i = 0; i < A_LOADS; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16,
+                    k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
+    #pragma unroll
+            for (int i = 0; i < B_LOADS; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16,
+                    k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
+        };
 
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Fragment reads: lane -> row (lane % 16) of a 16-row block, logical
+        // chunk 4 s + lane / 16 for read s (bf16: 8 k of the 32-k step s; MXFP8:
+        // the two 16-byte halves of the lane's operand).  Every block starts at
+        // a multiple of 16 rows, so the swizzle depends on lane only.
+        const int lrow = lane & 15;
+        const int lgrp = lane >> 4;
+        const int swz = (lrow / RPL) % CPR;
+        int chunk_off[KS];
+    #pragma unroll
+        for (int s = 0; s < KS; ++s)
+            chunk_off[s] = ((4 * s + lgrp) ^ swz) * 16;
+        const int a_frag = (wm * WTM + lrow) * RB;
+        const int b_frag = A_BYTES + (wn * WTN + lrow) * RB;
 
-    auto read_frags = [&](const char* base, int s, bf16x8 (&af)[FM], bf16x8 (&bf)[FN]) {
-#pragma unroll
+        f32x4 acc[FM][FN];
+    #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = *(const bf16x8*)(base + a_frag + i * 16 * RB + chunk_off[s]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bf[j] = *(const bf16x8*)(base + b_frag + j * 16 * RB + chunk_off[s]);
-    };
-    auto mfmas = [&](const bf16x8 (&af)[FM], const bf16x8 (&bf)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    };
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // MXFP8 scales.  Packed layout (mx_pack_kernel): for 64-row group R and
-    // stage kt, dword R * KT * 64 + kt * 64 + lane holds in byte f the scale
-    // of row 64 R + 16 f + lane % 16, block 4 kt + lane / 16: this lane's
-    // scale operand for 16-row block f of the group.  A wave's rows are SWA
-    // (B: SWB) whole groups; one dword load per group per stage.
-    constexpr int SWA = MX ? WTM / 64 : 1;
-    constexpr int SWB = MX ? WTN / 64 : 1;
-    const int KT = K / 128;
-    const __amdgpu_buffer_rsrc_t rsrc_sa = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)PSA, 0, MX ? ((M + 63) / 64) * KT * 256 : 0, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rsrc_sb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)PSB, 0, MX ? ((N + 63) / 64) * KT * 256 : 0, kBufferWord3);
-    const uint32_t sa_off0 = (uint32_t)(((m0 + wm * WTM) / 64) * KT) * 256u + (uint32_t)lane * 4u;
-    const uint32_t sb_off0 = (uint32_t)(((n0 + wn * WTN) / 64) * KT) * 256u + (uint32_t)lane * 4u;
-    uint32_t sa_cur[SWA], sb_cur[SWB], sa_nxt[SWA], sb_nxt[SWB];
-    // Scales of local stage t into the *_nxt registers (t past this
-    // workgroup's range reads the next split's or out-of-range zeros; such
-    // values are never used).
-    auto load_scales = [&](int t) {
-        if constexpr (MX) {
-            const uint32_t st = (uint32_t)(kt0 + t) * 256u;
-#pragma unroll
-            for (int r = 0; r < SWA; ++r)
-                sa_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
-#pragma unroll
-            for (int r = 0; r < SWB; ++r)
-                sb_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
-        }
-    };
-    auto take_scales = [&]() {
-        if constexpr (MX) {
-#pragma unroll
-            for (int r = 0; r < SWA; ++r)
-                sa_cur[r] = sa_nxt[r];
-#pragma unroll
-            for (int r = 0; r < SWB; ++r)
-                sb_cur[r] = sb_nxt[r];
-        }
-    };
-    // One 128-k stage of MXFP8 MFMAs: halves lo (chunk g) and hi (chunk 4 + g).
-    auto mfmas_mx = [&](const bf16x8 (&alo)[FM], const bf16x8 (&ahi)[FM], const bf16x8 (&blo)[FN],
-                        const bf16x8 (&bhi)[FN]) {
-        static_for<0, FM>([&](auto I) {
-            constexpr int i = decltype(I)::value;
-            const i32x8 av = mx_operand(alo[i], ahi[i]);
-            static_for<0, FN>([&](auto J) {
-                constexpr int j = decltype(J)::value;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    mx_operand(blo[j], bhi[j]), av, acc[i][j], 0, 0, j % 4, (int)sb_cur[j / 4], i % 4,
-                    (int)sa_cur[i / 4]);
-            });
-        });
-    };
-
-    auto compute = [&](int stage) {
-        const char* base = smem + stage * STAGE;
-        if constexpr (MX) {
-            bf16x8 alo[FM], blo[FN], ahi[FM], bhi[FN];
-            read_frags(base, 0, alo, blo);
-            read_frags(base, 1, ahi, bhi);
-            mfmas_mx(alo, ahi, blo, bhi);
-        } else if constexpr (SCHED == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                bf16x8 af[FM], bf[FN];
-                read_frags(base, s, af, bf);
-                mfmas(af, bf);
-            }
-        } else {
-            // Fragments of step s + 1 are read while the MFMAs of step s run:
-            // one LDS read between every few MFMAs, so each read has many
-            // MFMA cycles to land before its first use.
-            bf16x8 af[2][FM], bf[2][FN];
-            read_frags(base, 0, af[0], bf[0]);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int cur = s & 1;
-                if (s + 1 < KS)
-                    read_frags(base, s + 1, af[cur ^ 1], bf[cur ^ 1]);
-                mfmas(af[cur], bf[cur]);
-            }
-            if constexpr (KS > 1) {
-                constexpr int READS = FM + FN;
-                constexpr int MF = FM * FN;
-                constexpr int PER = MF / READS > 0 ? MF / READS : 1;
-                // first step: its reads were issued above the loop
-                __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
-#pragma unroll
-                for (int r = 0; r < READS; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, MF - PER * READS, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-            }
-        }
-    };
-
-    if constexpr (SCHED < 2) {
-        // K loop over a ring of STAGES buffers, prefetch distance STAGES - 1.
-        // At step t: this wave's copy of stage t has landed (vmcnt allows the
-        // later stages still in flight), all waves finished reading step t - 1
-        // (lgkmcnt + barrier), so buffer (t - 1) % STAGES is refilled with step
-        // t + STAGES - 1 while step t is computed.
-        // MXFP8 (two stages only): the scales of step t + 1 are loaded just
-        // before its copies, so the wait at the top of step t + 1 covers them.
-        static_assert(!MX || STAGES == 2, "MXFP8 ring: two stages");
-        load_scales(0);
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nk)
-                issue(s, s * BK);
-        int read_stage = 0;
-        int write_stage = STAGES - 1;
-        for (int t = 0; t < nk; ++t) {
-            sync_stage<L, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
-            take_scales();
-            load_scales(t + 1);
-            if (t + STAGES - 1 < nk)
-                issue(write_stage, (t + STAGES - 1) * BK);
-            compute(read_stage);
-            read_stage = read_stage + 1 == STAGES ? 0 : read_stage + 1;
-            write_stage = write_stage + 1 == STAGES ? 0 : write_stage + 1;
-        }
-    } else if constexpr (SCHED == 2 && !MX) {
-        // Register-pipelined loop.  Work proceeds in 32-k steps; the
-        // fragments of step u + 1 are read from LDS while the MFMAs of step u
-        // run.  Before the first read of a new stage every wave waits for its
-        // own reads of the previous stage (now in registers) and for its copy
-        // of the new stage, then joins the barrier: the previous stage's
-        // buffer is then free and is refilled right away with the stage
-        // STAGES ahead.  Copies past the end of K are issued with
-        // out-of-range offsets (they fill a buffer nobody reads), so the
-        // number of copies in flight, and with it every wait count, is the
-        // same on every step: the loop body has no branch around LDS reads,
-        // copies or waits.
-        constexpr int READS = FM + FN;
-        constexpr int MF = FM * FN;
-        static_assert(MF >= READS, "one MFMA per fragment read at least");
-        auto interleave = [&]() {
-#pragma unroll
-            for (int r = 0; r < READS; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, MF - READS, 0);
+        auto read_frags = [&](const char* base, int s, bf16x8 (&af)[FM], bf16x8 (&bf)[FN]) {
+    #pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *(const bf16x8*)(base + a_frag + i * 16 * RB + chunk_off[s]);
+    #pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *(const bf16x8*)(base + b_frag + j * 16 * RB + chunk_off[s]);
         };
-        auto stage_base = [&](int t) { return smem + (t % STAGES) * STAGE; };
-        auto new_stage = [&](int t) {      // about to read stage t + 1
-            wait_and_barrier<(STAGES - 2) * L>();
-            issue(t % STAGES, (t + STAGES) * BK);
-        };
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s)
-            issue(s, s * BK);
-        wait_and_barrier<(STAGES - 1) * L>();
-        bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
-        read_frags(smem, 0, af0, bf0);
-        static_assert(KS == 2, "the register-pipelined loop takes 64-k stages");
-        for (int t = 0; t < nk; ++t) {
-            mfmas(af0, bf0);
-            read_frags(stage_base(t), 1, af1, bf1);
-            interleave();
-            new_stage(t);
-            mfmas(af1, bf1);
-            read_frags(stage_base(t + 1), 0, af0, bf0);
-            interleave();
-        }
-        // Leave no copy in flight into LDS that is about to be released.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-        // Ping-pong (HipKittens talk notes, section 2, 8-wave schedule).
-        // Waves 0-3 (group 0) and 4-7 (group 1) put one wave on each SIMD
-        // and alternate a memory phase (LDS fragment reads of a whole
-        // stage, plus copies) with a compute phase (the stage's MFMAs),
-        // phases separated by workgroup barriers.  Group 1 joins one extra
-        // barrier at the start, so the groups run half a stage apart and
-        // each SIMD's matrix unit is fed by one wave while the other reads.
-        // Every copy is issued in a memory phase: a copy that the vector
-        // memory path cannot take yet stalls its wave, and in a compute
-        // phase that would stall the MFMAs too.  That needs these buffer
-        // lifetimes: group g alone reads A rows 128 g .. 128 g + 127
-        // (double-buffered per group), both groups read B (triple-
-        // buffered); 160 KiB of LDS in all.
-        // Phase j lies between barriers j and j + 1; group 0 reads stage t
-        // in phase 2t and computes it in 2t + 1, group 1 reads it in
-        // 2t + 1 and computes it in 2t + 2.  Copies, A first:
-        //   group 0, phase 2t:     A rows 0-127 of stage t + 1, B rows
-        //                          0-127 of stage t + 2
-        //   group 1, phase 2t + 1: A rows 128-255 of stage t + 1, B rows
-        //                          128-255 of stage t + 2
-        // Each lands in a buffer whose last reader finished before the
-        // phase began.  A wave waits for its A copies at the end of its
-        // next compute phase and for its B copies one memory phase later
-        // (group 1) or one compute phase later (group 0): in every case
-        // before the first phase that reads them.
-        // MXFP8: each memory phase starts by taking the scales loaded at the
-        // start of the previous one (landed: the waits since then cover
-        // them) and loading the next stage's ahead of its copies, so no wait
-        // for scales ever holds back a copy issued after them; 2 (SWA + SWB)
-        // VGPRs.
-        static_assert(SCHED == 5, "schedules 0, 1, 2 and 5");
-        static_assert(BM == 256 && BN == 256 && RB == 128 && NW == 8 && WM <= 4,
-                      "split-buffer ping-pong: 256 x 256 tile of 128-byte rows, 8 waves");
-        constexpr int HALF = 128 * RB;                  // 128 rows of one stage
-        constexpr int CPW = 128 / (RPW * 4);            // copies per half per wave
-        char* const a_buf = smem;                       // [group][stage % 2]
-        char* const b_buf = smem + 4 * HALF;            // [stage % 3]: rows 0-255
-        const int g = wave >> 2;
-        const int w4 = wave & 3;
-        // DMA source of this lane within a 128-row half (same swizzle rule
-        // as the copies above; a group's 4 waves fill 32 rows per round).
-        const int prow = w4 * RPW + lane / CPR;
-        const int pchunk = (lane % CPR) ^ ((prow / RPL) % CPR);
-        const uint32_t p_off = (uint32_t)(128 * g + prow) * row_bytes + (uint32_t)pchunk * 16u;
-        const int p_k = pchunk * KPC;
-        const uint32_t p_step = (uint32_t)(4 * RPW) * row_bytes;
-        static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a group's copies");
-        auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t) {
-            const int k0 = kbase + t * BK;
-            const bool k_out = k0 + p_k >= k_lim;
-            const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * (uint32_t)EB;
-#pragma unroll
-            for (int i = 0; i < CPW; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (w4 + 4 * i) * 1024), 16,
-                                                         k_out ? kOutOfRange : off0 + (uint32_t)i * p_step, 0,
-                                                         0, 0);
-        };
-        auto copy_a = [&](int t) { copy_half(rsrc_a, a_buf + (2 * g + (t & 1)) * HALF, t); };
-        auto copy_b = [&](int t) { copy_half(rsrc_b, b_buf + (t % 3) * 2 * HALF + g * HALF, t); };
-        const int a_row = wm * WTM - 128 * g + lrow;    // row within the group's A half
-        const int b_row = wn * WTN + lrow;
-        bf16x8 af[KS][FM], bf[KS][FN];
-        auto read_stage = [&](int t) {
-            const char* ab = a_buf + (2 * g + (t & 1)) * HALF + a_row * RB;
-            const char* bb = b_buf + (t % 3) * 2 * HALF + b_row * RB;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    af[s][i] = *(const bf16x8*)(ab + i * 16 * RB + chunk_off[s]);
-#pragma unroll
+        auto mfmas = [&](const bf16x8 (&af)[FM], const bf16x8 (&bf)[FN]) {
+    #pragma unroll
+            for (int i = 0; i < FM; ++i)
+    #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + chunk_off[s]);
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
         };
-        auto mfma_stage = [&]() {
+
+        // MXFP8 scales.  Packed layout (mx_pack_kernel): for 64-row group R and
+        // stage kt, dword R * KT * 64 + kt * 64 + lane holds in byte f the scale
+        // of row 64 R + 16 f + lane % 16, block 4 kt + lane / 16: this lane's
+        // scale operand for 16-row block f of the group.  A wave's rows are SWA
+        // (B: SWB) whole groups; one dword load per group per stage.
+        constexpr int SWA = MX ? WTM / 64 : 1;
+        constexpr int SWB = MX ? WTN / 64 : 1;
+        const int KT = K / 128;
+        const __amdgpu_buffer_rsrc_t rsrc_sa = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)PSA, 0, MX ? ((M + 63) / 64) * KT * 256 : 0, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsrc_sb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)PSB, 0, MX ? ((N + 63) / 64) * KT * 256 : 0, kBufferWord3);
+        const uint32_t sa_off0 = (uint32_t)(((m0 + wm * WTM) / 64) * KT) * 256u + (uint32_t)lane * 4u;
+        const uint32_t sb_off0 = (uint32_t)(((n0 + wn * WTN) / 64) * KT) * 256u + (uint32_t)lane * 4u;
+        uint32_t sa_cur[SWA], sb_cur[SWB], sa_nxt[SWA], sb_nxt[SWB];
+        // Scales of local stage t into the *_nxt registers (t past this
+        // workgroup's range reads the next split's or out-of-range zeros; such
+        // values are never used).
+        auto load_scales = [&](int t) {
             if constexpr (MX) {
-                mfmas_mx(af[0], af[1], bf[0], bf[1]);
+                const uint32_t st = (uint32_t)(kt0 + t) * 256u;
+    #pragma unroll
+                for (int r = 0; r < SWA; ++r)
+                    sa_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+    #pragma unroll
+                for (int r = 0; r < SWB; ++r)
+                    sb_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+            }
+        };
+        auto take_scales = [&]() {
+            if constexpr (MX) {
+    #pragma unroll
+                for (int r = 0; r < SWA; ++r)
+                    sa_cur[r] = sa_nxt[r];
+    #pragma unroll
+                for (int r = 0; r < SWB; ++r)
+                    sb_cur[r] = sb_nxt[r];
+            }
+        };
+        // One 128-k stage of MXFP8 MFMAs: halves lo (chunk g) and hi (chunk 4 + g).
+        auto mfmas_mx = [&](const bf16x8 (&alo)[FM], const bf16x8 (&ahi)[FM], const bf16x8 (&blo)[FN],
+                            const bf16x8 (&bhi)[FN]) {
+            static_for<0, FM>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const i32x8 av = mx_operand(alo[i], ahi[i]);
+                static_for<0, FN>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        mx_operand(blo[j], bhi[j]), av, acc[i][j], 0, 0, j % 4, (int)sb_cur[j / 4], i % 4,
+                        (int)sa_cur[i / 4]);
+                });
+            });
+        };
+
+        auto compute = [&](int stage) {
+            const char* base = smem + stage * STAGE;
+            if constexpr (MX) {
+                bf16x8 alo[FM], blo[FN], ahi[FM], bhi[FN];
+                read_frags(base, 0, alo, blo);
+                read_frags(base, 1, ahi, bhi);
+                mfmas_mx(alo, ahi, blo, bhi);
+            } else if constexpr (SCHED == 0) {
+    #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    bf16x8 af[FM], bf[FN];
+                    read_frags(base, s, af, bf);
+                    mfmas(af, bf);
+                }
             } else {
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    mfmas(af[s], bf[s]);
-            }
-        };
-        auto memory_phase_scales = [&](int t) {
-            take_scales();
-            load_scales(t + 1);
-        };
-        auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
-        auto phase_barrier = [&]() {
-            fence();
-            asm volatile("s_barrier" ::: "memory");
-            fence();
-        };
-        const bool g1 = g == 1;
-
-        // Prologue: stage 0, and this group's B rows of stage 1.
-        load_scales(0);
-        copy_a(0);
-        copy_b(0);
-        copy_b(1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
-        phase_barrier();
-        if (!g1) {
-            for (int t = 0; t < nk; ++t) {
-                memory_phase_scales(t);        // phase 2t: memory
-                read_stage(t);
-                fence();
-                copy_a(t + 1);
-                copy_b(t + 2);
-                fence();
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                phase_barrier();
-                mfma_stage();                  // phase 2t + 1: compute
-                fence();
-                // all but this phase's B copies: A of stage t + 1 and the
-                // B rows of stage t + 1 copied a memory phase earlier
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
-                phase_barrier();
-            }
-        } else {
-            phase_barrier();                   // phase 0: group 0 reads stage 0
-            for (int t = 0; t < nk; ++t) {
-                memory_phase_scales(t);        // phase 2t + 1: memory
-                read_stage(t);
-                fence();
-                copy_a(t + 1);
-                copy_b(t + 2);
-                fence();
-                // B rows of stage t + 1 (copied a memory phase earlier)
-                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * CPW) : "memory");
-                phase_barrier();
-                mfma_stage();                  // phase 2t + 2: compute
-                fence();
-                // A of stage t + 1
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
-                if (t + 1 < nk)
-                    phase_barrier();
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-
-    if constexpr (tile_split_capable(BM, BN, WM, WN)) if (split_k > 1) {
-        // Split-K: each workgroup writes its fp32 partial tile; the last one
-        // of the tile to arrive adds the partials in split order 0, 1, ...
-        // (the same order whichever split arrives last, so results are
-        // deterministic) and goes on to the rounding store below.  Partials
-        // are written and read with device-scope (sc1) accesses, which are
-        // coherent across the XCDs' L2 caches without flushing them; every
-        // store has completed (vmcnt) before the arrival is counted.
-        __shared__ int last_flag;
-        const int me = blockIdx.y;
-        const bool vec4 = (N & 3) == 0;
-        const int part_bytes = M * N * 4;          // below 2^31: checked by the planner
-        auto part = [&](int sp) { return ws + (size_t)sp * (size_t)M * (size_t)N; };
-        {
-            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(part(me), 0, part_bytes, kBufferWord3);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int m = m0 + wm * WTM + i * 16 + lrow;
-                if (m >= M)
-                    continue;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
-                    if (vec4 && n + 3 < N) {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r,
-                                                               (m * N + n) * 4, 0, kDeviceScope);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (n + q < N)
-                                __hip_atomic_store(part(me) + (size_t)m * N + n + q, acc[i][j][q], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+                // Fragments of step s + 1 are read while the MFMAs of step s run:
+                // one LDS read between every few MFMAs, so each read has many
+                // MFMA cycles to land before its first use.
+                bf16x8 af[2][FM], bf[2][FN];
+                read_frags(base, 0, af[0], bf[0]);
+    #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int cur = s & 1;
+                    if (s + 1 < KS)
+                        read_frags(base, s + 1, af[cur ^ 1], bf[cur ^ 1]);
+                    mfmas(af[cur], bf[cur]);
+                }
+                if constexpr (KS > 1) {
+                    constexpr int READS = FM + FN;
+                    constexpr int MF = FM * FN;
+                    constexpr int PER = MF / READS > 0 ? MF / READS : 1;
+                    // first step: its reads were issued above the loop
+                    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    #pragma unroll
+                    for (int r = 0; r < READS; ++r) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
                     }
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF - PER * READS, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
                 }
             }
+        };
+
+        if constexpr (SCHED < 2) {
+            // K loop over a ring of STAGES buffers, prefetch distance STAGES - 1.
+            // At step t: this wave's copy of stage t has landed (vmcnt allows the
+            // later stages still in flight), all waves finished reading step t - 1
+            // (lgkmcnt + barrier), so buffer (t - 1) % STAGES is refilled with step
+            // t + STAGES - 1 while step t is computed.
+            // MXFP8 (two stages only): the scales of step t + 1 are loaded just
+            // before its copies, so the wait at the top of step t + 1 covers them.
+            static_assert(!MX || STAGES == 2, "MXFP8 ring: two stages");
+            load_scales(0);
+    #pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < nk)
+                    issue(s, s * BK);
+            int read_stage = 0;
+            int write_stage = STAGES - 1;
+            for (int t = 0; t < nk; ++t) {
+                sync_stage<L, STAGES - 2>(min(STAGES - 2, nk - 1 - t));
+                take_scales();
+                load_scales(t + 1);
+                if (t + STAGES - 1 < nk)
+                    issue(write_stage, (t + STAGES - 1) * BK);
+                compute(read_stage);
+                read_stage = read_stage + 1 == STAGES ? 0 : read_stage + 1;
+                write_stage = write_stage + 1 == STAGES ? 0 : write_stage + 1;
+            }
+        } else if constexpr (SCHED == 2 && !MX) {
+            // Register-pipelined loop.  Work proceeds in 32-k steps; the
+            // fragments of step u + 1 are read from LDS while the MFMAs of step u
+            // run.  Before the first read of a new stage every wave waits for its
+            // own reads of the previous stage (now in registers) and for its copy
+            // of the new stage, then joins the barrier: the previous stage's
+            // buffer is then free and is refilled right away with the stage
+            // STAGES ahead.  Copies past the end of K are issued with
+            // out-of-range offsets (they fill a buffer nobody reads), so the
+            // number of copies in flight, and with it every wait count, is the
+            // same on every step: the loop body has no branch around LDS reads,
+            // copies or waits.
+            constexpr int READS = FM + FN;
+            constexpr int MF = FM * FN;
+            static_assert(MF >= READS, "one MFMA per fragment read at least");
+            auto interleave = [&]() {
+    #pragma unroll
+                for (int r = 0; r < READS; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MF - READS, 0);
+            };
+            auto stage_base = [&](int t) { return smem + (t % STAGES) * STAGE; };
+            auto new_stage = [&](int t) {      // about to read stage t + 1
+                wait_and_barrier<(STAGES - 2) * L>();
+                issue(t % STAGES, (t + STAGES) * BK);
+            };
+    #pragma unroll
+            for (int s = 0; s < STAGES; ++s)
+                issue(s, s * BK);
+            wait_and_barrier<(STAGES - 1) * L>();
+            bf16x8 af0[FM], bf0[FN], af1[FM], bf1[FN];
+            read_frags(smem, 0, af0, bf0);
+            static_assert(KS == 2, "the register-pipelined loop takes 64-k stages");
+            for (int t = 0; t < nk; ++t) {
+                mfmas(af0, bf0);
+                read_frags(stage_base(t), 1, af1, bf1);
+                interleave();
+                new_stage(t);
+                mfmas(af1, bf1);
+                read_frags(stage_base(t + 1), 0, af0, bf0);
+                interleave();
+            }
+            // Leave no copy in flight into LDS that is about to be released.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+            // Ping-pong (HipKittens talk notes, section 2, 8-wave schedule).
+            // Waves 0-3 (group 0) and 4-7 (group 1) put one wave on each SIMD
+            // and alternate a memory phase (LDS fragment reads of a whole
+            // stage, plus copies) with a compute phase (the stage's MFMAs),
+            // phases separated by workgroup barriers.  Group 1 joins one extra
+            // barrier at the start, so the groups run half a stage apart and
+            // each SIMD's matrix unit is fed by one wave while the other reads.
+            // Every copy is issued in a memory phase: a copy that the vector
+            // memory path cannot take yet stalls its wave, and in a compute
+            // phase that would stall the MFMAs too.  That needs these buffer
+            // lifetimes: group g alone reads A rows 128 g .. 128 g + 127
+            // (double-buffered per group), both groups read B (triple-
+            // buffered); 160 KiB of LDS in all.
+            // Phase j lies between barriers j and j + 1; group 0 reads stage t
+            // in phase 2t and computes it in 2t + 1, group 1 reads it in
+            // 2t + 1 and computes it in 2t + 2.  Copies, A first:
+            //   group 0, phase 2t:     A rows 0-127 of stage t + 1, B rows
+            //                          0-127 of stage t + 2
+            //   group 1, phase 2t + 1: A rows 128-255 of stage t + 1, B rows
+            //                          128-255 of stage t + 2
+            // Each lands in a buffer whose last reader finished before the
+            // phase began.  A wave waits for its A copies at the end of its
+            // next compute phase and for its B copies one memory phase later
+            // (group 1) or one compute phase later (group 0): in every case
+            // before the first phase that reads them.
+            // MXFP8: each memory phase starts by taking the scales loaded at the
+            // start of the previous one (landed: the waits since then cover
+            // them) and loading the next stage's ahead of its copies, so no wait
+            // for scales ever holds back a copy issued after them; 2 (SWA + SWB)
+            // VGPRs.
+            static_assert(SCHED == 5, "schedules 0, 1, 2 and 5");
+            static_assert(BM == 256 && BN == 256 && RB == 128 && NW == 8 && WM <= 4,
+                          "split-buffer ping-pong: 256 x 256 tile of 128-byte rows, 8 waves");
+            constexpr int HALF = 128 * RB;                  // 128 rows of one stage
+            constexpr int CPW = 128 / (RPW * 4);            // copies per half per wave
+            char* const a_buf = smem;                       // [group][stage % 2]
+            char* const b_buf = smem + 4 * HALF;            // [stage % 3]: rows 0-255
+            const int g = wave >> 2;
+            const int w4 = wave & 3;
+            // DMA source of this lane within a 128-row half (same swizzle rule
+            // as the copies above; a group's 4 waves fill 32 rows per round).
+            const int prow = w4 * RPW + lane / CPR;
+            const int pchunk = (lane % CPR) ^ ((prow / RPL) % CPR);
+            const uint32_t p_off = (uint32_t)(128 * g + prow) * row_bytes + (uint32_t)pchunk * 16u;
+            const int p_k = pchunk * KPC;
+            const uint32_t p_step = (uint32_t)(4 * RPW) * row_bytes;
+            static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a group's copies");
+            auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t) {
+                const int k0 = kbase + t * BK;
+                const bool k_out = k0 + p_k >= k_lim;
+                const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * (uint32_t)EB;
+    #pragma unroll
+                for (int i = 0; i < CPW; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (w4 + 4 * i) * 1024), 16,
+                                                             k_out ? kOutOfRange : off0 + (uint32_t)i * p_step, 0,
+                                                             0, 0);
+            };
+            auto copy_a = [&](int t) { copy_half(rsrc_a, a_buf + (2 * g + (t & 1)) * HALF, t); };
+            auto copy_b = [&](int t) { copy_half(rsrc_b, b_buf + (t % 3) * 2 * HALF + g * HALF, t); };
+            const int a_row = wm * WTM - 128 * g + lrow;    // row within the group's A half
+            const int b_row = wn * WTN + lrow;
+            bf16x8 af[KS][FM], bf[KS][FN];
+            auto read_stage = [&](int t) {
+                const char* ab = a_buf + (2 * g + (t & 1)) * HALF + a_row * RB;
+                const char* bb = b_buf + (t % 3) * 2 * HALF + b_row * RB;
+    #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+    #pragma unroll
+                    for (int i = 0; i < FM; ++i)
+                        af[s][i] = *(const bf16x8*)(ab + i * 16 * RB + chunk_off[s]);
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + chunk_off[s]);
+                }
+            };
+            auto mfma_stage = [&]() {
+                if constexpr (MX) {
+                    mfmas_mx(af[0], af[1], bf[0], bf[1]);
+                } else {
+    #pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        mfmas(af[s], bf[s]);
+                }
+            };
+            auto memory_phase_scales = [&](int t) {
+                take_scales();
+                load_scales(t + 1);
+            };
+            auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+            auto phase_barrier = [&]() {
+                fence();
+                asm volatile("s_barrier" ::: "memory");
+                fence();
+            };
+            const bool g1 = g == 1;
+
+            // Prologue: stage 0, and this group's B rows of stage 1.
+            load_scales(0);
+            copy_a(0);
+            copy_b(0);
+            copy_b(1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+            phase_barrier();
+            if (!g1) {
+                for (int t = 0; t < nk; ++t) {
+                    memory_phase_scales(t);        // phase 2t: memory
+                    read_stage(t);
+                    fence();
+                    copy_a(t + 1);
+                    copy_b(t + 2);
+                    fence();
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    phase_barrier();
+                    mfma_stage();                  // phase 2t + 1: compute
+                    fence();
+                    // all but this phase's B copies: A of stage t + 1 and the
+                    // B rows of stage t + 1 copied a memory phase earlier
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+                    phase_barrier();
+                }
+            } else {
+                phase_barrier();                   // phase 0: group 0 reads stage 0
+                for (int t = 0; t < nk; ++t) {
+                    memory_phase_scales(t);        // phase 2t + 1: memory
+                    read_stage(t);
+                    fence();
+                    copy_a(t + 1);
+                    copy_b(t + 2);
+                    fence();
+                    // B rows of stage t + 1 (copied a memory phase earlier)
+                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * CPW) : "memory");
+                    phase_barrier();
+                    mfma_stage();                  // phase 2t + 2: compute
+                    fence();
+                    // A of stage t + 1
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+                    if (t + 1 < nk)
+                        phase_barrier();
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const int tile = tm * tiles_n + tn;
-        if (threadIdx.x == 0) {
-            const int prev = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last_flag = (prev == split_k - 1);
-        }
-        __syncthreads();
-        if (!last_flag)
-            return;
-        // Sums are formed GR block rows at a time (at most 64 registers of
-        // running totals beside the accumulators).
-        constexpr int GR = FN >= 16 ? 1 : 16 / FN;
-#pragma unroll
-        for (int g = 0; g < FM; g += GR) {
-            f32x4 tot[GR][FN];
-            for (int sp = 0; sp < split_k; ++sp) {
-                const __amdgpu_buffer_rsrc_t r =
-                    __builtin_amdgcn_make_buffer_rsrc(part(sp), 0, part_bytes, kBufferWord3);
-#pragma unroll
-                for (int ii = 0; ii < GR; ++ii) {
-                    const int i = g + ii;
-                    if (i >= FM)
-                        break;
+
+        if constexpr (!GROUPED && tile_split_capable(BM, BN, WM, WN)) if (split_k > 1) {
+            // Split-K: each workgroup writes its fp32 partial tile; the last one
+            // of the tile to arrive adds the partials in split order 0, 1, ...
+            // (the same order whichever split arrives last, so results are
+            // deterministic) and goes on to the rounding store below.  Partials
+            // are written and read with device-scope (sc1) accesses, which are
+            // coherent across the XCDs' L2 caches without flushing them; every
+            // store has completed (vmcnt) before the arrival is counted.
+            const int me = blockIdx.y;
+            const bool vec4 = (N & 3) == 0;
+            const int part_bytes = M * N * 4;          // below 2^31: checked by the planner
+            auto part = [&](int sp) { return ws + (size_t)sp * (size_t)M * (size_t)N; };
+            {
+                const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(part(me), 0, part_bytes, kBufferWord3);
+    #pragma unroll
+                for (int i = 0; i < FM; ++i) {
                     const int m = m0 + wm * WTM + i * 16 + lrow;
-#pragma unroll
+                    if (m >= M)
+                        continue;
+    #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
-                        f32x4 v = acc[i][j];           // this split's own partial
-                        if (sp != me && m < M) {
-                            if (vec4 && n + 3 < N) {
-                                v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                  r, (m * N + n) * 4, 0, kDeviceScope));
-                            } else {
-#pragma unroll
-                                for (int q = 0; q < 4; ++q)
-                                    v[q] = n + q < N ? __hip_atomic_load(part(sp) + (size_t)m * N + n + q,
-                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                                     : 0.f;
-                            }
+                        if (vec4 && n + 3 < N) {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r,
+                                                                   (m * N + n) * 4, 0, kDeviceScope);
+                        } else {
+    #pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (n + q < N)
+                                    __hip_atomic_store(part(me) + (size_t)m * N + n + q, acc[i][j][q], __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
                         }
-                        tot[ii][j] = sp == 0 ? v : tot[ii][j] + v;
                     }
                 }
             }
-#pragma unroll
-            for (int ii = 0; ii < GR; ++ii)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    if (g + ii < FM)
-                        acc[g + ii][j] = tot[ii][j];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            const int tile = tm * tiles_n + tn;
+            if (threadIdx.x == 0) {
+                const int prev = __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_flag = (prev == split_k - 1);
+            }
+            __syncthreads();
+            if (!last_flag)
+                return;
+            // Sums are formed GR block rows at a time (at most 64 registers of
+            // running totals beside the accumulators).
+            constexpr int GR = FN >= 16 ? 1 : 16 / FN;
+    #pragma unroll
+            for (int g = 0; g < FM; g += GR) {
+                f32x4 tot[GR][FN];
+                for (int sp = 0; sp < split_k; ++sp) {
+                    const __amdgpu_buffer_rsrc_t r =
+                        __builtin_amdgcn_make_buffer_rsrc(part(sp), 0, part_bytes, kBufferWord3);
+    #pragma unroll
+                    for (int ii = 0; ii < GR; ++ii) {
+                        const int i = g + ii;
+                        if (i >= FM)
+                            break;
+                        const int m = m0 + wm * WTM + i * 16 + lrow;
+    #pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
+                            f32x4 v = acc[i][j];           // this split's own partial
+                            if (sp != me && m < M) {
+                                if (vec4 && n + 3 < N) {
+                                    v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      r, (m * N + n) * 4, 0, kDeviceScope));
+                                } else {
+    #pragma unroll
+                                    for (int q = 0; q < 4; ++q)
+                                        v[q] = n + q < N ? __hip_atomic_load(part(sp) + (size_t)m * N + n + q,
+                                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                         : 0.f;
+                                }
+                            }
+                            tot[ii][j] = sp == 0 ? v : tot[ii][j] + v;
+                        }
+                    }
+                }
+    #pragma unroll
+                for (int ii = 0; ii < GR; ++ii)
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        if (g + ii < FM)
+                            acc[g + ii][j] = tot[ii][j];
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 
-    const bool vec_ok = (N & 3) == 0;
-    if constexpr (EPI) {
-        // Fused epilogue (bias, activation) through LDS: each wave writes
-        // its fp32 accumulators, CH block rows at a time, into its own LDS
-        // region (rows padded by 16 bytes so the 16 rows of a block land on
-        // distinct banks), then walks the region four columns per lane in
-        // row order, applying bias and activation once per element (one
-        // copy of the activation code instead of one per accumulator
-        // register) and storing bf16 rows.
-        constexpr int REGION = SMEM / NW;               // bytes per wave
-        constexpr int ROWB = WTN * 4 + 16;              // padded fp32 row of a wave tile
-        constexpr int CH0 = REGION / (16 * ROWB);       // block rows that fit
-        constexpr int CH = CH0 >= FM ? FM : (CH0 >= 8 ? 8 : (CH0 >= 4 ? 4 : (CH0 >= 2 ? 2 : 1)));
-        constexpr int QPR = WTN / 4;                    // four-column groups per row
-        static_assert(CH0 >= 1 && FM % CH == 0, "epilogue staging needs a block row of LDS per wave");
-        static_assert(64 % QPR == 0, "a lane keeps its four columns across the walk");
-        // This lane's four columns are the same on every row of the walk:
-        // read their bias values once, before the barrier.
-        const int ncol = n0 + wn * WTN + (lane % QPR) * 4;
-        float bv[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            bv[rr] = ncol + rr < N ? __uint_as_float((uint32_t)bias[ncol + rr] << 16) : 0.f;
-        __syncthreads();                                // every wave is done with the stages
-        char* const wbuf = smem + wave * REGION;
-#pragma unroll
-        for (int c = 0; c < FM; c += CH) {
-#pragma unroll
-            for (int ii = 0; ii < CH; ++ii)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    *(f32x4*)(wbuf + (ii * 16 + lrow) * ROWB + (j * 16 + lgrp * 4) * 4) = acc[c + ii][j];
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            for (int q = lane; q < CH * 16 * QPR; q += 64) {
-                const int r = q / QPR;
-                const int col = (q - r * QPR) * 4;
-                const int m = m0 + wm * WTM + c * 16 + r;
-                const int n = n0 + wn * WTN + col;
-                if (m >= M)
-                    continue;
-                f32x4 v = *(const f32x4*)(wbuf + r * ROWB + col * 4);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    v[rr] = epi_activation(v[rr] + bv[rr], epi);
-                const uint2 h = pack_bf16x4(v);
-                uint16_t* crow = C + (size_t)m * (size_t)N;
+        const bool vec_ok = (N & 3) == 0;
+        if constexpr (EPI) {
+            // Fused epilogue (bias, activation) through LDS: each wave writes
+            // its fp32 accumulators, CH block rows at a time, into its own LDS
+            // region (rows padded by 16 bytes so the 16 rows of a block land on
+            // distinct banks), then walks the region four columns per lane in
+            // row order, applying bias and activation once per element (one
+            // copy of the activation code instead of one per accumulator
+            // register) and storing bf16 rows.
+            constexpr int REGION = SMEM / NW;               // bytes per wave
+            constexpr int ROWB = WTN * 4 + 16;              // padded fp32 row of a wave tile
+            constexpr int CH0 = REGION / (16 * ROWB);       // block rows that fit
+            constexpr int CH = CH0 >= FM ? FM : (CH0 >= 8 ? 8 : (CH0 >= 4 ? 4 : (CH0 >= 2 ? 2 : 1)));
+            constexpr int QPR = WTN / 4;                    // four-column groups per row
+            static_assert(CH0 >= 1 && FM % CH == 0, "epilogue staging needs a block row of LDS per wave");
+            static_assert(64 % QPR == 0, "a lane keeps its four columns across the walk");
+            // This lane's four columns are the same on every row of the walk:
+            // read their bias values once, before the barrier.
+            const int ncol = n0 + wn * WTN + (lane % QPR) * 4;
+            float bv[4];
+    #pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                bv[rr] = ncol + rr < N ? __uint_as_float((uint32_t)bias_t[ncol + rr] << 16) : 0.f;
+            __syncthreads();                                // every wave is done with the stages
+            char* const wbuf = smem + wave * REGION;
+    #pragma unroll
+            for (int c = 0; c < FM; c += CH) {
+    #pragma unroll
+                for (int ii = 0; ii < CH; ++ii)
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        *(f32x4*)(wbuf + (ii * 16 + lrow) * ROWB + (j * 16 + lgrp * 4) * 4) = acc[c + ii][j];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                for (int q = lane; q < CH * 16 * QPR; q += 64) {
+                    const int r = q / QPR;
+                    const int col = (q - r * QPR) * 4;
+                    const int m = m0 + wm * WTM + c * 16 + r;
+                    const int n = n0 + wn * WTN + col;
+                    if (m >= m_lim)
+                        continue;
+                    f32x4 v = *(const f32x4*)(wbuf + r * ROWB + col * 4);
+    #pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        v[rr] = epi_activation(v[rr] + bv[rr], epi);
+                    const uint2 h = pack_bf16x4(v);
+                    uint16_t* crow = C + (size_t)m * (size_t)N;
+                    if (vec_ok && n + 3 < N) {
+                        *(uint2*)(crow + n) = h;
+                    } else {
+    #pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            if (n + rr < N)
+                                crow[n + rr] = bf16_elem(h, rr);
+                    }
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // region reads done before the next chunk
+            }
+            return;
+        }
+
+        // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
+    #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * WTM + i * 16 + lrow;
+            if (m >= m_lim)
+                continue;
+            uint16_t* crow = C + (size_t)m * (size_t)N;
+    #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
+                // One block at a time: keeps the compiler from moving every
+                // accumulator into VGPRs at once (256 of them in 4-wave tiles).
+                __builtin_amdgcn_sched_barrier(0);
+                const uint2 h = pack_bf16x4(acc[i][j]);
                 if (vec_ok && n + 3 < N) {
                     *(uint2*)(crow + n) = h;
                 } else {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        if (n + rr < N)
-                            crow[n + rr] = bf16_elem(h, rr);
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            crow[n + r] = bf16_elem(h, r);
                 }
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // region reads done before the next chunk
         }
-        return;
-    }
+    };
 
-    // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WTM + i * 16 + lrow;
-        if (m >= M)
-            continue;
-        uint16_t* crow = C + (size_t)m * (size_t)N;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
-            // One block at a time: keeps the compiler from moving every
-            // accumulator into VGPRs at once (256 of them in 4-wave tiles).
-            __builtin_amdgcn_sched_barrier(0);
-            const uint2 h = pack_bf16x4(acc[i][j]);
-            if (vec_ok && n + 3 < N) {
-                *(uint2*)(crow + n) = h;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < N)
-                        crow[n + r] = bf16_elem(h, r);
+    if constexpr (!GROUPED) {
+        int tm, tn;
+        tile_order(blockIdx.x, tiles_m, tiles_n, win_w, chunk_c, tm, tn);
+        if (tm >= tiles_m || tn >= tiles_n)    // uniform per workgroup; never taken for a valid order
+            return;
+        run_tile(tm, tn, tm * BM, M, (const char*)Bv, bias);
+    } else {
+        // Grouped (mixture-of-experts) mode, a persistent grid (FlyDSL-in-
+        // PyTorch blog, grouped GEMM section).  Expert g owns rows
+        // [offs[g-1], offs[g]) of A and C and the N x K weight g of B.  The
+        // tiles of all experts form one list, expert after expert (empty
+        // experts have none), each expert's N-major: consecutive tiles share
+        // a B tile.  Workgroup b visits tiles b, b + P, ... (P = grid size),
+        // or, when chunk_c != 0 and the list holds at least P tiles, the
+        // list is cut into 8 contiguous parts and workgroups of XCD x
+        // (b mod 8 = x under round-robin dispatch) walk part x, so the tiles
+        // one XCD holds at a time are neighbours sharing B tiles and A rows
+        // in its L2.  Offsets are clamped into [0, M] and made non-
+        // decreasing per expert, so any offsets keep every access in bounds.
+        static_assert(!MX && SCHED != 1, "grouped mode: bf16 tiles");
+        auto expert_rows = [&](int g, int& r0, int& r1) {
+            r0 = g > 0 ? min(max(offs[g - 1], 0), M) : 0;
+            r1 = max(r0, min(offs[g], M));
+        };
+        // Wave-parallel walk over the experts, 64 at a time: lane l holds
+        // expert gb + l's tile count and the inclusive prefix over the chunk
+        // (64-bit: clamped offsets may overlap, so counts are not bounded by
+        // the tiles of C).
+        auto chunk = [&](int gb, int64_t& tiles_l, int64_t& incl_l) {
+            const int g = gb + lane;
+            tiles_l = 0;
+            if (g < G) {
+                int r0, r1;
+                expert_rows(g, r0, r1);
+                tiles_l = (int64_t)((r1 - r0 + BM - 1) / BM) * tiles_n;
             }
+            incl_l = tiles_l;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int64_t o = __shfl_up(incl_l, d, 64);
+                if (lane >= d)
+                    incl_l += o;
+            }
+        };
+        auto uniform64 = [](int64_t v) {
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+            return (int64_t)(((uint64_t)hi << 32) | lo);
+        };
+        int64_t total = 0;
+        for (int gb = 0; gb < G; gb += 64) {
+            int64_t tl, il;
+            chunk(gb, tl, il);
+            total += uniform64(__shfl(il, 63, 64));
+        }
+        const int64_t P = gridDim.x;
+        int64_t first = blockIdx.x, stride = P, limit = total;
+        if (chunk_c != 0 && P % 8 == 0 && total >= P) {
+            const int64_t x = blockIdx.x % 8;
+            first = total * x / 8 + blockIdx.x / 8;
+            stride = P / 8;
+            limit = total * (x + 1) / 8;
+        }
+        int gb = 0;
+        int64_t tb = 0;
+        for (int64_t t = first; t < limit; t += stride) {
+            // Advance to the chunk of experts holding tile t (tiles are
+            // visited in increasing order, so the walk only moves forward).
+            int64_t tiles_l, incl_l;
+            chunk(gb, tiles_l, incl_l);
+            int64_t chunk_total = uniform64(__shfl(incl_l, 63, 64));
+            while (t >= tb + chunk_total) {
+                tb += chunk_total;
+                gb += 64;
+                chunk(gb, tiles_l, incl_l);
+                chunk_total = uniform64(__shfl(incl_l, 63, 64));
+            }
+            const uint64_t hit = __ballot(tb + incl_l > t);
+            const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+            const int g = gb + l;
+            const int64_t t0 = tb + uniform64(__shfl(incl_l - tiles_l, l, 64));
+            int r0, r1;
+            expert_rows(g, r0, r1);
+            r0 = __builtin_amdgcn_readfirstlane(r0);
+            r1 = __builtin_amdgcn_readfirstlane(r1);
+            const int tiles_mg = (r1 - r0 + BM - 1) / BM;
+            const int u = (int)(t - t0);             // below tiles_mg * tiles_n
+            const int tn = u / tiles_mg;             // N-major inside an expert
+            const int tm = u - tn * tiles_mg;
+            __syncthreads();                         // LDS of the previous tile is free
+            run_tile(tm, tn, r0 + tm * BM, r1, (const char*)Bv + (size_t)g * (size_t)N * row_bytes,
+                     EPI ? bias + (size_t)g * (size_t)N : bias);
         }
     }
 }
@@ -779,9 +887,21 @@ hipError_t launch_tile_t(const void* A, const void* B, uint16_t* C, int M, int N
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, MX>), dim3(tiles_m * tiles_n, split_k),
-                       dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c,
-                       split_k, ws, counters, bias, epi, psa, psb);
+    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, MX, false>),
+                       dim3(tiles_m * tiles_n, split_k), dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m,
+                       tiles_n, win_w, chunk_c, split_k, ws, counters, bias, epi, psa, psb, nullptr, 0);
+    return hipGetLastError();
+}
+
+// Grouped form on a persistent grid of `grid` workgroups.
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI>
+hipError_t launch_grouped_t(const void* A, const void* B, const int* offs, int G, uint16_t* C, int M, int N, int K,
+                            int grid, int xcd_chunks, const uint16_t* bias, int epi, hipStream_t stream)
+{
+    const int tiles_n = (N + BN - 1) / BN;
+    hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, false, true>), dim3(grid), dim3(WM * WN * 64),
+                       0, stream, A, B, C, M, N, K, 0, tiles_n, 0, xcd_chunks, 1, nullptr, nullptr, bias, epi, nullptr,
+                       nullptr, offs, G);
     return hipGetLastError();
 }
 
