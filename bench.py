@@ -17,6 +17,9 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                bias + SiLU (decode) epilogue
   vendor_context  torch.mm (hipBLASLt) on the same inputs with the same
                timing, for comparison across machines whose clocks differ
+  grouped      the grouped (mixture-of-experts) GEMM on the uniform and ragged
+               MoE workloads (TFLOP/s of the experts' rows, 2 sum(M_g) N K per
+               call), with torch._grouped_mm for context
   mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
                mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
                MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
@@ -285,6 +288,37 @@ def bench_mx_decode(torch, hkg, steps, warmup):
                 launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
 
 
+def bench_grouped(torch, hkg, steps, warmup):
+    import workloads
+    out = {}
+    for name in ("moe_uniform_8x1024_4096x4096", "moe_ragged_16_8192_4096x4096"):
+        w = workloads.GROUPED_WORKLOADS[name]
+        A, B, offs = workloads.grouped_workload_inputs(name)
+        M, K = A.shape
+        G, N = B.shape[0], B.shape[1]
+        a, b = to_dev(A, torch), to_dev(B, torch)
+        o = torch.from_numpy(offs).to("cuda")
+        del A, B
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        plan = hkg.grouped_plan(G, M, N, K)
+        flops = 2.0 * float(sum(w["sizes"])) * N * K
+        ms = time_launches(torch, lambda: hkg.grouped_gemm(a, b, o, out=c), steps, warmup)
+        log("grouped %s: %s, %.3f ms (%.1f TFLOP/s)" % (name, plan.kernel_name.decode(), ms, flops / ms / 1e9))
+        ms_v = None
+        try:
+            bt = b.transpose(1, 2)
+            torch._grouped_mm(a, bt, offs=o, out_dtype=torch.bfloat16)
+            ms_v = time_launches(torch, lambda: torch._grouped_mm(a, bt, offs=o, out_dtype=torch.bfloat16),
+                                 steps, warmup)
+            log("grouped %s, torch._grouped_mm for context: %.3f ms (%.1f TFLOP/s)" % (name, ms_v, flops / ms_v / 1e9))
+        except Exception as ex:          # noqa: BLE001 - context figure only
+            log("torch._grouped_mm unavailable: %s" % str(ex)[:100])
+        out[name] = dict(ms=ms, tflops=flops / ms / 1e9, plan=plan, flops=flops,
+                         vendor_tflops=(flops / ms_v / 1e9) if ms_v else None)
+        del a, b, c
+    return out
+
+
 def calibration_copy(torch, mib=1024):
     """One device-to-device copy of a known size (mib MiB read, mib MiB
     written), the reference dispatch for scaling HBM byte counters."""
@@ -328,7 +362,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
-    ap.add_argument("--only", choices=["square", "decode", "mx"], help="time one leg only (profiler runs)")
+    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped"], help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -347,6 +381,10 @@ def main():
         print(json.dumps({"decode_gbps": round(dec["gbps"], 1), "us_per_call": round(dec["ms"] * 1e3, 3),
                           "llc_resident_gbps": round(dec["gbps_hot"], 1)}), flush=True)
         return 0
+    if args.only == "grouped":
+        grp = bench_grouped(torch, hkg, args.steps, args.warmup)
+        print(json.dumps({k: round(v["tflops"], 2) for k, v in grp.items()}), flush=True)
+        return 0
     if args.only == "mx":
         mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
         mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
@@ -360,6 +398,7 @@ def main():
     dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
     mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+    grp = bench_grouped(torch, hkg, args.steps, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
@@ -406,6 +445,15 @@ def main():
         "vendor_context": {"library": "torch.mm (hipBLASLt), same inputs and timing in the same run",
                            "square_tflops": round(sq["vendor_tflops"], 2),
                            "decode_gbps": round(dec["vendor_gbps"], 1)},
+        "grouped": {name: {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                           "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                        "traffic": measured_traffic(r["plan"].kernel_name.decode()),
+                                        "kernel": r["plan"].kernel_name.decode(),
+                                        "per_launch": "2 sum(M_g) N K = %.4g flop per launch" % r["flops"]},
+                           "vendor_grouped_mm_tflops": round(r["vendor_tflops"], 2) if r["vendor_tflops"] else None}
+                    for name, r in grp.items()},
         "mxfp8": {
             "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",
                        "tflops": round(mxs["tflops"], 2), "ms": round(mxs["ms"], 4),
