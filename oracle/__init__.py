@@ -50,6 +50,9 @@ def _bind(path):
     lib.hkg_oracle_gemm_entries.argtypes = [u16p, u16p, i64, i64, i64, i64p, i64p, i64,
                                             u16p, f64p, f64p, ctypes.c_int]
     lib.hkg_oracle_gemm_entries.restype = None
+    lib.hkg_oracle_gemm_layout_rows.argtypes = [u16p, i64, ctypes.c_int, u16p, i64, ctypes.c_int, i64, i64, i64,
+                                                i64, i64, u16p, f64p, f64p, ctypes.c_int]
+    lib.hkg_oracle_gemm_layout_rows.restype = None
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.hkg_oracle_grouped_gemm_rows.argtypes = [u16p, u16p, i32p, i64, i64, i64, i64, i64, i64,
                                                  u16p, f64p, f64p, ctypes.c_int]
@@ -136,6 +139,27 @@ class Oracle:
             self.lib.hkg_oracle_gemm_rows(
                 _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), M, N, K, r0, r1,
                 _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double),
+                _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+    def gemm_layout(self, A, lda, a_col, B, ldb, b_col, M, N, K, rows=None, nthreads=0):
+        """C = A * B^T with operands in stored form: A flat bf16 bits read as
+        a(i,k) = A[i lda + k] (a_col False) or A[k lda + i] (a_col True); B as
+        b(j,k) = B[j ldb + k] or B[k ldb + j].  Returns dense (C, S, absS)."""
+        A = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
+        B = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
+        need_a = ((K - 1) * lda + M if a_col else (M - 1) * lda + K) if M and K else 0
+        need_b = ((K - 1) * ldb + N if b_col else (N - 1) * ldb + K) if N and K else 0
+        if A.size < need_a or B.size < need_b or lda < (M if a_col else K) or ldb < (N if b_col else K):
+            raise ValueError("stored operands too small for the layout")
+        r0, r1 = (0, M) if rows is None else rows
+        C = np.zeros((r1 - r0, N), dtype=np.uint16)
+        S = np.zeros((r1 - r0, N), dtype=np.float64)
+        absS = np.zeros((r1 - r0, N), dtype=np.float64)
+        if r1 > r0 and N > 0:
+            self.lib.hkg_oracle_gemm_layout_rows(
+                _ptr(A, ctypes.c_uint16), int(lda), int(bool(a_col)), _ptr(B, ctypes.c_uint16), int(ldb),
+                int(bool(b_col)), M, N, K, r0, r1, _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double),
                 _ptr(absS, ctypes.c_double), int(nthreads))
         return C, S, absS
 
@@ -316,6 +340,10 @@ def max_threads():
 
 def gemm(A, B, rows=None, nthreads=0, want_sums=True):
     return default().gemm(A, B, rows, nthreads, want_sums)
+
+
+def gemm_layout(A, lda, a_col, B, ldb, b_col, M, N, K, rows=None, nthreads=0):
+    return default().gemm_layout(A, lda, a_col, B, ldb, b_col, M, N, K, rows, nthreads)
 
 
 def grouped_gemm(A, B, offs, rows=None, nthreads=0):

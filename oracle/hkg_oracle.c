@@ -37,6 +37,9 @@
  *   MXFP8: every E4M3 and E8M0 code against torch's float8_e4m3fn and
  *   float8_e8m0fnu conversions; all-ones with unit scales (C = K); scale
  *   changes multiply exactly by powers of two; exact rationals on tiny shapes.
+ *   Layouts: every (A, B) layout with padded leading dimensions equals the
+ *   dense oracle on the logical matrices, and padding (filled with NaN
+ *   patterns) is never read.
  *   Grouped GEMM: one expert equals the dense oracle; all-ones activations
  *   against expert weights filled with (g + 1) give C = K (g + 1) exactly in
  *   each expert's rows (boundaries, empty experts); permuting the experts
@@ -183,6 +186,48 @@ void hkg_oracle_gemm_entries(const uint16_t* A, const uint16_t* B,
 }
 
 int hkg_oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* ---- operand layouts and leading dimensions --------------------------------
+ * The FlyDSL-in-PyTorch blog (section "Dense GEMM") measures all four
+ * operand layouts; the FlyDSL "Prebuilt kernels guide" works with strided
+ * operands.  Read plainly: the logical operands stay A (M x K) and B (N x K)
+ * and C = A * B^T as above; only where element (i, k) lives changes:
+ *   A row layout (a_col = 0): a(i,k) = A[i * lda + k]   (K contiguous, lda >= K)
+ *   A column layout (a_col = 1): a(i,k) = A[k * lda + i] (stored K x M, lda >= M)
+ *   B row layout (b_col = 0): b(j,k) = B[j * ldb + k]   (stored N x K, ldb >= K)
+ *   B column layout (b_col = 1): b(j,k) = B[k * ldb + j] (stored K x N, ldb >= N)
+ *   C[i * ldc + j] for 0 <= j < N, ldc >= N (elements in between untouched).
+ * Sums and rounding exactly as hkg_oracle_gemm_rows; C is written here as a
+ * dense (row_end - row_begin) x N block like the other row functions.
+ */
+void hkg_oracle_gemm_layout_rows(const uint16_t* A, int64_t lda, int a_col, const uint16_t* B, int64_t ldb,
+                                 int b_col, int64_t M, int64_t N, int64_t K, int64_t row_begin, int64_t row_end,
+                                 uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    build_table();
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint16_t a = a_col ? A[k * lda + i] : A[i * lda + k];
+                const uint16_t b = b_col ? B[k * ldb + j] : B[j * ldb + k];
+                double p = g_val[a] * g_val[b];
+                s = s + p;
+                sa = sa + fabs(p);
+            }
+            int64_t o = (i - row_begin) * N + j;
+            C[o] = hkg_oracle_bf16_rne(s);
+            if (S)
+                S[o] = s;
+            if (absS)
+                absS[o] = sa;
+        }
+    }
+}
 
 /* ---- grouped GEMM ----------------------------------------------------------
  * The FlyDSL-in-PyTorch blog (grouped GEMM section, mixture of experts): the

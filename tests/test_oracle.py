@@ -391,6 +391,48 @@ def check_grouped_brute_force_tiny(O):
             assert C[i, j] == exact.round_exact(s)
 
 
+# ------------------------------------------------------------------ layouts
+def _stored(X, col, ld, fill):
+    """X (rows x K logical) stored in row layout (rows x ld) or column layout
+    (K x ld), padding filled with `fill`."""
+    rows, K = X.shape
+    if col:
+        st = np.full((K, ld), fill, dtype=np.uint16)
+        st[:, :rows] = X.T
+    else:
+        st = np.full((rows, ld), fill, dtype=np.uint16)
+        st[:, :K] = X
+    return st
+
+
+def check_layouts_equal_dense(O):
+    # Every layout pair with padded leading dimensions; padding is a NaN
+    # pattern, so a read of it would show as NaN sums.
+    A, B = workloads.make_inputs(13, 9, 40, seed=21)
+    C0, S0, a0 = O.gemm(A, B)
+    for a_col in (False, True):
+        for b_col in (False, True):
+            lda = (13 if a_col else 40) + 3
+            ldb = (9 if b_col else 40) + 5
+            C, S, absS = O.gemm_layout(_stored(A, a_col, lda, 0x7FC1), lda, a_col,
+                                       _stored(B, b_col, ldb, 0xFFC3), ldb, b_col, 13, 9, 40)
+            assert np.array_equal(C, C0) and np.array_equal(S, S0) and np.array_equal(absS, a0), (a_col, b_col)
+
+
+def check_layout_index_roles(O):
+    # A square case where a transposed read would be in bounds: column layout
+    # of A must read A^T's storage as A, not as A^T.
+    rng = np.random.default_rng(8)
+    A = workloads.draw(rng, (16, 16), ("uniform", -1.0, 1.0))
+    B = workloads.draw(rng, (16, 16), ("uniform", -1.0, 1.0))
+    C0, S0, _ = O.gemm(A, B)
+    C1, S1, _ = O.gemm_layout(np.ascontiguousarray(A.T), 16, True, B, 16, False, 16, 16, 16)
+    C2, S2, _ = O.gemm_layout(A, 16, False, np.ascontiguousarray(B.T), 16, True, 16, 16, 16)
+    assert np.array_equal(S1, S0) and np.array_equal(S2, S0)
+    C3, S3, _ = O.gemm(np.ascontiguousarray(A.T), B)
+    assert not np.array_equal(S3, S0)                       # the check above can fail
+
+
 ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
               check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
               check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
@@ -398,7 +440,8 @@ ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_t
               check_epilogue_odd_parts, check_epilogue_columns, check_e4m3_exhaustive,
               check_e8m0_exhaustive, check_mx_all_ones, check_mx_unit_scales_equal_bf16_gemm,
               check_mx_scales_are_powers_of_two, check_mx_brute_force_tiny, check_grouped_one_expert_is_dense,
-              check_grouped_expert_identity, check_grouped_permutation, check_grouped_brute_force_tiny]
+              check_grouped_expert_identity, check_grouped_permutation, check_grouped_brute_force_tiny,
+              check_layouts_equal_dense, check_layout_index_roles]
 
 
 @pytest.fixture(scope="module")
@@ -507,6 +550,10 @@ MUTANTS = {
                               "y = hkg_oracle_activation(S[t], epi) + hkg_oracle_bf16_value(bias[j]);"),
     "bias_shifted_column": ("const int64_t j = cols ? cols[t] : t % N;",
                             "const int64_t j = cols ? cols[t] : (t + 1) % N;"),
+    "layout_a_col_transposed": ("const uint16_t a = a_col ? A[k * lda + i] : A[i * lda + k];",
+                                "const uint16_t a = a_col ? A[i * lda + k] : A[i * lda + k];"),
+    "layout_b_stride_ignored": ("const uint16_t b = b_col ? B[k * ldb + j] : B[j * ldb + k];",
+                                "const uint16_t b = b_col ? B[k * ldb + j] : B[j * K + k];"),
     "group_boundary_inclusive": ("if ((int64_t)offs[mid] > i)", "if ((int64_t)offs[mid] >= i)"),
     "group_next_expert": ("dot_one(A + i * K, B + (g * N + j) * K, K, &s, &sa);",
                           "dot_one(A + i * K, B + (((g + 1) % G) * N + j) * K, K, &s, &sa);"),
