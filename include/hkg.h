@@ -244,6 +244,51 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
                                      int64_t K, int32_t epilogue, void* stream);
 
 /*
+ * Operand layouts and leading dimensions (the FlyDSL-in-PyTorch blog,
+ * section "Dense GEMM", measures all four layouts).  The logical operation is
+ * unchanged, C = epilogue(A * B^T + bias) with A M x K and B N x K; only where
+ * element (i, k) of A (j, k of B) lives changes:
+ *   HKG_LAYOUT_ROW  a(i,k) = A[i * lda + k]   (K contiguous, lda >= K)
+ *   HKG_LAYOUT_COL  a(i,k) = A[k * lda + i]   (stored K x M, lda >= M)
+ * and likewise b(j,k) = B[j * ldb + k] (ROW, ldb >= K) or B[k * ldb + j]
+ * (COL: B stored K x N, ldb >= N); C[i * ldc + j] with ldc >= N (elements in
+ * between are not touched).  In the usual names for C = op(A) op(B) with a
+ * row-major K x N second operand: NT = (ROW, ROW), NN = (ROW, COL),
+ * TN = (COL, COL), TT = (COL, ROW).
+ */
+typedef enum {
+    HKG_LAYOUT_ROW = 0,
+    HKG_LAYOUT_COL = 1
+} hkg_layout_t;
+
+/*
+ * C = epilogue(A * B^T + bias) in any layouts (above), on `stream`.
+ * ROW operands with 16-byte aligned pointers and leading dimensions (ld % 8
+ * == 0) and K % 8 == 0 run the fast kernels in place; a COL operand is first
+ * transposed into a library-owned device buffer (one extra pass over it; to
+ * avoid it for a fixed weight, pack it once with hkg_pack_bf16); anything
+ * else runs the general kernel, which reads every layout directly.
+ * Errors (before any device work): unknown layout, a leading dimension below
+ * its minimum (or above 2^31 - 1), null pointers with nonzero extent, C
+ * overlapping A or B -> HKG_ERR_INVALID_ARG; epilogue errors as
+ * hkg_gemm_bf16_epilogue.  The library's layout buffer is shared by all calls
+ * on a device, like the split-K workspace.
+ */
+hkg_status_t hkg_gemm_bf16_ex(const void* A, int64_t lda, int32_t a_layout, const void* B, int64_t ldb,
+                              int32_t b_layout, const void* bias, void* C, int64_t ldc, int64_t M, int64_t N,
+                              int64_t K, int32_t epilogue, void* stream);
+
+/*
+ * Offline pre-pack of an operand into the layout the fast kernels read: Y
+ * (rows x K bf16, K contiguous, dense) from X of `rows` logical rows in
+ * `layout` with leading dimension ldx (a weight stored K x N for x @ W is
+ * layout COL, rows = N).  Y is then passed as a ROW operand with ld = K.
+ * Device pointers, Y not overlapping X.  Errors as hkg_gemm_bf16_ex.
+ */
+hkg_status_t hkg_pack_bf16(const void* X, int64_t ldx, int32_t layout, void* Y, int64_t rows, int64_t K,
+                           void* stream);
+
+/*
  * Grouped GEMM for mixture-of-experts layers (FlyDSL-in-PyTorch blog,
  * grouped GEMM section: concatenated activations, one weight per expert,
  * cumulative row offsets, one launch on a persistent grid):

@@ -484,3 +484,33 @@ def test_grouped_no_device_status():
     G, M, N, K = 4, 256, 128, 64
     A, B, offs, C = [(1 << 30) + i * (1 << 24) for i in range(4)]
     assert hkg.hkg_grouped_gemm_bf16(A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_NO_DEVICE
+
+
+# ------------------------------------------------------------------ layouts
+def test_layout_argument_errors_precede_device_work():
+    M, N, K = 64, 48, 32
+    A, B, C = [(1 << 30) + i * (1 << 24) for i in range(3)]
+    f = hkg.hkg_gemm_bf16_ex
+    assert f(A, K, 2, B, K, 0, None, C, N, M, N, K) == hkg.HKG_ERR_INVALID_ARG      # unknown layout
+    assert f(A, K - 1, 0, B, K, 0, None, C, N, M, N, K) == hkg.HKG_ERR_INVALID_ARG  # lda < K (row)
+    assert f(A, M - 1, 1, B, K, 0, None, C, N, M, N, K) == hkg.HKG_ERR_INVALID_ARG  # lda < M (column)
+    assert f(A, K, 0, B, N - 1, 1, None, C, N, M, N, K) == hkg.HKG_ERR_INVALID_ARG  # ldb < N (column)
+    assert f(A, K, 0, B, K, 0, None, C, N - 1, M, N, K) == hkg.HKG_ERR_INVALID_ARG  # ldc < N
+    assert f(None, K, 0, B, K, 0, None, C, N, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    # C with a large ldc reaches into B
+    assert f(A, K, 0, C + 2 * 1000 * 10, K, 0, None, C, 1000, M, N, K) == hkg.HKG_ERR_INVALID_ARG
+    assert f(A, K, 0, B, K, 0, None, C, N, M, N, K, 2) == hkg.HKG_ERR_INVALID_ARG   # epilogue without bias
+    assert f(None, K, 0, B, K, 0, None, None, N, 0, N, K) == hkg.HKG_OK               # empty output
+    p = hkg.hkg_pack_bf16
+    assert p(A, K - 1, 0, B, M, K) == hkg.HKG_ERR_INVALID_ARG
+    assert p(A, M, 1, A + 16, M, K) == hkg.HKG_ERR_INVALID_ARG                        # overlap
+    assert p(A, K, 3, B, M, K) == hkg.HKG_ERR_INVALID_ARG
+    assert p(None, K, 0, None, 0, K) == hkg.HKG_OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device status; a GPU is present")
+def test_layout_no_device_status():
+    M, N, K = 64, 48, 32
+    A, B, C = [(1 << 30) + i * (1 << 24) for i in range(3)]
+    assert hkg.hkg_gemm_bf16_ex(A, M, 1, B, N, 1, None, C, N, M, N, K) == hkg.HKG_ERR_NO_DEVICE
+    assert hkg.hkg_pack_bf16(A, M, 1, B, M, K) == hkg.HKG_ERR_NO_DEVICE

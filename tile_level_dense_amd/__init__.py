@@ -9,8 +9,10 @@ the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_epilogue``,
 calls ``hkg_gemm_mxfp8``, ``hkg_gemm_mxfp8_plan``, ``hkg_mx_pack_scales``,
 ``hkg_mx_packed_scales_bytes``, ``hkg_gemm_mxfp8_prepacked``,
 ``hkg_gemm_mxfp8_run_plan``, and the grouped calls ``hkg_grouped_gemm_bf16``,
-``hkg_grouped_gemm_bf16_plan``, ``hkg_grouped_gemm_bf16_run_plan``); ``gemm``,
-``gemm_mxfp8`` and ``grouped_gemm`` are the torch-facing convenience wrappers (with ``bias=`` and ``epilogue=`` for the
+``hkg_grouped_gemm_bf16_plan``, ``hkg_grouped_gemm_bf16_run_plan``, and the
+layout calls ``hkg_gemm_bf16_ex``, ``hkg_pack_bf16``); ``gemm``, ``gemm_ex``,
+``pack``, ``gemm_mxfp8`` and ``grouped_gemm`` are the torch-facing convenience
+wrappers (with ``bias=`` and ``epilogue=`` for the
 fused epilogues).  torch supplies device memory and streams.
 
 There is no fallback: if the library is not built and cannot be built, or a
@@ -25,7 +27,8 @@ __all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_g
            "KERNEL_NAMES", "EPILOGUES", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
            "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan", "gemm_mxfp8",
            "mx_plan", "mx_pack_scales", "run_mx_plan", "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan",
-           "hkg_grouped_gemm_bf16_run_plan", "grouped_gemm", "grouped_plan"]
+           "hkg_grouped_gemm_bf16_run_plan", "grouped_gemm", "grouped_plan", "hkg_gemm_bf16_ex", "hkg_pack_bf16",
+           "gemm_ex", "pack", "LAYOUT_ROW", "LAYOUT_COL"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -45,6 +48,8 @@ KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "
 (HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE,
  HKG_KERNEL_GROUPED) = range(7)
 
+LAYOUT_ROW, LAYOUT_COL = 0, 1          # hkg_layout_t
+
 # hkg_epilogue_t codes by the FlyDSL guide's names
 EPILOGUES = {"none": 0, "bias": 1, "bias_relu": 2, "bias_silu": 3, "bias_gelu": 4}
 
@@ -52,7 +57,8 @@ EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_pl
                     "hkg_gemm_bf16_run_plan_epilogue", "hkg_status_string", "hkg_last_hip_error",
                     "hkg_abi_version", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
                     "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan",
-                    "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan", "hkg_grouped_gemm_bf16_run_plan"]
+                    "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan", "hkg_grouped_gemm_bf16_run_plan",
+                    "hkg_gemm_bf16_ex", "hkg_pack_bf16"]
 
 
 class Plan(ctypes.Structure):
@@ -149,6 +155,10 @@ def _load():
     lib.hkg_grouped_gemm_bf16_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
                                                    vp]
     lib.hkg_grouped_gemm_bf16_run_plan.restype = ctypes.c_int
+    lib.hkg_gemm_bf16_ex.argtypes = [vp, i64, i32, vp, i64, i32, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_bf16_ex.restype = ctypes.c_int
+    lib.hkg_pack_bf16.argtypes = [vp, i64, i32, vp, i64, i64, vp]
+    lib.hkg_pack_bf16.restype = ctypes.c_int
     if lib.hkg_abi_version() != HKG_ABI_VERSION:
         raise ImportError("libhkg.so ABI version %d, binding expects %d" % (lib.hkg_abi_version(), HKG_ABI_VERSION))
     _lib = lib
@@ -211,6 +221,15 @@ def hkg_gemm_mxfp8_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=
 
 def hkg_gemm_mxfp8_run_plan(plan_, A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
     return _load().hkg_gemm_mxfp8_run_plan(ctypes.byref(plan_), A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_bf16_ex(A, lda, a_layout, B, ldb, b_layout, bias, C, ldc, M, N, K, epilogue=0, stream=None):
+    """C-ABI call with raw device addresses (ints); returns the status code."""
+    return _load().hkg_gemm_bf16_ex(A, lda, a_layout, B, ldb, b_layout, bias, C, ldc, M, N, K, epilogue, stream)
+
+
+def hkg_pack_bf16(X, ldx, layout, Y, rows, K, stream=None):
+    return _load().hkg_pack_bf16(X, ldx, layout, Y, rows, K, stream)
 
 
 def hkg_grouped_gemm_bf16(A, B, offs, bias, C, G, M, N, K, epilogue=0, stream=None):
@@ -449,3 +468,65 @@ def grouped_gemm(a, b, offs, out=None, stream=None, bias=None, epilogue="none", 
     if st != HKG_OK:
         raise HkgError(st, "hkg_grouped_gemm_bf16")
     return out
+
+
+# ------------------------------------------------------------------ layouts
+def _layout_of(t, name):
+    """(layout, leading dimension) of a 2-D tensor view with one unit stride:
+    row layout when its last dimension is contiguous, column layout when its
+    first is (e.g. W.t() of a K x N weight W)."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    r, c = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 or c <= 1:
+        return LAYOUT_ROW, max(s0 if r > 1 else c, c, 1)
+    if s0 == 1 or r <= 1:
+        return LAYOUT_COL, max(s1 if c > 1 else r, r, 1)
+    raise ValueError("%s needs one unit stride (got strides %s)" % (name, (s0, s1)))
+
+
+def gemm_ex(a, b, out=None, stream=None, bias=None, epilogue="none"):
+    """C = epilogue(a @ b.T + bias) for bf16 device views a (M x K) and b
+    (N x K) in any layout: each may be row-major or a transposed view (one
+    unit stride), with any leading dimension; out may be a row-major view
+    with a leading dimension (its other elements are left alone)."""
+    import torch
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("A and B must be torch.bfloat16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1] or not (a.is_cuda and b.is_cuda) \
+            or a.device != b.device:
+        raise ValueError("A must be M x K and B N x K device views")
+    M, K = a.shape
+    N = b.shape[0]
+    la, lda = _layout_of(a, "A")
+    lb, ldb = _layout_of(b, "B")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or out.device != a.device or \
+            (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a bf16 %d x %d view with unit column stride" % (M, N))
+    ldc = max(out.stride(0) if M > 1 else N, N, 1)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
+    with torch.cuda.device(a.device):
+        st = _load().hkg_gemm_bf16_ex(a.data_ptr(), lda, la, b.data_ptr(), ldb, lb, bias_ptr or None,
+                                      out.data_ptr(), ldc, M, N, K, code, _stream_handle(stream, a.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_bf16_ex")
+    return out
+
+
+def pack(x, stream=None):
+    """Row-layout, dense copy (rows x K) of a bf16 device view x (rows x K) in
+    any layout, by hkg_pack_bf16: the form the fast kernels read in place."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("x must be a bf16 device tensor")
+    rows, K = x.shape
+    layout, ld = _layout_of(x, "x")
+    y = torch.empty((rows, K), dtype=torch.bfloat16, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _load().hkg_pack_bf16(x.data_ptr(), ld, layout, y.data_ptr(), rows, K, _stream_handle(stream, x.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_pack_bf16")
+    return y

@@ -59,6 +59,8 @@ struct DeviceState {
     size_t counter_count = 0;
     uint8_t* mx_ws = nullptr;     // packed MXFP8 scales of hkg_gemm_mxfp8
     size_t mx_ws_bytes = 0;
+    uint16_t* layout_ws = nullptr;  // row-layout copies of column-layout operands (hkg_gemm_bf16_ex)
+    size_t layout_ws_bytes = 0;
 };
 
 constexpr int kMaxDevices = 64;
@@ -152,6 +154,28 @@ hkg_status_t get_mx_workspace(int dev, size_t bytes, uint8_t** out)
         d.mx_ws_bytes = bytes;
     }
     *out = d.mx_ws;
+    return HKG_OK;
+}
+
+// Row-layout copies of column-layout operands for `dev`: grown on demand.
+hkg_status_t get_layout_workspace(int dev, size_t bytes, uint16_t** out)
+{
+    DeviceState& d = g_devices[dev];
+    std::lock_guard<std::mutex> lock(d.ws_mutex);
+    if (d.layout_ws_bytes < bytes) {
+        if (d.layout_ws)
+            (void)hipFree(d.layout_ws);
+        d.layout_ws = nullptr;
+        d.layout_ws_bytes = 0;
+        hipError_t e = hipMalloc((void**)&d.layout_ws, bytes);
+        if (e != hipSuccess) {
+            set_hip_error(e, "hipMalloc(layout workspace)");
+            d.layout_ws = nullptr;
+            return HKG_ERR_WORKSPACE;
+        }
+        d.layout_ws_bytes = bytes;
+    }
+    *out = d.layout_ws;
     return HKG_OK;
 }
 
@@ -418,8 +442,10 @@ bool plan_matches_library(const hkg_plan_t* p)
     }
 }
 
+// Leading dimensions: A rows lda apart, B rows ldb apart, C rows ldc apart
+// (elements); the dense calls pass K, K, N.
 hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, const uint16_t* bias, int epi,
-                 hipStream_t stream)
+                 hipStream_t stream, int64_t lda, int64_t ldb, int64_t ldc)
 {
     const int64_t M = p->M, N = p->N, K = p->K;
     if (p->kernel_id == HKG_KERNEL_NONE)
@@ -434,10 +460,10 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
     hipError_t e = hipSuccess;
     switch (p->kernel_id) {
     case HKG_KERNEL_ZERO:
-        e = launch_zero(c, M, N, bias, epi, stream);
+        e = launch_zero(c, ldc, M, N, bias, epi, stream);
         break;
     case HKG_KERNEL_GENERIC:
-        e = launch_generic(a, b, c, M, N, K, bias, epi, stream);
+        e = launch_generic(a, lda, 0, b, ldb, 0, c, ldc, M, N, K, bias, epi, stream);
         break;
     case HKG_KERNEL_TILE: {
         float* ws = nullptr;
@@ -449,7 +475,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
                 return st;
         }
         e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c,
-                        p->split_k, ws, counters, bias, epi, stream);
+                        p->split_k, ws, counters, bias, epi, (int)lda, (int)ldb, (int)ldc, stream);
         break;
     }
     case HKG_KERNEL_SKINNY: {
@@ -462,7 +488,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
                 return st;
         }
         e = launch_skinny(p->variant, a, b, c, (int)M, (int)N, (int)K, p->split_k, ws, counters, bias, epi,
-                          stream);
+                          (int)lda, (int)ldb, (int)ldc, stream);
         break;
     }
     default:
@@ -485,9 +511,12 @@ struct Cleanup {
                 (void)hipFree(d.counters);
             if (d.mx_ws)
                 (void)hipFree(d.mx_ws);
+            if (d.layout_ws)
+                (void)hipFree(d.layout_ws);
             d.ws = nullptr;
             d.counters = nullptr;
             d.mx_ws = nullptr;
+            d.layout_ws = nullptr;
         }
     }
 } g_cleanup;
@@ -525,7 +554,7 @@ hkg_status_t gemm(const void* A, const void* B, const void* bias, void* C, int64
     if ((p.kernel_id == HKG_KERNEL_TILE || p.kernel_id == HKG_KERNEL_SKINNY) &&
         !(aligned16(A) && aligned16(B) && aligned16(C)))
         plan_generic(M, N, &p, "pointers not 16-byte aligned");
-    return run(&p, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
+    return run(&p, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream, K, K, N);
 }
 
 hkg_status_t run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* bias, void* C,
@@ -549,7 +578,7 @@ hkg_status_t run_plan(const hkg_plan_t* plan, const void* A, const void* B, cons
     if ((plan->kernel_id == HKG_KERNEL_TILE || plan->kernel_id == HKG_KERNEL_SKINNY) &&
         !(aligned16(A) && aligned16(B) && aligned16(C)))
         return HKG_ERR_MISALIGNED;
-    return run(plan, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
+    return run(plan, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream, K, K, N);
 }
 
 // ------------------------------------------------------------------- MXFP8
@@ -690,7 +719,7 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
         return st;
     hipError_t e = hipSuccess;
     if (p->kernel_id == HKG_KERNEL_ZERO) {
-        e = launch_zero((uint16_t*)C, M, N, bias, epi, stream);
+        e = launch_zero((uint16_t*)C, N, M, N, bias, epi, stream);
     } else {
         float* ws = nullptr;
         int* counters = nullptr;
@@ -772,6 +801,101 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
     }
     return run_mx(&p, A, (const uint32_t*)ws, B, (const uint32_t*)(ws + pa), C, (const uint16_t*)bias, epi,
                   (hipStream_t)stream);
+}
+
+// ------------------------------------------------- layouts and strides
+// All four operand layouts (FlyDSL-in-PyTorch blog, "Dense GEMM") and leading
+// dimensions.  Row layout: a(i,k) = A[i lda + k]; column layout: a(i,k) =
+// A[k lda + i] (B likewise with j, ldb); C[i ldc + j].
+
+// Bytes spanned by an operand of `rows` logical rows in a layout.
+int64_t operand_extent(int64_t rows, int64_t K, int64_t ld, int col)
+{
+    if (rows == 0 || K == 0)
+        return 0;
+    return 2 * (col ? (K - 1) * ld + rows : (rows - 1) * ld + K);
+}
+
+// Largest leading dimension whose 256-row tile stays within 32-bit offsets.
+constexpr int64_t kMaxLd = (int64_t)(INT32_MAX / 2) / 256;
+
+hkg_status_t gemm_ex(const void* A, int64_t lda, int32_t a_layout, const void* B, int64_t ldb, int32_t b_layout,
+                     const void* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t epi,
+                     void* stream_v)
+{
+    hipStream_t stream = (hipStream_t)stream_v;
+    hkg_plan_t p;
+    hkg_status_t st = make_plan(M, N, K, &p);
+    if (st != HKG_OK)
+        return st;
+    if ((a_layout != HKG_LAYOUT_ROW && a_layout != HKG_LAYOUT_COL) ||
+        (b_layout != HKG_LAYOUT_ROW && b_layout != HKG_LAYOUT_COL))
+        return HKG_ERR_INVALID_ARG;
+    const int a_col = a_layout == HKG_LAYOUT_COL, b_col = b_layout == HKG_LAYOUT_COL;
+    // leading dimensions at least the contiguous extent (1 for empty operands)
+    if (lda < std::max<int64_t>(1, a_col ? M : K) || ldb < std::max<int64_t>(1, b_col ? N : K) ||
+        ldc < std::max<int64_t>(1, N) || lda > kMaxDim || ldb > kMaxDim || ldc > kMaxDim)
+        return HKG_ERR_INVALID_ARG;
+    const int64_t a_bytes = operand_extent(M, K, lda, a_col), b_bytes = operand_extent(N, K, ldb, b_col);
+    const int64_t c_bytes = (M && N) ? 2 * ((M - 1) * ldc + N) : 0;
+    if ((a_bytes && !A) || (b_bytes && !B) || (c_bytes && !C))
+        return HKG_ERR_INVALID_ARG;
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
+        return HKG_ERR_INVALID_ARG;
+    st = check_epilogue(bias, C, M, N, epi);
+    if (st != HKG_OK)
+        return st;
+    if (p.kernel_id == HKG_KERNEL_NONE)
+        return HKG_OK;
+    if (p.kernel_id == HKG_KERNEL_ZERO)
+        return run(&p, A, B, C, (const uint16_t*)bias, epi, stream, lda, ldb, ldc);
+    // Fast kernels read K-contiguous rows with 16-byte accesses: 16-byte
+    // aligned pointers and leading dimensions, K % 8 == 0 (the plan's own
+    // condition).  Otherwise the general kernel reads any layout directly.
+    const bool fast = p.kernel_id != HKG_KERNEL_GENERIC && aligned16(A) && aligned16(B) && aligned16(C) &&
+                      lda % 8 == 0 && ldb % 8 == 0 && lda <= kMaxLd && ldb <= kMaxLd;
+    if (!fast) {
+        int dev = 0;
+        st = current_device(&dev);
+        if (st != HKG_OK)
+            return st;
+        hipError_t e = launch_generic((const uint16_t*)A, lda, a_col, (const uint16_t*)B, ldb, b_col, (uint16_t*)C,
+                                      ldc, M, N, K, (const uint16_t*)bias, epi, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "kernel launch");
+            return HKG_ERR_HIP;
+        }
+        return HKG_OK;
+    }
+    // Column-layout operands are first transposed into a library buffer
+    // (row layout, leading dimension K), then the row-layout kernels run.
+    if (a_col || b_col) {
+        int dev = 0;
+        st = current_device(&dev);
+        if (st != HKG_OK)
+            return st;
+        const size_t a_ws = a_col ? (size_t)M * (size_t)K : 0, b_ws = b_col ? (size_t)N * (size_t)K : 0;
+        uint16_t* ws = nullptr;
+        st = get_layout_workspace(dev, (a_ws + b_ws) * sizeof(uint16_t), &ws);
+        if (st != HKG_OK)
+            return st;
+        hipError_t e = hipSuccess;
+        if (a_col) {
+            e = launch_transpose((const uint16_t*)A, lda, ws, K, M, K, stream);
+            A = ws;
+            lda = K;
+        }
+        if (e == hipSuccess && b_col) {
+            e = launch_transpose((const uint16_t*)B, ldb, ws + a_ws, K, N, K, stream);
+            B = ws + a_ws;
+            ldb = K;
+        }
+        if (e != hipSuccess) {
+            set_hip_error(e, "kernel launch");
+            return HKG_ERR_HIP;
+        }
+    }
+    return run(&p, A, B, C, (const uint16_t*)bias, epi, stream, lda, ldb, ldc);
 }
 
 // ------------------------------------------------------------ grouped GEMM
@@ -1025,6 +1149,43 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
         return HKG_ERR_MISALIGNED;
     return run_mx(plan, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epilogue,
                   (hipStream_t)stream);
+}
+
+hkg_status_t hkg_gemm_bf16_ex(const void* A, int64_t lda, int32_t a_layout, const void* B, int64_t ldb,
+                              int32_t b_layout, const void* bias, void* C, int64_t ldc, int64_t M, int64_t N,
+                              int64_t K, int32_t epilogue, void* stream)
+{
+    return gemm_ex(A, lda, a_layout, B, ldb, b_layout, bias, C, ldc, M, N, K, epilogue, stream);
+}
+
+hkg_status_t hkg_pack_bf16(const void* X, int64_t ldx, int32_t layout, void* Y, int64_t rows, int64_t K,
+                           void* stream)
+{
+    if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || (layout != HKG_LAYOUT_ROW && layout != HKG_LAYOUT_COL))
+        return HKG_ERR_INVALID_ARG;
+    if (rows == 0 || K == 0)
+        return HKG_OK;
+    const int col = layout == HKG_LAYOUT_COL;
+    if (ldx < (col ? rows : K))
+        return HKG_ERR_INVALID_ARG;
+    const int64_t x_bytes = operand_extent(rows, K, ldx, col), y_bytes = 2 * rows * K;
+    if (!X || !Y || overlaps(X, x_bytes, Y, y_bytes))
+        return HKG_ERR_INVALID_ARG;
+    int dev = 0;
+    hkg_status_t st = current_device(&dev);
+    if (st != HKG_OK)
+        return st;
+    hipError_t e;
+    if (col)
+        e = launch_transpose((const uint16_t*)X, ldx, (uint16_t*)Y, K, rows, K, (hipStream_t)stream);
+    else
+        e = hipMemcpy2DAsync(Y, (size_t)K * 2, X, (size_t)ldx * 2, (size_t)K * 2, (size_t)rows,
+                             hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, col ? "kernel launch" : "hipMemcpy2DAsync");
+        return HKG_ERR_HIP;
+    }
+    return HKG_OK;
 }
 
 hkg_status_t hkg_grouped_gemm_bf16_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* out)

@@ -69,9 +69,10 @@ int skinny_lds_bytes(int variant);
 // split_k == 1: plain launch.  split_k > 1: K divided across workgroups,
 // fp32 partials in `ws` (split_k * M * N floats) and per-tile arrival
 // counters in `counters` (one per output tile, zero on entry and on exit).
+// lda, ldb, ldc: leading dimensions (elements) of A (M x K), B (N x K), C.
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int xcd_chunk, int split_k, float* ws,
-                       int* counters, const uint16_t* bias, int epi, hipStream_t stream);
+                       int* counters, const uint16_t* bias, int epi, int lda, int ldb, int ldc, hipStream_t stream);
 
 // MXFP8 tile kernel: A, B E4M3 codes, K % 128 == 0, psa / psb the packed
 // scales (launch_mx_pack) of A and B; other arguments as launch_tile.
@@ -95,13 +96,20 @@ hipError_t launch_mx_pack(const uint8_t* S, uint32_t* P, int64_t rows, int64_t K
 // (grid_x ints, zero on entry and left zero on exit).
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                          int M, int N, int K, int split_k, float* ws, int* counters,
-                         const uint16_t* bias, int epi, hipStream_t stream);
+                         const uint16_t* bias, int epi, int lda, int ldb, int ldc, hipStream_t stream);
 
-hipError_t launch_generic(const uint16_t* A, const uint16_t* B, uint16_t* C,
-                          int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epi, hipStream_t stream);
+// a_col / b_col: the operand is stored in column layout (a(i,k) = A[k lda + i]).
+hipError_t launch_generic(const uint16_t* A, int64_t lda, int a_col, const uint16_t* B, int64_t ldb, int b_col,
+                          uint16_t* C, int64_t ldc, int64_t M, int64_t N, int64_t K, const uint16_t* bias, int epi,
+                          hipStream_t stream);
 
 // K == 0: C[i][n] = epilogue(+0) (the empty sum).
-hipError_t launch_zero(uint16_t* C, int64_t M, int64_t N, const uint16_t* bias, int epi, hipStream_t stream);
+hipError_t launch_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const uint16_t* bias, int epi,
+                       hipStream_t stream);
+
+// Y[r ldy + c] = X[c ldx + r], r < R, c < CC (column layout -> row layout).
+hipError_t launch_transpose(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t ldy, int64_t R, int64_t CC,
+                            hipStream_t stream);
 
 // Build-time resource figures of each kernel (filled by the generated
 // hkg_resources.inc; -1 where unknown).

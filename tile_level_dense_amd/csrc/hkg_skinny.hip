@@ -71,7 +71,7 @@ __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
                    float* __restrict__ ws, int* __restrict__ counters,
-                   const uint16_t* __restrict__ bias, int epi)
+                   const uint16_t* __restrict__ bias, int epi, int lda, int ldb, int ldc)
 {
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
@@ -97,15 +97,18 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     const int s_begin = min(wg_end, wg_begin + slice * per_wave);
     const int s_end = min(wg_end, s_begin + per_wave);
 
-    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const uint32_t a_rb = (uint32_t)lda * 2u;   // row strides in bytes (leading dimensions)
+    const uint32_t b_rb = (uint32_t)ldb * 2u;
     const int rows_b = min(16 * NB, N - n0);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + (size_t)n0 * (size_t)K), 0, (int)(rows_b * row_bytes), kBufferWord3);
+        (void*)(B + (size_t)n0 * (size_t)ldb), 0, (int)(rows_b * b_rb), kBufferWord3);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)A, 0, (int)((uint32_t)M * row_bytes), kBufferWord3);
+        (void*)A, 0, (int)((uint32_t)M * a_rb), kBufferWord3);
 
-    const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)lgrp * 16u;
-    const uint32_t block16 = 16u * row_bytes;    // next 16 rows
+    const uint32_t lane_off_a = (uint32_t)lrow * a_rb + (uint32_t)lgrp * 16u;
+    const uint32_t lane_off_b = (uint32_t)lrow * b_rb + (uint32_t)lgrp * 16u;
+    const uint32_t block16_a = 16u * a_rb;      // next 16 rows
+    const uint32_t block16_b = 16u * b_rb;
 
     f32x4 acc[NB][MB];
 #pragma unroll
@@ -121,13 +124,13 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
             const bool ok = step < s_end && step * 32 + lgrp * 8 < K;
-            const uint32_t off = lane_off + (uint32_t)step * 64u;
+            const uint32_t kb = (uint32_t)step * 64u;
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                bv[u][j] = load16<CP>(rb, ok ? off + (uint32_t)j * block16 : kOutOfRange);
+                bv[u][j] = load16<CP>(rb, ok ? lane_off_b + kb + (uint32_t)j * block16_b : kOutOfRange);
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                av[u][i] = load16<0>(ra, ok ? off + (uint32_t)i * block16 : kOutOfRange);
+                av[u][i] = load16<0>(ra, ok ? lane_off_a + kb + (uint32_t)i * block16_a : kOutOfRange);
         }
     };
     auto mfma_chunk = [&](const i32x4 (&bv)[U][NB], const i32x4 (&av)[U][MB]) {
@@ -177,7 +180,7 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
             red[slice][j * MB + i][lane] = acc[j][i];
     __syncthreads();
 
-    const bool vec_ok = (N & 3) == 0;
+    const bool vec_ok = ((N | ldc) & 3) == 0;
     for (int b = wave; b < NBLK; b += WK) {
         f32x4 sum = red[0][b][lane];
 #pragma unroll
@@ -195,7 +198,7 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
                         sum[r] = epi_apply(sum[r], bias, n + r, epi);
             }
             const uint2 h = pack_bf16x4(sum);
-            uint16_t* crow = C + (size_t)m * (size_t)N;
+            uint16_t* crow = C + (size_t)m * (size_t)ldc;
             if (vec_ok && n + 3 < N) {
                 *(uint2*)(crow + n) = h;
             } else {
@@ -242,7 +245,7 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (EPI)
             sum = epi_apply(sum, bias, n0 + c, epi);
-        C[(size_t)m * (size_t)N + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
+        C[(size_t)m * (size_t)ldc + n0 + c] = __builtin_bit_cast(uint16_t, (__bf16)sum);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -250,12 +253,12 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 
 template <int MB, int NB, int WK, int U, int CP, bool EPI>
 hipError_t launch_skinny_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                           int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
-                           hipStream_t stream)
+                           int split_k, float* ws, int* counters, const uint16_t* bias, int epi, int lda, int ldb,
+                           int ldc, hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
     hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
-                       A, B, C, M, N, K, split_k, ws, counters, bias, epi);
+                       A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc);
     return hipGetLastError();
 }
 
@@ -280,16 +283,16 @@ int skinny_lds_bytes(int variant)
 
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                          int M, int N, int K, int split_k, float* ws, int* counters,
-                         const uint16_t* bias, int epi, hipStream_t stream)
+                         const uint16_t* bias, int epi, int lda, int ldb, int ldc, hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(mb, nb, wk, u, cp) \
     if (v++ == variant)               \
         return epi == EPI_NONE                                                                                \
                    ? launch_skinny_t<mb, nb, wk, u, cp, false>(A, B, C, M, N, K, split_k, ws, counters, bias, epi, \
-                                                               stream)                                            \
+                                                               lda, ldb, ldc, stream)                             \
                    : launch_skinny_t<mb, nb, wk, u, cp, true>(A, B, C, M, N, K, split_k, ws, counters, bias, epi,  \
-                                                              stream);
+                                                              lda, ldb, ldc, stream);
     HKG_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;

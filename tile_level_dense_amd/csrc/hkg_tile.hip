@@ -27,7 +27,7 @@ int tile_lds_bytes(int variant)
 
 hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
                        int M, int N, int K, int win_w, int chunk_c, int split_k, float* ws, int* counters,
-                       const uint16_t* bias, int epi, hipStream_t stream)
+                       const uint16_t* bias, int epi, int lda, int ldb, int ldc, hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc) \
@@ -35,10 +35,12 @@ hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16
         return epi == EPI_NONE                                                                               \
                    ? launch_tile_t<bm, bn, bk, st, wm, wn, sc, false, false>(A, B, C, M, N, K, win_w, chunk_c,     \
                                                                              split_k, ws, counters, bias, epi,   \
-                                                                             nullptr, nullptr, stream)           \
+                                                                             nullptr, nullptr, lda, ldb, ldc,    \
+                                                                             stream)                             \
                    : launch_tile_t<bm, bn, bk, st, wm, wn, sc, true, false>(A, B, C, M, N, K, win_w, chunk_c,      \
                                                                             split_k, ws, counters, bias, epi,    \
-                                                                            nullptr, nullptr, stream);
+                                                                            nullptr, nullptr, lda, ldb, ldc,     \
+                                                                            stream);
     HKG_TILE_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;

@@ -148,7 +148,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                  int split_k, float* __restrict__ ws, int* __restrict__ counters,
                  const uint16_t* __restrict__ bias, int epi,
                  const uint32_t* __restrict__ PSA, const uint32_t* __restrict__ PSB,
-                 const int* __restrict__ offs, int G)
+                 const int* __restrict__ offs, int G, int lda, int ldb, int ldc)
 {
     constexpr int NW = WM * WN;
     constexpr int EB = MX ? 1 : 2;         // bytes per element
@@ -186,7 +186,10 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
-    const uint32_t row_bytes = (uint32_t)K * (uint32_t)EB;
+    // Row strides in bytes (leading dimensions); MXFP8 and grouped launches
+    // use dense operands, so there both operands share one stride.
+    const uint32_t a_rb = (uint32_t)lda * (uint32_t)EB;
+    const uint32_t b_rb = (MX || GROUPED) ? a_rb : (uint32_t)ldb * (uint32_t)EB;
     __shared__ int last_flag;               // split-K: this workgroup arrived last
 
     // One output tile: C rows [m0, min(m0 + BM, m_lim)) by columns
@@ -207,9 +210,9 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         const int rows_b = min(BN, N - n0);
 
         const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)Av + (size_t)m0 * row_bytes), 0, (int)(rows_a * row_bytes), kBufferWord3);
+            (void*)((const char*)Av + (size_t)m0 * a_rb), 0, (int)(rows_a * a_rb), kBufferWord3);
         const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(b_rows + (size_t)n0 * row_bytes), 0, (int)(rows_b * row_bytes), kBufferWord3);
+            (void*)(b_rows + (size_t)n0 * b_rb), 0, (int)(rows_b * b_rb), kBufferWord3);
 
         // LDS layout of a stage: row r holds its logical 16-byte chunk c at
         // position c ^ ((r / RPL) % CPR).  Sixteen consecutive rows read at one
@@ -226,9 +229,11 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         constexpr int COPY_ROWS = NW * RPW;
         const int lrow0 = wave * RPW + lane / CPR;
         const int lchunk = (lane % CPR) ^ ((lrow0 / RPL) % CPR);
-        const uint32_t src_off = (uint32_t)lrow0 * row_bytes + (uint32_t)lchunk * 16u;
+        const uint32_t src_off_a = (uint32_t)lrow0 * a_rb + (uint32_t)lchunk * 16u;
+        const uint32_t src_off_b = (uint32_t)lrow0 * b_rb + (uint32_t)lchunk * 16u;
         const int src_k = lchunk * KPC;
-        const uint32_t copy_step = (uint32_t)COPY_ROWS * row_bytes;
+        const uint32_t copy_step_a = (uint32_t)COPY_ROWS * a_rb;
+        const uint32_t copy_step_b = (uint32_t)COPY_ROWS * b_rb;
 
         // K range of this workgroup: stages [kt0, kt0 + nk) of BK k;
         // split_k > 1 divides K across workgroups (blockIdx.y).
@@ -243,17 +248,17 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             char* base = smem + stage * STAGE;
             const int k0 = kbase + kl;
             const bool k_out = k0 + src_k >= k_lim;  // this lane's chunk past the range
-            const uint32_t off0 = k_out ? kOutOfRange : src_off + (uint32_t)k0 * (uint32_t)EB;
+            const uint32_t koff = (uint32_t)k0 * (uint32_t)EB;
     #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16,
-                    k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
+                    k_out ? kOutOfRange : src_off_a + koff + (uint32_t)i * copy_step_a, 0, 0, 0);
     #pragma unroll
             for (int i = 0; i < B_LOADS; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16,
-                    k_out ? kOutOfRange : off0 + (uint32_t)i * copy_step, 0, 0, 0);
+                    k_out ? kOutOfRange : src_off_b + koff + (uint32_t)i * copy_step_b, 0, 0, 0);
         };
 
         // Fragment reads: lane -> row (lane % 16) of a 16-row block, logical
@@ -507,22 +512,23 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // as the copies above; a group's 4 waves fill 32 rows per round).
             const int prow = w4 * RPW + lane / CPR;
             const int pchunk = (lane % CPR) ^ ((prow / RPL) % CPR);
-            const uint32_t p_off = (uint32_t)(128 * g + prow) * row_bytes + (uint32_t)pchunk * 16u;
+            const uint32_t p_off_a = (uint32_t)(128 * g + prow) * a_rb + (uint32_t)pchunk * 16u;
+            const uint32_t p_off_b = (uint32_t)(128 * g + prow) * b_rb + (uint32_t)pchunk * 16u;
             const int p_k = pchunk * KPC;
-            const uint32_t p_step = (uint32_t)(4 * RPW) * row_bytes;
             static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a group's copies");
-            auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t) {
+            auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t, uint32_t p_off, uint32_t rb) {
                 const int k0 = kbase + t * BK;
                 const bool k_out = k0 + p_k >= k_lim;
                 const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * (uint32_t)EB;
+                const uint32_t p_step = (uint32_t)(4 * RPW) * rb;
     #pragma unroll
                 for (int i = 0; i < CPW; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (w4 + 4 * i) * 1024), 16,
                                                              k_out ? kOutOfRange : off0 + (uint32_t)i * p_step, 0,
                                                              0, 0);
             };
-            auto copy_a = [&](int t) { copy_half(rsrc_a, a_buf + (2 * g + (t & 1)) * HALF, t); };
-            auto copy_b = [&](int t) { copy_half(rsrc_b, b_buf + (t % 3) * 2 * HALF + g * HALF, t); };
+            auto copy_a = [&](int t) { copy_half(rsrc_a, a_buf + (2 * g + (t & 1)) * HALF, t, p_off_a, a_rb); };
+            auto copy_b = [&](int t) { copy_half(rsrc_b, b_buf + (t % 3) * 2 * HALF + g * HALF, t, p_off_b, b_rb); };
             const int a_row = wm * WTM - 128 * g + lrow;    // row within the group's A half
             const int b_row = wn * WTN + lrow;
             bf16x8 af[KS][FM], bf[KS][FN];
@@ -698,7 +704,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        const bool vec_ok = (N & 3) == 0;
+        const bool vec_ok = ((N | ldc) & 3) == 0;           // 8-byte stores of four columns
         if constexpr (EPI) {
             // Fused epilogue (bias, activation) through LDS: each wave writes
             // its fp32 accumulators, CH block rows at a time, into its own LDS
@@ -743,7 +749,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                     for (int rr = 0; rr < 4; ++rr)
                         v[rr] = epi_activation(v[rr] + bv[rr], epi);
                     const uint2 h = pack_bf16x4(v);
-                    uint16_t* crow = C + (size_t)m * (size_t)N;
+                    uint16_t* crow = C + (size_t)m * (size_t)ldc;
                     if (vec_ok && n + 3 < N) {
                         *(uint2*)(crow + n) = h;
                     } else {
@@ -764,7 +770,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             const int m = m0 + wm * WTM + i * 16 + lrow;
             if (m >= m_lim)
                 continue;
-            uint16_t* crow = C + (size_t)m * (size_t)N;
+            uint16_t* crow = C + (size_t)m * (size_t)ldc;
     #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int n = n0 + wn * WTN + j * 16 + lgrp * 4;
@@ -795,8 +801,8 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         // PyTorch blog, grouped GEMM section).  Expert g owns rows
         // [offs[g-1], offs[g]) of A and C and the N x K weight g of B.  The
         // tiles of all experts form one list, expert after expert (empty
-        // experts have none), each expert's N-major: consecutive tiles share
-        // a B tile.  Workgroup b visits tiles b, b + P, ... (P = grid size),
+        // experts have none), each expert's column-first in windows of 8
+        // tile rows: consecutive tiles share a B tile.  Workgroup b visits tiles b, b + P, ... (P = grid size),
         // or, when chunk_c != 0 and the list holds at least P tiles, the
         // list is cut into 8 contiguous parts and workgroups of XCD x
         // (b mod 8 = x under round-robin dispatch) walk part x, so the tiles
@@ -871,25 +877,30 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             r1 = __builtin_amdgcn_readfirstlane(r1);
             const int tiles_mg = (r1 - r0 + BM - 1) / BM;
             const int u = (int)(t - t0);             // below tiles_mg * tiles_n
-            const int tn = u / tiles_mg;             // N-major inside an expert
-            const int tm = u - tn * tiles_mg;
+            // Inside an expert: column-first in windows of 8 tile rows (the
+            // dense kernel's window walk), i.e. N-major for experts of at most
+            // 8 tile rows, with A's reuse distance bounded for larger ones.
+            int tm, tn;
+            tile_order(u, tiles_mg, tiles_n, 8, 0, tm, tn);
             __syncthreads();                         // LDS of the previous tile is free
-            run_tile(tm, tn, r0 + tm * BM, r1, (const char*)Bv + (size_t)g * (size_t)N * row_bytes,
+            run_tile(tm, tn, r0 + tm * BM, r1, (const char*)Bv + (size_t)g * (size_t)N * b_rb,
                      EPI ? bias + (size_t)g * (size_t)N : bias);
         }
     }
 }
 
+// lda, ldb, ldc: leading dimensions (elements) of A, B, C.
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI, bool MX>
 hipError_t launch_tile_t(const void* A, const void* B, uint16_t* C, int M, int N, int K, int win_w, int chunk_c,
                          int split_k, float* ws, int* counters, const uint16_t* bias, int epi, const uint32_t* psa,
-                         const uint32_t* psb, hipStream_t stream)
+                         const uint32_t* psb, int lda, int ldb, int ldc, hipStream_t stream)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, MX, false>),
                        dim3(tiles_m * tiles_n, split_k), dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m,
-                       tiles_n, win_w, chunk_c, split_k, ws, counters, bias, epi, psa, psb, nullptr, 0);
+                       tiles_n, win_w, chunk_c, split_k, ws, counters, bias, epi, psa, psb, nullptr, 0, lda, ldb,
+                       ldc);
     return hipGetLastError();
 }
 
@@ -901,7 +912,7 @@ hipError_t launch_grouped_t(const void* A, const void* B, const int* offs, int G
     const int tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, false, true>), dim3(grid), dim3(WM * WN * 64),
                        0, stream, A, B, C, M, N, K, 0, tiles_n, 0, xcd_chunks, 1, nullptr, nullptr, bias, epi, nullptr,
-                       nullptr, offs, G);
+                       nullptr, offs, G, K, K, N);
     return hipGetLastError();
 }
 

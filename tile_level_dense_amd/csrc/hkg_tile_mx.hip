@@ -80,10 +80,10 @@ hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint1
         return epi == EPI_NONE                                                                                   \
                    ? launch_tile_t<bm, bn, bk, st, wm, wn, sc, false, true>(A, B, C, M, N, K, win_w, chunk_c,    \
                                                                             split_k, ws, counters, bias, epi,  \
-                                                                            psa, psb, stream)                  \
+                                                                            psa, psb, K, K, N, stream)         \
                    : launch_tile_t<bm, bn, bk, st, wm, wn, sc, true, true>(A, B, C, M, N, K, win_w, chunk_c,     \
                                                                            split_k, ws, counters, bias, epi,   \
-                                                                           psa, psb, stream);
+                                                                           psa, psb, K, K, N, stream);
     HKG_MX_TILE_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
