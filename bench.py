@@ -20,6 +20,11 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
   grouped      the grouped (mixture-of-experts) GEMM on the uniform and ragged
                MoE workloads (TFLOP/s of the experts' rows, 2 sum(M_g) N K per
                call), with torch._grouped_mm for context
+  layouts      square_8192 with the weight in column layout (x @ W, W stored
+               K x N: "NN") and with both operands in column layout ("TN"), through
+               hkg_gemm_bf16_ex (per-call transpose of the column operands),
+               and the transpose pass alone (GB/s); torch.mm on the same views
+               for context
   mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
                mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
                MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
@@ -319,6 +324,30 @@ def bench_grouped(torch, hkg, steps, warmup):
     return out
 
 
+def bench_layouts(torch, hkg, steps, warmup):
+    import workloads
+    A, B = workloads.workload_inputs("square_8192")
+    M, K = A.shape
+    N = B.shape[0]
+    a, b = to_dev(A, torch), to_dev(B, torch)
+    del A, B
+    at = a.t().contiguous()                 # A stored K x M (column layout)
+    bt = b.t().contiguous()                 # B stored K x N (column layout): x @ W
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * M * N * K
+    ms_nn = time_launches(torch, lambda: hkg.gemm_ex(a, bt.t(), out=c), steps, warmup)
+    ms_tn = time_launches(torch, lambda: hkg.gemm_ex(at.t(), bt.t(), out=c), steps, warmup)
+    y = torch.empty_like(b)
+    ms_pack = time_launches(torch, lambda: hkg.pack(bt.t()), steps, warmup)
+    ms_v = time_launches(torch, lambda: torch.mm(a, bt, out=c), steps, warmup)
+    log("layouts: NN %.3f ms (%.1f TFLOP/s), TN %.3f ms (%.1f), transpose of one operand %.3f ms (%.0f GB/s); "
+        "torch.mm NN %.3f ms" % (ms_nn, flops / ms_nn / 1e9, ms_tn, flops / ms_tn / 1e9, ms_pack,
+                                 4.0 * N * K / ms_pack / 1e6, ms_v))
+    del y
+    return dict(nn_tflops=flops / ms_nn / 1e9, tn_tflops=flops / ms_tn / 1e9, nn_ms=ms_nn, tn_ms=ms_tn,
+                transpose_ms=ms_pack, transpose_gbps=4.0 * N * K / ms_pack / 1e6, vendor_nn_tflops=flops / ms_v / 1e9)
+
+
 def calibration_copy(torch, mib=1024):
     """One device-to-device copy of a known size (mib MiB read, mib MiB
     written), the reference dispatch for scaling HBM byte counters."""
@@ -362,7 +391,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
-    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped"], help="time one leg only (profiler runs)")
+    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts"],
+                    help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -380,6 +410,10 @@ def main():
         dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
         print(json.dumps({"decode_gbps": round(dec["gbps"], 1), "us_per_call": round(dec["ms"] * 1e3, 3),
                           "llc_resident_gbps": round(dec["gbps_hot"], 1)}), flush=True)
+        return 0
+    if args.only == "layouts":
+        lay = bench_layouts(torch, hkg, args.steps, args.warmup)
+        print(json.dumps({k: round(v, 3) for k, v in lay.items()}), flush=True)
         return 0
     if args.only == "grouped":
         grp = bench_grouped(torch, hkg, args.steps, args.warmup)
@@ -399,6 +433,7 @@ def main():
     mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
     mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     grp = bench_grouped(torch, hkg, args.steps, args.warmup)
+    lay = bench_layouts(torch, hkg, args.steps, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
@@ -454,6 +489,11 @@ def main():
                                         "per_launch": "2 sum(M_g) N K = %.4g flop per launch" % r["flops"]},
                            "vendor_grouped_mm_tflops": round(r["vendor_tflops"], 2) if r["vendor_tflops"] else None}
                     for name, r in grp.items()},
+        "layouts": {"workload": "square_8192 with column-layout operands (per-call transpose)",
+                    "nn_tflops": round(lay["nn_tflops"], 2), "tn_tflops": round(lay["tn_tflops"], 2),
+                    "transpose_ms": round(lay["transpose_ms"], 4), "transpose_gbps": round(lay["transpose_gbps"], 1),
+                    "prepacked_nn": "equals the square_8192 value: a pre-packed weight runs the row-layout kernel",
+                    "vendor_nn_tflops": round(lay["vendor_nn_tflops"], 2)},
         "mxfp8": {
             "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",
                        "tflops": round(mxs["tflops"], 2), "ms": round(mxs["ms"], 4),

@@ -58,6 +58,14 @@ void zero_kernel(uint16_t* __restrict__ C, int64_t ldc, int64_t count, int64_t N
 // tile column spread over the banks); reads run along X's rows and writes
 // along Y's rows, so both sides are coalesced.  Tile columns beyond grid y
 // are walked in a loop.
+//
+// With VEC (X, Y 16-byte aligned, ldx and ldy multiples of 8) interior tiles
+// move 16 bytes per access: each thread reads two 8-element pieces of X rows
+// and writes two 8-element pieces of Y rows (the transposed gather happens in
+// LDS); edge tiles take the element path.
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+template <bool VEC>
 __global__ __launch_bounds__(256)
 void transpose_kernel(const uint16_t* __restrict__ X, int64_t ldx, uint16_t* __restrict__ Y, int64_t ldy, int64_t R,
                       int64_t CC)
@@ -66,6 +74,30 @@ void transpose_kernel(const uint16_t* __restrict__ X, int64_t ldx, uint16_t* __r
     const int t = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * 64;
     for (int64_t c0 = (int64_t)blockIdx.y * 64; c0 < CC; c0 += (int64_t)gridDim.y * 64) {
+        if (VEC && r0 + 64 <= R && c0 + 64 <= CC) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = t + 256 * h;                  // 512 pieces: X row c0 + q / 8, elements 8 (q % 8)
+                const int cl = q >> 3, rl = (q & 7) * 8;
+                const u16x8 v = *(const u16x8*)(X + (c0 + cl) * ldx + r0 + rl);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    tile[cl][rl + e] = v[e];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = t + 256 * h;                  // Y row r0 + q / 8, elements 8 (q % 8)
+                const int rl = q >> 3, cl = (q & 7) * 8;
+                u16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = tile[cl + e][rl];
+                *(u16x8*)(Y + (r0 + rl) * ldy + c0 + cl) = v;
+            }
+            __syncthreads();
+            continue;
+        }
         {
             const int cl = t >> 2, rl = (t & 3) * 16;       // X row c0 + cl, 16 elements from r0 + rl
             const int64_t c = c0 + cl;
@@ -131,7 +163,13 @@ hipError_t launch_transpose(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t
         gy = 65535;
     if (gx > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, X, ldx, Y, ldy, R, CC);
+    const bool vec = ((uintptr_t)X & 15u) == 0 && ((uintptr_t)Y & 15u) == 0 && ldx % 8 == 0 && ldy % 8 == 0;
+    if (vec)
+        hipLaunchKernelGGL(transpose_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, X, ldx, Y,
+                           ldy, R, CC);
+    else
+        hipLaunchKernelGGL(transpose_kernel<false>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, X, ldx,
+                           Y, ldy, R, CC);
     return hipGetLastError();
 }
 
