@@ -69,7 +69,8 @@ typedef enum {
     HKG_KERNEL_GENERIC = 3,     /* any alignment, any K: correctness fallback */
     HKG_KERNEL_ZERO = 4,        /* K == 0: C is the empty sum, +0 (then the epilogue) */
     HKG_KERNEL_MX_TILE = 5,     /* MXFP8 large-tile kernel (scaled MFMA) */
-    HKG_KERNEL_GROUPED = 6      /* grouped (mixture-of-experts) tile kernel, persistent grid */
+    HKG_KERNEL_GROUPED = 6,     /* grouped (mixture-of-experts) tile kernel, persistent grid */
+    HKG_KERNEL_MX_SKINNY = 7    /* MXFP8 small-M kernel: streams B once, split-K */
 } hkg_kernel_t;
 
 /*

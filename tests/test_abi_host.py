@@ -264,7 +264,7 @@ def test_build_resources_have_no_scratch():
     if not os.path.exists(path):
         hkg_build.build()
     res = json.load(open(path))
-    entries = res["tile"] + res["mx_tile"] + res["grouped"] + res["skinny"] + [res["generic"]]
+    entries = res["tile"] + res["mx_tile"] + res["grouped"] + res["skinny"] + res["mx_skinny"] + [res["generic"]]
     for e in entries:
         assert e["scratch"] == 0 and e["vgpr_spill"] <= 0, e
 
@@ -343,18 +343,20 @@ def test_tile_order_chiplet_blocks(lib):
 
 
 # ------------------------------------------------------------------ MXFP8
-@pytest.mark.parametrize("shape,variant,split", [
-    ((8192, 8192, 8192), 0, 1),          # 32 x 32 ping-pong tiles fill the device
-    ((4096, 4096, 12288), 0, 1),
-    ((32, 4096, 4096), 1, 8),            # decode: 32 tiles of 128, split to 256 workgroups
-    ((128, 12288, 4096), 1, 3),
-    ((256, 256, 256), 1, 1),             # 4 tiles; K / 128 / 4 = 0 splits -> 1
-    ((1000, 1000, 384), 1, 1),
+@pytest.mark.parametrize("shape,kernel,variant,split", [
+    ((8192, 8192, 8192), "MX_TILE", 0, 1),     # 32 x 32 ping-pong tiles fill the device
+    ((4096, 4096, 12288), "MX_TILE", 0, 1),
+    ((32, 4096, 4096), "MX_SKINNY", 1, 1),     # decode: 256 column blocks of 16 already fill it
+    ((16, 2048, 4096), "MX_SKINNY", 0, 2),     # 128 column blocks: split 2 (at least 2 steps per wave)
+    ((33, 4096, 4096), "MX_TILE", 1, 8),       # above 32 rows: 32 tiles of 128 x 128, split to fill
+    ((128, 12288, 4096), "MX_TILE", 1, 3),
+    ((256, 256, 256), "MX_TILE", 1, 1),        # 4 tiles; K / 128 / 4 = 0 splits -> 1
+    ((1000, 1000, 384), "MX_TILE", 1, 1),
 ])
-def test_mx_plan_selection(shape, variant, split):
+def test_mx_plan_selection(shape, kernel, variant, split):
     p = hkg.mx_plan(*shape)
     M, N, K = shape
-    assert p.kernel_id == hkg.HKG_KERNEL_MX_TILE and p.variant == variant and p.split_k == split, p
+    assert hkg.KERNEL_NAMES[p.kernel_id] == kernel and p.variant == variant and p.split_k == split, p
     assert p.tile_k == 128 and p.flops == 2.0 * M * N * K
     assert p.algorithmic_bytes == M * K + N * K + (M + N) * (K // 32) + 2 * M * N
     assert p.workspace_bytes == (split * M * N * 4 if split > 1 else 0)

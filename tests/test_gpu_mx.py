@@ -1,7 +1,7 @@
 """GPU parity of the MXFP8 (block-scaled FP8) GEMM against the oracle.
 
 Every MXFP8 kernel variant (the 256 x 256 ping-pong, the 128 x 128 ring,
-with and without split-K) runs through the C ABI on seeded inputs; each
+the small-M kernels, with and without split-K) runs through the C ABI on seeded inputs; each
 output is compared with the oracle's exact sum under the MXFP8 gate of
 tests/gates.py (compare_mx: the bf16 rounding, the scaled MFMA's measured
 group truncation and fp32 accumulation).  Inputs whose every product and
@@ -66,7 +66,22 @@ def check(C, A, SA, B, SB, bias=None, epi="none"):
 
 
 def forced(hkg, variant, split=1):
+    """Plan edit forcing one kernel variant: an int picks an MXFP8 tile
+    variant, "s<i>" the small-M (skinny) variant i."""
     from tile_level_dense_amd import build as hkg_build
+    if isinstance(variant, str):
+        mb, nb, wk, u, cp = hkg_build.skinny_configs(mx=True)[int(variant[1:])]
+
+        def edit(p):
+            assert p.M <= 16 * mb
+            p.kernel_id = hkg.HKG_KERNEL_MX_SKINNY
+            p.variant = int(variant[1:])
+            p.tile_m, p.tile_n, p.tile_k, p.waves = 16 * mb, 16 * nb, 128, wk
+            p.split_k = split
+            p.grid_x = -(-p.N // (16 * nb))
+            p.grid_y = split
+            p.workspace_bytes = split * p.M * p.N * 4 if split > 1 else 0
+        return edit
     bm, bn, bk, stages, wm, wn, _ = hkg_build.tile_configs(mx=True)[variant]
 
     def edit(p):
@@ -112,6 +127,17 @@ CASES = [
     ("ring_split3", (200, 333, 1536), 1, 3),
     ("ring_split2_decode", (32, 512, 1024), 1, 2),
     ("single_element", (1, 1, 128), 1, 1),
+    # small-M kernel: 16-row and 32-row covers, ragged N, split-K with
+    # splits that get unequal (or no) steps of 128 k
+    ("skinny16_single", (1, 1, 128), "s0", 1),
+    ("skinny16_ragged", (13, 300, 1024), "s0", 1),
+    ("skinny16_split4", (7, 2000, 4096), "s0", 4),
+    ("skinny16_split3_short", (16, 48, 384), "s0", 3),
+    ("skinny16_split5_uneven", (16, 100, 896), "s0", 5),
+    ("skinny32_ragged", (17, 260, 256), "s1", 1),
+    ("skinny32_split2", (32, 512, 1024), "s1", 2),
+    ("skinny32_one_row", (1, 70, 512), "s1", 3),
+    ("planner_decode_small", (16, 2048, 4096), None, 1),
 ]
 
 
@@ -141,7 +167,8 @@ def _exact_inputs(M, N, K, seed):
 
 
 @pytest.mark.parametrize("variant,split,shape", [(0, 1, (256, 512, 512)), (1, 1, (200, 136, 512)),
-                                                 (1, 4, (64, 256, 1024))])
+                                                 (1, 4, (64, 256, 1024)), ("s0", 1, (16, 256, 512)),
+                                                 ("s1", 4, (32, 272, 1024))])
 def test_mx_exact_inputs_bit_exact(hkg, variant, split, shape):
     M, N, K = shape
     _say("exact", variant, split, shape)
@@ -153,7 +180,8 @@ def test_mx_exact_inputs_bit_exact(hkg, variant, split, shape):
 
 
 @pytest.mark.parametrize("epi", ["bias", "bias_relu", "bias_silu", "bias_gelu"])
-@pytest.mark.parametrize("variant,split,shape", [(0, 1, (300, 260, 256)), (1, 2, (100, 200, 1024))])
+@pytest.mark.parametrize("variant,split,shape", [(0, 1, (300, 260, 256)), (1, 2, (100, 200, 1024)),
+                                                 ("s0", 1, (9, 130, 256)), ("s1", 2, (20, 200, 1024))])
 def test_mx_epilogue_parity(hkg, epi, variant, split, shape):
     M, N, K = shape
     _say("epilogue", epi, variant, split, shape)
@@ -212,6 +240,7 @@ def test_mx_workload_decode_whole_output(hkg):
     # mx_decode_32x4096x4096: a decode projection, every output checked.
     _say("workload mx_decode_32x4096x4096")
     A, SA, B, SB = workloads.mx_workload_inputs("mx_decode_32x4096x4096")
+    assert hkg.mx_plan(*A.shape, B.shape[0]).kernel_id == hkg.HKG_KERNEL_MX_SKINNY
     C = run(hkg, A, SA, B, SB)
     check(C, A, SA, B, SB)
 

@@ -44,9 +44,10 @@ HKG_ERR_NO_DEVICE = -4
 HKG_ERR_ARCH = -5
 HKG_ERR_HIP = -6
 HKG_ERR_WORKSPACE = -7
-KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE", 6: "GROUPED"}
+KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE", 6: "GROUPED",
+                7: "MX_SKINNY"}
 (HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE,
- HKG_KERNEL_GROUPED) = range(7)
+ HKG_KERNEL_GROUPED, HKG_KERNEL_MX_SKINNY) = range(8)
 
 LAYOUT_ROW, LAYOUT_COL = 0, 1          # hkg_layout_t
 

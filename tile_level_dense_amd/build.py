@@ -46,15 +46,18 @@ def tile_configs(mx=False, grouped=False):
 TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
 GROUPED_VARIANTS = tile_configs(grouped=True)
-def skinny_configs():
-    """(MB, NB, WK, U, CP) per skinny variant, from hkg_skinny_configs.h."""
+def skinny_configs(mx=False):
+    """(MB, NB, WK, U, CP) per skinny variant (MXFP8 with mx=True), from hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
-    body = text[text.index("#define HKG_SKINNY_CONFIGS(X)"):]
+    body = text[text.index("#define HKG_MX_SKINNY_CONFIGS(X)" if mx else "#define HKG_SKINNY_CONFIGS(X)"):]
+    end = body.find("#define", 10)
+    body = body if end < 0 else body[:end]
     return [tuple(int(v) for v in m) for m in re.findall(
         r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", body)]
 
 
 SKINNY_VARIANTS = skinny_configs()
+MX_SKINNY_VARIANTS = skinny_configs(mx=True)
 
 
 class BuildError(RuntimeError):
@@ -110,6 +113,7 @@ def _table(resources):
     mx_tile = [None] * len(MX_TILE_VARIANTS)
     grouped = [None] * len(GROUPED_VARIANTS)
     skinny = [None] * len(SKINNY_VARIANTS)
+    mx_skinny = [None] * len(MX_SKINNY_VARIANTS)
     generic = None
     for mangled, r in resources.items():
         # The table holds the plain instantiations (no fused epilogue); the
@@ -126,11 +130,14 @@ def _table(resources):
             elif plain and mx and key in MX_TILE_VARIANTS:
                 mx_tile[MX_TILE_VARIANTS.index(key)] = _entry("mxtile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
-        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])E", mangled)
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E", mangled)
         if m:
             key = tuple(int(g) for g in m.groups()[:5])
-            if key in SKINNY_VARIANTS and m.group(6) == "0":
-                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_n%d_w%d_u%d_c%d" % ((16 * key[0], 16 * key[1]) + key[2:]), r)
+            label = (16 * key[0], 16 * key[1]) + key[2:]
+            if m.group(6) == "0" and m.group(7) == "0" and key in SKINNY_VARIANTS:
+                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_n%d_w%d_u%d_c%d" % label, r)
+            elif m.group(6) == "0" and m.group(7) == "1" and key in MX_SKINNY_VARIANTS:
+                mx_skinny[MX_SKINNY_VARIANTS.index(key)] = _entry("mxskinny_m%d_n%d_w%d_u%d_c%d" % label, r)
             continue
         if "generic_kernel" in mangled:
             generic = _entry("generic", r)
@@ -139,10 +146,11 @@ def _table(resources):
     missing = [i for i, e in enumerate(tile) if e is None] + \
               [100 + i for i, e in enumerate(skinny) if e is None] + \
               [200 + i for i, e in enumerate(mx_tile) if e is None] + \
-              [300 + i for i, e in enumerate(grouped) if e is None] + ([-1] if generic is None else [])
+              [300 + i for i, e in enumerate(grouped) if e is None] + \
+              [400 + i for i, e in enumerate(mx_skinny) if e is None] + ([-1] if generic is None else [])
     if missing:
         raise BuildError("resource report missing kernels: %s" % missing)
-    return tile, mx_tile, grouped, skinny, generic
+    return tile, mx_tile, grouped, skinny, mx_skinny, generic
 
 
 def _gate(entries):
@@ -155,7 +163,7 @@ def _gate(entries):
         raise BuildError("kernels use scratch / spill registers (refused): %s" % bad)
 
 
-def _write_inc(tile, mx_tile, grouped, skinny, generic):
+def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, generic):
     def row(e):
         return '{"%s", %d, %d, %d, %d, %d}' % (e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"])
     text = "// generated by tile_level_dense_amd/build.py -- do not edit\n"
@@ -163,12 +171,14 @@ def _write_inc(tile, mx_tile, grouped, skinny, generic):
     text += "const KernelResources kMxTileResources[] = {\n    " + ",\n    ".join(row(e) for e in mx_tile) + "};\n"
     text += "const KernelResources kGroupedResources[] = {\n    " + ",\n    ".join(row(e) for e in grouped) + "};\n"
     text += "const KernelResources kSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in skinny) + "};\n"
+    text += "const KernelResources kMxSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in mx_skinny) + "};\n"
     text += "const KernelResources kGenericResources = " + row(generic) + ";\n"
     path = os.path.join(BUILD, "hkg_resources.inc")
     with open(path, "w") as f:
         f.write(text)
     with open(os.path.join(BUILD, "kernel_resources.json"), "w") as f:
-        json.dump(dict(tile=tile, mx_tile=mx_tile, grouped=grouped, skinny=skinny, generic=generic), f, indent=1)
+        json.dump(dict(tile=tile, mx_tile=mx_tile, grouped=grouped, skinny=skinny, mx_skinny=mx_skinny,
+                       generic=generic), f, indent=1)
 
 
 def build(verbose=False):
@@ -181,16 +191,16 @@ def build(verbose=False):
     res = {}
     for _, r in results:
         res.update(r)
-    tile, mx_tile, grouped, skinny, generic = _table(res)
+    tile, mx_tile, grouped, skinny, mx_skinny, generic = _table(res)
     _gate([_entry(name, r) for name, r in res.items()])
-    _write_inc(tile, mx_tile, grouped, skinny, generic)
+    _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, generic)
     with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
         objs += [f.result()[0] for f in [ex.submit(_compile, s, False) for s in HOST_SOURCES]]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if verbose:
-        for e in tile + mx_tile + grouped + skinny + [generic]:
+        for e in tile + mx_tile + grouped + skinny + mx_skinny + [generic]:
             print("%-18s vgpr %3d agpr %3d sgpr %3d scratch %d lds %6d occ %d" % (
                 e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"], e["occupancy"]))
     return LIB

@@ -619,6 +619,32 @@ void fill_mx_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t 
                   (long long)tn, s.bm, s.bn, (long long)split);
 }
 
+void fill_mx_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
+{
+    const SkinnyShape s = mx_skinny_shape(variant);
+    const int64_t col_blocks = cdiv(N, 16 * s.nblocks);
+    p->kernel_id = HKG_KERNEL_MX_SKINNY;
+    p->variant = variant;
+    p->tile_m = 16 * s.mblocks;
+    p->tile_n = 16 * s.nblocks;
+    p->tile_k = 128;
+    p->waves = s.waves;
+    p->split_k = (int32_t)split;
+    p->grid_x = (int32_t)col_blocks;
+    p->grid_y = (int32_t)split;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->xcd_window_w = 0;
+    p->xcd_chunk_c = 0;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    p->lds_bytes = s.waves * s.mblocks * s.nblocks * 64 * 16 + 4;
+    fill_resources(p, mx_skinny_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "mxskinny_m%d_n%d_w%d_u%d_c%d", 16 * s.mblocks,
+                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy);
+    std::snprintf(p->reason, sizeof p->reason, "MXFP8, M <= %d: %lld column blocks of %d, split-K %lld",
+                  16 * s.mblocks, (long long)col_blocks, 16 * s.nblocks, (long long)split);
+}
+
 hkg_status_t make_mx_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
     std::memset(p, 0, sizeof *p);
@@ -652,6 +678,22 @@ hkg_status_t make_mx_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     }
     if (!mx_shape_supported(M, N, K))
         return HKG_ERR_UNSUPPORTED;
+    // Decode shapes: the skinny kernel streams B once (smallest A cover that
+    // holds M), split across workgroups only when the column blocks leave
+    // compute units idle, keeping at least 2 steps of 128 k per wave.
+    for (int v = 0; v < MX_SKINNY_NUM_VARIANTS; ++v) {
+        const SkinnyShape ss = mx_skinny_shape(v);
+        if (M > 16 * (int64_t)ss.mblocks)
+            continue;
+        const int64_t col_blocks = cdiv(N, 16 * ss.nblocks);
+        int64_t split = 1;
+        if (col_blocks < kNumCUs) {
+            split = std::min<int64_t>(cdiv(kNumCUs, col_blocks), (K / 128) / (2 * ss.waves));
+            split = std::max<int64_t>(1, std::min<int64_t>(split, 64));
+        }
+        fill_mx_skinny(p, v, split, M, N);
+        return HKG_OK;
+    }
     // 256 x 256 ping-pong when its tiles fill the device; otherwise the
     // 128 x 128 tile, with split-K (at least 4 stages of 128 k per split)
     // while the grid is under one workgroup per compute unit.
@@ -677,6 +719,14 @@ bool mx_plan_matches_library(const hkg_plan_t* p)
         return p->M == 0 || p->N == 0;
     case HKG_KERNEL_ZERO:
         return p->K == 0 && p->M > 0 && p->N > 0;
+    case HKG_KERNEL_MX_SKINNY: {
+        if (p->variant < 0 || p->variant >= MX_SKINNY_NUM_VARIANTS)
+            return false;
+        const SkinnyShape s = mx_skinny_shape(p->variant);
+        return p->M <= 16 * s.mblocks && p->tile_n == 16 * s.nblocks && p->split_k >= 1 && p->split_k <= 64 &&
+               (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->K > 0 && p->K % 128 == 0 &&
+               mx_shape_supported(p->M, p->N, p->K);
+    }
     case HKG_KERNEL_MX_TILE: {
         if (p->variant < 0 || p->variant >= MX_TILE_NUM_VARIANTS)
             return false;
@@ -729,8 +779,13 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
             if (st != HKG_OK)
                 return st;
         }
-        e = launch_tile_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N, (int)K,
-                           p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA, PB, stream);
+        if (p->kernel_id == HKG_KERNEL_MX_SKINNY)
+            e = launch_skinny_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
+                                 (int)K, p->split_k, ws, counters, bias, epi, PA, PB, stream);
+        else
+            e = launch_tile_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
+                               (int)K, p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA, PB,
+                               stream);
     }
     if (e != hipSuccess) {
         set_hip_error(e, "kernel launch");
@@ -739,7 +794,9 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
     return HKG_OK;
 }
 
-// The MXFP8 tile kernel reads A, B with 16-byte accesses, stores C in 8-byte
+bool mx_kernel(int id) { return id == HKG_KERNEL_MX_TILE || id == HKG_KERNEL_MX_SKINNY; }
+
+// The MXFP8 kernels read A, B with 16-byte accesses, store C in 8-byte
 // groups and reads packed scales as dwords.
 bool mx_aligned(const void* A, const void* PA, const void* B, const void* PB, const void* C)
 {
@@ -760,7 +817,7 @@ hkg_status_t gemm_mx_prepacked(const void* A, const void* PA, const void* B, con
     st = check_epilogue(bias, C, M, N, epi);
     if (st != HKG_OK)
         return st;
-    if (p.kernel_id == HKG_KERNEL_MX_TILE && !mx_aligned(A, PA, B, PB, C))
+    if (mx_kernel(p.kernel_id) && !mx_aligned(A, PA, B, PB, C))
         return HKG_ERR_MISALIGNED;
     return run_mx(&p, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epi,
                   (hipStream_t)stream);
@@ -779,7 +836,7 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
     st = check_epilogue(bias, C, M, N, epi);
     if (st != HKG_OK)
         return st;
-    if (p.kernel_id != HKG_KERNEL_MX_TILE)
+    if (!mx_kernel(p.kernel_id))
         return run_mx(&p, A, nullptr, B, nullptr, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
     if (!(aligned16(A) && aligned16(B) && aligned16(C)))
         return HKG_ERR_MISALIGNED;
@@ -1145,7 +1202,7 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
         return st;
     if (!mx_plan_matches_library(plan))
         return HKG_ERR_UNSUPPORTED;
-    if (plan->kernel_id == HKG_KERNEL_MX_TILE && !mx_aligned(A, PA, B, PB, C))
+    if (mx_kernel(plan->kernel_id) && !mx_aligned(A, PA, B, PB, C))
         return HKG_ERR_MISALIGNED;
     return run_mx(plan, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epilogue,
                   (hipStream_t)stream);

@@ -38,6 +38,13 @@ constexpr int GROUPED_NUM_VARIANTS = 0
 // Default tile ladder of the planner, largest first (variant indices).
 constexpr int TILE_LADDER[] = {0, 1, 2};
 
+// MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
+constexpr int MX_SKINNY_NUM_VARIANTS = 0
+#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp) +1
+    HKG_MX_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
+#undef HKG_COUNT_SKINNY
+    ;
+
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
 // rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.
 constexpr int SKINNY_NUM_VARIANTS = 0
@@ -61,6 +68,7 @@ int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
 
 struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy; };
 SkinnyShape skinny_shape(int variant);
+SkinnyShape mx_skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 
 // Launchers: enqueue one kernel on `stream`; return the launch error.
@@ -86,6 +94,12 @@ hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint1
 hipError_t launch_grouped(int variant, const uint16_t* A, const uint16_t* B, const int* offs, int G, uint16_t* C,
                           int M, int N, int K, int grid, int xcd_chunks, const uint16_t* bias, int epi,
                           hipStream_t stream);
+
+// MXFP8 skinny kernel (M <= 16 MB): packed scales as launch_tile_mx;
+// split-K as launch_skinny.
+hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                            int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
+                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
 
 // Packs rows x (K / 32) E8M0 codes S into the tile kernel's layout P
 // (mx_packed_scale_bytes(rows, K) bytes, 4-byte aligned).
@@ -118,6 +132,7 @@ const KernelResources* tile_resources(int variant);
 const KernelResources* mx_tile_resources(int variant);
 const KernelResources* grouped_resources(int variant);
 const KernelResources* skinny_resources(int variant);
+const KernelResources* mx_skinny_resources(int variant);
 const KernelResources* generic_resources();
 
 }  // namespace hkg

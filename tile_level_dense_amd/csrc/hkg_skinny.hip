@@ -20,11 +20,19 @@
 //    order (split-K on fp32 partials: same guide, section 3c).  The fused
 //    epilogue (bias, activation) acts on the fp32 total, which is then
 //    rounded to bf16 once.
+//  * MXFP8 mode (E4M3 operands, E8M0 scale per 32 k; FlyDSL-in-PyTorch blog,
+//    MXFP section): steps of 128 k, each lane loading the two 16-byte halves
+//    of its scaled-MFMA operand (k 16 g .. and 64 + 16 g .., g = lane / 16)
+//    from each B row, and its scale dwords from the packed layout of the
+//    tile kernel (byte f of dword lane = block f of a 64-row group).
+#include <type_traits>
+
 #include "hkg_internal.h"
 
 namespace hkg {
 namespace {
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -63,16 +71,32 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 b, i32x4 a, f32x4 c)
                                                    c, 0, 0, 0);
 }
 
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // MB: 16-row blocks of A (M <= 16 MB).  NB: 16-row blocks of B per
-// workgroup.  WK: waves per workgroup, splitting K.  U: 32-k steps per chunk
-// of loads.  CP: cache-policy bits of the B loads (B is streamed once).
-template <int MB, int NB, int WK, int U, int CP, bool EPI>
+// workgroup.  WK: waves per workgroup, splitting K.  U: steps per chunk of
+// loads (32 k, MXFP8 128 k).  CP: cache-policy bits of the B loads (B is
+// streamed once).  MX: E4M3 operands with packed E8M0 scales PSA / PSB.
+template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX>
 __global__ __launch_bounds__(WK * 64, 1)
-void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
                    float* __restrict__ ws, int* __restrict__ counters,
-                   const uint16_t* __restrict__ bias, int epi, int lda, int ldb, int ldc)
+                   const uint16_t* __restrict__ bias, int epi, int lda, int ldb, int ldc,
+                   const uint32_t* __restrict__ PSA, const uint32_t* __restrict__ PSB)
 {
+    constexpr int EB = MX ? 1 : 2;           // bytes per element
+    constexpr int SK = MX ? 128 : 32;        // k per step
+    constexpr int SBY = SK * EB;             // bytes of one row per step
+    typedef std::conditional_t<MX, i32x8, i32x4> frag_t;
+    static_assert(!MX || MB <= 4, "MXFP8 skinny: one 64-row scale group of A");
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
     __shared__ int last_flag;
@@ -88,7 +112,7 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     // the 8 XCDs round-robin, so the ones sharing an XCD (and its L2) read
     // different parts of A at the same time.  Partial sums are combined in
     // slice order, so the result does not depend on the rotation.
-    const int steps = (K + 31) >> 5;
+    const int steps = (K + SK - 1) / SK;
     const int per_wg = (steps + split_k - 1) / split_k;
     const int wg_begin = min(steps, (int)blockIdx.y * per_wg);
     const int wg_end = min(steps, wg_begin + per_wg);
@@ -97,13 +121,20 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     const int s_begin = min(wg_end, wg_begin + slice * per_wave);
     const int s_end = min(wg_end, s_begin + per_wave);
 
-    const uint32_t a_rb = (uint32_t)lda * 2u;   // row strides in bytes (leading dimensions)
-    const uint32_t b_rb = (uint32_t)ldb * 2u;
+    const uint32_t a_rb = (uint32_t)lda * (uint32_t)EB;   // row strides in bytes (leading dimensions)
+    const uint32_t b_rb = (uint32_t)ldb * (uint32_t)EB;
     const int rows_b = min(16 * NB, N - n0);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + (size_t)n0 * (size_t)ldb), 0, (int)(rows_b * b_rb), kBufferWord3);
+        (void*)((const char*)Bv + (size_t)n0 * b_rb), 0, (int)(rows_b * b_rb), kBufferWord3);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)A, 0, (int)((uint32_t)M * a_rb), kBufferWord3);
+        (void*)Av, 0, (int)((uint32_t)M * a_rb), kBufferWord3);
+    // MXFP8 scales: A's 16-row block i is byte i of the lane's dword of
+    // group 0; B's block j is byte ((n0 + 16 j) / 16) % 4 of its group's dword.
+    const int KT = K / 128;
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)PSA, 0, MX ? ((M + 63) / 64) * KT * 256 : 0, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)PSB, 0, MX ? ((N + 63) / 64) * KT * 256 : 0, kBufferWord3);
 
     const uint32_t lane_off_a = (uint32_t)lrow * a_rb + (uint32_t)lgrp * 16u;
     const uint32_t lane_off_b = (uint32_t)lrow * b_rb + (uint32_t)lgrp * 16u;
@@ -119,28 +150,64 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 
     // Steps past s_end (or k past K) load from an out-of-range offset and
     // read zero, which the MFMA adds exactly; so chunks need no tail code.
-    auto load_chunk = [&](int s, i32x4 (&bv)[U][NB], i32x4 (&av)[U][MB]) {
+    // MXFP8 operands are the bytes at k 16 g .. and 64 + 16 g .. of the step.
+    auto load_frag = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok, auto cp) -> frag_t {
+        constexpr int P = decltype(cp)::value;
+        if constexpr (MX) {
+            const i32x4 lo = load16<P>(r, ok ? off : kOutOfRange);
+            const i32x4 hi = load16<P>(r, ok ? off + 64u : kOutOfRange);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return load16<P>(r, ok ? off : kOutOfRange);
+        }
+    };
+    constexpr int SWA = MX ? 1 : 0, SWB = MX ? NB : 0;
+    auto load_chunk = [&](int s, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
+                          uint32_t (&sb)[U][SWB + 1]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
-            const bool ok = step < s_end && step * 32 + lgrp * 8 < K;
-            const uint32_t kb = (uint32_t)step * 64u;
+            const bool ok = step < s_end && step * SK + lgrp * (16 / EB) < K;
+            const uint32_t kb = (uint32_t)step * (uint32_t)SBY;
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                bv[u][j] = load16<CP>(rb, ok ? lane_off_b + kb + (uint32_t)j * block16_b : kOutOfRange);
+                bv[u][j] = load_frag(rb, lane_off_b + kb + (uint32_t)j * block16_b, ok,
+                                     std::integral_constant<int, CP>{});
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                av[u][i] = load16<0>(ra, ok ? lane_off_a + kb + (uint32_t)i * block16_a : kOutOfRange);
+                av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok,
+                                     std::integral_constant<int, 0>{});
+            if constexpr (MX) {
+                const uint32_t st = (uint32_t)step * 256u + (uint32_t)lane * 4u;
+                sa[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, ok ? st : kOutOfRange, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int row = n0 + 16 * j;
+                    sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rsb, ok ? (uint32_t)((row / 64) * KT) * 256u + st : kOutOfRange, 0, 0);
+                }
+            }
         }
     };
-    auto mfma_chunk = [&](const i32x4 (&bv)[U][NB], const i32x4 (&av)[U][MB]) {
+    auto mfma_chunk = [&](const frag_t (&bv)[U][NB], const frag_t (&av)[U][MB], const uint32_t (&sa)[U][SWA + 1],
+                          const uint32_t (&sb)[U][SWB + 1]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
+            for (int j = 0; j < NB; ++j) {
+                if constexpr (MX) {
+                    const int bsc = (int)(sb[u][j] >> (8 * (((n0 + 16 * j) >> 4) & 3)));
+                    static_for<0, MB>([&](auto I) {
+                        constexpr int i = decltype(I)::value;
+                        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bv[u][j], av[u][i], acc[j][i], 0, 0, 0, bsc, i, (int)sa[u][0]);
+                    });
+                } else {
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    acc[j][i] = mfma16(bv[u][j], av[u][i], acc[j][i]);
+                    for (int i = 0; i < MB; ++i)
+                        acc[j][i] = mfma16(bv[u][j], av[u][i], acc[j][i]);
+                }
+            }
     };
 
     // Chunks c and c + 1 are in flight while chunk c is multiplied.  Empty
@@ -148,26 +215,27 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     // below the current chunk's MFMAs (which would put one full memory round
     // trip per chunk on the critical path).
     auto fence = [] { asm volatile("" ::: "memory"); };
-    i32x4 b0[U][NB], a0[U][MB], b1[U][NB], a1[U][MB];
+    frag_t b0[U][NB], a0[U][MB], b1[U][NB], a1[U][MB];
+    uint32_t sa0[U][SWA + 1], sb0[U][SWB + 1], sa1[U][SWA + 1], sb1[U][SWB + 1];
     const int nch = (s_end - s_begin + U - 1) / U;
     if (nch > 0) {
-        load_chunk(s_begin, b0, a0);
+        load_chunk(s_begin, b0, a0, sa0, sb0);
         fence();
         if (nch > 1)
-            load_chunk(s_begin + U, b1, a1);
+            load_chunk(s_begin + U, b1, a1, sa1, sb1);
         fence();
         for (int c = 0; c < nch; c += 2) {
-            mfma_chunk(b0, a0);
+            mfma_chunk(b0, a0, sa0, sb0);
             fence();
             if (c + 2 < nch)
-                load_chunk(s_begin + (c + 2) * U, b0, a0);
+                load_chunk(s_begin + (c + 2) * U, b0, a0, sa0, sb0);
             fence();
             if (c + 1 >= nch)      // odd chunk count: buffer 1 holds an old chunk
                 break;
-            mfma_chunk(b1, a1);
+            mfma_chunk(b1, a1, sa1, sb1);
             fence();
             if (c + 3 < nch)
-                load_chunk(s_begin + (c + 3) * U, b1, a1);
+                load_chunk(s_begin + (c + 3) * U, b1, a1, sa1, sb1);
             fence();
         }
     }
@@ -251,14 +319,14 @@ void skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int U, int CP, bool EPI>
-hipError_t launch_skinny_t(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                           int split_k, float* ws, int* counters, const uint16_t* bias, int epi, int lda, int ldb,
-                           int ldc, hipStream_t stream)
+template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX>
+hipError_t launch_skinny_t(const void* A, const void* B, uint16_t* C, int M, int N, int K, int split_k, float* ws,
+                           int* counters, const uint16_t* bias, int epi, int lda, int ldb, int ldc,
+                           const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI>), dim3(col_blocks, split_k), dim3(WK * 64), 0, stream,
-                       A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc);
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI, MX>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
+                       stream, A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc, psa, psb);
     return hipGetLastError();
 }
 
@@ -289,11 +357,41 @@ hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint
 #define HKG_LAUNCH(mb, nb, wk, u, cp) \
     if (v++ == variant)               \
         return epi == EPI_NONE                                                                                \
-                   ? launch_skinny_t<mb, nb, wk, u, cp, false>(A, B, C, M, N, K, split_k, ws, counters, bias, epi, \
-                                                               lda, ldb, ldc, stream)                             \
-                   : launch_skinny_t<mb, nb, wk, u, cp, true>(A, B, C, M, N, K, split_k, ws, counters, bias, epi,  \
-                                                              lda, ldb, ldc, stream);
+                   ? launch_skinny_t<mb, nb, wk, u, cp, false, false>(A, B, C, M, N, K, split_k, ws, counters,    \
+                                                                      bias, epi, lda, ldb, ldc, nullptr, nullptr, \
+                                                                      stream)                                     \
+                   : launch_skinny_t<mb, nb, wk, u, cp, true, false>(A, B, C, M, N, K, split_k, ws, counters,     \
+                                                                     bias, epi, lda, ldb, ldc, nullptr, nullptr,  \
+                                                                     stream);
     HKG_SKINNY_CONFIGS(HKG_LAUNCH)
+#undef HKG_LAUNCH
+    return hipErrorInvalidValue;
+}
+
+SkinnyShape mx_skinny_shape(int variant)
+{
+    int v = 0;
+#define HKG_SHAPE(mb, nb, wk, u, cp) \
+    if (v++ == variant)              \
+        return SkinnyShape{mb, nb, wk, u, cp};
+    HKG_MX_SKINNY_CONFIGS(HKG_SHAPE)
+#undef HKG_SHAPE
+    return SkinnyShape{0, 0, 0, 0, 0};
+}
+
+hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                            int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
+                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
+{
+    int v = 0;
+#define HKG_LAUNCH(mb, nb, wk, u, cp)                                                                             \
+    if (v++ == variant)                                                                                          \
+        return epi == EPI_NONE                                                                                   \
+                   ? launch_skinny_t<mb, nb, wk, u, cp, false, true>(A, B, C, M, N, K, split_k, ws, counters,    \
+                                                                     bias, epi, K, K, N, psa, psb, stream)       \
+                   : launch_skinny_t<mb, nb, wk, u, cp, true, true>(A, B, C, M, N, K, split_k, ws, counters,     \
+                                                                    bias, epi, K, K, N, psa, psb, stream);
+    HKG_MX_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
 }

@@ -19,3 +19,8 @@
     X(2, 4, 8, 2, 0)          \
     X(4, 2, 8, 2, 0)          \
     X(8, 2, 8, 1, 0)
+
+// MXFP8 instantiations, same fields; U counts steps of 128 k.
+#define HKG_MX_SKINNY_CONFIGS(X) \
+    X(1, 1, 8, 4, 0)             \
+    X(2, 1, 8, 2, 0)
