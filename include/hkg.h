@@ -192,11 +192,13 @@ hkg_status_t hkg_gemm_bf16_run_plan_epilogue(const hkg_plan_t* plan, const void*
  * running sum in fp32.  So |C - exact| <= 2^-8 |C| + (truncation of each
  * group: below 7 * 2^-13 of its largest product) + fp32 accumulation.
  *
- * Scale packing.  The kernel consumes scales in a packed layout: for each
- * 64-row group of an operand and each 128-k stage, 256 bytes (see
+ * Scale packing.  The tile kernel consumes scales in a packed layout: for
+ * each 64-row group of an operand and each 128-k stage, 256 bytes (see
  * hkg_mx_pack_scales).  hkg_gemm_mxfp8 packs SA and SB itself into a
- * library-owned device buffer on every call; callers with fixed weights
- * pack once with hkg_mx_pack_scales and call hkg_gemm_mxfp8_prepacked.
+ * library-owned device buffer on every call, except on the small-M kernel
+ * (HKG_KERNEL_MX_SKINNY) with 4-byte aligned SA and SB, which reads the
+ * natural scales directly; callers with fixed weights pack once with
+ * hkg_mx_pack_scales and call hkg_gemm_mxfp8_prepacked.
  *
  * Pointers: A, B, C 16-byte aligned, packed scales 4-byte aligned (else
  * HKG_ERR_MISALIGNED), all device memory owned by the caller; C overlaps

@@ -236,6 +236,30 @@ def test_mx_prepacked_equals_natural_and_is_deterministic(hkg):
     assert torch.equal(c1.view(torch.int16), c3.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [(13, 300, 1024), (32, 260, 256), (1, 70, 512), (7, 2000, 4096), (16, 48, 384)])
+def test_mx_small_m_natural_scales(hkg, shape):
+    # The small-M kernel reads natural-layout scales itself: the result must
+    # match the packed path bit for bit and the oracle under the gate; scale
+    # arrays at an odd address take the packing path and agree as well.
+    M, N, K = shape
+    _say("natural scales", shape)
+    p = hkg.mx_plan(M, N, K)
+    assert p.kernel_id == hkg.HKG_KERNEL_MX_SKINNY
+    A, SA, B, SB = workloads.make_mx_inputs(M, N, K, b=("normal", 0.0, 0.02), seed=M + N)
+    a, b, sa, sb = dev8(A), dev8(B), dev8(SA), dev8(SB)
+    c_nat = hkg.gemm_mxfp8(a, sa, b, sb)
+    c_pk = hkg.gemm_mxfp8(a, hkg.mx_pack_scales(sa, K), b, hkg.mx_pack_scales(sb, K), packed=True)
+    odd_a = torch.empty(SA.size + 1, dtype=torch.uint8, device="cuda")[1:].view(SA.shape)
+    odd_b = torch.empty(SB.size + 1, dtype=torch.uint8, device="cuda")[1:].view(SB.shape)
+    odd_a.copy_(sa)
+    odd_b.copy_(sb)
+    c_odd = hkg.gemm_mxfp8(a, odd_a, b, odd_b)
+    torch.cuda.synchronize()
+    assert torch.equal(c_nat.view(torch.int16), c_pk.view(torch.int16))
+    assert torch.equal(c_nat.view(torch.int16), c_odd.view(torch.int16))
+    check(host(c_nat), A, SA, B, SB)
+
+
 def test_mx_workload_decode_whole_output(hkg):
     # mx_decode_32x4096x4096: a decode projection, every output checked.
     _say("workload mx_decode_32x4096x4096")

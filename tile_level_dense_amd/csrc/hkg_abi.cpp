@@ -757,8 +757,10 @@ hkg_status_t check_mx_pointers(const void* A, const void* SA, int64_t sa_bytes, 
     return HKG_OK;
 }
 
+// PA, PB: packed scales, or (natural, small-M kernel only) the natural
+// scale arrays.
 hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, const void* B, const uint32_t* PB,
-                    void* C, const uint16_t* bias, int epi, hipStream_t stream)
+                    void* C, const uint16_t* bias, int epi, hipStream_t stream, bool natural = false)
 {
     const int64_t M = p->M, N = p->N, K = p->K;
     if (p->kernel_id == HKG_KERNEL_NONE)
@@ -781,7 +783,7 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
         }
         if (p->kernel_id == HKG_KERNEL_MX_SKINNY)
             e = launch_skinny_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
-                                 (int)K, p->split_k, ws, counters, bias, epi, PA, PB, stream);
+                                 (int)K, p->split_k, ws, counters, bias, epi, PA, PB, natural, stream);
         else
             e = launch_tile_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
                                (int)K, p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA, PB,
@@ -840,6 +842,10 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
         return run_mx(&p, A, nullptr, B, nullptr, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
     if (!(aligned16(A) && aligned16(B) && aligned16(C)))
         return HKG_ERR_MISALIGNED;
+    // The small-M kernel reads natural scales itself (dword loads): no packing.
+    if (p.kernel_id == HKG_KERNEL_MX_SKINNY && ((uintptr_t)SA & 3u) == 0 && ((uintptr_t)SB & 3u) == 0)
+        return run_mx(&p, A, (const uint32_t*)SA, B, (const uint32_t*)SB, C, (const uint16_t*)bias, epi,
+                      (hipStream_t)stream, true);
     int dev = 0;
     st = current_device(&dev);
     if (st != HKG_OK)

@@ -95,11 +95,12 @@ hipError_t launch_grouped(int variant, const uint16_t* A, const uint16_t* B, con
                           int M, int N, int K, int grid, int xcd_chunks, const uint16_t* bias, int epi,
                           hipStream_t stream);
 
-// MXFP8 skinny kernel (M <= 16 MB): packed scales as launch_tile_mx;
+// MXFP8 skinny kernel (M <= 16 MB): packed scales as launch_tile_mx, or with
+// natural the M x K/32 and N x K/32 scale arrays themselves (4-byte aligned);
 // split-K as launch_skinny.
 hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
                             int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
-                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
+                            const uint32_t* psa, const uint32_t* psb, bool natural, hipStream_t stream);
 
 // Packs rows x (K / 32) E8M0 codes S into the tile kernel's layout P
 // (mx_packed_scale_bytes(rows, K) bytes, 4-byte aligned).

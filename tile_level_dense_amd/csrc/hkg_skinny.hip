@@ -24,7 +24,11 @@
 //    MXFP section): steps of 128 k, each lane loading the two 16-byte halves
 //    of its scaled-MFMA operand (k 16 g .. and 64 + 16 g .., g = lane / 16)
 //    from each B row, and its scale dwords from the packed layout of the
-//    tile kernel (byte f of dword lane = block f of a 64-row group).
+//    tile kernel (byte f of dword lane = block f of a 64-row group), or, with
+//    NAT, straight from the natural M x K/32 and N x K/32 scale arrays: the
+//    dword at row r, byte 4 s of the array holds the row's four blocks of
+//    step s, and lane l takes byte l / 16 of it (row l % 16 of the block),
+//    which is what the scaled MFMA reads with op_sel 0.
 #include <type_traits>
 
 #include "hkg_internal.h"
@@ -83,8 +87,9 @@ __device__ __forceinline__ void static_for(F&& f)
 // MB: 16-row blocks of A (M <= 16 MB).  NB: 16-row blocks of B per
 // workgroup.  WK: waves per workgroup, splitting K.  U: steps per chunk of
 // loads (32 k, MXFP8 128 k).  CP: cache-policy bits of the B loads (B is
-// streamed once).  MX: E4M3 operands with packed E8M0 scales PSA / PSB.
-template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX>
+// streamed once).  MX: E4M3 operands with packed E8M0 scales PSA / PSB
+// (NAT: natural-layout scales, row stride K / 32 bytes).
+template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX, bool NAT>
 __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
@@ -97,6 +102,7 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     constexpr int SBY = SK * EB;             // bytes of one row per step
     typedef std::conditional_t<MX, i32x8, i32x4> frag_t;
     static_assert(!MX || MB <= 4, "MXFP8 skinny: one 64-row scale group of A");
+    static_assert(MX || !NAT, "natural scales are MXFP8 only");
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
     __shared__ int last_flag;
@@ -130,11 +136,12 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         (void*)Av, 0, (int)((uint32_t)M * a_rb), kBufferWord3);
     // MXFP8 scales: A's 16-row block i is byte i of the lane's dword of
     // group 0; B's block j is byte ((n0 + 16 j) / 16) % 4 of its group's dword.
+    // Natural layout: rows past M (N) fall outside the range and read zero.
     const int KT = K / 128;
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)PSA, 0, MX ? ((M + 63) / 64) * KT * 256 : 0, kBufferWord3);
+        (void*)PSA, 0, !MX ? 0 : NAT ? M * KT * 4 : ((M + 63) / 64) * KT * 256, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)PSB, 0, MX ? ((N + 63) / 64) * KT * 256 : 0, kBufferWord3);
+        (void*)PSB, 0, !MX ? 0 : NAT ? N * KT * 4 : ((N + 63) / 64) * KT * 256, kBufferWord3);
 
     const uint32_t lane_off_a = (uint32_t)lrow * a_rb + (uint32_t)lgrp * 16u;
     const uint32_t lane_off_b = (uint32_t)lrow * b_rb + (uint32_t)lgrp * 16u;
@@ -161,7 +168,7 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             return load16<P>(r, ok ? off : kOutOfRange);
         }
     };
-    constexpr int SWA = MX ? 1 : 0, SWB = MX ? NB : 0;
+    constexpr int SWA = MX ? (NAT ? MB : 1) : 0, SWB = MX ? NB : 0;
     auto load_chunk = [&](int s, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
                           uint32_t (&sb)[U][SWB + 1]) {
 #pragma unroll
@@ -177,7 +184,18 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             for (int i = 0; i < MB; ++i)
                 av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok,
                                      std::integral_constant<int, 0>{});
-            if constexpr (MX) {
+            if constexpr (NAT) {
+                // row r's dword of step s at byte (r KT + s) 4; this lane's
+                // scale is byte lgrp (shifted down when it is used)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    sa[u][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rsa, ok ? (uint32_t)((16 * i + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rsb, ok ? (uint32_t)((n0 + 16 * j + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+            } else if constexpr (MX) {
                 const uint32_t st = (uint32_t)step * 256u + (uint32_t)lane * 4u;
                 sa[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, ok ? st : kOutOfRange, 0, 0);
 #pragma unroll
@@ -195,7 +213,14 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                if constexpr (MX) {
+                if constexpr (NAT) {
+                    const int bsc = (int)(sb[u][j] >> (8 * lgrp));
+                    static_for<0, MB>([&](auto I) {
+                        constexpr int i = decltype(I)::value;
+                        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bv[u][j], av[u][i], acc[j][i], 0, 0, 0, bsc, 0, (int)(sa[u][i] >> (8 * lgrp)));
+                    });
+                } else if constexpr (MX) {
                     const int bsc = (int)(sb[u][j] >> (8 * (((n0 + 16 * j) >> 4) & 3)));
                     static_for<0, MB>([&](auto I) {
                         constexpr int i = decltype(I)::value;
@@ -319,13 +344,13 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX>
+template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX, bool NAT>
 hipError_t launch_skinny_t(const void* A, const void* B, uint16_t* C, int M, int N, int K, int split_k, float* ws,
                            int* counters, const uint16_t* bias, int epi, int lda, int ldb, int ldc,
                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI, MX>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI, MX, NAT>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
                        stream, A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc, psa, psb);
     return hipGetLastError();
 }
@@ -357,12 +382,12 @@ hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint
 #define HKG_LAUNCH(mb, nb, wk, u, cp) \
     if (v++ == variant)               \
         return epi == EPI_NONE                                                                                \
-                   ? launch_skinny_t<mb, nb, wk, u, cp, false, false>(A, B, C, M, N, K, split_k, ws, counters,    \
-                                                                      bias, epi, lda, ldb, ldc, nullptr, nullptr, \
-                                                                      stream)                                     \
-                   : launch_skinny_t<mb, nb, wk, u, cp, true, false>(A, B, C, M, N, K, split_k, ws, counters,     \
-                                                                     bias, epi, lda, ldb, ldc, nullptr, nullptr,  \
-                                                                     stream);
+                   ? launch_skinny_t<mb, nb, wk, u, cp, false, false, false>(A, B, C, M, N, K, split_k, ws,      \
+                                                                             counters, bias, epi, lda, ldb, ldc, \
+                                                                             nullptr, nullptr, stream)           \
+                   : launch_skinny_t<mb, nb, wk, u, cp, true, false, false>(A, B, C, M, N, K, split_k, ws,       \
+                                                                            counters, bias, epi, lda, ldb, ldc,  \
+                                                                            nullptr, nullptr, stream);
     HKG_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
@@ -381,18 +406,25 @@ SkinnyShape mx_skinny_shape(int variant)
 
 hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
                             int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
-                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
+                            const uint32_t* psa, const uint32_t* psb, bool natural, hipStream_t stream)
 {
     int v = 0;
-#define HKG_LAUNCH(mb, nb, wk, u, cp)                                                                             \
-    if (v++ == variant)                                                                                          \
-        return epi == EPI_NONE                                                                                   \
-                   ? launch_skinny_t<mb, nb, wk, u, cp, false, true>(A, B, C, M, N, K, split_k, ws, counters,    \
-                                                                     bias, epi, K, K, N, psa, psb, stream)       \
-                   : launch_skinny_t<mb, nb, wk, u, cp, true, true>(A, B, C, M, N, K, split_k, ws, counters,     \
-                                                                    bias, epi, K, K, N, psa, psb, stream);
+#define HKG_LAUNCH_NAT(mb, nb, wk, u, cp, nat)                                                                    \
+    return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, false, true, nat>(A, B, C, M, N, K, split_k, ws,  \
+                                                                                  counters, bias, epi, K, K, N,   \
+                                                                                  psa, psb, stream)               \
+                           : launch_skinny_t<mb, nb, wk, u, cp, true, true, nat>(A, B, C, M, N, K, split_k, ws,   \
+                                                                                 counters, bias, epi, K, K, N,    \
+                                                                                 psa, psb, stream);
+#define HKG_LAUNCH(mb, nb, wk, u, cp)              \
+    if (v++ == variant) {                          \
+        if (natural)                               \
+            HKG_LAUNCH_NAT(mb, nb, wk, u, cp, true) \
+        HKG_LAUNCH_NAT(mb, nb, wk, u, cp, false)   \
+    }
     HKG_MX_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
+#undef HKG_LAUNCH_NAT
     return hipErrorInvalidValue;
 }
 
