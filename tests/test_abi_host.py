@@ -93,7 +93,7 @@ def test_status_strings(lib):
 WORKLOAD_PLANS = {
     (256, 256, 256): ("TILE", "tile_128x128x64_"),
     (16, 4096, 4096): ("SKINNY", "skinny_m16"),
-    (128, 12288, 4096): ("TILE", "tile_128x128x64_"),
+    (128, 12288, 4096): ("TILE", "tile_64x64x64_s4"),
     (4096, 4096, 12288): ("TILE", "tile_256x256x64_"),
     (8192, 8192, 8192): ("TILE", "tile_256x256x64_"),
 }
@@ -131,10 +131,12 @@ def test_plan_decode_geometry():
 
 
 def test_plan_boundaries():
-    assert hkg.KERNEL_NAMES[hkg.plan(32, 4096, 4096).kernel_id] == "SKINNY"
-    assert hkg.KERNEL_NAMES[hkg.plan(33, 4096, 4096).kernel_id] == "TILE"
-    p = hkg.plan(128, 12288, 4096)       # one 128-row tile band, split-K 3
-    assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.split_k) == (128, 3)
+    assert hkg.KERNEL_NAMES[hkg.plan(16, 4096, 4096).kernel_id] == "SKINNY"
+    assert hkg.KERNEL_NAMES[hkg.plan(17, 4096, 4096).kernel_id] == "TILE"
+    assert hkg.KERNEL_NAMES[hkg.plan(16, 4112, 4096).kernel_id] == "TILE"      # 257 column blocks
+    assert hkg.KERNEL_NAMES[hkg.plan(32, 4096, 4096).kernel_id] == "TILE"
+    p = hkg.plan(128, 12288, 4096)       # 2 x 192 tiles of 64 x 64 fill the device unsplit
+    assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.tile_n, p.split_k) == (64, 64, 1)
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 100).kernel_id] == "GENERIC"     # K % 8
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 0).kernel_id] == "ZERO"
     assert hkg.KERNEL_NAMES[hkg.plan(0, 512, 64).kernel_id] == "NONE"
@@ -143,21 +145,31 @@ def test_plan_boundaries():
     # small N at decode M: split-K across workgroups with a workspace
     p = hkg.plan(16, 256, 8192)
     assert p.split_k > 1 and p.workspace_bytes == p.split_k * 16 * 256 * 4
+    # streaming tiles: the fewest splits that keep one workgroup per CU
+    p = hkg.plan(256, 4096, 4096)        # 128 x 128 needs split 4, 64 x 64 fills unsplit
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (64, 64, 1, 256)
+    p = hkg.plan(512, 4096, 4096)        # 128 x 128 needs split 2, 64 x 64 fills unsplit
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (64, 64, 1, 512)
+    p = hkg.plan(256, 12288, 4096)       # both unsplit: the larger tile
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 128, 1, 192)
     # tile grid under one workgroup per CU: split-K across workgroups,
-    # at least 4 k-tiles per split
-    p = hkg.plan(256, 4096, 4096)
-    assert (p.tile_m, p.tile_n) == (128, 128) and p.grid_x == 64
-    assert p.split_k == 4 and p.grid_y == 4 and p.workspace_bytes == 4 * 256 * 4096 * 4
-    p = hkg.plan(256, 4096, 512)
+    # at least 4 k-tiles per split; the 128-row tile is skipped at M = 64
+    # (half its rows would be padding)
+    p = hkg.plan(64, 4096, 4096)
+    assert (p.tile_m, p.tile_n) == (64, 64) and p.grid_x == 64
+    assert p.split_k == 4 and p.grid_y == 4 and p.workspace_bytes == 4 * 64 * 4096 * 4
+    p = hkg.plan(64, 4096, 512)
     assert p.split_k == 2
-    p = hkg.plan(256, 4096, 128)
+    p = hkg.plan(64, 4096, 128)
     assert p.split_k == 1 and p.workspace_bytes == 0
-    # tile ladder: a grid that would underfill at 256x256 steps down
-    for shape in [(2048, 2048, 1024), (4096, 2048, 1024), (1024, 8192, 4096)]:
+    # compute-bound ladder: 256 x 256 from 3/4 of the CUs on, then the
+    # two-stage 128 x 128 tile while its tiles outnumber the CUs
+    for shape, name in [((3072, 4096, 1024), "tile_256x256x64_s2"), ((2048, 2048, 1024), "tile_128x128x64_s4"),
+                        ((4096, 2048, 1024), "tile_128x128x64_s2"), ((1024, 8192, 4096), "tile_128x128x64_s2"),
+                        ((8192, 8192, 8192), "tile_256x256x64_s2")]:
         p = hkg.plan(*shape)
-        assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE"
-        assert p.grid_x >= 256 or p.tile_m * p.tile_n == 128 * 128, p
-        assert (p.tile_m, p.tile_n) != (256, 256), p
+        assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and p.split_k == 1
+        assert p.kernel_name.decode().startswith(name), (shape, p)
 
 
 @pytest.mark.parametrize("shape", [(-1, 4, 8), (4, -1, 8), (4, 4, -8), (2**31, 4, 8), (4, 4, 2**31),

@@ -23,11 +23,13 @@ namespace {
 // correctly.
 constexpr int kNumCUs = 256;
 
-// Skinny path for M up to this many rows (decode shapes).  Above it the
-// tile kernel with a 128-row tile (B still read once) and split-K measured
-// faster on MI355X at N = 4096 .. 12288, K = 4096 .. 12288 (M = 64: 1.1-1.7x
-// except at N = K = 4096; M = 128: 1.0-2.2x).
-constexpr int64_t kSkinnyMaxM = 32;
+// Skinny path for M up to this many rows (decode shapes) when its column
+// blocks of 16 fit one per compute unit (N <= 16 * 256).  Otherwise the
+// 4-stage 64 x 64 tile (B read once per 64 rows) measured faster on MI355X:
+// M = 16: N = 12288, K = 4096 26 vs 31 us; M = 32: N = K = 4096 12 vs 16 us,
+// N = 12288 27 vs 42 us; at M = 16, N = K = 4096 the skinny kernel leads,
+// 11.1 vs 11.6 us.
+constexpr int64_t kSkinnyMaxM = 16;
 // Largest split-K factor of the tile kernel.
 constexpr int64_t kMaxTileSplit = 16;
 
@@ -211,27 +213,54 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N);
 
 void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
-    // Largest tile that still gives every compute unit a workgroup; the
-    // smallest rung otherwise (FlyDSL "Prebuilt kernels guide", section 3c,
-    // tile selection; 256 x 256 first: HipKittens talk notes, Table 2).
-    int variant = TILE_LADDER[sizeof(TILE_LADDER) / sizeof(TILE_LADDER[0]) - 1];
-    for (int v : TILE_LADDER) {
-        const TileShape s = tile_shape(v);
-        if (cdiv(M, s.bm) * cdiv(N, s.bn) >= kNumCUs) {
-            variant = v;
-            break;
+    // Compute-bound shapes, largest tile first (output-tile size dominates:
+    // HipKittens talk notes, Table 2; tile selection by grid fill: FlyDSL
+    // "Prebuilt kernels guide", section 3c).  The 256 x 256 ping-pong tile
+    // when its tiles fill at least three quarters of the compute units;
+    // else, while 128 x 128 tiles outnumber the compute units, the two-stage
+    // 128 x 128 tile, two workgroups per compute unit.  Measured on MI355X
+    // against the 256 x 128 tile: M = 3072, N = K = 4096 (192 tiles of
+    // 256 x 256) 93 vs 160 us; M = 1536 68 vs 88 us; M = 1024, N = K = 8192
+    // 139 vs 159 us.
+    {
+        const TileShape s = tile_shape(TILE_LADDER[0]);
+        if (4 * cdiv(M, s.bm) * cdiv(N, s.bn) >= 3 * kNumCUs) {
+            fill_tile(p, TILE_LADDER[0], 1, M, N);
+            return;
+        }
+        const TileShape t = tile_shape(TILE_LADDER[1]);
+        if (cdiv(M, t.bm) * cdiv(N, t.bn) > kNumCUs) {
+            fill_tile(p, TILE_LADDER[1], 1, M, N);
+            return;
         }
     }
-    const TileShape s = tile_shape(variant);
-    const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
-    // Split K across workgroups when even the smallest rung leaves compute
-    // units idle, keeping at least 4 k-tiles per split (the pipeline depth).
-    int64_t split = 1;
-    if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {   // fp32 partials addressed in 32 bits
-        split = std::min<int64_t>(cdiv(kNumCUs, tm * tn), cdiv(K, s.bk) / 4);
-        split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
+    // Smaller outputs: the operands are streamed from HBM a few times at most
+    // and the kernel is bound by memory, so the grid should put one workgroup
+    // with a deep copy pipeline on every compute unit.  For each streaming tile, split K so
+    // the grid stays within one workgroup per compute unit (at least 4 k-tiles
+    // per split; split-K adds fp32 partial traffic), then take the tile with
+    // the fewest splits, the larger tile on a tie.  A tile whose rows would be
+    // more than a quarter padding is skipped unless it is the last one.
+    int best = -1;
+    int64_t best_split = 0;
+    const int n_stream = (int)(sizeof(STREAM_TILES) / sizeof(STREAM_TILES[0]));
+    for (int i = 0; i < n_stream; ++i) {
+        const int v = STREAM_TILES[i];
+        const TileShape s = tile_shape(v);
+        const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
+        if (i + 1 < n_stream && 4 * (tm * s.bm - M) > tm * s.bm)
+            continue;
+        int64_t split = 1;
+        if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {   // fp32 partials addressed in 32 bits
+            split = std::min<int64_t>(kNumCUs / (tm * tn), cdiv(K, s.bk) / 4);
+            split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
+        }
+        if (best < 0 || split < best_split) {
+            best = v;
+            best_split = split;
+        }
     }
-    fill_tile(p, variant, split, M, N);
+    fill_tile(p, best, best_split, M, N);
 }
 
 // Fill the tile-kernel fields of p for (variant, split).
@@ -381,7 +410,7 @@ hkg_status_t make_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
         plan_generic(M, N, p, "K too large for 32-bit buffer offsets of a tile");
         return HKG_OK;
     }
-    if (M <= kSkinnyMaxM) {
+    if (M <= kSkinnyMaxM && cdiv(N, 16) <= kNumCUs) {
         plan_skinny(M, N, K, p);
         return HKG_OK;
     }

@@ -35,8 +35,12 @@ constexpr int GROUPED_NUM_VARIANTS = 0
 #undef HKG_COUNT_TILE
     ;
 
-// Default tile ladder of the planner, largest first (variant indices).
-constexpr int TILE_LADDER[] = {0, 1, 2};
+// Planner's tiles (variant indices): the compute-bound ladder (256 x 256
+// ping-pong, two-stage 128 x 128), then the streaming tiles (4-stage
+// 128 x 128 and 64 x 64) for shapes that read their operands only a few
+// times.
+constexpr int TILE_LADDER[] = {0, 2};
+constexpr int STREAM_TILES[] = {8, 7};
 
 // MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
 constexpr int MX_SKINNY_NUM_VARIANTS = 0

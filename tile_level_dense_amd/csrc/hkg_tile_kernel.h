@@ -102,6 +102,32 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
+// The 128-bit buffer descriptor of __builtin_amdgcn_make_buffer_rsrc(p, 0,
+// bytes, kBufferWord3), as four dwords (base, base high bits with stride 0,
+// range, word 3).
+__device__ __forceinline__ i32x4 rsrc_words(const void* p, int bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes, kBufferWord3};
+}
+
+// One buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i's bytes at offset voff of the buffer land at LDS address lds + 16 i.
+// Written as inline asm so that the compiler does not order later LDS reads
+// after it: for the builtin it waits for every copy in flight (vmcnt(0))
+// before each LDS read it cannot prove disjoint, which leaves no copy in
+// flight across a K step.  Callers order reads after copies with their own
+// vmcnt waits and barriers.  M0 holds the LDS address; one wait state
+// separates its write from the copy.
+__device__ __forceinline__ void copy_to_lds(i32x4 rsrc, const char* lds, uint32_t voff)
+{
+    const uint32_t m0 = (uint32_t)(size_t)(lds_void*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 // Wait until at most N of this wave's buffer->LDS copies are in flight and
 // its LDS reads are done, then join the workgroup barrier.
 template <int N>
@@ -213,6 +239,8 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             (void*)((const char*)Av + (size_t)m0 * a_rb), 0, (int)(rows_a * a_rb), kBufferWord3);
         const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(b_rows + (size_t)n0 * b_rb), 0, (int)(rows_b * b_rb), kBufferWord3);
+        const i32x4 words_a = rsrc_words((const char*)Av + (size_t)m0 * a_rb, (int)(rows_a * a_rb));
+        const i32x4 words_b = rsrc_words(b_rows + (size_t)n0 * b_rb, (int)(rows_b * b_rb));
 
         // LDS layout of a stage: row r holds its logical 16-byte chunk c at
         // position c ^ ((r / RPL) % CPR).  Sixteen consecutive rows read at one
@@ -251,14 +279,12 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             const uint32_t koff = (uint32_t)k0 * (uint32_t)EB;
     #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_a, (lds_void*)(base + (wave + i * NW) * 1024), 16,
-                    k_out ? kOutOfRange : src_off_a + koff + (uint32_t)i * copy_step_a, 0, 0, 0);
+                copy_to_lds(words_a, base + (wave + i * NW) * 1024,
+                            k_out ? kOutOfRange : src_off_a + koff + (uint32_t)i * copy_step_a);
     #pragma unroll
             for (int i = 0; i < B_LOADS; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_b, (lds_void*)(base + A_BYTES + (wave + i * NW) * 1024), 16,
-                    k_out ? kOutOfRange : src_off_b + koff + (uint32_t)i * copy_step_b, 0, 0, 0);
+                copy_to_lds(words_b, base + A_BYTES + (wave + i * NW) * 1024,
+                            k_out ? kOutOfRange : src_off_b + koff + (uint32_t)i * copy_step_b);
         };
 
         // Fragment reads: lane -> row (lane % 16) of a 16-row block, logical
