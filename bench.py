@@ -25,6 +25,9 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                hkg_gemm_bf16_ex (per-call transpose of the column operands),
                and the transpose pass alone (GB/s); torch.mm on the same views
                for context
+  other_configs  the tiny, MLP-up (128 x 12288 x 4096) and prefill-down
+               (4096 x 4096 x 12288) workloads in the planner's configuration,
+               per call over rotating buffer sets (graph), torch.mm for context
   mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
                mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
                MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
@@ -293,6 +296,55 @@ def bench_mx_decode(torch, hkg, steps, warmup):
                 launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
 
 
+def bench_configs(torch, hkg):
+    """The remaining dense workloads (tiny, MLP-up, prefill-down) in the
+    planner's launch configuration: per-call time over buffer sets rotated
+    across 2x the last-level cache, launches captured in a graph; torch.mm
+    over the same buffers for context."""
+    import workloads
+    out = {}
+    stream = torch.cuda.Stream()
+    for name in ("tiny_256", "mlp_up_128x12288x4096", "prefill_down_4096x4096x12288"):
+        w = workloads.WORKLOADS[name]
+        M, N, K = w["M"], w["N"], w["K"]
+        A, B = workloads.workload_inputs(name)
+        a0, b0 = to_dev(A, torch), to_dev(B, torch)
+        del A, B
+        per_set = 2 * (M * K + N * K + M * N)
+        sets = int(min(64, max(2, np.ceil(2 * LLC_BYTES / per_set))))
+        bufs = [(a0.clone(), b0.clone(), torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+                for _ in range(sets)]
+        plan = hkg.plan(M, N, K)
+
+        def graph_of(call):
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for a, b, c in bufs:
+                    call(a, b, c)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for a, b, c in bufs:
+                    call(a, b, c)
+            return g
+
+        flops = 2.0 * M * N * K
+        est = max(flops / 1.0e15, per_set / 4.0e12, 5e-6)          # rough seconds per call
+        reps = int(min(200, max(3, 0.2 / (est * sets))))
+        g = graph_of(lambda a, b, c: hkg.gemm(a, b, out=c))
+        ms = time_launches(torch, g.replay, reps, 3) / sets
+        gv = graph_of(lambda a, b, c: torch.mm(a, b.t(), out=c))
+        ms_v = time_launches(torch, gv.replay, reps, 3) / sets
+        log("%s: %s, %.2f us/call (%.1f TFLOP/s, %.0f GB/s); torch.mm %.2f us"
+            % (name, plan.kernel_name.decode(), ms * 1e3, flops / (ms * 1e-3) / 1e12,
+               per_set / (ms * 1e-3) / 1e9, ms_v * 1e3))
+        out[name] = dict(us=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12, gbps=per_set / (ms * 1e-3) / 1e9,
+                         kernel=plan.kernel_name.decode(), split_k=plan.split_k, vendor_us=ms_v * 1e3, sets=sets)
+        del bufs, a0, b0
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_grouped(torch, hkg, steps, warmup):
     import workloads
     out = {}
@@ -391,7 +443,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
-    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts"],
+    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts", "configs"],
                     help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -419,6 +471,10 @@ def main():
         grp = bench_grouped(torch, hkg, args.steps, args.warmup)
         print(json.dumps({k: round(v["tflops"], 2) for k, v in grp.items()}), flush=True)
         return 0
+    if args.only == "configs":
+        cfg = bench_configs(torch, hkg)
+        print(json.dumps({k: round(v["us"], 3) for k, v in cfg.items()}), flush=True)
+        return 0
     if args.only == "mx":
         mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
         mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
@@ -434,6 +490,7 @@ def main():
     mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     grp = bench_grouped(torch, hkg, args.steps, args.warmup)
     lay = bench_layouts(torch, hkg, args.steps, args.warmup)
+    cfg = bench_configs(torch, hkg)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
@@ -494,6 +551,10 @@ def main():
                     "transpose_ms": round(lay["transpose_ms"], 4), "transpose_gbps": round(lay["transpose_gbps"], 1),
                     "prepacked_nn": "equals the square_8192 value: a pre-packed weight runs the row-layout kernel",
                     "vendor_nn_tflops": round(lay["vendor_nn_tflops"], 2)},
+        "other_configs": {name: {"us_per_call": round(r["us"], 3), "tflops": round(r["tflops"], 2),
+                                 "gbps": round(r["gbps"], 1), "kernel": r["kernel"], "split_k": r["split_k"],
+                                 "rotating_sets": r["sets"], "vendor_us": round(r["vendor_us"], 3)}
+                          for name, r in cfg.items()},
         "mxfp8": {
             "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",
                        "tflops": round(mxs["tflops"], 2), "ms": round(mxs["ms"], 4),

@@ -36,11 +36,11 @@ constexpr int GROUPED_NUM_VARIANTS = 0
     ;
 
 // Planner's tiles (variant indices): the compute-bound ladder (256 x 256
-// ping-pong, two-stage 128 x 128), then the streaming tiles (4-stage
-// 128 x 128 and 64 x 64) for shapes that read their operands only a few
-// times.
+// ping-pong, two-stage 128 x 128), then the 4-stage streaming tiles, largest
+// first (128 x 128, 128 x 64, 64 x 128, 64 x 64), for shapes that read their
+// operands only a few times.
 constexpr int TILE_LADDER[] = {0, 2};
-constexpr int STREAM_TILES[] = {8, 7};
+constexpr int STREAM_TILES[] = {8, 10, 9, 7};
 
 // MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
 constexpr int MX_SKINNY_NUM_VARIANTS = 0
