@@ -443,6 +443,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny / MLP-up / prefill-down leg (counter runs)")
     ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts", "configs"],
                     help="time one leg only (profiler runs)")
     args = ap.parse_args()
@@ -490,7 +492,7 @@ def main():
     mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     grp = bench_grouped(torch, hkg, args.steps, args.warmup)
     lay = bench_layouts(torch, hkg, args.steps, args.warmup)
-    cfg = bench_configs(torch, hkg)
+    cfg = {} if args.no_configs else bench_configs(torch, hkg)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
