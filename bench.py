@@ -25,9 +25,10 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                hkg_gemm_bf16_ex (per-call transpose of the column operands),
                and the transpose pass alone (GB/s); torch.mm on the same views
                for context
-  other_configs  the tiny, MLP-up (128 x 12288 x 4096) and prefill-down
-               (4096 x 4096 x 12288) workloads in the planner's configuration,
-               per call over rotating buffer sets (graph), torch.mm for context
+  other_configs  the tiny and MLP-up (128 x 12288 x 4096) workloads (with
+               --only configs also prefill-down, 4096 x 4096 x 12288) in the
+               planner's configuration, per call over rotating buffer sets
+               (graph), torch.mm for context
   mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
                mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
                MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
@@ -296,15 +297,22 @@ def bench_mx_decode(torch, hkg, steps, warmup):
                 launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
 
 
-def bench_configs(torch, hkg):
-    """The remaining dense workloads (tiny, MLP-up, prefill-down) in the
-    planner's launch configuration: per-call time over buffer sets rotated
-    across 2x the last-level cache, launches captured in a graph; torch.mm
-    over the same buffers for context."""
+CONFIG_LEG = ("tiny_256", "mlp_up_128x12288x4096")
+ALL_CONFIGS = CONFIG_LEG + ("prefill_down_4096x4096x12288",)
+
+
+def bench_configs(torch, hkg, names=CONFIG_LEG):
+    """The remaining dense workloads (tiny, MLP-up; with --only configs also
+    prefill-down, which runs the square kernel at another size and is left
+    out of the full run so that the square kernel's average launch time in a
+    kernel trace of the full run is the square workload's) in the planner's
+    launch configuration: per-call time over buffer sets rotated across 2x
+    the last-level cache, launches captured in a graph; torch.mm over the
+    same buffers for context."""
     import workloads
     out = {}
     stream = torch.cuda.Stream()
-    for name in ("tiny_256", "mlp_up_128x12288x4096", "prefill_down_4096x4096x12288"):
+    for name in names:
         w = workloads.WORKLOADS[name]
         M, N, K = w["M"], w["N"], w["K"]
         A, B = workloads.workload_inputs(name)
@@ -474,7 +482,7 @@ def main():
         print(json.dumps({k: round(v["tflops"], 2) for k, v in grp.items()}), flush=True)
         return 0
     if args.only == "configs":
-        cfg = bench_configs(torch, hkg)
+        cfg = bench_configs(torch, hkg, ALL_CONFIGS)
         print(json.dumps({k: round(v["us"], 3) for k, v in cfg.items()}), flush=True)
         return 0
     if args.only == "mx":

@@ -118,14 +118,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* p, int bytes)
 // before each LDS read it cannot prove disjoint, which leaves no copy in
 // flight across a K step.  Callers order reads after copies with their own
 // vmcnt waits and barriers.  M0 holds the LDS address; one wait state
-// separates its write from the copy.
+// separates its write from the copy.  M0 is not named as clobbered: the
+// compiler reserves it and sets it right before each of its own uses (the
+// kernels that use this helper have none).
 __device__ __forceinline__ void copy_to_lds(i32x4 rsrc, const char* lds, uint32_t voff)
 {
     const uint32_t m0 = (uint32_t)(size_t)(lds_void*)lds;
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // Wait until at most N of this wave's buffer->LDS copies are in flight and
