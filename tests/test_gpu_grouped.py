@@ -1,6 +1,6 @@
 """GPU parity of the grouped (mixture-of-experts) GEMM against the oracle.
 
-Both grouped tile variants run through the C ABI on the persistent grid, with
+Every grouped tile variant runs through the C ABI on the persistent grid, with
 the planner's grid and with forced grids (one workgroup walking every tile,
 grids that are not a multiple of the 8 chiplets, the chiplet-contiguous walk
 on and off), on ragged expert sizes with empty experts, more than 64 experts
@@ -97,6 +97,12 @@ CASES = [
     ("v128_grid16_xcd", [129, 0, 0, 511, 64], 270, 200, 1, 16, 1),
     ("v256_grid24_xcd", [513, 0, 257], 530, 128, 0, 24, 1),
     ("leading_empty_experts", [0, 0, 0, 70, 0], 96, 64, 1, None, None),
+    # the ping-pong tile (variant 2): several tiles per workgroup, one-stage
+    # and ragged K, XCD-chunked walk
+    ("pp_ragged", [1, 255, 0, 300, 17], 300, 192, 2, None, None),
+    ("pp_one_workgroup_one_stage", [300, 5, 0, 260], 260, 64, 2, 1, 0),
+    ("pp_grid3_ragged_k", [300, 70], 260, 520, 2, 3, None),
+    ("pp_grid24_xcd", [513, 0, 257], 530, 128, 2, 24, 1),
     ("single_expert", [300], 200, 264, None, None, None),
 ]
 
@@ -116,7 +122,7 @@ def test_grouped_many_experts(hkg):
     sizes[rng.random(150) < 0.33] = 0
     _say("many experts", int(sizes.sum()))
     A, B, offs = workloads.make_grouped_inputs(sizes, 72, 64, seed=41)
-    for variant, grid in ((1, None), (0, 5)):
+    for variant, grid in ((1, None), (0, 5), (2, 5)):
         C = run(hkg, A, B, offs, variant, grid)
         check(C, A, B, offs)
 
@@ -143,7 +149,7 @@ def test_grouped_epilogue(hkg, epi):
     A, B, offs = workloads.make_grouped_inputs([70, 0, 130, 3], 200, 256, seed=len(epi))
     rng = np.random.default_rng(5)
     bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, size=(4, 200)).astype(np.float32))
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         C = run(hkg, A, B, offs, variant, bias=bias, epi=epi)
         check(C, A, B, offs, bias=bias, epi=epi)
 

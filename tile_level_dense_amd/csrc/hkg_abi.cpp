@@ -1006,6 +1006,7 @@ void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
     // tile, two for the 64 KiB 128 x 128 tile; never more than the tiles
     // the experts can have.
     const int64_t per_cu = s.bm >= 256 ? 1 : 2;
+    const int64_t row_bytes = (int64_t)s.bk * 2;
     const int64_t bound = (cdiv(M, s.bm) + G) * tn;
     const int64_t grid = std::min<int64_t>(kNumCUs * per_cu, bound);
     p->kernel_id = HKG_KERNEL_GROUPED;
@@ -1022,7 +1023,9 @@ void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
     p->workspace_bytes = 0;
     p->xcd_window_w = 0;
     p->xcd_chunk_c = 1;                 // chiplet-contiguous walk when the grid is a multiple of 8
-    p->lds_bytes = s.stages * (s.bm + s.bn) * s.bk * 2;
+    // the ping-pong keeps A halves double- and B triple-buffered
+    p->lds_bytes = (int32_t)(s.sched == 5 ? 4 * (s.bm / 2) * row_bytes + 3 * s.bn * row_bytes
+                                          : s.stages * (s.bm + s.bn) * row_bytes);
     fill_resources(p, grouped_resources(variant));
     std::snprintf(p->kernel_name, sizeof p->kernel_name, "grouped_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
                   s.stages, s.wm, s.wn, s.sched);
@@ -1056,10 +1059,15 @@ hkg_status_t make_grouped_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_p
     }
     if (K % 8 != 0 || K > (int64_t)(INT32_MAX / 2) / 256)
         return HKG_ERR_UNSUPPORTED;
-    // 256 x 256 tiles when the experts average at least 256 rows and those
-    // tiles fill the device; 128 x 128 otherwise.
-    const TileShape big = grouped_shape(0);
-    const int variant = (M / G >= big.bm && cdiv(M, big.bm) * cdiv(N, big.bn) >= kNumCUs) ? 0 : 1;
+    // The 256 x 256 ping-pong tile when the experts average at least 256
+    // rows and those tiles fill the device; the 128 x 128 tile otherwise.
+    // Measured on MI355X, ping-pong vs the 8-wave register-pipelined 256 x 256
+    // tile: 8 experts x 4096 rows, N = 14336, K = 4096 1296 vs 1236 TFLOP/s;
+    // 16 ragged experts, 8192 rows, N = K = 4096 960 vs 898; 8 x 1024 rows
+    // 1236 vs 1237.
+    const TileShape big = grouped_shape(kGroupedPingPong);
+    const int variant =
+        (M / G >= big.bm && cdiv(M, big.bm) * cdiv(N, big.bn) >= kNumCUs) ? kGroupedPingPong : kGroupedSmall;
     const TileShape s = grouped_shape(variant);
     if ((cdiv(M, s.bm) + G) * cdiv(N, s.bn) > INT32_MAX)
         return HKG_ERR_UNSUPPORTED;

@@ -28,7 +28,10 @@ constexpr int MX_TILE_NUM_VARIANTS = 0
     ;
 
 // Grouped-GEMM instantiations (plan.variant for HKG_KERNEL_GROUPED): the
-// rows of HKG_GROUPED_CONFIGS.
+// rows of HKG_GROUPED_CONFIGS; the planner's two (the 256 x 256 ping-pong and
+// the 128 x 128 tile).
+constexpr int kGroupedPingPong = 2;
+constexpr int kGroupedSmall = 1;
 constexpr int GROUPED_NUM_VARIANTS = 0
 #define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1
     HKG_GROUPED_CONFIGS(HKG_COUNT_TILE)

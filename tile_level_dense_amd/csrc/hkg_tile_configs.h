@@ -35,7 +35,9 @@
     X(128, 128, 128, 2, 2, 2, 0)
 
 // Grouped (mixture-of-experts) instantiations on a persistent grid, same
-// fields; bf16 only, no split-K.
+// fields; bf16 only, no split-K.  Variant 2 (the ping-pong) and 1 are the
+// planner's; 0 is kept as the register-pipelined alternative.
 #define HKG_GROUPED_CONFIGS(X)     \
     X(256, 256, 64, 2, 2, 4, 2)    \
-    X(128, 128, 64, 2, 2, 2, 2)
+    X(128, 128, 64, 2, 2, 2, 2)    \
+    X(256, 256, 64, 2, 4, 2, 5)

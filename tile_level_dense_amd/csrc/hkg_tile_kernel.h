@@ -544,9 +544,26 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             const uint32_t p_off_b = (uint32_t)(128 * g + prow) * b_rb + (uint32_t)pchunk * 16u;
             const int p_k = pchunk * KPC;
             static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a group's copies");
+            // Grouped mode recomputes the lane-derived offsets at each use from
+            // an opaque copy of the lane id, so they are not held in registers
+            // through the compute phases (the persistent loop's state needs
+            // those registers).
+            auto fresh_lane = [&]() {
+                int l = threadIdx.x & 63;
+                asm volatile("" : "+v"(l));
+                return l;
+            };
             auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t, uint32_t p_off, uint32_t rb) {
+                int pk = p_k;
+                if constexpr (GROUPED) {
+                    const int l = fresh_lane();
+                    const int row = w4 * RPW + l / CPR;
+                    const int ch = (l % CPR) ^ ((row / RPL) % CPR);
+                    p_off = (uint32_t)(128 * g + row) * rb + (uint32_t)ch * 16u;
+                    pk = ch * KPC;
+                }
                 const int k0 = kbase + t * BK;
-                const bool k_out = k0 + p_k >= k_lim;
+                const bool k_out = k0 + pk >= k_lim;
                 const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * (uint32_t)EB;
                 const uint32_t p_step = (uint32_t)(4 * RPW) * rb;
     #pragma unroll
@@ -561,16 +578,30 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             const int b_row = wn * WTN + lrow;
             bf16x8 af[KS][FM], bf[KS][FN];
             auto read_stage = [&](int t) {
-                const char* ab = a_buf + (2 * g + (t & 1)) * HALF + a_row * RB;
-                const char* bb = b_buf + (t % 3) * 2 * HALF + b_row * RB;
+                int ar = a_row, br = b_row;
+                int co[KS];
+    #pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    co[s] = chunk_off[s];
+                if constexpr (GROUPED) {
+                    const int l = fresh_lane();
+                    const int lr = l & 15;
+                    ar = wm * WTM - 128 * g + lr;
+                    br = wn * WTN + lr;
+    #pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        co[s] = ((4 * s + (l >> 4)) ^ ((lr / RPL) % CPR)) * 16;
+                }
+                const char* ab = a_buf + (2 * g + (t & 1)) * HALF + ar * RB;
+                const char* bb = b_buf + (t % 3) * 2 * HALF + br * RB;
     #pragma unroll
                 for (int s = 0; s < KS; ++s) {
     #pragma unroll
                     for (int i = 0; i < FM; ++i)
-                        af[s][i] = *(const bf16x8*)(ab + i * 16 * RB + chunk_off[s]);
+                        af[s][i] = *(const bf16x8*)(ab + i * 16 * RB + co[s]);
     #pragma unroll
                     for (int j = 0; j < FN; ++j)
-                        bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + chunk_off[s]);
+                        bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + co[s]);
                 }
             };
             auto mfma_stage = [&]() {
