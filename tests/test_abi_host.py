@@ -125,6 +125,19 @@ def test_plan_square_8192_geometry():
     assert p.workspace_bytes == 0 and p.split_k == 1
 
 
+@pytest.mark.parametrize("M,lds", [(16, True), (9, True), (8, False), (1, False)])
+def test_plan_small_m_a_staging(M, lds):
+    # A goes through LDS once more than half of the 16-row block is used;
+    # with fewer rows the direct fragment loads (rows past M read zero
+    # without a fetch) are kept.  Both are the 16 x 16-column, 8-wave kernel.
+    p = hkg.plan(M, 4096, 4096)
+    name = p.kernel_name.decode()
+    assert name.startswith("skinny_m16_n16_w8_u8_c0")
+    assert name.endswith("_lds") == lds
+    a_bufs = 8 * 2 * 16 * 8 * 64          # per wave: two chunks of 16 rows x 512 bytes
+    assert (p.lds_bytes >= a_bufs) == lds
+
+
 def test_plan_decode_geometry():
     p = hkg.plan(16, 4096, 4096)
     assert p.grid_x == 256 and p.split_k == 1 and p.workspace_bytes == 0

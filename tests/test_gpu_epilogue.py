@@ -81,7 +81,7 @@ def _tile(hkg, variant, split=1):
 
 def _skinny(hkg, variant, split):
     from tile_level_dense_amd import build as hkg_build
-    mb, nb, wk, u, cp = hkg_build.skinny_configs()[variant]
+    mb, nb, wk, u, cp, al = hkg_build.skinny_configs()[variant]
 
     def edit(p):
         p.kernel_id = hkg.HKG_KERNEL_SKINNY
@@ -110,6 +110,7 @@ CASES = [
     ("planner_skinny", (16, 1000, 2056), None),
     ("skinny_split3", (20, 300, 4096), lambda h: _skinny(h, 1, 3)),
     ("skinny_nb4", (9, 100, 520), lambda h: _skinny(h, 5, 1)),
+    ("skinny_lds_split3", (12, 300, 4104), lambda h: _skinny(h, 10, 3)),
     ("generic", (70, 45, 100), lambda h: _generic(h)),
 ]
 

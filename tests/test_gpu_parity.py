@@ -253,7 +253,7 @@ def test_forced_skinny_split(hkg, variant, split, shape):
     _say("skinny variant", variant, "split", split, shape)
     A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=split)
 
-    mb, nb, wk, u, cp = _skinny_configs()[variant]
+    mb, nb, wk, u, cp, al = _skinny_configs()[variant]
 
     def edit(p):
         p.kernel_id = hkg.HKG_KERNEL_SKINNY

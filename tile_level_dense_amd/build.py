@@ -47,13 +47,14 @@ TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
 GROUPED_VARIANTS = tile_configs(grouped=True)
 def skinny_configs(mx=False):
-    """(MB, NB, WK, U, CP) per skinny variant (MXFP8 with mx=True), from hkg_skinny_configs.h."""
+    """(MB, NB, WK, U, CP, AL) per skinny variant, or (MB, NB, WK, U, CP) per MXFP8
+    skinny variant with mx=True, from hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
     body = text[text.index("#define HKG_MX_SKINNY_CONFIGS(X)" if mx else "#define HKG_SKINNY_CONFIGS(X)"):]
     end = body.find("#define", 10)
     body = body if end < 0 else body[:end]
-    return [tuple(int(v) for v in m) for m in re.findall(
-        r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", body)]
+    fields = r"X\(" + r",\s*".join([r"(\d+)"] * (5 if mx else 6)) + r"\)"
+    return [tuple(int(v) for v in m) for m in re.findall(fields, body)]
 
 
 SKINNY_VARIANTS = skinny_configs()
@@ -130,13 +131,16 @@ def _table(resources):
             elif plain and mx and key in MX_TILE_VARIANTS:
                 mx_tile[MX_TILE_VARIANTS.index(key)] = _entry("mxtile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
-        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E", mangled)
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E",
+                      mangled)
         if m:
             key = tuple(int(g) for g in m.groups()[:5])
+            al, plain, mx = int(m.group(6)), m.group(7) == "0", m.group(8) == "1"
             label = (16 * key[0], 16 * key[1]) + key[2:]
-            if m.group(6) == "0" and m.group(7) == "0" and key in SKINNY_VARIANTS:
-                skinny[SKINNY_VARIANTS.index(key)] = _entry("skinny_m%d_n%d_w%d_u%d_c%d" % label, r)
-            elif m.group(6) == "0" and m.group(7) == "1" and key in MX_SKINNY_VARIANTS:
+            if plain and not mx and key + (al,) in SKINNY_VARIANTS:
+                skinny[SKINNY_VARIANTS.index(key + (al,))] = _entry(
+                    "skinny_m%d_n%d_w%d_u%d_c%d" % label + ("_lds" if al else ""), r)
+            elif plain and mx and key in MX_SKINNY_VARIANTS:
                 mx_skinny[MX_SKINNY_VARIANTS.index(key)] = _entry("mxskinny_m%d_n%d_w%d_u%d_c%d" % label, r)
             continue
         if "generic_kernel" in mangled:

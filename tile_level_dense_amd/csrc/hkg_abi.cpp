@@ -30,6 +30,10 @@ constexpr int kNumCUs = 256;
 // N = 12288 27 vs 42 us; at M = 16, N = K = 4096 the skinny kernel leads,
 // 11.1 vs 11.6 us.
 constexpr int64_t kSkinnyMaxM = 16;
+// The skinny kernel stages A through LDS above this many rows (one 16-row
+// block): at N = K = 4096 on MI355X, M = 16 10.5 vs 11.0 us with the direct
+// fragment loads, M = 8 10.1 vs 9.6 us, M = 1 9.6 vs 8.8 us.
+constexpr int64_t kSkinnyLdsMinM = 8;
 // Largest split-K factor of the tile kernel.
 constexpr int64_t kMaxTileSplit = 16;
 
@@ -318,8 +322,8 @@ void fill_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N
     p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
     p->lds_bytes = skinny_lds_bytes(variant);
     fill_resources(p, skinny_resources(variant));
-    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d_n%d_w%d_u%d_c%d", 16 * s.mblocks,
-                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy);
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "skinny_m%d_n%d_w%d_u%d_c%d%s", 16 * s.mblocks,
+                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy, s.a_lds ? "_lds" : "");
     std::snprintf(p->reason, sizeof p->reason, "M <= %d; %lld column blocks of %d, split-K %lld%s%s",
                   (int)kSkinnyMaxM, (long long)col_blocks, 16 * s.nblocks, (long long)split, why ? "; " : "",
                   why ? why : "");
@@ -328,14 +332,19 @@ void fill_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N
 void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
     // Smallest A coverage (16-row blocks) that holds M; one B block per
-    // workgroup; split K across workgroups only when the column blocks
-    // underfill the device, keeping at least 8 steps (256 k) per wave.
-    int variant = -1, best_mb = 1 << 30;
+    // workgroup; A through LDS when more than half of the 16-row block is
+    // filled (below that, rows past M read zero without fetching and the
+    // direct loads fetch less than the copies cost); split K across
+    // workgroups only when the column blocks underfill the device, keeping
+    // at least 8 steps (256 k) per wave.
+    const int want_lds = M > kSkinnyLdsMinM ? 1 : 0;
+    int variant = -1, best = 1 << 30;
     for (int v = 0; v < SKINNY_NUM_VARIANTS; ++v) {
         const SkinnyShape s = skinny_shape(v);
-        if (s.nblocks == 1 && 16 * (int64_t)s.mblocks >= M && s.mblocks < best_mb) {
+        const int rank = 2 * s.mblocks + (s.a_lds != want_lds);
+        if (s.nblocks == 1 && 16 * (int64_t)s.mblocks >= M && rank < best) {
             variant = v;
-            best_mb = s.mblocks;
+            best = rank;
         }
     }
     const SkinnyShape s = skinny_shape(variant);

@@ -55,7 +55,7 @@ constexpr int MX_SKINNY_NUM_VARIANTS = 0
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
 // rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.
 constexpr int SKINNY_NUM_VARIANTS = 0
-#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp) +1
+#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp, al) +1
     HKG_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
 #undef HKG_COUNT_SKINNY
     ;
@@ -73,7 +73,7 @@ int mx_tile_lds_bytes(int variant);
 // Bytes of the packed scales of `rows` rows (rows rounded up to 64).
 int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
 
-struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy; };
+struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy, a_lds; };
 SkinnyShape skinny_shape(int variant);
 SkinnyShape mx_skinny_shape(int variant);
 int skinny_lds_bytes(int variant);

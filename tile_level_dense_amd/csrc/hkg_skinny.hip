@@ -13,6 +13,12 @@
 //    each 16-row block of A (small, read from L2) is the second.  An A
 //    fragment feeds NB MFMAs, so covering more B rows per workgroup cuts
 //    the A bytes each compute unit must take in per B byte.
+//  * With one 16-row block of A (bf16), each wave stages its share of A
+//    through LDS: buffer -> LDS copies of 1 KB of consecutive row bytes per
+//    instruction, then fragment reads from LDS.  Read straight into
+//    registers, a fragment instruction touches 16 rows x 64 bytes, twice the
+//    cache lines per byte, and every compute unit reads all of A (as many
+//    bytes as its share of B) through its L1.
 //  * Waves reduce through LDS in a fixed order (the wave-level reduction
 //    followed by an LDS combine of the FlyDSL "Prebuilt kernels guide",
 //    section 1.1).  Workgroups that share a column block along K (split-K)
@@ -32,6 +38,7 @@
 #include <type_traits>
 
 #include "hkg_internal.h"
+#include "hkg_lds_copy.h"
 
 namespace hkg {
 namespace {
@@ -87,9 +94,10 @@ __device__ __forceinline__ void static_for(F&& f)
 // MB: 16-row blocks of A (M <= 16 MB).  NB: 16-row blocks of B per
 // workgroup.  WK: waves per workgroup, splitting K.  U: steps per chunk of
 // loads (32 k, MXFP8 128 k).  CP: cache-policy bits of the B loads (B is
-// streamed once).  MX: E4M3 operands with packed E8M0 scales PSA / PSB
-// (NAT: natural-layout scales, row stride K / 32 bytes).
-template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX, bool NAT>
+// streamed once).  AL: A staged through LDS (bf16, MB == 1).  MX: E4M3
+// operands with packed E8M0 scales PSA / PSB (NAT: natural-layout scales,
+// row stride K / 32 bytes).
+template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT>
 __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
@@ -106,6 +114,23 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
     __shared__ int last_flag;
+    // A through LDS (MB == 1, bf16): per wave two buffers of one chunk of A,
+    // 16 rows x AROW bytes; row r holds its 16-byte piece c at position
+    // c ^ a_swz(r), so 16 lanes reading one piece of 16 consecutive rows
+    // cover all 64 banks.
+    constexpr bool ALDS = AL;
+    static_assert(!AL || (!MX && MB == 1), "A through LDS: bf16, one 16-row block");
+    constexpr int AROW = U * SBY;                     // bytes of a row per chunk
+    constexpr int ACH = AROW / 16;                    // 16-byte pieces per row
+    constexpr int RPI = 1024 / AROW;                  // rows per copy instruction
+    constexpr int ABUF = 16 * AROW;
+    static_assert(!ALDS || (AROW <= 1024 && 1024 % AROW == 0), "a chunk row divides a copy instruction");
+    __shared__ __attribute__((aligned(16))) char a_lds[ALDS ? WK * 2 * ABUF : 16];
+    auto a_swz = [](int r) {
+        constexpr int RPB = AROW < 256 ? 256 / AROW : 1;  // rows per 64 banks
+        constexpr int SW = ACH < 16 ? ACH : 16;
+        return (r / RPB) % SW;
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,6 +159,7 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         (void*)((const char*)Bv + (size_t)n0 * b_rb), 0, (int)(rows_b * b_rb), kBufferWord3);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)Av, 0, (int)((uint32_t)M * a_rb), kBufferWord3);
+    const dma::i32x4 words_a = dma::rsrc_words(Av, (int)((uint32_t)M * a_rb));
     // MXFP8 scales: A's 16-row block i is byte i of the lane's dword of
     // group 0; B's block j is byte ((n0 + 16 j) / 16) % 4 of its group's dword.
     // Natural layout: rows past M (N) fall outside the range and read zero.
@@ -168,9 +194,35 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             return load16<P>(r, ok ? off : kOutOfRange);
         }
     };
+    // A through LDS: the chunk of U steps from step s into buffer abuf of
+    // this wave (U copies; the earlier fragment reads of that buffer have
+    // finished first), and its fragments out of the buffer.
+    auto copy_a_chunk = [&](int s, int abuf) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const char* dst = a_lds + (wave * 2 + abuf) * ABUF;
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int r = q * RPI + lane / ACH;
+            const int c = (lane % ACH) ^ a_swz(r);
+            const int step = s + c / 4;
+            const bool ok = step < s_end && step * SK + (c % 4) * 8 < K;
+            dma::copy_to_lds(words_a, dst + q * 1024,
+                             ok ? (uint32_t)r * a_rb + (uint32_t)step * SBY + (uint32_t)(c % 4) * 16u
+                                : kOutOfRange);
+        }
+    };
+    auto read_a_chunk = [&](int abuf, frag_t (&av)[U][MB]) {
+        const char* src = a_lds + (wave * 2 + abuf) * ABUF + lrow * AROW;
+        const int sw = a_swz(lrow);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            av[u][0] = *(const frag_t*)(src + ((4 * u + lgrp) ^ sw) * 16);
+    };
     constexpr int SWA = MX ? (NAT ? MB : 1) : 0, SWB = MX ? NB : 0;
-    auto load_chunk = [&](int s, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
+    auto load_chunk = [&](int s, int abuf, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
                           uint32_t (&sb)[U][SWB + 1]) {
+        if constexpr (ALDS)
+            copy_a_chunk(s, abuf);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
@@ -180,10 +232,12 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             for (int j = 0; j < NB; ++j)
                 bv[u][j] = load_frag(rb, lane_off_b + kb + (uint32_t)j * block16_b, ok,
                                      std::integral_constant<int, CP>{});
+            if constexpr (!ALDS) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok,
-                                     std::integral_constant<int, 0>{});
+                for (int i = 0; i < MB; ++i)
+                    av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok,
+                                         std::integral_constant<int, 0>{});
+            }
             if constexpr (NAT) {
                 // row r's dword of step s at byte (r KT + s) 4; this lane's
                 // scale is byte lgrp (shifted down when it is used)
@@ -238,29 +292,53 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     // Chunks c and c + 1 are in flight while chunk c is multiplied.  Empty
     // asm statements keep the compiler from sinking the next chunk's loads
     // below the current chunk's MFMAs (which would put one full memory round
-    // trip per chunk on the critical path).
+    // trip per chunk on the critical path).  (The compiler's own waits count
+    // a conditionally loaded chunk as not issued, so past the first two
+    // chunks they also drain the next chunk before the current one's last
+    // MFMA; loading past the end unconditionally to keep its counts exact
+    // measured slower, 11.8 vs 10.4 us at 16 x 4096 x 4096: out-of-range
+    // loads still cost their issue and return.)
     auto fence = [] { asm volatile("" ::: "memory"); };
+    // A through LDS: a chunk's A copies are issued before its B loads, and
+    // chunk c + 1 (if any) before chunk c is multiplied, so waiting for the
+    // copies of chunk c leaves its B loads and chunk c + 1 in flight.
+    auto wait_a = [&](bool next) {
+        if constexpr (ALDS) {
+            if (next)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NB * U + U) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NB * U) : "memory");
+        }
+    };
     frag_t b0[U][NB], a0[U][MB], b1[U][NB], a1[U][MB];
     uint32_t sa0[U][SWA + 1], sb0[U][SWB + 1], sa1[U][SWA + 1], sb1[U][SWB + 1];
     const int nch = (s_end - s_begin + U - 1) / U;
     if (nch > 0) {
-        load_chunk(s_begin, b0, a0, sa0, sb0);
+        load_chunk(s_begin, 0, b0, a0, sa0, sb0);
         fence();
         if (nch > 1)
-            load_chunk(s_begin + U, b1, a1, sa1, sb1);
+            load_chunk(s_begin + U, 1, b1, a1, sa1, sb1);
         fence();
         for (int c = 0; c < nch; c += 2) {
+            if constexpr (ALDS) {
+                wait_a(c + 1 < nch);
+                read_a_chunk(0, a0);
+            }
             mfma_chunk(b0, a0, sa0, sb0);
             fence();
             if (c + 2 < nch)
-                load_chunk(s_begin + (c + 2) * U, b0, a0, sa0, sb0);
+                load_chunk(s_begin + (c + 2) * U, 0, b0, a0, sa0, sb0);
             fence();
             if (c + 1 >= nch)      // odd chunk count: buffer 1 holds an old chunk
                 break;
+            if constexpr (ALDS) {
+                wait_a(c + 2 < nch);
+                read_a_chunk(1, a1);
+            }
             mfma_chunk(b1, a1, sa1, sb1);
             fence();
             if (c + 3 < nch)
-                load_chunk(s_begin + (c + 3) * U, b1, a1, sa1, sb1);
+                load_chunk(s_begin + (c + 3) * U, 1, b1, a1, sa1, sb1);
             fence();
         }
     }
@@ -344,13 +422,13 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int U, int CP, bool EPI, bool MX, bool NAT>
+template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT>
 hipError_t launch_skinny_t(const void* A, const void* B, uint16_t* C, int M, int N, int K, int split_k, float* ws,
                            int* counters, const uint16_t* bias, int epi, int lda, int ldb, int ldc,
                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, EPI, MX, NAT>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, AL, EPI, MX, NAT>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
                        stream, A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc, psa, psb);
     return hipGetLastError();
 }
@@ -360,18 +438,19 @@ hipError_t launch_skinny_t(const void* A, const void* B, uint16_t* C, int M, int
 SkinnyShape skinny_shape(int variant)
 {
     int v = 0;
-#define HKG_SHAPE(mb, nb, wk, u, cp) \
-    if (v++ == variant)              \
-        return SkinnyShape{mb, nb, wk, u, cp};
+#define HKG_SHAPE(mb, nb, wk, u, cp, al) \
+    if (v++ == variant)                  \
+        return SkinnyShape{mb, nb, wk, u, cp, al};
     HKG_SKINNY_CONFIGS(HKG_SHAPE)
 #undef HKG_SHAPE
-    return SkinnyShape{0, 0, 0, 0, 0};
+    return SkinnyShape{0, 0, 0, 0, 0, 0};
 }
 
 int skinny_lds_bytes(int variant)
 {
     const SkinnyShape s = skinny_shape(variant);
-    return s.waves * s.mblocks * s.nblocks * 64 * 16 + 4;
+    const int a_bufs = s.a_lds ? s.waves * 2 * 16 * s.unroll * 64 : 0;   // A through LDS
+    return s.waves * s.mblocks * s.nblocks * 64 * 16 + a_bufs + 4;
 }
 
 hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint16_t* C,
@@ -379,15 +458,15 @@ hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint
                          const uint16_t* bias, int epi, int lda, int ldb, int ldc, hipStream_t stream)
 {
     int v = 0;
-#define HKG_LAUNCH(mb, nb, wk, u, cp) \
-    if (v++ == variant)               \
+#define HKG_LAUNCH(mb, nb, wk, u, cp, al)                                                                          \
+    if (v++ == variant)                                                                                       \
         return epi == EPI_NONE                                                                                \
-                   ? launch_skinny_t<mb, nb, wk, u, cp, false, false, false>(A, B, C, M, N, K, split_k, ws,      \
-                                                                             counters, bias, epi, lda, ldb, ldc, \
-                                                                             nullptr, nullptr, stream)           \
-                   : launch_skinny_t<mb, nb, wk, u, cp, true, false, false>(A, B, C, M, N, K, split_k, ws,       \
-                                                                            counters, bias, epi, lda, ldb, ldc,  \
-                                                                            nullptr, nullptr, stream);
+                   ? launch_skinny_t<mb, nb, wk, u, cp, al, false, false, false>(A, B, C, M, N, K, split_k, ws,  \
+                                                                                 counters, bias, epi, lda, ldb,  \
+                                                                                 ldc, nullptr, nullptr, stream)  \
+                   : launch_skinny_t<mb, nb, wk, u, cp, al, true, false, false>(A, B, C, M, N, K, split_k, ws,   \
+                                                                                counters, bias, epi, lda, ldb,   \
+                                                                                ldc, nullptr, nullptr, stream);
     HKG_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
@@ -398,10 +477,10 @@ SkinnyShape mx_skinny_shape(int variant)
     int v = 0;
 #define HKG_SHAPE(mb, nb, wk, u, cp) \
     if (v++ == variant)              \
-        return SkinnyShape{mb, nb, wk, u, cp};
+        return SkinnyShape{mb, nb, wk, u, cp, 0};
     HKG_MX_SKINNY_CONFIGS(HKG_SHAPE)
 #undef HKG_SHAPE
-    return SkinnyShape{0, 0, 0, 0, 0};
+    return SkinnyShape{0, 0, 0, 0, 0, 0};
 }
 
 hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
@@ -410,12 +489,10 @@ hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uin
 {
     int v = 0;
 #define HKG_LAUNCH_NAT(mb, nb, wk, u, cp, nat)                                                                    \
-    return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, false, true, nat>(A, B, C, M, N, K, split_k, ws,  \
-                                                                                  counters, bias, epi, K, K, N,   \
-                                                                                  psa, psb, stream)               \
-                           : launch_skinny_t<mb, nb, wk, u, cp, true, true, nat>(A, B, C, M, N, K, split_k, ws,   \
-                                                                                 counters, bias, epi, K, K, N,    \
-                                                                                 psa, psb, stream);
+    return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, false, false, true, nat>(                         \
+                                 A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream)   \
+                           : launch_skinny_t<mb, nb, wk, u, cp, false, true, true, nat>(                          \
+                                 A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream);
 #define HKG_LAUNCH(mb, nb, wk, u, cp)              \
     if (v++ == variant) {                          \
         if (natural)                               \

@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "hkg_internal.h"
+#include "hkg_lds_copy.h"
 #include "hkg_tile_order.h"
 
 namespace hkg {
@@ -102,33 +103,8 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
-// The 128-bit buffer descriptor of __builtin_amdgcn_make_buffer_rsrc(p, 0,
-// bytes, kBufferWord3), as four dwords (base, base high bits with stride 0,
-// range, word 3).
-__device__ __forceinline__ i32x4 rsrc_words(const void* p, int bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes, kBufferWord3};
-}
-
-// One buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
-// lane i's bytes at offset voff of the buffer land at LDS address lds + 16 i.
-// Written as inline asm so that the compiler does not order later LDS reads
-// after it: for the builtin it waits for every copy in flight (vmcnt(0))
-// before each LDS read it cannot prove disjoint, which leaves no copy in
-// flight across a K step.  Callers order reads after copies with their own
-// vmcnt waits and barriers.  M0 holds the LDS address; one wait state
-// separates its write from the copy.  M0 is not named as clobbered: the
-// compiler reserves it and sets it right before each of its own uses (the
-// kernels that use this helper have none).
-__device__ __forceinline__ void copy_to_lds(i32x4 rsrc, const char* lds, uint32_t voff)
-{
-    const uint32_t m0 = (uint32_t)(size_t)(lds_void*)lds;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voff), "s"(rsrc)
-                 : "memory");
-}
+using dma::copy_to_lds;
+using dma::rsrc_words;
 
 // Wait until at most N of this wave's buffer->LDS copies are in flight and
 // its LDS reads are done, then join the workgroup barrier.
