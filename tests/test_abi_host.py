@@ -371,8 +371,13 @@ def test_tile_order_chiplet_blocks(lib):
 @pytest.mark.parametrize("shape,kernel,variant,split", [
     ((8192, 8192, 8192), "MX_TILE", 0, 1),     # 32 x 32 ping-pong tiles fill the device
     ((4096, 4096, 12288), "MX_TILE", 0, 1),
-    ((32, 4096, 4096), "MX_SKINNY", 1, 1),     # decode: 256 column blocks of 16 already fill it
-    ((16, 2048, 4096), "MX_SKINNY", 0, 2),     # 128 column blocks: split 2 (at least 2 steps per wave)
+    ((32, 4096, 4096), "MX_SKINNY", 3, 1),     # decode: 256 column blocks of 16 already fill it
+    ((16, 2048, 4096), "MX_SKINNY", 2, 2),     # 128 column blocks: split 2 (at least 2 steps per wave)
+    # A through LDS (variants 2, 3) once M fills more than half of the
+    # cover: 16-row cover up to 16 rows, 32-row cover above
+    ((8, 4096, 4096), "MX_SKINNY", 0, 1),
+    ((9, 4096, 4096), "MX_SKINNY", 2, 1),
+    ((17, 4096, 4096), "MX_SKINNY", 3, 1),
     ((33, 4096, 4096), "MX_TILE", 1, 8),       # above 32 rows: 32 tiles of 128 x 128, split to fill
     ((128, 12288, 4096), "MX_TILE", 1, 3),
     ((256, 256, 256), "MX_TILE", 1, 1),        # 4 tiles; K / 128 / 4 = 0 splits -> 1

@@ -70,7 +70,7 @@ def forced(hkg, variant, split=1):
     variant, "s<i>" the small-M (skinny) variant i."""
     from tile_level_dense_amd import build as hkg_build
     if isinstance(variant, str):
-        mb, nb, wk, u, cp = hkg_build.skinny_configs(mx=True)[int(variant[1:])]
+        mb, nb, wk, u, cp, al = hkg_build.skinny_configs(mx=True)[int(variant[1:])]
 
         def edit(p):
             assert p.M <= 16 * mb
@@ -137,6 +137,14 @@ CASES = [
     ("skinny32_ragged", (17, 260, 256), "s1", 1),
     ("skinny32_split2", (32, 512, 1024), "s1", 2),
     ("skinny32_one_row", (1, 70, 512), "s1", 3),
+    # the same covers with A staged through LDS
+    ("skinny16_lds_ragged", (13, 300, 1024), "s2", 1),
+    ("skinny16_lds_split3_short", (16, 48, 384), "s2", 3),
+    ("skinny16_lds_single", (1, 1, 128), "s2", 1),
+    ("skinny32_lds_ragged", (17, 260, 256), "s3", 1),
+    ("skinny32_lds_split5_uneven", (32, 100, 1792), "s3", 5),
+    ("skinny32_lds_long_k", (29, 64, 8192), "s3", 1),
+    ("planner_decode_32", (32, 1024, 4096), None, 1),
     ("planner_decode_small", (16, 2048, 4096), None, 1),
 ]
 
@@ -168,7 +176,8 @@ def _exact_inputs(M, N, K, seed):
 
 @pytest.mark.parametrize("variant,split,shape", [(0, 1, (256, 512, 512)), (1, 1, (200, 136, 512)),
                                                  (1, 4, (64, 256, 1024)), ("s0", 1, (16, 256, 512)),
-                                                 ("s1", 4, (32, 272, 1024))])
+                                                 ("s1", 4, (32, 272, 1024)), ("s2", 2, (16, 256, 512)),
+                                                 ("s3", 1, (32, 272, 1024))])
 def test_mx_exact_inputs_bit_exact(hkg, variant, split, shape):
     M, N, K = shape
     _say("exact", variant, split, shape)

@@ -47,13 +47,12 @@ TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
 GROUPED_VARIANTS = tile_configs(grouped=True)
 def skinny_configs(mx=False):
-    """(MB, NB, WK, U, CP, AL) per skinny variant, or (MB, NB, WK, U, CP) per MXFP8
-    skinny variant with mx=True, from hkg_skinny_configs.h."""
+    """(MB, NB, WK, U, CP, AL) per skinny variant (MXFP8 with mx=True), from hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
     body = text[text.index("#define HKG_MX_SKINNY_CONFIGS(X)" if mx else "#define HKG_SKINNY_CONFIGS(X)"):]
     end = body.find("#define", 10)
     body = body if end < 0 else body[:end]
-    fields = r"X\(" + r",\s*".join([r"(\d+)"] * (5 if mx else 6)) + r"\)"
+    fields = r"X\(" + r",\s*".join([r"(\d+)"] * 6) + r"\)"
     return [tuple(int(v) for v in m) for m in re.findall(fields, body)]
 
 
@@ -140,8 +139,9 @@ def _table(resources):
             if plain and not mx and key + (al,) in SKINNY_VARIANTS:
                 skinny[SKINNY_VARIANTS.index(key + (al,))] = _entry(
                     "skinny_m%d_n%d_w%d_u%d_c%d" % label + ("_lds" if al else ""), r)
-            elif plain and mx and key in MX_SKINNY_VARIANTS:
-                mx_skinny[MX_SKINNY_VARIANTS.index(key)] = _entry("mxskinny_m%d_n%d_w%d_u%d_c%d" % label, r)
+            elif plain and mx and key + (al,) in MX_SKINNY_VARIANTS:
+                mx_skinny[MX_SKINNY_VARIANTS.index(key + (al,))] = _entry(
+                    "mxskinny_m%d_n%d_w%d_u%d_c%d" % label + ("_lds" if al else ""), r)
             continue
         if "generic_kernel" in mangled:
             generic = _entry("generic", r)

@@ -679,10 +679,10 @@ void fill_mx_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_
     p->xcd_window_w = 0;
     p->xcd_chunk_c = 0;
     p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
-    p->lds_bytes = s.waves * s.mblocks * s.nblocks * 64 * 16 + 4;
+    p->lds_bytes = mx_skinny_lds_bytes(variant);
     fill_resources(p, mx_skinny_resources(variant));
-    std::snprintf(p->kernel_name, sizeof p->kernel_name, "mxskinny_m%d_n%d_w%d_u%d_c%d", 16 * s.mblocks,
-                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy);
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "mxskinny_m%d_n%d_w%d_u%d_c%d%s", 16 * s.mblocks,
+                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy, s.a_lds ? "_lds" : "");
     std::snprintf(p->reason, sizeof p->reason, "MXFP8, M <= %d: %lld column blocks of %d, split-K %lld",
                   16 * s.mblocks, (long long)col_blocks, 16 * s.nblocks, (long long)split);
 }
@@ -721,12 +721,21 @@ hkg_status_t make_mx_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     if (!mx_shape_supported(M, N, K))
         return HKG_ERR_UNSUPPORTED;
     // Decode shapes: the skinny kernel streams B once (smallest A cover that
-    // holds M), split across workgroups only when the column blocks leave
-    // compute units idle, keeping at least 2 steps of 128 k per wave.
+    // holds M; A through LDS when M fills more than half of it), split
+    // across workgroups only when the column blocks leave compute units
+    // idle, keeping at least 2 steps of 128 k per wave.
+    int mx_variant = -1, mx_best = 1 << 30;
     for (int v = 0; v < MX_SKINNY_NUM_VARIANTS; ++v) {
         const SkinnyShape ss = mx_skinny_shape(v);
-        if (M > 16 * (int64_t)ss.mblocks)
-            continue;
+        const int rank = 2 * ss.mblocks + (ss.a_lds != (M > 8 * (int64_t)ss.mblocks ? 1 : 0));
+        if (M <= 16 * (int64_t)ss.mblocks && rank < mx_best) {
+            mx_variant = v;
+            mx_best = rank;
+        }
+    }
+    if (mx_variant >= 0) {
+        const int v = mx_variant;
+        const SkinnyShape ss = mx_skinny_shape(v);
         const int64_t col_blocks = cdiv(N, 16 * ss.nblocks);
         int64_t split = 1;
         if (col_blocks < kNumCUs) {

@@ -47,7 +47,7 @@ constexpr int STREAM_TILES[] = {8, 10, 9, 7};
 
 // MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
 constexpr int MX_SKINNY_NUM_VARIANTS = 0
-#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp) +1
+#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp, al) +1
     HKG_MX_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
 #undef HKG_COUNT_SKINNY
     ;
@@ -77,6 +77,7 @@ struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy, a_lds; }
 SkinnyShape skinny_shape(int variant);
 SkinnyShape mx_skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
+int mx_skinny_lds_bytes(int variant);
 
 // Launchers: enqueue one kernel on `stream`; return the launch error.
 // Every launcher takes the fused epilogue (`epi`, an EPI_* code, and `bias`,

@@ -114,17 +114,20 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
     __shared__ int last_flag;
-    // A through LDS (MB == 1, bf16): per wave two buffers of one chunk of A,
-    // 16 rows x AROW bytes; row r holds its 16-byte piece c at position
-    // c ^ a_swz(r), so 16 lanes reading one piece of 16 consecutive rows
-    // cover all 64 banks.
+    // A through LDS: per wave two buffers of one chunk of A, 16 MB rows x
+    // AROW bytes; row r holds its 16-byte piece c at position c ^ a_swz(r),
+    // so 16 lanes reading one piece of 16 consecutive rows cover all 64
+    // banks.  NCOPY copies of 1 KB fill a buffer.
     constexpr bool ALDS = AL;
-    static_assert(!AL || (!MX && MB == 1), "A through LDS: bf16, one 16-row block");
+    static_assert(!AL || MB <= 2, "A through LDS: one or two 16-row blocks");
     constexpr int AROW = U * SBY;                     // bytes of a row per chunk
     constexpr int ACH = AROW / 16;                    // 16-byte pieces per row
+    constexpr int PPS = SBY / 16;                     // pieces per step
     constexpr int RPI = 1024 / AROW;                  // rows per copy instruction
-    constexpr int ABUF = 16 * AROW;
+    constexpr int ABUF = 16 * MB * AROW;
+    constexpr int NCOPY = ABUF / 1024;
     static_assert(!ALDS || (AROW <= 1024 && 1024 % AROW == 0), "a chunk row divides a copy instruction");
+    static_assert(!ALDS || WK * 2 * ABUF + WK * NBLK * 1024 <= 160 * 1024, "LDS is 160 KiB per CU");
     __shared__ __attribute__((aligned(16))) char a_lds[ALDS ? WK * 2 * ABUF : 16];
     auto a_swz = [](int r) {
         constexpr int RPB = AROW < 256 ? 256 / AROW : 1;  // rows per 64 banks
@@ -195,28 +198,40 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         }
     };
     // A through LDS: the chunk of U steps from step s into buffer abuf of
-    // this wave (U copies; the earlier fragment reads of that buffer have
-    // finished first), and its fragments out of the buffer.
+    // this wave (NCOPY copies; the earlier fragment reads of that buffer
+    // have finished first), and its fragments out of the buffer: piece
+    // PPS u + g of the row for bf16, pieces PPS u + g and PPS u + 4 + g for
+    // the two halves of an MXFP8 operand (g = lane / 16).
     auto copy_a_chunk = [&](int s, int abuf) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const char* dst = a_lds + (wave * 2 + abuf) * ABUF;
 #pragma unroll
-        for (int q = 0; q < U; ++q) {
+        for (int q = 0; q < NCOPY; ++q) {
             const int r = q * RPI + lane / ACH;
             const int c = (lane % ACH) ^ a_swz(r);
-            const int step = s + c / 4;
-            const bool ok = step < s_end && step * SK + (c % 4) * 8 < K;
+            const int step = s + c / PPS;
+            const bool ok = step < s_end && step * SK + (c % PPS) * (16 / EB) < K;
             dma::copy_to_lds(words_a, dst + q * 1024,
-                             ok ? (uint32_t)r * a_rb + (uint32_t)step * SBY + (uint32_t)(c % 4) * 16u
+                             ok ? (uint32_t)r * a_rb + (uint32_t)step * SBY + (uint32_t)(c % PPS) * 16u
                                 : kOutOfRange);
         }
     };
     auto read_a_chunk = [&](int abuf, frag_t (&av)[U][MB]) {
-        const char* src = a_lds + (wave * 2 + abuf) * ABUF + lrow * AROW;
-        const int sw = a_swz(lrow);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            av[u][0] = *(const frag_t*)(src + ((4 * u + lgrp) ^ sw) * 16);
+        for (int i = 0; i < MB; ++i) {
+            const char* src = a_lds + (wave * 2 + abuf) * ABUF + (16 * i + lrow) * AROW;
+            const int sw = a_swz(16 * i + lrow);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if constexpr (MX) {
+                    const i32x4 lo = *(const i32x4*)(src + ((PPS * u + lgrp) ^ sw) * 16);
+                    const i32x4 hi = *(const i32x4*)(src + ((PPS * u + 4 + lgrp) ^ sw) * 16);
+                    av[u][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    av[u][i] = *(const frag_t*)(src + ((PPS * u + lgrp) ^ sw) * 16);
+                }
+            }
+        }
     };
     constexpr int SWA = MX ? (NAT ? MB : 1) : 0, SWB = MX ? NB : 0;
     auto load_chunk = [&](int s, int abuf, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
@@ -302,12 +317,16 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     // A through LDS: a chunk's A copies are issued before its B loads, and
     // chunk c + 1 (if any) before chunk c is multiplied, so waiting for the
     // copies of chunk c leaves its B loads and chunk c + 1 in flight.
+    // Vector-memory instructions a chunk issues after its A copies: B (two
+    // per fragment for MXFP8) and the scale dwords.
+    constexpr int LPC = U * (NB * (MX ? 2 : 1) + (MX ? SWA + SWB : 0));
+    static_assert(2 * LPC + NCOPY <= 63, "vmcnt holds at most 63");
     auto wait_a = [&](bool next) {
         if constexpr (ALDS) {
             if (next)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NB * U + U) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPC + NCOPY) : "memory");
             else
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NB * U) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPC) : "memory");
         }
     };
     frag_t b0[U][NB], a0[U][MB], b1[U][NB], a1[U][MB];
@@ -475,12 +494,19 @@ hipError_t launch_skinny(int variant, const uint16_t* A, const uint16_t* B, uint
 SkinnyShape mx_skinny_shape(int variant)
 {
     int v = 0;
-#define HKG_SHAPE(mb, nb, wk, u, cp) \
-    if (v++ == variant)              \
-        return SkinnyShape{mb, nb, wk, u, cp, 0};
+#define HKG_SHAPE(mb, nb, wk, u, cp, al) \
+    if (v++ == variant)                  \
+        return SkinnyShape{mb, nb, wk, u, cp, al};
     HKG_MX_SKINNY_CONFIGS(HKG_SHAPE)
 #undef HKG_SHAPE
     return SkinnyShape{0, 0, 0, 0, 0, 0};
+}
+
+int mx_skinny_lds_bytes(int variant)
+{
+    const SkinnyShape s = mx_skinny_shape(variant);
+    const int a_bufs = s.a_lds ? s.waves * 2 * 16 * s.mblocks * s.unroll * 128 : 0;   // A through LDS
+    return s.waves * s.mblocks * s.nblocks * 64 * 16 + a_bufs + 4;
 }
 
 hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
@@ -488,16 +514,16 @@ hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uin
                             const uint32_t* psa, const uint32_t* psb, bool natural, hipStream_t stream)
 {
     int v = 0;
-#define HKG_LAUNCH_NAT(mb, nb, wk, u, cp, nat)                                                                    \
-    return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, false, false, true, nat>(                         \
+#define HKG_LAUNCH_NAT(mb, nb, wk, u, cp, al, nat)                                                              \
+    return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, al, false, true, nat>(                            \
                                  A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream)   \
-                           : launch_skinny_t<mb, nb, wk, u, cp, false, true, true, nat>(                          \
+                           : launch_skinny_t<mb, nb, wk, u, cp, al, true, true, nat>(                             \
                                  A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream);
-#define HKG_LAUNCH(mb, nb, wk, u, cp)              \
-    if (v++ == variant) {                          \
-        if (natural)                               \
-            HKG_LAUNCH_NAT(mb, nb, wk, u, cp, true) \
-        HKG_LAUNCH_NAT(mb, nb, wk, u, cp, false)   \
+#define HKG_LAUNCH(mb, nb, wk, u, cp, al)              \
+    if (v++ == variant) {                              \
+        if (natural)                                   \
+            HKG_LAUNCH_NAT(mb, nb, wk, u, cp, al, true) \
+        HKG_LAUNCH_NAT(mb, nb, wk, u, cp, al, false)   \
     }
     HKG_MX_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH

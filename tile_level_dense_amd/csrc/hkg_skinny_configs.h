@@ -5,8 +5,8 @@
 //   WK   waves per workgroup, splitting the workgroup's K range
 //   U    32-k steps per chunk of loads (two chunks in flight per wave)
 //   CP   cache-policy bits of the streamed B loads (0 default, 2 non-temporal)
-//   AL   1: A staged through LDS by 1 KB copies (MB == 1 only); 0: A
-//        fragments loaded straight into registers
+//   AL   1: A staged through LDS by 1 KB copies (MB <= 2); 0: A fragments
+//        loaded straight into registers
 // The build script reads this list to map code objects to variants.
 #pragma once
 
@@ -23,7 +23,9 @@
     X(8, 2, 8, 1, 0, 0)       \
     X(1, 1, 8, 8, 0, 1)
 
-// MXFP8 instantiations, the first five fields; U counts steps of 128 k.
+// MXFP8 instantiations, same fields; U counts steps of 128 k.
 #define HKG_MX_SKINNY_CONFIGS(X) \
-    X(1, 1, 8, 4, 0)             \
-    X(2, 1, 8, 2, 0)
+    X(1, 1, 8, 4, 0, 0)          \
+    X(2, 1, 8, 2, 0, 0)          \
+    X(1, 1, 8, 4, 0, 1)          \
+    X(2, 1, 8, 2, 0, 1)
