@@ -48,6 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -234,10 +236,17 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         }
     };
     constexpr int SWA = MX ? (NAT ? MB : 1) : 0, SWB = MX ? NB : 0;
+    constexpr bool NAT_RUN_CHUNK = NAT && AL && (U == 2 || U == 4);
     auto load_chunk = [&](int s, int abuf, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
                           uint32_t (&sb)[U][SWB + 1]) {
         if constexpr (ALDS)
             copy_a_chunk(s, abuf);
+        // Natural-layout scales (A through LDS): when the chunk's steps lie
+        // inside the row, one 4 U-byte load per row takes them all (steps
+        // past the wave's range are zeroed: their data reads zero);
+        // otherwise a dword per row and step.
+        constexpr bool NAT_RUN = NAT_RUN_CHUNK;
+        const bool run = NAT_RUN && s + U <= KT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
@@ -256,14 +265,16 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             if constexpr (NAT) {
                 // row r's dword of step s at byte (r KT + s) 4; this lane's
                 // scale is byte lgrp (shifted down when it is used)
+                if (!run) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    sa[u][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rsa, ok ? (uint32_t)((16 * i + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+                    for (int i = 0; i < MB; ++i)
+                        sa[u][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rsa, ok ? (uint32_t)((16 * i + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rsb, ok ? (uint32_t)((n0 + 16 * j + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+                    for (int j = 0; j < NB; ++j)
+                        sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rsb, ok ? (uint32_t)((n0 + 16 * j + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+                }
             } else if constexpr (MX) {
                 const uint32_t st = (uint32_t)step * 256u + (uint32_t)lane * 4u;
                 sa[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, ok ? st : kOutOfRange, 0, 0);
@@ -273,6 +284,33 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                     sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
                         rsb, ok ? (uint32_t)((row / 64) * KT) * 256u + st : kOutOfRange, 0, 0);
                 }
+            }
+        }
+        if constexpr (NAT_RUN) {
+            if (run) {
+                auto take = [&](__amdgpu_buffer_rsrc_t r, int row, auto&& put) {
+                    const uint32_t off = (uint32_t)(row * KT + s) * 4u;
+                    uint32_t w[U];
+                    if constexpr (U == 4) {
+                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            w[u] = v[u];
+                    } else {
+                        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+                        w[0] = v[0];
+                        w[1] = v[1];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        put(u, s + u < s_end ? w[u] : 0u);
+                };
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    take(rsa, 16 * i + lrow, [&](int u, uint32_t x) { sa[u][i] = x; });
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    take(rsb, n0 + 16 * j + lrow, [&](int u, uint32_t x) { sb[u][j] = x; });
             }
         }
     };
@@ -318,8 +356,11 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     // chunk c + 1 (if any) before chunk c is multiplied, so waiting for the
     // copies of chunk c leaves its B loads and chunk c + 1 in flight.
     // Vector-memory instructions a chunk issues after its A copies: B (two
-    // per fragment for MXFP8) and the scale dwords.
-    constexpr int LPC = U * (NB * (MX ? 2 : 1) + (MX ? SWA + SWB : 0));
+    // per fragment for MXFP8) and the scale loads (the fewest a chunk can
+    // issue: natural scales may come as one load per row; a chunk that
+    // issues more only makes this wait stricter).
+    constexpr int SCL = !MX ? 0 : NAT_RUN_CHUNK ? SWA + SWB : U * (SWA + SWB);
+    constexpr int LPC = U * NB * (MX ? 2 : 1) + SCL;
     static_assert(2 * LPC + NCOPY <= 63, "vmcnt holds at most 63");
     auto wait_a = [&](bool next) {
         if constexpr (ALDS) {
