@@ -30,10 +30,6 @@ constexpr int kNumCUs = 256;
 // N = 12288 27 vs 42 us; at M = 16, N = K = 4096 the skinny kernel leads,
 // 11.1 vs 11.6 us.
 constexpr int64_t kSkinnyMaxM = 16;
-// The skinny kernel stages A through LDS above this many rows (one 16-row
-// block): at N = K = 4096 on MI355X, M = 16 10.5 vs 11.0 us with the direct
-// fragment loads, M = 8 10.1 vs 9.6 us, M = 1 9.6 vs 8.8 us.
-constexpr int64_t kSkinnyLdsMinM = 8;
 // Largest split-K factor of the tile kernel.
 constexpr int64_t kMaxTileSplit = 16;
 
@@ -332,16 +328,15 @@ void fill_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N
 void plan_skinny(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
     // Smallest A coverage (16-row blocks) that holds M; one B block per
-    // workgroup; A through LDS when more than half of the 16-row block is
-    // filled (below that, rows past M read zero without fetching and the
-    // direct loads fetch less than the copies cost); split K across
-    // workgroups only when the column blocks underfill the device, keeping
-    // at least 8 steps (256 k) per wave.
-    const int want_lds = M > kSkinnyLdsMinM ? 1 : 0;
+    // workgroup; A through LDS where a variant stages it (the 16-row cover:
+    // at N = K = 4096 on MI355X, 9.9 vs 11.0 us with the direct fragment
+    // loads at M = 16, 9.2 vs 9.6 at M = 8, 8.9 vs 8.8 at M = 1); split K
+    // across workgroups only when the column blocks underfill the device,
+    // keeping at least 8 steps (256 k) per wave.
     int variant = -1, best = 1 << 30;
     for (int v = 0; v < SKINNY_NUM_VARIANTS; ++v) {
         const SkinnyShape s = skinny_shape(v);
-        const int rank = 2 * s.mblocks + (s.a_lds != want_lds);
+        const int rank = 2 * s.mblocks + (s.a_lds ? 0 : 1);
         if (s.nblocks == 1 && 16 * (int64_t)s.mblocks >= M && rank < best) {
             variant = v;
             best = rank;

@@ -21,7 +21,7 @@
     X(2, 4, 8, 2, 0, 0)       \
     X(4, 2, 8, 2, 0, 0)       \
     X(8, 2, 8, 1, 0, 0)       \
-    X(1, 1, 8, 8, 0, 1)
+    X(1, 1, 8, 4, 0, 1)
 
 // MXFP8 instantiations, same fields; U counts steps of 128 k.
 #define HKG_MX_SKINNY_CONFIGS(X) \
