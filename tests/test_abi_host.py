@@ -91,7 +91,7 @@ def test_status_strings(lib):
 
 
 WORKLOAD_PLANS = {
-    (256, 256, 256): ("TILE", "tile_128x128x64_"),
+    (256, 256, 256): ("TILE", "tile_64x64x64_s4"),
     (16, 4096, 4096): ("SKINNY", "skinny_m16"),
     (128, 12288, 4096): ("TILE", "tile_128x64x64_s4"),
     (4096, 4096, 12288): ("TILE", "tile_256x256x64_"),
@@ -163,13 +163,19 @@ def test_plan_boundaries():
     p = hkg.plan(256, 12288, 4096)       # both unsplit: the larger tile
     assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 128, 1, 192)
     # tile grid under one workgroup per CU: split-K across workgroups,
-    # at least 4 k-tiles per split; the 128-row tile is skipped at M = 64
+    # at least 8 k-tiles per split; the 128-row tile is skipped at M = 64
     # (half its rows would be padding)
     p = hkg.plan(64, 4096, 4096)
     assert (p.tile_m, p.tile_n) == (64, 64) and p.grid_x == 64
     assert p.split_k == 4 and p.grid_y == 4 and p.workspace_bytes == 4 * 64 * 4096 * 4
-    p = hkg.plan(64, 4096, 512)
+    p = hkg.plan(64, 4096, 1024)
     assert p.split_k == 2
+    p = hkg.plan(64, 4096, 512)
+    assert p.split_k == 1
+    # equal splits: the smallest tile whose grid fits one workgroup per CU
+    for shape in [(256, 256, 256), (512, 512, 512), (1024, 1024, 1024)]:
+        p = hkg.plan(*shape)
+        assert (p.tile_m, p.tile_n, p.split_k) == (64, 64, 1), shape
     p = hkg.plan(64, 4096, 128)
     assert p.split_k == 1 and p.workspace_bytes == 0
     # compute-bound ladder: 256 x 256 from 3/4 of the CUs on, then the

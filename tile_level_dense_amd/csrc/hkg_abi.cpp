@@ -237,16 +237,21 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     // Smaller outputs: the operands are streamed from HBM a few times at most
     // and the kernel is bound by memory, so the grid should put one workgroup
     // with a deep copy pipeline on every compute unit.  For each streaming tile, split K so
-    // the grid stays within one workgroup per compute unit (at least 4 k-tiles
-    // per split; split-K adds fp32 partial traffic), then take the tile with
-    // the fewest splits, the larger tile on a tie (the taller one between
-    // 128 x 64 and 64 x 128).  A tile whose rows would be more than a quarter
-    // padding is skipped unless it is the last one.  Measured on MI355X:
-    // M = 128, N = 12288, K = 4096: 128 x 64 unsplit 35.9 us, 128 x 128 split
-    // 2 39.5 us, 64 x 64 unsplit 41.6 us; M = 256, N = K = 4096: 64 x 64
-    // unsplit 21.9 us, 128 x 64 split 2 22.6 us.
+    // the grid stays within one workgroup per compute unit (at least 8 k-tiles
+    // per split; split-K adds fp32 partial traffic and a reduction), then take
+    // the tile with the fewest splits; on a tie, the smallest tile whose grid
+    // still fits one workgroup per compute unit (each workgroup's chain of
+    // loads and MFMAs is then shortest), the taller one between 128 x 64 and
+    // 64 x 128.  A tile whose rows would be more than a quarter padding is
+    // skipped unless it is the last one.  Measured on MI355X: M = 128,
+    // N = 12288, K = 4096: 128 x 64 unsplit 35.9 us, 128 x 128 split 2
+    // 39.5 us, 64 x 64 unsplit (384 tiles) 41.6 us; M = 256, N = K = 4096:
+    // 64 x 64 unsplit 21.9 us, 128 x 64 split 2 22.6 us; 256^3: 64 x 64 3.8 us,
+    // 128 x 128 7.2 us; 512^3: 64 x 64 unsplit 5.1 us, split 2 6.7 us,
+    // 128 x 128 split 2 13.1 us.
     int best = -1;
-    int64_t best_split = 0;
+    int64_t best_split = 0, best_area = 0;
+    bool best_fits = false;
     const int n_stream = (int)(sizeof(STREAM_TILES) / sizeof(STREAM_TILES[0]));
     for (int i = 0; i < n_stream; ++i) {
         const int v = STREAM_TILES[i];
@@ -256,12 +261,17 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
             continue;
         int64_t split = 1;
         if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {   // fp32 partials addressed in 32 bits
-            split = std::min<int64_t>(kNumCUs / (tm * tn), cdiv(K, s.bk) / 4);
+            split = std::min<int64_t>(kNumCUs / (tm * tn), cdiv(K, s.bk) / 8);
             split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
         }
-        if (best < 0 || split < best_split) {
+        const bool fits = tm * tn <= kNumCUs;
+        const int64_t area = (int64_t)s.bm * s.bn;
+        if (best < 0 || split < best_split ||
+            (split == best_split && fits && (!best_fits || area < best_area))) {
             best = v;
             best_split = split;
+            best_area = area;
+            best_fits = fits;
         }
     }
     fill_tile(p, best, best_split, M, N);
