@@ -472,7 +472,7 @@ def main():
                     help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         return 2
     import torch
