@@ -179,6 +179,20 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     const uint32_t block16_a = 16u * a_rb;      // next 16 rows
     const uint32_t block16_b = 16u * b_rb;
 
+    // Fused epilogue: the bias of the first block this wave stores is loaded
+    // now, so its memory round trip overlaps the K loop instead of following
+    // the reduction.
+    float bias_pre[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI) {
+        if (split_k == 1 && wave < NBLK) {
+            const int n = n0 + (wave / MB) * 16 + lgrp * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N)
+                    bias_pre[r] = __uint_as_float((uint32_t)bias[n + r] << 16);
+        }
+    }
+
     f32x4 acc[NB][MB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -426,7 +440,8 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (n + r < N)
-                        sum[r] = epi_apply(sum[r], bias, n + r, epi);
+                        sum[r] = b == wave ? epi_activation(sum[r] + bias_pre[r], epi)
+                                           : epi_apply(sum[r], bias, n + r, epi);
             }
             const uint2 h = pack_bf16x4(sum);
             uint16_t* crow = C + (size_t)m * (size_t)ldc;
