@@ -29,17 +29,22 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* p, int bytes)
 // own vmcnt waits; callers wait for them explicitly, and the compiler's waits
 // for its own loads only become stricter by the copies issued after them.
 // M0 holds the LDS address; one wait state separates its write from the
-// copy.  M0 is not named as clobbered: the compiler reserves it and sets it
-// right before each of its own uses (the kernels that use this helper have
-// none).
+// copy.  M0 is named as clobbered, so the compiler re-establishes it before
+// any later use of its own (the buffer->LDS builtin and LDS-direct forms
+// also take their LDS address from M0).
+// (clang notes that M0 is a reserved register; the clobber still marks the
+// asm statement as defining it, which is what later M0 users need.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy_to_lds(i32x4 rsrc, const char* lds, uint32_t voff)
 {
     const uint32_t m0 = (uint32_t)(size_t)(lds_void*)lds;
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(voff), "s"(rsrc)
-                 : "memory");
+                 : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 }  // namespace dma
 }  // namespace hkg
