@@ -79,6 +79,26 @@ SkinnyShape mx_skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 int mx_skinny_lds_bytes(int variant);
 
+// Split-K arrival protocol (tile and skinny kernels).  Each workgroup of a
+// split writes its fp32 partials with agent-scope relaxed atomic stores or
+// buffer stores with the sc1 cache-policy bit (the same encoding the
+// compiler emits for agent-scope relaxed atomics on gfx950: written through
+// the XCD's L2 to the device coherence point), then every wave executes
+// s_waitcnt vmcnt(0), which on gfx9 counts stores too and returns only when
+// they are acknowledged at that point, and joins s_barrier.  Only then does
+// one lane count the workgroup's arrival with an agent-scope atomic add.  The
+// counter's modification order is device-wide, so the workgroup that sees
+// split_k - 1 earlier arrivals knows every other split's partials were
+// complete at the coherence point before their increments.  It reads them
+// with agent-scope (sc1) loads, which are served from that point rather than
+// from a possibly stale L1 or L2 line, and it issues them only after its own
+// atomic has returned: the returned value reaches every wave through LDS and
+// s_barrier before any load.  The argument rests on gfx9's completion
+// counters, not on C++ happens-before between relaxed atomics; a release /
+// acquire fence pair would give that too but writes back and invalidates
+// the whole L2 (measured about 8x slower).  The last arriver resets the
+// counter to zero, so counters are zero between calls on one stream.
+
 // Launchers: enqueue one kernel on `stream`; return the launch error.
 // Every launcher takes the fused epilogue (`epi`, an EPI_* code, and `bias`,
 // N bf16 values; bias is not read when epi == EPI_NONE).

@@ -468,7 +468,8 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     // partials in split order 0, 1, ... (deterministic) and rounds once.
     // Partials are written and read with device-scope accesses (coherent
     // across the XCDs' L2 caches without flushing them); every store has
-    // completed (vmcnt) before the workgroup's arrival is counted.
+    // completed (vmcnt) before the workgroup's arrival is counted (the
+    // ordering argument is the split-K arrival protocol in hkg_internal.h).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {

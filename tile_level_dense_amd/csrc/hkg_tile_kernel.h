@@ -655,7 +655,9 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // deterministic) and goes on to the rounding store below.  Partials
             // are written and read with device-scope (sc1) accesses, which are
             // coherent across the XCDs' L2 caches without flushing them; every
-            // store has completed (vmcnt) before the arrival is counted.
+            // store has completed (vmcnt) before the arrival is counted (the
+            // ordering argument is the split-K arrival protocol in
+            // hkg_internal.h).
             const int me = blockIdx.y;
             const bool vec4 = (N & 3) == 0;
             const int part_bytes = M * N * 4;          // below 2^31: checked by the planner
