@@ -27,17 +27,31 @@
  *   `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *   calls are asynchronous with respect to the host; faults inside a kernel
  *   surface at the caller's next synchronisation, as in HIP.
- *   The library keeps per-device state (device checks, split-K workspace)
- *   that it allocates on first use on a device and frees at unload.
+ *   The library keeps per-device state (device checks) and per-(device,
+ *   stream) workspaces: the split-K fp32 partials and arrival counters, the
+ *   packed scales of hkg_gemm_mxfp8 and the row-layout copies of
+ *   hkg_gemm_bf16_ex.  A workspace is allocated by the first call on that
+ *   stream that needs it (outside stream capture: growing one while the
+ *   stream is being captured returns HKG_ERR_WORKSPACE, so run a call once
+ *   before capturing it) and grows geometrically; an outgrown buffer is kept,
+ *   not freed, until the library is unloaded, because a launch in flight or
+ *   a captured graph may still use it.
  *
  * Errors
  *   Every argument check happens on the host, before any launch, and is
  *   reported as a status code; nothing is thrown across this ABI.
  *
  * Thread safety
- *   Calls may be made from several host threads and on several streams.
- *   Calls that use a split-K workspace on one device are serialised by
- *   stream order only if they share a stream; see hkg_plan_t.workspace_bytes.
+ *   Calls may be made from several host threads and on several streams at
+ *   once: each stream has its own workspaces, so calls on different streams
+ *   never share scratch, and calls on one stream are ordered by the stream.
+ *   (hipStreamPerThread has one workspace per host thread.)  Two cases do
+ *   share scratch: a graph captured on stream S uses S's workspace when it
+ *   is replayed, so it must not be replayed concurrently with other calls on
+ *   S or with another replay of a graph captured on S; and a stream handle
+ *   reused after hipStreamDestroy gets the old stream's workspace, so the old
+ *   stream's work must have finished first.  Plans are computed per call;
+ *   there is no shared plan cache.
  */
 #ifndef HKG_H
 #define HKG_H
@@ -59,7 +73,8 @@ typedef enum {
     HKG_ERR_NO_DEVICE = -4,     /* no HIP device is visible */
     HKG_ERR_ARCH = -5,          /* the current device is not gfx950 */
     HKG_ERR_HIP = -6,           /* a HIP runtime call or launch failed; see hkg_last_hip_error */
-    HKG_ERR_WORKSPACE = -7      /* a library workspace (split-K partials, packed MXFP8 scales) could not be allocated */
+    HKG_ERR_WORKSPACE = -7      /* a library workspace (split-K partials, packed MXFP8 scales, layout copies)
+                                   could not be allocated, or would have to grow while the stream is captured */
 } hkg_status_t;
 
 typedef enum {
@@ -108,7 +123,7 @@ typedef struct {
     int32_t grid_x, grid_y, grid_z, block_x;
     int32_t xcd_window_w;       /* tile-order window height W (tile rows), 0 = plain row-major order */
     int32_t xcd_chunk_c;        /* consecutive tiles kept on one chiplet (XCD), 0 = no de-interleave */
-    int64_t workspace_bytes;    /* library-owned fp32 workspace this plan uses, 0 if none */
+    int64_t workspace_bytes;    /* library-owned fp32 workspace this plan uses (per stream), 0 if none */
     int32_t lds_bytes;          /* LDS per workgroup */
     int32_t vgprs, agprs, sgprs, scratch_bytes;   /* resource use of the kernel's code object (build-time) */
     int64_t M, N, K;            /* the shape this plan was made for */
@@ -204,9 +219,8 @@ hkg_status_t hkg_gemm_bf16_run_plan_epilogue(const hkg_plan_t* plan, const void*
  * HKG_ERR_MISALIGNED), all device memory owned by the caller; C overlaps
  * no input.  bias / epilogue as in hkg_gemm_bf16_epilogue.  Shapes whose
  * packed scales reach 2^31 bytes, or K above 8388480, give
- * HKG_ERR_UNSUPPORTED.  The library's packed-scale buffer (like the split-K
- * workspace) is shared by all calls on a device: calls on different streams
- * of one device must not overlap in time.
+ * HKG_ERR_UNSUPPORTED.  The packed scales of hkg_gemm_mxfp8 go to the
+ * stream's library-owned workspace (see "Thread safety" above).
  */
 
 /* The plan an MXFP8 call of this shape uses (host only, no device). */
@@ -274,8 +288,8 @@ typedef enum {
  * Errors (before any device work): unknown layout, a leading dimension below
  * its minimum (or above 2^31 - 1), null pointers with nonzero extent, C
  * overlapping A or B -> HKG_ERR_INVALID_ARG; epilogue errors as
- * hkg_gemm_bf16_epilogue.  The library's layout buffer is shared by all calls
- * on a device, like the split-K workspace.
+ * hkg_gemm_bf16_epilogue.  The transposed copies go to the stream's
+ * library-owned workspace (see "Thread safety" above).
  */
 hkg_status_t hkg_gemm_bf16_ex(const void* A, int64_t lda, int32_t a_layout, const void* B, int64_t ldb,
                               int32_t b_layout, const void* bias, void* C, int64_t ldc, int64_t M, int64_t N,

@@ -11,8 +11,12 @@
 #include <climits>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <mutex>
 #include <string>
+#include <thread>
+#include <vector>
 
 namespace hkg {
 namespace {
@@ -51,18 +55,41 @@ void copy_str(char* dst, size_t cap, const char* src)
 }
 
 // ---------------------------------------------------------------- per device
-struct DeviceState {
-    std::once_flag once;
-    hkg_status_t status = HKG_ERR_NO_DEVICE;
-    std::mutex ws_mutex;
+// Library-owned scratch of one (device, stream): the split-K fp32 partials
+// and arrival counters, the packed MXFP8 scales of hkg_gemm_mxfp8 and the
+// row-layout copies of column-layout operands (hkg_gemm_bf16_ex).  Calls on
+// one stream run in order, so they can share it; calls on different streams
+// each have their own, so they do not race.
+struct Workspace {
     float* ws = nullptr;          // split-K partials
     size_t ws_bytes = 0;
     int* counters = nullptr;      // split-K arrival counters (kept zero between calls)
     size_t counter_count = 0;
-    uint8_t* mx_ws = nullptr;     // packed MXFP8 scales of hkg_gemm_mxfp8
+    uint8_t* mx_ws = nullptr;     // packed MXFP8 scales
     size_t mx_ws_bytes = 0;
-    uint16_t* layout_ws = nullptr;  // row-layout copies of column-layout operands (hkg_gemm_bf16_ex)
+    uint16_t* layout_ws = nullptr;
     size_t layout_ws_bytes = 0;
+};
+
+struct StreamKey {
+    hipStream_t stream;
+    std::thread::id thread;       // only for hipStreamPerThread (one stream per host thread)
+    bool operator<(const StreamKey& o) const
+    {
+        return stream != o.stream ? std::less<hipStream_t>()(stream, o.stream) : thread < o.thread;
+    }
+};
+
+struct DeviceState {
+    std::once_flag once;
+    hkg_status_t status = HKG_ERR_NO_DEVICE;
+    std::mutex ws_mutex;
+    std::map<StreamKey, Workspace> per_stream;
+    // Outgrown buffers.  A launch still in flight, or a captured graph, may
+    // hold their addresses, so they are released only when the library is
+    // unloaded, never earlier.  Growth is geometric, so they add up to less
+    // than the buffers in use.
+    std::vector<void*> retired;
 };
 
 constexpr int kMaxDevices = 64;
@@ -100,85 +127,102 @@ hkg_status_t current_device(int* dev_out)
     return d.status;
 }
 
-// Split-K scratch for `dev`: grown on demand, never shrunk, freed at exit.
-hkg_status_t get_workspace(int dev, size_t ws_bytes, size_t counters, float** ws, int** cnt)
+StreamKey stream_key(hipStream_t stream)
 {
-    DeviceState& d = g_devices[dev];
-    std::lock_guard<std::mutex> lock(d.ws_mutex);
-    if (d.ws_bytes < ws_bytes) {
-        if (d.ws)
-            (void)hipFree(d.ws);
-        d.ws = nullptr;
-        d.ws_bytes = 0;
-        hipError_t e = hipMalloc((void**)&d.ws, ws_bytes);
-        if (e != hipSuccess) {
-            set_hip_error(e, "hipMalloc(split-K workspace)");
-            d.ws = nullptr;
-            return HKG_ERR_WORKSPACE;
-        }
-        d.ws_bytes = ws_bytes;
+    return StreamKey{stream, stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+}
+
+// A workspace buffer may only grow outside stream capture: allocating (and
+// zeroing counters) are not stream-ordered work a graph could replay, and a
+// buffer allocated for one capture would be shared by every replay.
+hkg_status_t check_not_capturing(hipStream_t stream, const char* what)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) {
+        set_hip_error(e, "hipStreamIsCapturing");
+        return HKG_ERR_HIP;
     }
-    if (d.counter_count < counters) {
-        if (d.counters)
-            (void)hipFree(d.counters);
-        d.counters = nullptr;
-        d.counter_count = 0;
-        hipError_t e = hipMalloc((void**)&d.counters, counters * sizeof(int));
-        if (e == hipSuccess)
-            e = hipMemset(d.counters, 0, counters * sizeof(int));
-        if (e != hipSuccess) {
-            set_hip_error(e, "hipMalloc(split-K counters)");
-            return HKG_ERR_WORKSPACE;
-        }
-        d.counter_count = counters;
+    if (cs != hipStreamCaptureStatusNone) {
+        char buf[256];
+        std::snprintf(buf, sizeof buf,
+                      "%s must grow while the stream is being captured: run the same call once "
+                      "outside capture first", what);
+        g_last_hip_error = buf;
+        return HKG_ERR_WORKSPACE;
     }
-    *ws = d.ws;
-    *cnt = d.counters;
     return HKG_OK;
 }
 
-// Packed-scale buffer of hkg_gemm_mxfp8 for `dev`: grown on demand.
-hkg_status_t get_mx_workspace(int dev, size_t bytes, uint8_t** out)
+// Grow *buf to at least `bytes` (geometrically; the old buffer is retired,
+// not freed).  Called with the device's ws_mutex held.
+template <typename T>
+hkg_status_t grow(DeviceState& d, hipStream_t stream, T** buf, size_t* have, size_t bytes, const char* what,
+                  bool zero)
 {
-    DeviceState& d = g_devices[dev];
-    std::lock_guard<std::mutex> lock(d.ws_mutex);
-    if (d.mx_ws_bytes < bytes) {
-        if (d.mx_ws)
-            (void)hipFree(d.mx_ws);
-        d.mx_ws = nullptr;
-        d.mx_ws_bytes = 0;
-        hipError_t e = hipMalloc((void**)&d.mx_ws, bytes);
-        if (e != hipSuccess) {
-            set_hip_error(e, "hipMalloc(MXFP8 scale workspace)");
-            d.mx_ws = nullptr;
-            return HKG_ERR_WORKSPACE;
-        }
-        d.mx_ws_bytes = bytes;
+    if (*have >= bytes)
+        return HKG_OK;
+    hkg_status_t st = check_not_capturing(stream, what);
+    if (st != HKG_OK)
+        return st;
+    const size_t want = std::max(bytes, 2 * *have);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, want);
+    if (e == hipSuccess && zero)
+        e = hipMemset(p, 0, want);
+    if (e != hipSuccess) {
+        set_hip_error(e, what);
+        if (p)
+            (void)hipFree(p);
+        return HKG_ERR_WORKSPACE;
     }
-    *out = d.mx_ws;
+    if (*buf)
+        d.retired.push_back((void*)*buf);
+    *buf = (T*)p;
+    *have = want;
     return HKG_OK;
 }
 
-// Row-layout copies of column-layout operands for `dev`: grown on demand.
-hkg_status_t get_layout_workspace(int dev, size_t bytes, uint16_t** out)
+// Split-K scratch of (dev, stream): partials of ws_bytes, `counters` zeroed
+// arrival counters.
+hkg_status_t get_workspace(int dev, hipStream_t stream, size_t ws_bytes, size_t counters, float** ws, int** cnt)
 {
     DeviceState& d = g_devices[dev];
     std::lock_guard<std::mutex> lock(d.ws_mutex);
-    if (d.layout_ws_bytes < bytes) {
-        if (d.layout_ws)
-            (void)hipFree(d.layout_ws);
-        d.layout_ws = nullptr;
-        d.layout_ws_bytes = 0;
-        hipError_t e = hipMalloc((void**)&d.layout_ws, bytes);
-        if (e != hipSuccess) {
-            set_hip_error(e, "hipMalloc(layout workspace)");
-            d.layout_ws = nullptr;
-            return HKG_ERR_WORKSPACE;
-        }
-        d.layout_ws_bytes = bytes;
-    }
-    *out = d.layout_ws;
+    Workspace& w = d.per_stream[stream_key(stream)];
+    hkg_status_t st = grow(d, stream, &w.ws, &w.ws_bytes, ws_bytes, "split-K workspace", false);
+    if (st != HKG_OK)
+        return st;
+    size_t cnt_bytes = w.counter_count * sizeof(int);
+    st = grow(d, stream, &w.counters, &cnt_bytes, counters * sizeof(int), "split-K counters", true);
+    if (st != HKG_OK)
+        return st;
+    w.counter_count = cnt_bytes / sizeof(int);
+    *ws = w.ws;
+    *cnt = w.counters;
     return HKG_OK;
+}
+
+// Packed-scale buffer of hkg_gemm_mxfp8 for (dev, stream).
+hkg_status_t get_mx_workspace(int dev, hipStream_t stream, size_t bytes, uint8_t** out)
+{
+    DeviceState& d = g_devices[dev];
+    std::lock_guard<std::mutex> lock(d.ws_mutex);
+    Workspace& w = d.per_stream[stream_key(stream)];
+    hkg_status_t st = grow(d, stream, &w.mx_ws, &w.mx_ws_bytes, bytes, "MXFP8 scale workspace", false);
+    *out = w.mx_ws;
+    return st;
+}
+
+// Row-layout copies of column-layout operands for (dev, stream).
+hkg_status_t get_layout_workspace(int dev, hipStream_t stream, size_t bytes, uint16_t** out)
+{
+    DeviceState& d = g_devices[dev];
+    std::lock_guard<std::mutex> lock(d.ws_mutex);
+    Workspace& w = d.per_stream[stream_key(stream)];
+    hkg_status_t st = grow(d, stream, &w.layout_ws, &w.layout_ws_bytes, bytes, "layout workspace", false);
+    *out = w.layout_ws;
+    return st;
 }
 
 // --------------------------------------------------------------------- plan
@@ -516,7 +560,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
         float* ws = nullptr;
         int* counters = nullptr;
         if (p->split_k > 1) {
-            st = get_workspace(dev, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+            st = get_workspace(dev, stream, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)(cdiv(M, p->tile_m) * cdiv(N, p->tile_n)), &ws, &counters);
             if (st != HKG_OK)
                 return st;
@@ -529,7 +573,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
         float* ws = nullptr;
         int* counters = nullptr;
         if (p->split_k > 1) {
-            st = get_workspace(dev, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+            st = get_workspace(dev, stream, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)cdiv(N, 16), &ws, &counters);
             if (st != HKG_OK)
                 return st;
@@ -548,22 +592,21 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
     return HKG_OK;
 }
 
+// Every library-owned buffer is released when the library is unloaded.
 struct Cleanup {
     ~Cleanup()
     {
         for (auto& d : g_devices) {
-            if (d.ws)
-                (void)hipFree(d.ws);
-            if (d.counters)
-                (void)hipFree(d.counters);
-            if (d.mx_ws)
-                (void)hipFree(d.mx_ws);
-            if (d.layout_ws)
-                (void)hipFree(d.layout_ws);
-            d.ws = nullptr;
-            d.counters = nullptr;
-            d.mx_ws = nullptr;
-            d.layout_ws = nullptr;
+            for (auto& kv : d.per_stream) {
+                Workspace& w = kv.second;
+                for (void* p : {(void*)w.ws, (void*)w.counters, (void*)w.mx_ws, (void*)w.layout_ws})
+                    if (p)
+                        (void)hipFree(p);
+            }
+            d.per_stream.clear();
+            for (void* p : d.retired)
+                (void)hipFree(p);
+            d.retired.clear();
         }
     }
 } g_cleanup;
@@ -832,7 +875,7 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
         float* ws = nullptr;
         int* counters = nullptr;
         if (p->split_k > 1) {
-            st = get_workspace(dev, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+            st = get_workspace(dev, stream, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)(cdiv(M, p->tile_m) * cdiv(N, p->tile_n)), &ws, &counters);
             if (st != HKG_OK)
                 return st;
@@ -908,7 +951,7 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
         return st;
     const int64_t pa = mx_packed_scale_bytes(M, K), pb = mx_packed_scale_bytes(N, K);
     uint8_t* ws = nullptr;
-    st = get_mx_workspace(dev, (size_t)(pa + pb), &ws);
+    st = get_mx_workspace(dev, (hipStream_t)stream, (size_t)(pa + pb), &ws);
     if (st != HKG_OK)
         return st;
     hipError_t e = launch_mx_pack((const uint8_t*)SA, (uint32_t*)ws, M, K, (hipStream_t)stream);
@@ -995,7 +1038,7 @@ hkg_status_t gemm_ex(const void* A, int64_t lda, int32_t a_layout, const void* B
             return st;
         const size_t a_ws = a_col ? (size_t)M * (size_t)K : 0, b_ws = b_col ? (size_t)N * (size_t)K : 0;
         uint16_t* ws = nullptr;
-        st = get_layout_workspace(dev, (a_ws + b_ws) * sizeof(uint16_t), &ws);
+        st = get_layout_workspace(dev, stream, (a_ws + b_ws) * sizeof(uint16_t), &ws);
         if (st != HKG_OK)
             return st;
         hipError_t e = hipSuccess;
