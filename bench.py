@@ -74,18 +74,19 @@ def source_digest(fname):
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM-side bytes per launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE scaled by a reference copy), if they were taken
-    on the current source of that kernel; else None."""
+def measured_traffic(workload, kernel):
+    """HBM-side bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a reference
+    copy), if they were taken on that kernel and its current source; else
+    None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    e = rec.get(kernel)
-    if not e or e.get("source_digest") != source_digest(e.get("source", "")):
+    e = rec.get("workloads", {}).get(workload)
+    if not e or e.get("kernel") != kernel or e.get("source_digest") != source_digest(e.get("source", "")):
         return None
     return e.get("bytes_per_launch")
 
@@ -99,18 +100,137 @@ def graph_warmup(warmup, sets):
     return max(50, warmup // sets)
 
 
-def time_launches(torch, fn, steps, warmup):
+# Timing protocol of every leg: W warm-up calls, then an untimed clock-settle
+# period of back-to-back calls (SETTLE_S seconds of device time: the engine
+# clock needs a few hundred milliseconds of sustained load to reach its
+# loaded level, and a 5-launch warm-up timed the ramp, ~10% slow at 8192^3),
+# then WINDOWS windows of K calls each, every window bracketed by device
+# synchronisation and timed with HIP events on the stream the calls are
+# launched on; the leg's figure is the median window.  SCLK / MCLK are
+# sampled during the windows (amdsmi; null where unavailable).
+SETTLE_S = 0.5
+WINDOWS = 5
+TIMINGS = {}
+
+
+class ClockSampler:
+    """Background sampling of the GPU's current engine and memory clocks and
+    activity through amdsmi (optional: every failure leaves the figures null)."""
+
+    def __init__(self):
+        self.handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                self.amdsmi = amdsmi
+                self.handle = handles[0]
+                self.read()
+        except Exception as ex:            # noqa: BLE001 - clocks are context only
+            log("clock sampling unavailable: %s" % str(ex)[:120])
+            self.handle = None
+        self.samples = []
+        self._thread = None
+        self._stop = None
+
+    def read(self):
+        a = self.amdsmi
+        sclk = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"]
+        mclk = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.MEM)["clk"]
+        act = a.amdsmi_get_gpu_activity(self.handle).get("gfx_activity")
+        return sclk, mclk, act
+
+    def activity(self, n=5, gap_s=0.02):
+        """gfx activity % over n samples with nothing of ours running (idle check)."""
+        if self.handle is None:
+            return None
+        out = []
+        for _ in range(n):
+            try:
+                out.append(self.read()[2])
+            except Exception:              # noqa: BLE001
+                return None
+            time.sleep(gap_s)
+        return out
+
+    def start(self):
+        self.samples = []
+        if self.handle is None:
+            return
+        import threading
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self.read())
+                except Exception:          # noqa: BLE001
+                    return
+                self._stop.wait(0.01)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+        if not self.samples:
+            return None
+        sc = [x[0] for x in self.samples if x[0] is not None]
+        mc = [x[1] for x in self.samples if x[1] is not None]
+        return dict(samples=len(self.samples),
+                    sclk_mhz_median=float(np.median(sc)) if sc else None,
+                    sclk_mhz_min=float(min(sc)) if sc else None, sclk_mhz_max=float(max(sc)) if sc else None,
+                    mclk_mhz_median=float(np.median(mc)) if mc else None)
+
+
+CLOCKS = None
+
+
+def time_launches(torch, fn, steps, warmup, label=None, per_call=1):
+    """Median ms per fn() over WINDOWS windows of `steps` calls each, after
+    `warmup` calls and SETTLE_S seconds of untimed calls; per_call divides
+    (fn launching that many GEMMs, e.g. a graph over rotating buffers)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    # Estimate one call's device time, then settle the clocks.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(steps):
-        fn()
+    fn()
     stop.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps          # ms per call
+    est_ms = max(start.elapsed_time(stop), 1e-3)
+    settle = int(min(200000, max(1, np.ceil(SETTLE_S * 1e3 / est_ms))))
+    done = 0
+    while done < settle:
+        chunk = min(settle - done, max(1, int(20.0 / est_ms)))     # ~20 ms between host syncs
+        for _ in range(chunk):
+            fn()
+        done += chunk
+        torch.cuda.synchronize()
+    if CLOCKS is not None:
+        CLOCKS.start()
+    wins = []
+    for _ in range(WINDOWS):
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        wins.append(start.elapsed_time(stop) / steps / per_call)
+    clk = CLOCKS.stop() if CLOCKS is not None else None
+    med = float(np.median(wins))
+    if label:
+        TIMINGS[label] = dict(ms_per_call_median=round(med, 6), windows=[round(w, 6) for w in wins],
+                              calls_per_window=steps * per_call, warmup_calls=warmup * per_call,
+                              settle_calls=settle * per_call, settle_ms=round(settle * est_ms, 1),
+                              spread_pct=round(100.0 * (max(wins) - min(wins)) / med, 2), clocks=clk)
+    return med
 
 
 def bench_square(torch, hkg, steps, warmup):
@@ -125,17 +245,18 @@ def bench_square(torch, hkg, steps, warmup):
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     plan = hkg.plan(M, N, K)
     log("plan", plan.kernel_name.decode(), plan.reason.decode())
-    ms = time_launches(torch, lambda: hkg.gemm(a, b, out=c), steps, warmup)
+    ms = time_launches(torch, lambda: hkg.gemm(a, b, out=c), steps, warmup, label="square")
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     log("square: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
     # Fused epilogue (bias + GELU, one bias value per column) on the same
     # inputs: its cost over the plain GEMM.
     bias = torch.linspace(-1.0, 1.0, N, device="cuda").to(torch.bfloat16)
-    ms_e = time_launches(torch, lambda: hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_gelu"), steps, warmup)
+    ms_e = time_launches(torch, lambda: hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_gelu"), steps, warmup,
+                         label="square_bias_gelu")
     log("square with bias+GELU epilogue: %.3f ms/step, %.1f TFLOP/s" % (ms_e, flops / (ms_e * 1e-3) / 1e12))
     # Context only: the vendor library on the same inputs, same protocol.
-    ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup)
+    ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup, label="square_torch_mm")
     tflops_v = flops / (ms_v * 1e-3) / 1e12
     log("square, torch.mm (hipBLASLt) for context: %.3f ms/step, %.1f TFLOP/s" % (ms_v, tflops_v))
     return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v,
@@ -170,14 +291,15 @@ def bench_decode(torch, hkg, steps, warmup):
         for a, b, c in bufs:
             hkg.gemm(a, b, out=c)
     reps = max(1, steps // sets)
-    ms_rot = time_launches(torch, graph.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms_rot = time_launches(torch, graph.replay, reps, graph_warmup(warmup, sets), label="decode", per_call=sets)
     # Hot buffers (B resident in the last-level cache) for context.
     a, b, c = bufs[0]
     graph_hot = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_hot, stream=stream):
         for _ in range(sets):
             hkg.gemm(a, b, out=c)
-    ms_hot = time_launches(torch, graph_hot.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms_hot = time_launches(torch, graph_hot.replay, reps, graph_warmup(warmup, sets), label="decode_llc_resident",
+                            per_call=sets)
     gbps = alg_bytes / (ms_rot * 1e-3) / 1e9
     gbps_hot = alg_bytes / (ms_hot * 1e-3) / 1e9
     # Fused bias + SiLU epilogue over the same rotating buffers.
@@ -190,7 +312,8 @@ def bench_decode(torch, hkg, steps, warmup):
     with torch.cuda.graph(graph_e, stream=stream):
         for a, b, c in bufs:
             hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_silu")
-    ms_e = time_launches(torch, graph_e.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms_e = time_launches(torch, graph_e.replay, reps, graph_warmup(warmup, sets), label="decode_bias_silu",
+                         per_call=sets)
     log("decode with bias+SiLU epilogue: %.2f us/call rotating (%.0f GB/s)"
         % (ms_e * 1e3, (alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9))
     log("decode: %.2f us/call rotating (%.0f GB/s), %.2f us hot (%.0f GB/s)"
@@ -204,7 +327,8 @@ def bench_decode(torch, hkg, steps, warmup):
     with torch.cuda.graph(graph_v, stream=stream):
         for a, b, c in bufs:
             torch.mm(a, b.t(), out=c)
-    ms_v = time_launches(torch, graph_v.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms_v = time_launches(torch, graph_v.replay, reps, graph_warmup(warmup, sets), label="decode_torch_mm",
+                         per_call=sets)
     gbps_v = alg_bytes / (ms_v * 1e-3) / 1e9
     log("decode, torch.mm (hipBLASLt) for context: %.2f us/call rotating (%.0f GB/s)" % (ms_v * 1e3, gbps_v))
     return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
@@ -243,12 +367,14 @@ def bench_mx_square(torch, hkg, steps, warmup):
     plan = hkg.mx_plan(M, N, K)
     log("mx plan", plan.kernel_name.decode(), plan.reason.decode())
     flops = 2.0 * M * N * K
-    ms = time_launches(torch, lambda: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True), steps, warmup)
-    ms_nat = time_launches(torch, lambda: hkg.gemm_mxfp8(a, sa, b, sb, out=c), steps, warmup)
+    ms = time_launches(torch, lambda: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True), steps, warmup,
+                       label="mx_square")
+    ms_nat = time_launches(torch, lambda: hkg.gemm_mxfp8(a, sa, b, sb, out=c), steps, warmup,
+                           label="mx_square_per_call_packing")
     log("mx square: %.3f ms/step (%.1f TFLOP/s) packed scales, %.3f ms with per-call packing"
         % (ms, flops / ms / 1e9, ms_nat))
     fn = vendor_fp8(torch, a, b, c)
-    ms_v = time_launches(torch, fn, steps, warmup) if fn else None
+    ms_v = time_launches(torch, fn, steps, warmup, label="mx_square_scaled_mm") if fn else None
     if ms_v:
         log("mx square, torch._scaled_mm per-tensor fp8 for context: %.3f ms (%.1f TFLOP/s)" % (ms_v, flops / ms_v / 1e9))
     return dict(M=M, N=N, K=K, ms=ms, tflops=flops / ms / 1e9, ms_nat=ms_nat, tflops_nat=flops / ms_nat / 1e9,
@@ -288,9 +414,10 @@ def bench_mx_decode(torch, hkg, steps, warmup):
         return g
 
     g_pk = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True))
-    ms = time_launches(torch, g_pk.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms = time_launches(torch, g_pk.replay, reps, graph_warmup(warmup, sets), label="mx_decode", per_call=sets)
     g_nat = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, sa, b, sb, out=c))
-    ms_nat = time_launches(torch, g_nat.replay, reps, graph_warmup(warmup, sets)) / sets
+    ms_nat = time_launches(torch, g_nat.replay, reps, graph_warmup(warmup, sets), label="mx_decode_natural_scales",
+                           per_call=sets)
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     log("mx decode: %.2f us/call rotating (%.0f GB/s) packed scales, %.2f us from natural-layout scales"
         % (ms * 1e3, gbps, ms_nat * 1e3))
@@ -300,24 +427,24 @@ def bench_mx_decode(torch, hkg, steps, warmup):
         g_v = graph_of(lambda a, sa, pa, b, sb, pb, c: torch._scaled_mm(
             a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn).t(), scale_a=one, scale_b=one,
             out_dtype=torch.bfloat16))
-        ms_v = time_launches(torch, g_v.replay, reps, graph_warmup(warmup, sets)) / sets
+        ms_v = time_launches(torch, g_v.replay, reps, graph_warmup(warmup, sets), label="mx_decode_scaled_mm",
+                             per_call=sets)
         log("mx decode, torch._scaled_mm per-tensor fp8 for context: %.2f us" % (ms_v * 1e3))
     return dict(M=M, N=N, K=K, ms=ms, gbps=gbps, ms_nat=ms_nat, alg_bytes=alg_bytes, sets=sets, plan=plan,
                 launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
 
 
-CONFIG_LEG = ("tiny_256", "mlp_up_128x12288x4096")
-ALL_CONFIGS = CONFIG_LEG + ("prefill_down_4096x4096x12288",)
+ALL_CONFIGS = ("tiny_256", "mlp_up_128x12288x4096", "prefill_down_4096x4096x12288")
 
 
-def bench_configs(torch, hkg, names=CONFIG_LEG):
-    """The remaining dense workloads (tiny, MLP-up; with --only configs also
-    prefill-down, which runs the square kernel at another size and is left
-    out of the full run so that the square kernel's average launch time in a
-    kernel trace of the full run is the square workload's) in the planner's
-    launch configuration: per-call time over buffer sets rotated across 2x
-    the last-level cache, launches captured in a graph; torch.mm over the
-    same buffers for context."""
+def bench_configs(torch, hkg, names=ALL_CONFIGS):
+    """The remaining dense workloads (tiny, MLP-up, prefill-down) in the
+    planner's launch configuration: per-call time over buffer sets rotated
+    across 2x the last-level cache, launches captured in a graph; torch.mm
+    over the same buffers for context.  (Prefill-down runs the square
+    workload's kernel at another size: a kernel trace of the full run mixes
+    the two in that kernel's average; the per-workload traces come from
+    --only runs.)"""
     import workloads
     out = {}
     stream = torch.cuda.Stream()
@@ -347,17 +474,19 @@ def bench_configs(torch, hkg, names=CONFIG_LEG):
 
         flops = 2.0 * M * N * K
         est = max(flops / 1.0e15, per_set / 4.0e12, 5e-6)          # rough seconds per call
-        reps = int(min(200, max(3, 0.2 / (est * sets))))
+        # each window: at least 100 calls and ~20 ms of device time
+        reps = int(min(200, max(np.ceil(100 / sets), np.ceil(0.02 / (est * sets)))))
         warm = int(max(3, 0.02 / (est * sets)))                    # ~20 ms of untimed replays
         g = graph_of(lambda a, b, c: hkg.gemm(a, b, out=c))
-        ms = time_launches(torch, g.replay, reps, warm) / sets
+        ms = time_launches(torch, g.replay, reps, warm, label=name, per_call=sets)
         gv = graph_of(lambda a, b, c: torch.mm(a, b.t(), out=c))
-        ms_v = time_launches(torch, gv.replay, reps, warm) / sets
+        ms_v = time_launches(torch, gv.replay, reps, warm, label=name + "_torch_mm", per_call=sets)
         log("%s: %s, %.2f us/call (%.1f TFLOP/s, %.0f GB/s); torch.mm %.2f us"
             % (name, plan.kernel_name.decode(), ms * 1e3, flops / (ms * 1e-3) / 1e12,
                per_set / (ms * 1e-3) / 1e9, ms_v * 1e3))
         out[name] = dict(us=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12, gbps=per_set / (ms * 1e-3) / 1e9,
-                         kernel=plan.kernel_name.decode(), split_k=plan.split_k, vendor_us=ms_v * 1e3, sets=sets)
+                         kernel=plan.kernel_name.decode(), split_k=plan.split_k, vendor_us=ms_v * 1e3, sets=sets,
+                         flops=flops, alg_bytes=float(per_set), launches=reps * sets)
         del bufs, a0, b0
         torch.cuda.empty_cache()
     return out
@@ -377,14 +506,14 @@ def bench_grouped(torch, hkg, steps, warmup):
         c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         plan = hkg.grouped_plan(G, M, N, K)
         flops = 2.0 * float(sum(w["sizes"])) * N * K
-        ms = time_launches(torch, lambda: hkg.grouped_gemm(a, b, o, out=c), steps, warmup)
+        ms = time_launches(torch, lambda: hkg.grouped_gemm(a, b, o, out=c), steps, warmup, label=name)
         log("grouped %s: %s, %.3f ms (%.1f TFLOP/s)" % (name, plan.kernel_name.decode(), ms, flops / ms / 1e9))
         ms_v = None
         try:
             bt = b.transpose(1, 2)
             torch._grouped_mm(a, bt, offs=o, out_dtype=torch.bfloat16)
             ms_v = time_launches(torch, lambda: torch._grouped_mm(a, bt, offs=o, out_dtype=torch.bfloat16),
-                                 steps, warmup)
+                                 steps, warmup, label=name + "_grouped_mm")
             log("grouped %s, torch._grouped_mm for context: %.3f ms (%.1f TFLOP/s)" % (name, ms_v, flops / ms_v / 1e9))
         except Exception as ex:          # noqa: BLE001 - context figure only
             log("torch._grouped_mm unavailable: %s" % str(ex)[:100])
@@ -405,11 +534,11 @@ def bench_layouts(torch, hkg, steps, warmup):
     bt = b.t().contiguous()                 # B stored K x N (column layout): x @ W
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     flops = 2.0 * M * N * K
-    ms_nn = time_launches(torch, lambda: hkg.gemm_ex(a, bt.t(), out=c), steps, warmup)
-    ms_tn = time_launches(torch, lambda: hkg.gemm_ex(at.t(), bt.t(), out=c), steps, warmup)
+    ms_nn = time_launches(torch, lambda: hkg.gemm_ex(a, bt.t(), out=c), steps, warmup, label="layouts_nn")
+    ms_tn = time_launches(torch, lambda: hkg.gemm_ex(at.t(), bt.t(), out=c), steps, warmup, label="layouts_tn")
     y = torch.empty_like(b)
-    ms_pack = time_launches(torch, lambda: hkg.pack(bt.t()), steps, warmup)
-    ms_v = time_launches(torch, lambda: torch.mm(a, bt, out=c), steps, warmup)
+    ms_pack = time_launches(torch, lambda: hkg.pack(bt.t()), steps, warmup, label="layouts_transpose")
+    ms_v = time_launches(torch, lambda: torch.mm(a, bt, out=c), steps, warmup, label="layouts_nn_torch_mm")
     log("layouts: NN %.3f ms (%.1f TFLOP/s), TN %.3f ms (%.1f), transpose of one operand %.3f ms (%.0f GB/s); "
         "torch.mm NN %.3f ms" % (ms_nn, flops / ms_nn / 1e9, ms_tn, flops / ms_tn / 1e9, ms_pack,
                                  4.0 * N * K / ms_pack / 1e6, ms_v))
@@ -452,9 +581,38 @@ def cpu_baseline(target_s=15.0):
     dt = time.perf_counter() - t0
     tflops = 2.0 * rows * N * K / dt / 1e12
     log("cpu oracle: %d rows x %d x %d in %.1f s on %d threads: %.2e TFLOP/s" % (rows, N, K, dt, threads, tflops))
-    return dict(value=tflops, unit="TFLOP/s", cores=threads, kind="oracle",
+    return dict(value=tflops, unit="TFLOP/s", cores=threads, kind="oracle", cpu_model=cpu_model(),
+                host_cpus_visible=len(os.sched_getaffinity(0)),
                 sample="rows 0..%d of the 8192^3 workload (%d x 8192 outputs, K = 8192), %.1f s"
                        % (rows - 1, rows, dt))
+
+
+def config_roofline(name, r):
+    """Roofline of one of the remaining dense workloads: HBM-bound below the
+    machine balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop per byte), MFMA-bound
+    above it; the tiny workload is bound by launch latency (no peak)."""
+    if name.startswith("tiny"):
+        return {"bound": "latency", "achieved": round(r["us"], 3), "unit": "us per call", "peak": None,
+                "frac": None, "traffic": None, "kernel": r["kernel"]}
+    if r["flops"] / r["alg_bytes"] < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        return {"bound": "hbm", "achieved": round(r["gbps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(r["gbps"] / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(name, r["kernel"]),
+                "kernel": r["kernel"],
+                "per_launch": "2 (M K + N K + M N) = %d bytes per launch" % r["alg_bytes"]}
+    return {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name, r["kernel"]),
+            "kernel": r["kernel"], "per_launch": "2 M N K = %.4g flop per launch" % r["flops"]}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -482,6 +640,11 @@ def main():
     import tile_level_dense_amd as hkg
     hkg.lib()
 
+    global CLOCKS
+    CLOCKS = ClockSampler()
+    idle = CLOCKS.activity()
+    if idle and max(idle) > 5:
+        log("device not idle before timing: gfx activity %s %%" % idle)
     calibration_copy(torch)
     if args.only == "decode":
         dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
@@ -520,8 +683,8 @@ def main():
 
     tile_kernel = sq["plan"].kernel_name.decode()
     skinny_kernel = dec["plan"].kernel_name.decode()
-    tr = measured_traffic(tile_kernel)
-    tr_dec = measured_traffic(skinny_kernel)
+    tr = measured_traffic("square_8192", tile_kernel)
+    tr_dec = measured_traffic("decode_16x4096x4096", skinny_kernel)
     line = {
         "metric": METRIC,
         "value": round(sq["tflops"], 2),
@@ -542,7 +705,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(sq["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(sq["tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": tr, "kernel": tile_kernel,
-                     "per_launch": "2 M N K = %.4g flop per launch (one launch per step)" % sq["flops"]},
+                     "per_launch": "2 M N K = %.4g flop per launch (one launch per step)" % sq["flops"],
+                     "clocks_during_timing": (TIMINGS.get("square") or {}).get("clocks")},
         "decode": {"workload": "decode_16x4096x4096: M = 16, N = 4096, K = 4096",
                    "value": round(dec["gbps"], 1), "unit": "GB/s",
                    "frac_of_hbm": round(dec["gbps"] / PEAK_HBM_GBPS, 4),
@@ -566,7 +730,7 @@ def main():
                            "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
-                                        "traffic": measured_traffic(r["plan"].kernel_name.decode()),
+                                        "traffic": measured_traffic(name, r["plan"].kernel_name.decode()),
                                         "kernel": r["plan"].kernel_name.decode(),
                                         "per_launch": "2 sum(M_g) N K = %.4g flop per launch" % r["flops"]},
                            "vendor_grouped_mm_tflops": round(r["vendor_tflops"], 2) if r["vendor_tflops"] else None}
@@ -578,15 +742,23 @@ def main():
                     "vendor_nn_tflops": round(lay["vendor_nn_tflops"], 2)},
         "other_configs": {name: {"us_per_call": round(r["us"], 3), "tflops": round(r["tflops"], 2),
                                  "gbps": round(r["gbps"], 1), "kernel": r["kernel"], "split_k": r["split_k"],
-                                 "rotating_sets": r["sets"], "vendor_us": round(r["vendor_us"], 3)}
+                                 "rotating_sets": r["sets"], "launches_per_window": r["launches"],
+                                 "vendor_us": round(r["vendor_us"], 3),
+                                 "roofline": config_roofline(name, r)}
                           for name, r in cfg.items()},
+        "timing": {"protocol": "per leg: W warm-up calls, then untimed back-to-back calls for %.2f s of device "
+                               "time (clock settle), then %d windows of K calls, each bracketed by device "
+                               "synchronisation and timed with HIP events on the launch stream; the figure is "
+                               "the median window; clocks sampled with amdsmi during the windows" % (SETTLE_S, WINDOWS),
+                   "settle_s": SETTLE_S, "windows": WINDOWS,
+                   "idle_gfx_activity_pct_before": idle, "legs": TIMINGS},
         "mxfp8": {
             "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",
                        "tflops": round(mxs["tflops"], 2), "ms": round(mxs["ms"], 4),
                        "per_call_packing_tflops": round(mxs["tflops_nat"], 2),
                        "roofline": {"bound": "mfma", "achieved": round(mxs["tflops"], 2), "peak": PEAK_FP8_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(mxs["tflops"] / PEAK_FP8_TFLOPS, 4),
-                                    "traffic": measured_traffic(mxs["plan"].kernel_name.decode()),
+                                    "traffic": measured_traffic("mx_square_8192", mxs["plan"].kernel_name.decode()),
                                     "kernel": mxs["plan"].kernel_name.decode(),
                                     "per_launch": "2 M N K = %.4g flop per launch" % mxs["flops"]},
                        "vendor_fp8_per_tensor_tflops": round(mxs["vendor_tflops"], 2) if mxs["vendor_tflops"] else None},
@@ -595,7 +767,7 @@ def main():
                        "natural_scales_us": round(mxd["ms_nat"] * 1e3, 3),
                        "roofline": {"bound": "hbm", "achieved": round(mxd["gbps"], 1), "peak": PEAK_HBM_GBPS,
                                     "unit": "GB/s", "frac": round(mxd["gbps"] / PEAK_HBM_GBPS, 4),
-                                    "traffic": measured_traffic(mxd["plan"].kernel_name.decode()),
+                                    "traffic": measured_traffic("mx_decode_32x4096x4096", mxd["plan"].kernel_name.decode()),
                                     "kernel": mxd["plan"].kernel_name.decode(),
                                     "per_launch": "M K + N K + (M + N) K / 32 + 2 M N = %d bytes" % mxd["alg_bytes"]},
                        "rotating_sets": mxd["sets"], "launches_timed": mxd["launches"],
