@@ -337,6 +337,25 @@ hkg_status_t hkg_grouped_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* 
                                             const void* bias, void* C, int64_t G, int64_t M, int64_t N, int64_t K,
                                             int32_t epilogue, void* stream);
 
+/* ------------------------------------------------------ without allocation
+ * hkg_gemm_bf16_noalloc: hkg_gemm_bf16 for callers that cannot allocate
+ * device memory -- code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, plan, kernels and results as
+ * hkg_gemm_bf16 (bit-identical output), but the split-K partials and arrival
+ * counters live in a fixed device array of the library (16 MiB of partials
+ * and 16384 counters per device, held until the process ends) instead of a
+ * workspace the library allocates; the call itself allocates nothing.
+ * Every plan the library chooses fits (split plans need at most 256 x 128 x
+ * 128 fp32 partials); a plan needing more returns HKG_ERR_WORKSPACE.
+ * All calls on one device share the array: calls that overlap in time on
+ * one device (on different streams, or a captured graph replayed beside
+ * another call) race and give wrong results; calls on one stream are
+ * ordered.  The first call on a device finds the array's address and, when
+ * its stream is not being captured, clears the counters (synchronously).
+ */
+hkg_status_t hkg_gemm_bf16_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                   void* stream);
+
 /* Static description of a status code. */
 const char* hkg_status_string(hkg_status_t status);
 

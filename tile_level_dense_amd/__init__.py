@@ -28,7 +28,7 @@ __all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_g
            "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan", "gemm_mxfp8",
            "mx_plan", "mx_pack_scales", "run_mx_plan", "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan",
            "hkg_grouped_gemm_bf16_run_plan", "grouped_gemm", "grouped_plan", "hkg_gemm_bf16_ex", "hkg_pack_bf16",
-           "gemm_ex", "pack", "LAYOUT_ROW", "LAYOUT_COL"]
+           "gemm_ex", "pack", "LAYOUT_ROW", "LAYOUT_COL", "hkg_gemm_bf16_noalloc"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -59,7 +59,7 @@ EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_pl
                     "hkg_abi_version", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
                     "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan",
                     "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan", "hkg_grouped_gemm_bf16_run_plan",
-                    "hkg_gemm_bf16_ex", "hkg_pack_bf16"]
+                    "hkg_gemm_bf16_ex", "hkg_pack_bf16", "hkg_gemm_bf16_noalloc"]
 
 
 class Plan(ctypes.Structure):
@@ -121,6 +121,8 @@ def _load():
     i64 = ctypes.c_int64
     lib.hkg_gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.hkg_gemm_bf16.restype = ctypes.c_int
+    lib.hkg_gemm_bf16_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.hkg_gemm_bf16_noalloc.restype = ctypes.c_int
     lib.hkg_gemm_bf16_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
     lib.hkg_gemm_bf16_plan.restype = ctypes.c_int
     lib.hkg_gemm_bf16_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, i64, i64, i64, vp]
@@ -174,6 +176,11 @@ def lib():
 def hkg_gemm_bf16(A, B, C, M, N, K, stream=None):
     """C-ABI call with raw device addresses (ints); returns the status code."""
     return _load().hkg_gemm_bf16(A, B, C, M, N, K, stream)
+
+
+def hkg_gemm_bf16_noalloc(A, B, C, M, N, K, stream=None):
+    """C-ABI call of the no-allocation form (raw device addresses); status code."""
+    return _load().hkg_gemm_bf16_noalloc(A, B, C, M, N, K, stream)
 
 
 def hkg_gemm_bf16_plan(M, N, K):

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libhkg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNEL_SOURCES = ["hkg_tile.hip", "hkg_tile_mx.hip", "hkg_skinny.hip", "hkg_generic.hip"]
+KERNEL_SOURCES = ["hkg_tile.hip", "hkg_tile_mx.hip", "hkg_skinny.hip", "hkg_generic.hip", "hkg_noalloc.hip"]
 HOST_SOURCES = ["hkg_resources.cpp", "hkg_abi.cpp"]
 
 # -packed-fp32-ops: no v_pk_*_f32 from the compiler (kept off on this target).

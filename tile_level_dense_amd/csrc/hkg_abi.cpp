@@ -533,10 +533,31 @@ bool plan_matches_library(const hkg_plan_t* p)
     }
 }
 
+// Split-K scratch of a split plan: from the caller's fixed buffers when
+// `fixed` is given (the no-allocation entry point), else the stream's
+// library workspace.
+hkg_status_t split_scratch(int dev, hipStream_t stream, const FixedScratch* fixed, size_t ws_bytes, size_t counters,
+                           float** ws, int** cnt)
+{
+    if (!fixed)
+        return get_workspace(dev, stream, ws_bytes, counters, ws, cnt);
+    if (ws_bytes > fixed->ws_bytes || counters > fixed->counters) {
+        char buf[256];
+        std::snprintf(buf, sizeof buf,
+                      "split-K scratch of %zu bytes and %zu counters exceeds the fixed %zu bytes and %zu counters",
+                      ws_bytes, counters, fixed->ws_bytes, fixed->counters);
+        g_last_hip_error = buf;
+        return HKG_ERR_WORKSPACE;
+    }
+    *ws = fixed->ws;
+    *cnt = fixed->counter_base;
+    return HKG_OK;
+}
+
 // Leading dimensions: A rows lda apart, B rows ldb apart, C rows ldc apart
 // (elements); the dense calls pass K, K, N.
 hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, const uint16_t* bias, int epi,
-                 hipStream_t stream, int64_t lda, int64_t ldb, int64_t ldc)
+                 hipStream_t stream, int64_t lda, int64_t ldb, int64_t ldc, const FixedScratch* fixed = nullptr)
 {
     const int64_t M = p->M, N = p->N, K = p->K;
     if (p->kernel_id == HKG_KERNEL_NONE)
@@ -560,7 +581,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
         float* ws = nullptr;
         int* counters = nullptr;
         if (p->split_k > 1) {
-            st = get_workspace(dev, stream, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+            st = split_scratch(dev, stream, fixed, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)(cdiv(M, p->tile_m) * cdiv(N, p->tile_n)), &ws, &counters);
             if (st != HKG_OK)
                 return st;
@@ -573,7 +594,7 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
         float* ws = nullptr;
         int* counters = nullptr;
         if (p->split_k > 1) {
-            st = get_workspace(dev, stream, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
+            st = split_scratch(dev, stream, fixed, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)cdiv(N, 16), &ws, &counters);
             if (st != HKG_OK)
                 return st;
@@ -629,7 +650,7 @@ hkg_status_t check_epilogue(const void* bias, const void* C, int64_t M, int64_t 
 }
 
 hkg_status_t gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
-                  int32_t epi, void* stream)
+                  int32_t epi, void* stream, const FixedScratch* fixed = nullptr)
 {
     hkg_plan_t p;
     hkg_status_t st = make_plan(M, N, K, &p);
@@ -644,7 +665,7 @@ hkg_status_t gemm(const void* A, const void* B, const void* bias, void* C, int64
     if ((p.kernel_id == HKG_KERNEL_TILE || p.kernel_id == HKG_KERNEL_SKINNY) &&
         !(aligned16(A) && aligned16(B) && aligned16(C)))
         plan_generic(M, N, &p, "pointers not 16-byte aligned");
-    return run(&p, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream, K, K, N);
+    return run(&p, A, B, C, (const uint16_t*)bias, epi, (hipStream_t)stream, K, K, N, fixed);
 }
 
 hkg_status_t run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* bias, void* C,
@@ -1207,6 +1228,13 @@ hkg_status_t grouped(const hkg_plan_t* plan, const void* A, const void* B, const
 }
 
 }  // namespace
+
+hkg_status_t gemm_fixed_scratch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, void* stream,
+                                const FixedScratch& scratch)
+{
+    return gemm(A, B, nullptr, C, M, N, K, HKG_EPILOGUE_NONE, stream, &scratch);
+}
+
 }  // namespace hkg
 
 using namespace hkg;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hkg.h"
 #include "hkg_epilogue.h"
 #include "hkg_skinny_configs.h"
 #include "hkg_tile_configs.h"
@@ -153,6 +154,21 @@ hipError_t launch_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, const uin
 // Y[r ldy + c] = X[c ldx + r], r < R, c < CC (column layout -> row layout).
 hipError_t launch_transpose(const uint16_t* X, int64_t ldx, uint16_t* Y, int64_t ldy, int64_t R, int64_t CC,
                             hipStream_t stream);
+
+// Split-K scratch supplied by the caller instead of the stream's library
+// workspace: ws_bytes of fp32 partials at ws, `counters` arrival counters
+// at counter_base (zero between calls).
+struct FixedScratch {
+    float* ws;
+    size_t ws_bytes;
+    int* counter_base;
+    size_t counters;
+};
+
+// hkg_gemm_bf16 with split-K scratch from `scratch` (no allocation); a plan
+// that needs more returns HKG_ERR_WORKSPACE.  Defined in hkg_abi.cpp.
+hkg_status_t gemm_fixed_scratch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, void* stream,
+                                const FixedScratch& scratch);
 
 // Build-time resource figures of each kernel (filled by the generated
 // hkg_resources.inc; -1 where unknown).
