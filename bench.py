@@ -616,6 +616,7 @@ def cpu_model():
 
 
 def main():
+    global CLOCKS, SETTLE_S
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -623,6 +624,8 @@ def main():
     # MFMA load within a few tens of launches; shorter warm-ups time the ramp.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=2000)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls before each leg's timed windows (clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the tiny / MLP-up / prefill-down leg (counter runs)")
@@ -640,7 +643,7 @@ def main():
     import tile_level_dense_amd as hkg
     hkg.lib()
 
-    global CLOCKS
+    SETTLE_S = args.settle
     CLOCKS = ClockSampler()
     idle = CLOCKS.activity()
     if idle and max(idle) > 5:

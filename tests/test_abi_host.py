@@ -118,7 +118,9 @@ def test_plan_for_workloads(shape):
 def test_plan_square_8192_geometry():
     p = hkg.plan(8192, 8192, 8192)
     assert (p.tile_m, p.tile_n, p.tile_k, p.waves) == (256, 256, 64, 8)
-    assert p.grid_x == 1024 and p.block_x == 512
+    # persistent ping-pong: one workgroup per compute unit, 4 tiles each
+    assert p.grid_x == 256 and p.block_x == 512
+    assert p.kernel_name.decode().endswith("_p6")
     assert p.xcd_window_w == 8 and p.xcd_chunk_c == 32
     # ping-pong schedule: A halves double-, B triple-buffered
     assert p.lds_bytes == (4 * 128 + 3 * 256) * 64 * 2

@@ -236,6 +236,54 @@ def test_forced_tile_split(hkg, variant, split, shape):
     assert np.array_equal(C1, C2)
 
 
+def _persistent_variant():
+    from tile_level_dense_amd import build as hkg_build
+    return [v for v, c in enumerate(hkg_build.tile_configs()) if c[6] == 6][0]
+
+
+# More tiles than the persistent grid's 256 workgroups, so workgroups walk
+# two to four tiles: ragged M, N and K; one stage per tile (K = 64: the
+# copies running ahead are always in the next tile); three or four tiles.
+PERSISTENT_SHAPES = [(4400, 4200, 200), (4352, 4352, 64), (7168, 7000, 72), (4608, 4352, 8)]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_persistent_pingpong_multi_tile(hkg, shape):
+    """The persistent ping-pong over every output of shapes whose workgroups
+    walk several tiles; a second run is bit-identical."""
+    M, N, K = shape
+    v = _persistent_variant()
+    _say("persistent ping-pong", shape, "tiles", -(-M // 256) * -(-N // 256))
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=M + K)
+    C1 = forced(hkg, A, B, lambda p: force_tile(hkg, p, v))
+    full_check(C1, A, B)
+    C2 = forced(hkg, A, B, lambda p: force_tile(hkg, p, v))
+    assert np.array_equal(C1, C2)
+
+
+def test_persistent_pingpong_strided(hkg):
+    """Row-layout operands and C with padded leading dimensions on the
+    persistent ping-pong (through the layout entry point's in-place path)."""
+    M, N, K = 4352, 4224, 136
+    lda, ldb, ldc = K + 24, K + 8, N + 40
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=3)
+    As = np.full((M, lda), 0x7FC1, dtype=np.uint16)
+    As[:, :K] = A
+    Bs = np.full((N, ldb), 0xFFC3, dtype=np.uint16)
+    Bs[:, :K] = B
+    a, b = dev(As), dev(Bs)
+    c = dev(np.full((M, ldc), 0x4B80, dtype=np.uint16))
+    p = hkg.plan(M, N, K)
+    _say("persistent strided plan", p.kernel_name.decode())
+    st = hkg.hkg_gemm_bf16_ex(a.data_ptr(), lda, hkg.LAYOUT_ROW, b.data_ptr(), ldb, hkg.LAYOUT_ROW, None,
+                              c.data_ptr(), ldc, M, N, K, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == hkg.HKG_OK
+    torch.cuda.synchronize()
+    Cs = host(c)
+    assert (Cs[:, N:] == 0x4B80).all()
+    full_check(np.ascontiguousarray(Cs[:, :N]), A, B)
+
+
 def _skinny_configs():
     from tile_level_dense_amd import build as hkg_build
     return hkg_build.skinny_configs()

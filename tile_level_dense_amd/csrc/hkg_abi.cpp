@@ -333,7 +333,8 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
     p->tile_k = s.bk;
     p->waves = s.waves;
     p->split_k = (int32_t)split;
-    p->grid_x = (int32_t)(tm * tn);
+    // the persistent schedule runs at most one workgroup per compute unit
+    p->grid_x = (int32_t)(s.sched == 6 ? std::min<int64_t>(tm * tn, kPersistentGrid) : tm * tn);
     p->grid_y = (int32_t)split;
     p->grid_z = 1;
     p->block_x = s.waves * 64;
@@ -347,8 +348,9 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
     fill_resources(p, tile_resources(variant));
     std::snprintf(p->kernel_name, sizeof p->kernel_name, "tile_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
                   s.stages, s.wm, s.wn, s.sched);
-    std::snprintf(p->reason, sizeof p->reason, "%lldx%lld tiles of %dx%d (%d stages), split-K %lld on %d CUs",
-                  (long long)tm, (long long)tn, s.bm, s.bn, s.stages, (long long)split, kNumCUs);
+    std::snprintf(p->reason, sizeof p->reason, "%lldx%lld tiles of %dx%d (%d stages), split-K %lld on %d CUs%s",
+                  (long long)tm, (long long)tn, s.bm, s.bn, s.stages, (long long)split, kNumCUs,
+                  s.sched == 6 ? ", persistent" : "");
 }
 
 // Fill the skinny-kernel fields of p for (variant, split).

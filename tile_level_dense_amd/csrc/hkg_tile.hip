@@ -20,7 +20,7 @@ TileShape tile_shape(int variant)
 int tile_lds_bytes(int variant)
 {
     const TileShape s = tile_shape(variant);
-    if (s.sched == 5)                   // A halves double-, B triple-buffered
+    if (s.sched == 5 || s.sched == 6)   // A halves double-, B triple-buffered
         return (4 * (s.bm / 2) + 3 * s.bn) * s.bk * 2;
     return s.stages * (s.bm + s.bn) * s.bk * 2;
 }

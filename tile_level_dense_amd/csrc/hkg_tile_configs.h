@@ -10,7 +10,10 @@
 //             overlap the current MFMAs; branch-free ring with STAGES - 1
 //             copies ahead; 5: ping-pong of two 4-wave groups (256 x 256 x
 //             64 tile, 8 waves; STAGES is not used), copies issued only in
-//             memory phases, A halves double- and B triple-buffered
+//             memory phases, A halves double- and B triple-buffered; 6: the
+//             same ping-pong on a persistent grid of one workgroup per CU,
+//             each walking several tiles as one stream of stages (without a
+//             fused epilogue; with one, it runs as 5)
 // The build script reads this list to map code objects to variants.
 #pragma once
 
@@ -25,7 +28,8 @@
     X(64, 64, 64, 4, 2, 2, 2)     \
     X(128, 128, 64, 4, 2, 2, 2)   \
     X(64, 128, 64, 4, 2, 2, 2)    \
-    X(128, 64, 64, 4, 2, 2, 2)
+    X(128, 64, 64, 4, 2, 2, 2)     \
+    X(256, 256, 64, 2, 4, 2, 6)
 
 // MXFP8 instantiations (E4M3 operands, E8M0 scale per 32 k), same fields;
 // BK = 128 k (128 bytes per row, as the bf16 BK = 64), SCHED 5 or 0 (a

@@ -49,6 +49,7 @@
 #include "hkg_internal.h"
 #include "hkg_lds_copy.h"
 #include "hkg_tile_order.h"
+#include "hkg_tile_persistent.h"
 
 namespace hkg {
 namespace {
@@ -178,12 +179,22 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
-    // SCHED 5 keeps A halves double-buffered and B triple-buffered.
-    constexpr int SMEM = SCHED == 5 ? 4 * (BM / 2) * RB + 3 * B_BYTES : STAGES * STAGE;
+    // SCHED 5 (and 6, its persistent form) keeps A halves double-buffered and
+    // B triple-buffered.
+    constexpr bool PINGPONG = SCHED == 5 || SCHED == 6;
+    constexpr int SMEM = PINGPONG ? 4 * (BM / 2) * RB + 3 * B_BYTES : STAGES * STAGE;
     static_assert(SMEM <= 160 * 1024, "LDS is 160 KiB per CU");
     static_assert((STAGES - 2) * L <= 63, "vmcnt holds at most 63");
 
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+    // SCHED 6: the persistent ping-pong (one workgroup per compute unit
+    // walking several tiles, hkg_tile_persistent.h); with a fused epilogue,
+    // which stages through LDS, the one-tile ping-pong below.
+    if constexpr (SCHED == 6 && !EPI && !MX && !GROUPED) {
+        pingpong_persistent<WM, WN>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc, smem);
+        return;
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -503,7 +514,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // them) and loading the next stage's ahead of its copies, so no wait
             // for scales ever holds back a copy issued after them; 2 (SWA + SWB)
             // VGPRs.
-            static_assert(SCHED == 5, "schedules 0, 1, 2 and 5");
+            static_assert(PINGPONG, "schedules 0, 1, 2, 5 and 6");
             static_assert(BM == 256 && BN == 256 && RB == 128 && NW == 8 && WM <= 4,
                           "split-buffer ping-pong: 256 x 256 tile of 128-byte rows, 8 waves");
             constexpr int HALF = 128 * RB;                  // 128 rows of one stage
@@ -934,8 +945,10 @@ hipError_t launch_tile_t(const void* A, const void* B, uint16_t* C, int M, int N
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
+    // the persistent schedule: at most one workgroup per compute unit
+    const int grid = (SCHED == 6 && !EPI && !MX) ? min(tiles_m * tiles_n, kPersistentGrid) : tiles_m * tiles_n;
     hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, MX, false>),
-                       dim3(tiles_m * tiles_n, split_k), dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m,
+                       dim3(grid, split_k), dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m,
                        tiles_n, win_w, chunk_c, split_k, ws, counters, bias, epi, psa, psb, nullptr, 0, lda, ldb,
                        ldc);
     return hipGetLastError();
