@@ -93,7 +93,7 @@ def test_status_strings(lib):
 WORKLOAD_PLANS = {
     (256, 256, 256): ("TILE", "tile_64x64x64_s4"),
     (16, 4096, 4096): ("SKINNY", "skinny_m16"),
-    (128, 12288, 4096): ("TILE", "tile_128x64x64_s4"),
+    (128, 12288, 4096): ("TILE", "tile_64x96x64_s4"),
     (4096, 4096, 12288): ("TILE", "tile_256x256x64_"),
     (8192, 8192, 8192): ("TILE", "tile_256x256x64_"),
 }
@@ -147,8 +147,8 @@ def test_plan_boundaries():
     assert hkg.KERNEL_NAMES[hkg.plan(17, 4096, 4096).kernel_id] == "TILE"
     assert hkg.KERNEL_NAMES[hkg.plan(16, 4112, 4096).kernel_id] == "TILE"      # 257 column blocks
     assert hkg.KERNEL_NAMES[hkg.plan(32, 4096, 4096).kernel_id] == "TILE"
-    p = hkg.plan(128, 12288, 4096)       # 192 tiles of 128 x 64: three quarters of the CUs, unsplit
-    assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.tile_n, p.split_k) == (128, 64, 1)
+    p = hkg.plan(128, 12288, 4096)       # 256 tiles of 64 x 96: one per CU, unsplit
+    assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (64, 96, 1, 256)
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 100).kernel_id] == "GENERIC"     # K % 8
     assert hkg.KERNEL_NAMES[hkg.plan(512, 512, 0).kernel_id] == "ZERO"
     assert hkg.KERNEL_NAMES[hkg.plan(0, 512, 64).kernel_id] == "NONE"

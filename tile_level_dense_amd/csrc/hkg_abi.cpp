@@ -288,8 +288,10 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     // loads and MFMAs is then shortest), the taller one between 128 x 64 and
     // 64 x 128.  A tile whose rows would be more than a quarter padding is
     // skipped unless it is the last one.  Measured on MI355X: M = 128,
-    // N = 12288, K = 4096: 128 x 64 unsplit 35.9 us, 128 x 128 split 2
-    // 39.5 us, 64 x 64 unsplit (384 tiles) 41.6 us; M = 256, N = K = 4096:
+    // N = 12288, K = 4096 (graph-timed over rotating buffers): 64 x 96
+    // unsplit (exactly 256 tiles) 32.5 us, 128 x 64 unsplit (192 tiles)
+    // 34.7 us, 128 x 48 (256 tiles, 2 waves) 35.9 us, 64 x 64 unsplit (384
+    // tiles) 39.1 us, 128 x 128 split 2 44.8 us; M = 256, N = K = 4096:
     // 64 x 64 unsplit 21.9 us, 128 x 64 split 2 22.6 us; 256^3: 64 x 64 3.8 us,
     // 128 x 128 7.2 us; 512^3: 64 x 64 unsplit 5.1 us, split 2 6.7 us,
     // 128 x 128 split 2 13.1 us.

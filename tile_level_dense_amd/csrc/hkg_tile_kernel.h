@@ -767,14 +767,16 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             constexpr int CH = CH0 >= FM ? FM : (CH0 >= 8 ? 8 : (CH0 >= 4 ? 4 : (CH0 >= 2 ? 2 : 1)));
             constexpr int QPR = WTN / 4;                    // four-column groups per row
             static_assert(CH0 >= 1 && FM % CH == 0, "epilogue staging needs a block row of LDS per wave");
-            static_assert(64 % QPR == 0, "a lane keeps its four columns across the walk");
-            // This lane's four columns are the same on every row of the walk:
-            // read their bias values once, before the barrier.
+            // When 64 lanes cover whole rows of the walk (QPR divides 64), a
+            // lane's four columns are the same on every row: their bias
+            // values are read once, before the barrier; otherwise (48-column
+            // wave tiles) per element.
+            constexpr bool HOIST = 64 % QPR == 0;
             const int ncol = n0 + wn * WTN + (lane % QPR) * 4;
             float bv[4];
     #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                bv[rr] = ncol + rr < N ? __uint_as_float((uint32_t)bias_t[ncol + rr] << 16) : 0.f;
+                bv[rr] = HOIST && ncol + rr < N ? __uint_as_float((uint32_t)bias_t[ncol + rr] << 16) : 0.f;
             __syncthreads();                                // every wave is done with the stages
             char* const wbuf = smem + wave * REGION;
     #pragma unroll
@@ -794,8 +796,12 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                         continue;
                     f32x4 v = *(const f32x4*)(wbuf + r * ROWB + col * 4);
     #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        v[rr] = epi_activation(v[rr] + bv[rr], epi);
+                    for (int rr = 0; rr < 4; ++rr) {
+                        float bb = bv[rr];
+                        if constexpr (!HOIST)
+                            bb = n + rr < N ? __uint_as_float((uint32_t)bias_t[n + rr] << 16) : 0.f;
+                        v[rr] = epi_activation(v[rr] + bb, epi);
+                    }
                     const uint2 h = pack_bf16x4(v);
                     uint16_t* crow = C + (size_t)m * (size_t)ldc;
                     if (vec_ok && n + 3 < N) {
