@@ -259,8 +259,17 @@ def bench_square(torch, hkg, steps, warmup):
     ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup, label="square_torch_mm")
     tflops_v = flops / (ms_v * 1e-3) / 1e12
     log("square, torch.mm (hipBLASLt) for context: %.3f ms/step, %.1f TFLOP/s" % (ms_v, tflops_v))
+    # Context: the same kernel on constant operands (every element 0.01147),
+    # where the matrix cores switch little and draw less power, so the engine
+    # clock stays higher; the gap to the uniform [-1, 1] inputs above is the
+    # power limit, not the schedule.
+    ac = torch.full((M, K), 0.01147, dtype=torch.bfloat16, device="cuda")
+    bc = torch.full((N, K), 0.01147, dtype=torch.bfloat16, device="cuda")
+    ms_c = time_launches(torch, lambda: hkg.gemm(ac, bc, out=c), steps, warmup, label="square_constant_inputs")
+    del ac, bc
+    log("square on constant inputs (power context): %.3f ms/step, %.1f TFLOP/s" % (ms_c, flops / (ms_c * 1e-3) / 1e12))
     return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v,
-                epi_ms=ms_e, epi_tflops=flops / (ms_e * 1e-3) / 1e12)
+                epi_ms=ms_e, epi_tflops=flops / (ms_e * 1e-3) / 1e12, const_tflops=flops / (ms_c * 1e-3) / 1e12)
 
 
 def bench_decode(torch, hkg, steps, warmup):
@@ -331,9 +340,23 @@ def bench_decode(torch, hkg, steps, warmup):
                          per_call=sets)
     gbps_v = alg_bytes / (ms_v * 1e-3) / 1e9
     log("decode, torch.mm (hipBLASLt) for context: %.2f us/call rotating (%.0f GB/s)" % (ms_v * 1e3, gbps_v))
+    # Launch floor of a per-call figure: back-to-back launches of a kernel
+    # that does almost nothing (a one-element fill), captured in a graph the
+    # same way.  A call can take no less than this plus its bytes at the HBM
+    # peak, which caps the per-call rate of this workload.
+    tiny = torch.zeros(1, device="cuda")
+    graph_f = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_f, stream=stream):
+        for _ in range(sets):
+            tiny.fill_(1.0)
+    ms_f = time_launches(torch, graph_f.replay, reps, graph_warmup(warmup, sets), label="launch_floor", per_call=sets)
+    cap = alg_bytes / ((ms_f * 1e-3) + alg_bytes / (PEAK_HBM_GBPS * 1e9)) / 1e9
+    log("launch floor %.2f us per graph launch: a per-call decode reaches at most %.0f GB/s (%.1f%% of 8 TB/s)"
+        % (ms_f * 1e3, cap, 100 * cap / PEAK_HBM_GBPS))
     return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
                 alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets, vendor_gbps=gbps_v,
-                epi_ms=ms_e, epi_gbps=(alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9)
+                epi_ms=ms_e, epi_gbps=(alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9, floor_us=ms_f * 1e3,
+                floor_cap_gbps=cap)
 
 
 def mx_to_dev(x, torch):
@@ -719,7 +742,11 @@ def main():
                                 "traffic": tr_dec, "kernel": skinny_kernel,
                                 "per_launch": "2 (M K + N K + M N) = %d bytes per launch" % dec["alg_bytes"]},
                    "rotating_sets": dec["sets"], "launches_timed": dec["launches"],
-                   "llc_resident_gbps": round(dec["gbps_hot"], 1)},
+                   "llc_resident_gbps": round(dec["gbps_hot"], 1),
+                   "launch_floor_us": round(dec["floor_us"], 3),
+                   "per_call_cap_gbps": round(dec["floor_cap_gbps"], 1),
+                   "per_call_cap_note": "per-call rate of this workload if its bytes moved at the 8 TB/s peak "
+                                        "after the measured launch floor of a graph of one-element fills"},
         "cpu_baseline": cpu,
         "epilogue": {"square_bias_gelu_tflops": round(sq["epi_tflops"], 2),
                      "square_bias_gelu_ms": round(sq["epi_ms"], 4),
@@ -729,6 +756,9 @@ def main():
         "vendor_context": {"library": "torch.mm (hipBLASLt), same inputs and timing in the same run",
                            "square_tflops": round(sq["vendor_tflops"], 2),
                            "decode_gbps": round(dec["vendor_gbps"], 1)},
+        "power_context": {"square_constant_inputs_tflops": round(sq["const_tflops"], 2),
+                          "note": "the same square kernel with every operand element 0.01147: little "
+                                  "switching in the matrix cores, less power, a higher engine clock"},
         "grouped": {name: {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                            "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2),
                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
