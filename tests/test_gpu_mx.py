@@ -278,20 +278,39 @@ def test_mx_workload_decode_whole_output(hkg):
     check(C, A, SA, B, SB)
 
 
+def _tile_edges(n, tile):
+    """First and last index of every tile along one dimension, and the 17th."""
+    idx = {0, n - 1}
+    for t in range(0, n, tile):
+        idx.update({t, min(n - 1, t + tile - 1), min(n - 1, t + 17)})
+    return np.array(sorted(idx), dtype=np.int64)
+
+
 def test_mx_workload_square_sampled(hkg):
-    # mx_square_8192 in the planner's launch configuration: 4096 sampled
-    # outputs (and the four corners) against the oracle, one by one.
+    # mx_square_8192 in the planner's launch configuration, checked against
+    # the oracle entry by entry: every tile's edge rows crossed with every
+    # tile's edge columns, the two whole rows and the two whole columns on
+    # each side of the first tile boundary, and 4096 random outputs.
     _say("workload mx_square_8192")
     A, SA, B, SB = workloads.mx_workload_inputs("mx_square_8192")
     M, K = A.shape
     N = B.shape[0]
     p = hkg.mx_plan(M, N, K)
     assert p.kernel_id == hkg.HKG_KERNEL_MX_TILE and p.variant == 0
+    tm, tn = p.tile_m, p.tile_n
     C = run(hkg, A, SA, B, SB)
     rng = np.random.default_rng(8)
-    ii = np.concatenate([rng.integers(0, M, 4096), [0, 0, M - 1, M - 1]])
-    jj = np.concatenate([rng.integers(0, N, 4096), [0, N - 1, 0, N - 1]])
+    er, ec = _tile_edges(M, tm), _tile_edges(N, tn)
+    gi, gj = np.meshgrid(er, ec, indexing="ij")
+    full = np.arange(N, dtype=np.int64)
+    fullm = np.arange(M, dtype=np.int64)
+    ii = np.concatenate([gi.ravel(), np.full(N, tm - 1), np.full(N, tm), fullm, fullm,
+                         rng.integers(0, M, 4096)])
+    jj = np.concatenate([gj.ravel(), full, full, np.full(M, tn - 1), np.full(M, tn),
+                         rng.integers(0, N, 4096)])
+    _say("mx_square_8192: %d entries (%d edge rows x %d edge columns)" % (ii.size, er.size, ec.size))
     Cr, S, absS = oracle.mx_gemm_entries(A, SA, B, SB, ii, jj)
     T = gates.mx_truncation_allowance(gates.mx_operand(A, SA, e4m3), gates.mx_operand(B, SB, e4m3), ii=ii, jj=jj)
-    gates.compare_mx(C[ii, jj], Cr, S, absS, T, K)
+    stats = gates.compare_mx(C[ii, jj], Cr, S, absS, T, K)
+    _say("mx_square_8192", stats)
     assert np.isfinite(exact.widen(C)).all()
