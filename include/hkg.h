@@ -326,13 +326,25 @@ hkg_status_t hkg_pack_bf16(const void* X, int64_t ldx, int32_t layout, void* Y, 
  *   A, B, C 16-byte aligned, offs 4-byte aligned, K % 8 == 0 (else
  *   HKG_ERR_MISALIGNED / HKG_ERR_UNSUPPORTED; there is no general fallback).
  *   M, N or G == 0 launches nothing.  Rounding as hkg_gemm_bf16.
+ *   Tiles form one list over the experts, walked in rounds of grid_x
+ *   workgroups.  When the last round's tiles fill at most half the grid and
+ *   the plan's split_k is 2 (K of at least two stages), each of those tiles
+ *   is computed as two halves of K whose fp32 sums are added once (in either
+ *   order: the result is the same) before the rounding; the partials use
+ *   the stream's workspace (workspace_bytes of the plan, grid_x tiles of
+ *   fp32), allocated as for split-K of hkg_gemm_bf16.  While the stream is
+ *   being captured and its workspace is smaller than that (it never grows
+ *   during capture), the call runs every tile whole: correct, but its
+ *   last-round tiles may differ in the last bit from an eager call's.
+ *   Otherwise results are deterministic run to run.
  */
 hkg_status_t hkg_grouped_gemm_bf16_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* out);
 
 hkg_status_t hkg_grouped_gemm_bf16(const void* A, const void* B, const void* offs, const void* bias, void* C,
                                    int64_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream);
 
-/* Runs a grouped plan (variant, grid_x >= 1 and xcd_chunk_c may be edited). */
+/* Runs a grouped plan (variant, grid_x >= 1, xcd_chunk_c and split_k 1 or 2
+ * may be edited). */
 hkg_status_t hkg_grouped_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* A, const void* B, const void* offs,
                                             const void* bias, void* C, int64_t G, int64_t M, int64_t N, int64_t K,
                                             int32_t epilogue, void* stream);

@@ -478,7 +478,9 @@ def test_grouped_plan_selection(shape, variant, grid):
     G, M, N, K = shape
     p = hkg.grouped_plan(*shape)
     assert p.kernel_id == hkg.HKG_KERNEL_GROUPED and p.variant == variant and p.grid_x == grid, p
-    assert p.split_k == 1 and p.workspace_bytes == 0 and p.xcd_chunk_c == 1
+    # a last round filling at most half the grid is split over K (two halves)
+    assert p.split_k == 2 and p.xcd_chunk_c == 1
+    assert p.workspace_bytes == grid * p.tile_m * p.tile_n * 4
     assert p.algorithmic_bytes == 2 * (M * K + G * N * K + M * N)
     assert p.vgprs > 0 and p.scratch_bytes == 0
     assert p.lds_bytes == (160 * 1024 if variant == 2 else 2 * (p.tile_m + p.tile_n) * 128)
@@ -488,6 +490,9 @@ def test_grouped_plan_edges():
     for shape in ((0, 64, 64, 64), (4, 0, 64, 64), (4, 64, 0, 64)):
         st, p = hkg.hkg_grouped_gemm_bf16_plan(*shape)
         assert st == hkg.HKG_OK and p.kernel_id == hkg.HKG_KERNEL_NONE
+    # one stage of K: nothing to split
+    p = hkg.grouped_plan(4, 512, 256, 64)
+    assert p.split_k == 1 and p.workspace_bytes == 0
     assert hkg.hkg_grouped_gemm_bf16_plan(-1, 64, 64, 64)[0] == hkg.HKG_ERR_INVALID_ARG
     assert hkg.hkg_grouped_gemm_bf16_plan(4, 64, 64, 100)[0] == hkg.HKG_ERR_UNSUPPORTED     # K % 8
 
@@ -514,6 +519,9 @@ def test_grouped_argument_errors_precede_device_work():
     assert r(hkg.plan(M, N, K), A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
     q = hkg.Plan.from_buffer_copy(p)
     q.grid_x = 0
+    assert r(q, A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
+    q = hkg.Plan.from_buffer_copy(p)
+    q.split_k = 3
     assert r(q, A, B, offs, None, C, G, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
 
 

@@ -3,7 +3,8 @@
 Every grouped tile variant runs through the C ABI on the persistent grid, with
 the planner's grid and with forced grids (one workgroup walking every tile,
 grids that are not a multiple of the 8 chiplets, the chiplet-contiguous walk
-on and off), on ragged expert sizes with empty experts, more than 64 experts
+on and off, a last round split into two halves of K and the same launches
+unsplit), on ragged expert sizes with empty experts, more than 64 experts
 (several steps of the wave-parallel expert walk), every epilogue, and the
 MoE workloads on row ranges across expert boundaries.  Each row of an expert
 is compared element by element with the oracle (tests/gates.py); rows that
@@ -44,12 +45,12 @@ def host(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(hkg, A, B, offs, variant=None, grid=None, xcd=None, bias=None, epi="none"):
+def run(hkg, A, B, offs, variant=None, grid=None, xcd=None, bias=None, epi="none", split=None):
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
     out = torch.from_numpy(np.full((M, N), SENTINEL, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to("cuda")
     plan = None
-    if variant is not None or grid is not None or xcd is not None:
+    if variant is not None or grid is not None or xcd is not None or split is not None:
         from tile_level_dense_amd import build as hkg_build
         plan = hkg.grouped_plan(G, M, N, K)
         if variant is not None:
@@ -59,6 +60,9 @@ def run(hkg, A, B, offs, variant=None, grid=None, xcd=None, bias=None, epi="none
             plan.grid_x = grid
         if xcd is not None:
             plan.xcd_chunk_c = xcd
+        if split is not None:
+            plan.split_k = split
+            plan.workspace_bytes = plan.grid_x * plan.tile_m * plan.tile_n * 4 if split == 2 else 0
     offs_t = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.int32)).to("cuda")
     hkg.grouped_gemm(dev(A), dev(B), offs_t, out=out, bias=dev(bias) if bias is not None else None, epilogue=epi,
                      plan=plan)
@@ -115,6 +119,71 @@ def test_grouped_parity(hkg, name, sizes, N, K, variant, grid, xcd):
     check(C, A, B, offs)
 
 
+def last_round(sizes, N, tile_m, tile_n, grid):
+    """(tiles, tiles in the last round, experts holding a tile of it) of the
+    grouped tile list: experts in order, ceil(rows / tile_m) x ceil(N / tile_n)
+    tiles each."""
+    per = [-(-int(r) // tile_m) * -(-N // tile_n) for r in sizes]
+    total = sum(per)
+    rem = total % grid
+    ends = np.cumsum(per)
+    experts = [g for g in range(len(sizes)) if per[g] and ends[g] > total - rem]
+    return total, rem, experts
+
+
+# name, sizes, N, K, variant, grid, xcd: each with a last round of at most
+# half the grid, so its tiles are split into two halves of K.
+SPLIT_CASES = [
+    # 20 tiles on 8 workgroups: two whole rounds (chiplet walk), 4 tiles split
+    # in 8 halves; 5 stages of K (halves of 3 and 2)
+    ("pp_whole_rounds_then_split", [1000, 300, 500, 260], 512, 320, 2, 8, 1),
+    # every tile in the split round; ragged K (halves of 2 and 2 stages, the
+    # last one partial)
+    ("pp_all_split_ragged_k", [300, 0, 17, 260], 300, 200, 2, 24, 0),
+    # two stages: one each
+    ("pp_two_stages", [513, 0, 257], 530, 128, 2, 32, 1),
+    ("v128_split", [129, 0, 0, 511, 64], 270, 200, 1, 48, 1),
+    ("v256_ring_split", [300, 5, 0, 260], 260, 320, 0, 8, 0),
+]
+
+
+@pytest.mark.parametrize("name,sizes,N,K,variant,grid,xcd", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_grouped_last_round_split(hkg, name, sizes, N, K, variant, grid, xcd):
+    from tile_level_dense_amd import build as hkg_build
+    bm, bn = hkg_build.tile_configs(grouped=True)[variant][:2]
+    total, rem, _ = last_round(sizes, N, bm, bn, grid)
+    assert 0 < rem and 2 * rem <= grid, (total, rem)
+    _say(name, sizes, N, K, variant, grid, xcd, "tiles", total, "split", rem)
+    A, B, offs = workloads.make_grouped_inputs(sizes, N, K, seed=len(name) + K)
+    C2 = run(hkg, A, B, offs, variant, grid, xcd, split=2)
+    check(C2, A, B, offs)
+    assert np.array_equal(run(hkg, A, B, offs, variant, grid, xcd, split=2), C2), "split run not deterministic"
+    C1 = run(hkg, A, B, offs, variant, grid, xcd, split=1)
+    check(C1, A, B, offs)
+
+
+def test_grouped_split_with_one_stage_is_whole(hkg):
+    # K of one stage: split_k 2 in the plan leaves every tile whole, so the
+    # output equals the unsplit run's bit for bit.
+    sizes = [300, 0, 17, 260]
+    assert last_round(sizes, 300, 256, 256, 24)[1] == 10
+    A, B, offs = workloads.make_grouped_inputs(sizes, 300, 64, seed=12)
+    C2 = run(hkg, A, B, offs, 2, 24, 0, split=2)
+    check(C2, A, B, offs)
+    assert np.array_equal(C2, run(hkg, A, B, offs, 2, 24, 0, split=1))
+
+
+@pytest.mark.parametrize("epi", ["bias", "bias_gelu"])
+def test_grouped_split_epilogue(hkg, epi):
+    sizes, N, K = [1000, 300, 500, 260], 512, 320
+    assert last_round(sizes, N, 256, 256, 8)[1] == 4
+    A, B, offs = workloads.make_grouped_inputs(sizes, N, K, seed=31)
+    rng = np.random.default_rng(6)
+    bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, size=(4, N)).astype(np.float32))
+    C = run(hkg, A, B, offs, 2, 8, 1, bias=bias, epi=epi, split=2)
+    check(C, A, B, offs, bias=bias, epi=epi)
+
+
 def test_grouped_many_experts(hkg):
     # 150 experts (three steps of the 64-expert walk), a third of them empty.
     rng = np.random.default_rng(40)
@@ -164,6 +233,14 @@ def test_grouped_workloads_rows(hkg, name):
     bounds = sorted(set(int(o) for o in offs))
     picks = [(0, 4)] + [(max(0, b - 3), min(int(offs[-1]), b + 3)) for b in bounds[:-1]] + \
             [(int(offs[-1]) - 4, int(offs[-1]))]
+    # every row of the experts whose tiles fall in the last round (split over
+    # K when it fills at most half the grid)
+    p = hkg.grouped_plan(len(offs), A.shape[0], B.shape[1], A.shape[1])
+    sizes = np.diff(np.concatenate([[0], offs]))
+    total, rem, experts = last_round(sizes, B.shape[1], p.tile_m, p.tile_n, p.grid_x)
+    _say(name, "tiles", total, "last round", rem, "experts", experts)
+    for g in experts:
+        picks.append((int(offs[g - 1]) if g else 0, int(offs[g])))
     for r0, r1 in picks:
         if r1 > r0:
             check(C, A, B, offs, rows=(r0, r1))

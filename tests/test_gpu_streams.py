@@ -246,3 +246,58 @@ def test_graph_outlives_workspace_growth(hkg):
     finally:
         torch.cuda.synchronize()
         hip.hipStreamDestroy(h)
+
+
+def test_grouped_capture_without_workspace_runs_whole_tiles(hkg):
+    # A grouped plan that splits its last round (72 tiles of 128 x 128 on 64
+    # workgroups: 8 tiles split in two halves of K) captured on a stream that
+    # has no workspace yet: the captured call runs every tile whole (the
+    # unsplit eager result, bit for bit); once an eager call has allocated
+    # the workspace, a new capture splits (the split eager result).
+    sizes, N, K = [1000, 300, 500, 260], 512, 320
+    A, B, offs = workloads.make_grouped_inputs(sizes, N, K, seed=51)
+    G, M = len(sizes), A.shape[0]
+    a, b = dev16(A), dev16(B)
+    offs_t = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.int32)).to("cuda")
+
+    def plan(split):
+        p = hkg.grouped_plan(G, M, N, K)
+        assert p.tile_m == 128 and p.tile_n == 128, p.kernel_name
+        p.grid_x = 64
+        p.split_k = split
+        return p
+
+    def eager(split):
+        c = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        hkg.grouped_gemm(a, b, offs_t, out=c, plan=plan(split))
+        torch.cuda.synchronize()
+        return host16(c)
+
+    whole, split = eager(1), eager(2)
+    Cr, S, absS = oracle.grouped_gemm(A, B, offs)
+    gates.compare(whole, Cr, S, absS)
+    gates.compare(split, Cr, S, absS)
+    assert not np.array_equal(whole, split), "the split should change some roundings"
+    for allocated, want in ((False, whole), (True, split)):
+        hip, h, s = _new_stream()
+        try:
+            if allocated:
+                with torch.cuda.stream(s):
+                    hkg.grouped_gemm(a, b, offs_t, out=torch.zeros((M, N), dtype=torch.bfloat16, device="cuda"),
+                                     plan=plan(2))
+            torch.cuda.synchronize()
+            c = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                hkg.grouped_gemm(a, b, offs_t, out=c, plan=plan(2))
+            for r in range(3):
+                c.fill_(0)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(host16(c), want), ("allocated", allocated, "replay", r)
+            _say("grouped capture, workspace allocated before:", allocated)
+            del g
+        finally:
+            torch.cuda.synchronize()
+            hip.hipStreamDestroy(h)

@@ -1089,7 +1089,13 @@ hkg_status_t gemm_ex(const void* A, int64_t lda, int32_t a_layout, const void* B
 // Mixture-of-experts GEMM (FlyDSL-in-PyTorch blog, grouped GEMM section) on a
 // persistent grid: expert g owns rows [offs[g-1], offs[g]) of A and C.
 
-void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
+// Partial tiles of the grouped kernel's split last round: one per workgroup.
+size_t grouped_workspace_bytes(const hkg_plan_t* p)
+{
+    return p->split_k == 2 ? (size_t)p->grid_x * (size_t)p->tile_m * (size_t)p->tile_n * sizeof(float) : 0;
+}
+
+void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N, int64_t K)
 {
     const TileShape s = grouped_shape(variant);
     const int64_t tn = cdiv(N, s.bn);
@@ -1106,12 +1112,15 @@ void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
     p->tile_n = s.bn;
     p->tile_k = s.bk;
     p->waves = s.waves;
-    p->split_k = 1;
+    // The tiles of a last round that fills at most half the grid are split
+    // into two halves of K (decided on the device, where the offsets are);
+    // the rounds before it run whole tiles.
+    p->split_k = cdiv(K, s.bk) >= 2 ? 2 : 1;
     p->grid_x = (int32_t)std::max<int64_t>(grid, 1);
     p->grid_y = 1;
     p->grid_z = 1;
     p->block_x = s.waves * 64;
-    p->workspace_bytes = 0;
+    p->workspace_bytes = (int64_t)grouped_workspace_bytes(p);
     p->xcd_window_w = 0;
     p->xcd_chunk_c = 1;                 // chiplet-contiguous walk when the grid is a multiple of 8
     // the ping-pong keeps A halves double- and B triple-buffered
@@ -1120,8 +1129,9 @@ void fill_grouped(hkg_plan_t* p, int variant, int64_t G, int64_t M, int64_t N)
     fill_resources(p, grouped_resources(variant));
     std::snprintf(p->kernel_name, sizeof p->kernel_name, "grouped_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
                   s.stages, s.wm, s.wn, s.sched);
-    std::snprintf(p->reason, sizeof p->reason, "grouped: %lld experts, %d x %d tiles on a persistent grid of %lld",
-                  (long long)G, s.bm, s.bn, (long long)grid);
+    std::snprintf(p->reason, sizeof p->reason,
+                  "grouped: %lld experts, %d x %d tiles on a persistent grid of %lld%s", (long long)G, s.bm, s.bn,
+                  (long long)grid, p->split_k == 2 ? ", a last round of at most half the grid split over K" : "");
 }
 
 hkg_status_t make_grouped_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
@@ -1162,7 +1172,7 @@ hkg_status_t make_grouped_plan(int64_t G, int64_t M, int64_t N, int64_t K, hkg_p
     const TileShape s = grouped_shape(variant);
     if ((cdiv(M, s.bm) + G) * cdiv(N, s.bn) > INT32_MAX)
         return HKG_ERR_UNSUPPORTED;
-    fill_grouped(p, variant, G, M, N);
+    fill_grouped(p, variant, G, M, N, K);
     return HKG_OK;
 }
 
@@ -1173,7 +1183,8 @@ bool grouped_plan_matches_library(const hkg_plan_t* p, int64_t G)
     if (p->kernel_id != HKG_KERNEL_GROUPED || p->variant < 0 || p->variant >= GROUPED_NUM_VARIANTS)
         return false;
     const TileShape s = grouped_shape(p->variant);
-    return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves && p->split_k == 1 &&
+    return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
+           (p->split_k == 1 || p->split_k == 2) &&
            p->grid_x >= 1 && p->xcd_chunk_c >= 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
            (cdiv(p->M, s.bm) + G) * cdiv(p->N, s.bn) <= INT32_MAX;
 }
@@ -1221,8 +1232,32 @@ hkg_status_t grouped(const hkg_plan_t* plan, const void* A, const void* B, const
     hkg_status_t st = current_device(&dev);
     if (st != HKG_OK)
         return st;
+    // split_k 2 permits splitting the last round; under stream capture with
+    // a workspace too small for it (which may not grow then) the call runs
+    // every tile whole instead, which needs no workspace.
+    float* ws = nullptr;
+    int* cnt = nullptr;
+    int split = p->split_k;
+    if (split == 2) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t ce = hipStreamIsCapturing((hipStream_t)stream, &cs);
+        if (ce != hipSuccess) {
+            set_hip_error(ce, "hipStreamIsCapturing");
+            return HKG_ERR_HIP;
+        }
+        const std::string before = g_last_hip_error;
+        st = get_workspace(dev, (hipStream_t)stream, grouped_workspace_bytes(p), (size_t)p->grid_x, &ws, &cnt);
+        if (st == HKG_ERR_WORKSPACE && cs != hipStreamCaptureStatusNone) {
+            split = 1;
+            ws = nullptr;
+            cnt = nullptr;
+            g_last_hip_error = before;
+        } else if (st != HKG_OK) {
+            return st;
+        }
+    }
     hipError_t e = launch_grouped(p->variant, (const uint16_t*)A, (const uint16_t*)B, (const int*)offs, (int)G,
-                                  (uint16_t*)C, (int)M, (int)N, (int)K, p->grid_x, p->xcd_chunk_c,
+                                  (uint16_t*)C, (int)M, (int)N, (int)K, p->grid_x, p->xcd_chunk_c, split, ws, cnt,
                                   (const uint16_t*)bias, epi, (hipStream_t)stream);
     if (e != hipSuccess) {
         set_hip_error(e, "kernel launch");

@@ -126,10 +126,13 @@ hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint1
 
 // Grouped GEMM: A (M x K), B (G x N x K), offs (G row ends, device int32),
 // C (M x N), bias G x N when epi != EPI_NONE; `grid` persistent workgroups,
-// xcd_chunks != 0 for the chiplet-contiguous tile walk.
+// xcd_chunks != 0 for the chiplet-contiguous tile walk.  split_k 2: the tiles
+// of a last round that fills at most half the grid are split into two halves
+// of K, with grouped_workspace_bytes(variant, grid) of partials in ws and
+// grid / 2 zeroed arrival counters (left zero); split_k 1 uses neither.
 hipError_t launch_grouped(int variant, const uint16_t* A, const uint16_t* B, const int* offs, int G, uint16_t* C,
-                          int M, int N, int K, int grid, int xcd_chunks, const uint16_t* bias, int epi,
-                          hipStream_t stream);
+                          int M, int N, int K, int grid, int xcd_chunks, int split_k, float* ws, int* counters,
+                          const uint16_t* bias, int epi, hipStream_t stream);
 
 // MXFP8 skinny kernel (M <= 16 MB): packed scales as launch_tile_mx, or with
 // natural the M x K/32 and N x K/32 scale arrays themselves (4-byte aligned);

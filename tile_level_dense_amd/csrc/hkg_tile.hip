@@ -58,18 +58,19 @@ TileShape grouped_shape(int variant)
 }
 
 hipError_t launch_grouped(int variant, const uint16_t* A, const uint16_t* B, const int* offs, int G, uint16_t* C,
-                          int M, int N, int K, int grid, int xcd_chunks, const uint16_t* bias, int epi,
-                          hipStream_t stream)
+                          int M, int N, int K, int grid, int xcd_chunks, int split_k, float* ws, int* counters,
+                          const uint16_t* bias, int epi, hipStream_t stream)
 {
     int v = 0;
 #define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc)                                                                     \
     if (v++ == variant)                                                                                           \
-        return epi == EPI_NONE ? launch_grouped_t<bm, bn, bk, st, wm, wn, sc, false>(A, B, offs, G, C, M, N, K,  \
-                                                                                     grid, xcd_chunks, bias, epi,  \
-                                                                                     stream)                       \
-                               : launch_grouped_t<bm, bn, bk, st, wm, wn, sc, true>(A, B, offs, G, C, M, N, K,   \
-                                                                                    grid, xcd_chunks, bias, epi,   \
-                                                                                    stream);
+        return epi == EPI_NONE                                                                                    \
+                   ? launch_grouped_t<bm, bn, bk, st, wm, wn, sc, false>(A, B, offs, G, C, M, N, K, grid,         \
+                                                                         xcd_chunks, split_k, ws, counters, bias, \
+                                                                         epi, stream)                             \
+                   : launch_grouped_t<bm, bn, bk, st, wm, wn, sc, true>(A, B, offs, G, C, M, N, K, grid,          \
+                                                                        xcd_chunks, split_k, ws, counters, bias,  \
+                                                                        epi, stream);
     HKG_GROUPED_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;

@@ -210,9 +210,14 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     // One output tile: C rows [m0, min(m0 + BM, m_lim)) by columns
     // [tn BN, tn BN + BN), from A rows m0.. and rows tn BN.. of b_rows (the
     // tile's N x K operand; an expert's weight in grouped mode), with bias_t
-    // the bias row of that operand.  tm, tn index split-K's arrival counters
-    // (dense mode only).
-    auto run_tile = [&](int tm, int tn, int m0, int m_lim, const char* b_rows, const uint16_t* bias_t) {
+    // the bias row of that operand, over part k_part of k_parts equal parts of
+    // K.  tm, tn index split-K's arrival counters (dense mode); in grouped mode
+    // a tile split in two (k_parts = 2) is unit `unit` of the last round, whose
+    // partial goes to slot `unit` of ws and whose arrivals are counted at
+    // counters[unit / 2].
+    auto run_tile = [&](int tm, int tn, int m0, int m_lim, const char* b_rows, const uint16_t* bias_t, int k_part,
+                        int k_parts, int unit) {
+        (void)unit;
         (void)tm;
         // In the persistent loop the lane-derived offsets are recomputed per
         // tile (an opaque copy of the lane id) rather than kept live across
@@ -252,11 +257,11 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         const uint32_t copy_step_a = (uint32_t)COPY_ROWS * a_rb;
         const uint32_t copy_step_b = (uint32_t)COPY_ROWS * b_rb;
 
-        // K range of this workgroup: stages [kt0, kt0 + nk) of BK k;
-        // split_k > 1 divides K across workgroups (blockIdx.y).
+        // K range of this workgroup: stages [kt0, kt0 + nk) of BK k, part
+        // k_part of k_parts (dense split-K: blockIdx.y of split_k).
         const int nk_all = (K + BK - 1) / BK;
-        const int per_split = (nk_all + split_k - 1) / split_k;
-        const int kt0 = min(nk_all, (int)blockIdx.y * per_split);
+        const int per_split = (nk_all + k_parts - 1) / k_parts;
+        const int kt0 = min(nk_all, k_part * per_split);
         const int nk = min(nk_all, kt0 + per_split) - kt0;
         const int kbase = kt0 * BK;
         const int k_lim = min(K, (kt0 + nk) * BK);
@@ -669,7 +674,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // store has completed (vmcnt) before the arrival is counted (the
             // ordering argument is the split-K arrival protocol in
             // hkg_internal.h).
-            const int me = blockIdx.y;
+            const int me = k_part;
             const bool vec4 = (N & 3) == 0;
             const int part_bytes = M * N * 4;          // below 2^31: checked by the planner
             auto part = [&](int sp) { return ws + (size_t)sp * (size_t)M * (size_t)N; };
@@ -750,6 +755,68 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             }
             if (threadIdx.x == 0)
                 __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        if constexpr (GROUPED) if (k_parts == 2) {
+            // A tile of the last round split in two halves of K: each half
+            // writes its whole fp32 accumulator tile to its own slot (tile-
+            // local, BN floats per row, device-scope stores), and the half that
+            // arrives second adds the other's partial to its own and goes on
+            // to the store.  fp32 addition is commutative, so the sum is the
+            // same whichever half arrives second.  The ordering argument is the
+            // split-K arrival protocol in hkg_internal.h.
+            constexpr int SLOT = BM * BN;
+            const __amdgpu_buffer_rsrc_t mine =
+                __builtin_amdgcn_make_buffer_rsrc(ws + (size_t)unit * SLOT, 0, SLOT * 4, kBufferWord3);
+    #pragma unroll
+            for (int i = 0; i < FM; ++i)
+    #pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int off = ((wm * WTM + i * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), mine, off, 0,
+                                                           kDeviceScope);
+                }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // Every wave is past its last read of the stages: the first word
+            // of LDS carries the arrival result (the ping-pong's stages take
+            // all 160 KiB, so no separate flag is allocated).
+            __syncthreads();
+            int* const arrived = (int*)smem;
+            if (threadIdx.x == 0)
+                *arrived = __hip_atomic_fetch_add(&counters[unit >> 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (*arrived != 1)
+                return;
+            const __amdgpu_buffer_rsrc_t other =
+                __builtin_amdgcn_make_buffer_rsrc(ws + (size_t)(unit ^ 1) * SLOT, 0, SLOT * 4, kBufferWord3);
+            // RBLK block rows at a time (at most 16 loads, 64 VGPRs, in flight
+            // beside the accumulators); each sum is formed here (the empty asm
+            // keeps the compiler from sinking the additions into the store
+            // branches, which would keep every loaded partial live until then).
+            constexpr int RBLK = FN >= 16 ? 1 : (16 / FN < FM ? 16 / FN : FM);
+            static_assert(FM % RBLK == 0, "whole groups of block rows");
+    #pragma unroll
+            for (int i0 = 0; i0 < FM; i0 += RBLK) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 o[RBLK][FN];
+    #pragma unroll
+                for (int ii = 0; ii < RBLK; ++ii)
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int off = ((wm * WTM + (i0 + ii) * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                        o[ii][j] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(other, off, 0, kDeviceScope));
+                    }
+    #pragma unroll
+                for (int ii = 0; ii < RBLK; ++ii)
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        acc[i0 + ii][j] += o[ii][j];
+                        asm volatile("" : "+v"(acc[i0 + ii][j]));
+                    }
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&counters[unit >> 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
         const bool vec_ok = ((N | ldc) & 3) == 0;           // 8-byte stores of four columns
@@ -849,7 +916,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         tile_order(blockIdx.x, tiles_m, tiles_n, win_w, chunk_c, tm, tn);
         if (tm >= tiles_m || tn >= tiles_n)    // uniform per workgroup; never taken for a valid order
             return;
-        run_tile(tm, tn, tm * BM, M, (const char*)Bv, bias);
+        run_tile(tm, tn, tm * BM, M, (const char*)Bv, bias, (int)blockIdx.y, split_k, 0);
     } else {
         // Grouped (mixture-of-experts) mode, a persistent grid (FlyDSL-in-
         // PyTorch blog, grouped GEMM section).  Expert g owns rows
@@ -900,18 +967,28 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             total += uniform64(__shfl(il, 63, 64));
         }
         const int64_t P = gridDim.x;
-        int64_t first = blockIdx.x, stride = P, limit = total;
-        if (chunk_c != 0 && P % 8 == 0 && total >= P) {
+        // The last round: when its R tiles (total mod P) fill at most half the
+        // grid and split_k is 2, each of them is split into two halves of K
+        // (units 2r and 2r + 1 of tile r), so the round takes half a tile's
+        // time instead of a whole one.  The tiles before it form whole rounds,
+        // walked as above.
+        const int nk_all = (K + BK - 1) / BK;
+        const int64_t rem = total % P;
+        const bool tail_split = split_k == 2 && rem > 0 && 2 * rem <= P && nk_all >= 2;
+        const int64_t whole = tail_split ? total - rem : total;
+        int64_t first = blockIdx.x, stride = P, limit = whole;
+        if (chunk_c != 0 && P % 8 == 0 && whole >= P) {
             const int64_t x = blockIdx.x % 8;
-            first = total * x / 8 + blockIdx.x / 8;
+            first = whole * x / 8 + blockIdx.x / 8;
             stride = P / 8;
-            limit = total * (x + 1) / 8;
+            limit = whole * (x + 1) / 8;
         }
         int gb = 0;
         int64_t tb = 0;
-        for (int64_t t = first; t < limit; t += stride) {
-            // Advance to the chunk of experts holding tile t (tiles are
-            // visited in increasing order, so the walk only moves forward).
+        // Tile t of the list, over part k_part of k_parts of K (tiles are
+        // visited in increasing order, so the walk over experts only moves
+        // forward).
+        auto visit = [&](int64_t t, int k_part, int k_parts, int unit) {
             int64_t tiles_l, incl_l;
             chunk(gb, tiles_l, incl_l);
             int64_t chunk_total = uniform64(__shfl(incl_l, 63, 64));
@@ -938,7 +1015,33 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             tile_order(u, tiles_mg, tiles_n, 8, 0, tm, tn);
             __syncthreads();                         // LDS of the previous tile is free
             run_tile(tm, tn, r0 + tm * BM, r1, (const char*)Bv + (size_t)g * (size_t)N * b_rb,
-                     EPI ? bias + (size_t)g * (size_t)N : bias);
+                     EPI ? bias + (size_t)g * (size_t)N : bias, k_part, k_parts, unit);
+        };
+        // The split round's units u = 2 r + h (half h of its tile r) are cut
+        // into 8 contiguous parts and part x goes to workgroups x, x + 8, ...
+        // (XCD x under round-robin dispatch), so the units one XCD holds are
+        // neighbouring tiles sharing B tiles and A rows in its L2, as in the
+        // whole rounds.  Part x has at most ceil(2 rem / 8) <= P / 8 units.
+        int unit = -1;
+        if (tail_split) {
+            const int64_t units = 2 * rem;
+            const int64_t x = blockIdx.x % 8, i = blockIdx.x / 8;
+            const int64_t u0 = units * x / 8, u1 = units * (x + 1) / 8;
+            if (P % 8 == 0) {
+                if (u0 + i < u1)
+                    unit = (int)(u0 + i);
+            } else if ((int64_t)blockIdx.x < units) {
+                unit = (int)blockIdx.x;
+            }
+        }
+        // Whole tiles first, then this workgroup's unit of the split round
+        // (one loop, so the tile code is instantiated once).
+        const int64_t n_whole = first < limit ? (limit - first + stride - 1) / stride : 0;
+        const int64_t n_items = n_whole + (unit >= 0 ? 1 : 0);
+        for (int64_t j = 0; j < n_items; ++j) {
+            const bool half = j == n_whole;
+            visit(half ? whole + unit / 2 : first + j * stride, half ? (unit & 1) : 0, half ? 2 : 1,
+                  half ? unit : 0);
         }
     }
 }
@@ -960,15 +1063,19 @@ hipError_t launch_tile_t(const void* A, const void* B, uint16_t* C, int M, int N
     return hipGetLastError();
 }
 
-// Grouped form on a persistent grid of `grid` workgroups.
+// Grouped form on a persistent grid of `grid` workgroups; split_k 2 splits
+// the tiles of a last round that fills at most half the grid into two halves
+// of K, with ws holding grid partial tiles (BM x BN fp32 each) and counters
+// grid / 2 arrival counters, zero on entry and left zero.
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI>
 hipError_t launch_grouped_t(const void* A, const void* B, const int* offs, int G, uint16_t* C, int M, int N, int K,
-                            int grid, int xcd_chunks, const uint16_t* bias, int epi, hipStream_t stream)
+                            int grid, int xcd_chunks, int split_k, float* ws, int* counters, const uint16_t* bias,
+                            int epi, hipStream_t stream)
 {
     const int tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, false, true>), dim3(grid), dim3(WM * WN * 64),
-                       0, stream, A, B, C, M, N, K, 0, tiles_n, 0, xcd_chunks, 1, nullptr, nullptr, bias, epi, nullptr,
-                       nullptr, offs, G, K, K, N);
+                       0, stream, A, B, C, M, N, K, 0, tiles_n, 0, xcd_chunks, split_k, ws, counters, bias, epi,
+                       nullptr, nullptr, offs, G, K, K, N);
     return hipGetLastError();
 }
 
