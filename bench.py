@@ -353,10 +353,29 @@ def bench_decode(torch, hkg, steps, warmup):
     cap = alg_bytes / ((ms_f * 1e-3) + alg_bytes / (PEAK_HBM_GBPS * 1e9)) / 1e9
     log("launch floor %.2f us per graph launch: a per-call decode reaches at most %.0f GB/s (%.1f%% of 8 TB/s)"
         % (ms_f * 1e3, cap, 100 * cap / PEAK_HBM_GBPS))
+    # Context: a plain device copy moving the same bytes per call (half of
+    # them read, half written) over rotating buffers, graph-launched the same
+    # way: what a streaming kernel of this size reaches per call here.
+    half = per_set // 4                          # bf16 elements: half the bytes read, half written
+    copies = [(torch.empty(half, dtype=torch.bfloat16, device="cuda").fill_(1.0),
+               torch.empty(half, dtype=torch.bfloat16, device="cuda")) for _ in range(sets)]
+    with torch.cuda.stream(stream):
+        for src, dst in copies:
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    graph_c = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_c, stream=stream):
+        for src, dst in copies:
+            dst.copy_(src)
+    ms_c = time_launches(torch, graph_c.replay, reps, graph_warmup(warmup, sets), label="decode_copy_same_bytes",
+                         per_call=sets)
+    gbps_c = 4.0 * half / (ms_c * 1e-3) / 1e9
+    log("copy of the same bytes per call (torch copy_, context): %.2f us/call (%.0f GB/s)" % (ms_c * 1e3, gbps_c))
+    del copies
     return dict(M=M, N=N, K=K, ms=ms_rot, gbps=gbps, gbps_hot=gbps_hot, ms_hot=ms_hot,
                 alg_bytes=alg_bytes, sets=sets, plan=plan, launches=reps * sets, vendor_gbps=gbps_v,
                 epi_ms=ms_e, epi_gbps=(alg_bytes + 2 * N) / (ms_e * 1e-3) / 1e9, floor_us=ms_f * 1e3,
-                floor_cap_gbps=cap)
+                floor_cap_gbps=cap, copy_us=ms_c * 1e3, copy_gbps=gbps_c)
 
 
 def mx_to_dev(x, torch):
@@ -746,7 +765,11 @@ def main():
                    "launch_floor_us": round(dec["floor_us"], 3),
                    "per_call_cap_gbps": round(dec["floor_cap_gbps"], 1),
                    "per_call_cap_note": "per-call rate of this workload if its bytes moved at the 8 TB/s peak "
-                                        "after the measured launch floor of a graph of one-element fills"},
+                                        "after the measured launch floor of a graph of one-element fills",
+                   "copy_same_bytes_gbps": round(dec["copy_gbps"], 1),
+                   "copy_same_bytes_us": round(dec["copy_us"], 3),
+                   "copy_note": "torch copy_ moving the same bytes per call (half read, half written), rotating "
+                                "buffers, graph-launched: a streaming kernel's per-call rate at this size"},
         "cpu_baseline": cpu,
         "epilogue": {"square_bias_gelu_tflops": round(sq["epi_tflops"], 2),
                      "square_bias_gelu_ms": round(sq["epi_ms"], 4),
