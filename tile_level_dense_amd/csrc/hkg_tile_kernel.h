@@ -540,19 +540,21 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // an opaque copy of the lane id, so they are not held in registers
             // through the compute phases (the persistent loop's state needs
             // those registers).
+            // (unsigned: the divisions below by powers of two are then plain
+            // shifts and masks, with no sign corrections)
             auto fresh_lane = [&]() {
-                int l = threadIdx.x & 63;
+                uint32_t l = threadIdx.x & 63u;
                 asm volatile("" : "+v"(l));
                 return l;
             };
             auto copy_half = [&](__amdgpu_buffer_rsrc_t rsrc, char* dst, int t, uint32_t p_off, uint32_t rb) {
                 int pk = p_k;
                 if constexpr (GROUPED) {
-                    const int l = fresh_lane();
-                    const int row = w4 * RPW + l / CPR;
-                    const int ch = (l % CPR) ^ ((row / RPL) % CPR);
-                    p_off = (uint32_t)(128 * g + row) * rb + (uint32_t)ch * 16u;
-                    pk = ch * KPC;
+                    const uint32_t l = fresh_lane();
+                    const uint32_t row = (uint32_t)(w4 * RPW) + l / CPR;
+                    const uint32_t ch = (l % CPR) ^ ((row / RPL) % CPR);
+                    p_off = ((uint32_t)(128 * g) + row) * rb + ch * 16u;
+                    pk = (int)(ch * KPC);
                 }
                 const int k0 = kbase + t * BK;
                 const bool k_out = k0 + pk >= k_lim;
@@ -576,13 +578,13 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 for (int s = 0; s < KS; ++s)
                     co[s] = chunk_off[s];
                 if constexpr (GROUPED) {
-                    const int l = fresh_lane();
-                    const int lr = l & 15;
-                    ar = wm * WTM - 128 * g + lr;
-                    br = wn * WTN + lr;
+                    const uint32_t l = fresh_lane();
+                    const uint32_t lr = l & 15u;
+                    ar = wm * WTM - 128 * g + (int)lr;
+                    br = wn * WTN + (int)lr;
     #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        co[s] = ((4 * s + (l >> 4)) ^ ((lr / RPL) % CPR)) * 16;
+                        co[s] = (int)((((uint32_t)(4 * s) + (l >> 4)) ^ ((lr / RPL) % CPR)) * 16u);
                 }
                 const char* ab = a_buf + (2 * g + (t & 1)) * HALF + ar * RB;
                 const char* bb = b_buf + (t % 3) * 2 * HALF + br * RB;
