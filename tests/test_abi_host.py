@@ -469,8 +469,8 @@ def test_mx_no_device_status():
 
 # ------------------------------------------------------------ grouped GEMM
 @pytest.mark.parametrize("shape,variant,grid", [
-    ((8, 8192, 4096, 4096), 2, 256),      # experts of 1024 rows: 256 x 256 ping-pong, one workgroup per CU
-    ((16, 8192, 4096, 4096), 2, 256),
+    ((8, 8192, 4096, 4096), 3, 256),      # experts of 1024 rows: 256 x 256 ping-pong, one workgroup per CU
+    ((16, 8192, 4096, 4096), 3, 256),
     ((64, 4096, 2048, 1024), 1, 512),     # 64 rows per expert: 128 x 128, two per CU
     ((4, 256, 256, 256), 1, 12),          # grid capped at the most tiles the experts can have
 ])
@@ -483,7 +483,8 @@ def test_grouped_plan_selection(shape, variant, grid):
     assert p.workspace_bytes == grid * p.tile_m * p.tile_n * 4
     assert p.algorithmic_bytes == 2 * (M * K + G * N * K + M * N)
     assert p.vgprs > 0 and p.scratch_bytes == 0
-    assert p.lds_bytes == (160 * 1024 if variant == 2 else 2 * (p.tile_m + p.tile_n) * 128)
+    assert p.lds_bytes == (160 * 1024 if variant == 3 else 2 * (p.tile_m + p.tile_n) * 128)
+    assert p.kernel_name.decode() == ("grouped_256x256x64_s2_w4x2_p6" if variant == 3 else "grouped_128x128x64_s2_w2x2_p2")
 
 
 def test_grouped_plan_edges():

@@ -107,6 +107,15 @@ CASES = [
     ("pp_one_workgroup_one_stage", [300, 5, 0, 260], 260, 64, 2, 1, 0),
     ("pp_grid3_ragged_k", [300, 70], 260, 520, 2, 3, None),
     ("pp_grid24_xcd", [513, 0, 257], 530, 128, 2, 24, 1),
+    # the ping-pong whose workgroups stream their tiles' stages (variant 3):
+    # items crossing experts of different row counts, one-stage and ragged
+    # K, round-robin and chiplet walks
+    ("ps_ragged", [1, 255, 0, 300, 17], 300, 192, 3, None, None),
+    ("ps_one_workgroup_one_stage", [300, 5, 0, 260], 260, 64, 3, 1, 0),
+    ("ps_one_workgroup_many_experts", [300, 0, 1, 257, 600, 0, 40], 520, 200, 3, 1, 0),
+    ("ps_grid3_ragged_k", [300, 70], 260, 520, 3, 3, None),
+    ("ps_grid7_two_stages", [700, 3, 0, 513], 300, 128, 3, 7, 1),
+    ("ps_grid24_xcd", [513, 0, 257], 530, 128, 3, 24, 1),
     ("single_expert", [300], 200, 264, None, None, None),
 ]
 
@@ -144,6 +153,13 @@ SPLIT_CASES = [
     ("pp_two_stages", [513, 0, 257], 530, 128, 2, 32, 1),
     ("v128_split", [129, 0, 0, 511, 64], 270, 200, 1, 48, 1),
     ("v256_ring_split", [300, 5, 0, 260], 260, 320, 0, 8, 0),
+    # the streaming ping-pong: its unit is the last item of a workgroup's
+    # stream (after whole tiles, or alone), halves of 3 and 2, 2 and 2 (the
+    # last partial), 1 and 1 stages
+    ("ps_whole_rounds_then_split", [1000, 300, 500, 260], 512, 320, 3, 8, 1),
+    ("ps_split_after_round", [700, 3, 0, 513, 90], 300, 320, 3, 12, 0),
+    ("ps_all_split_ragged_k", [300, 0, 17, 260], 300, 200, 3, 24, 0),
+    ("ps_two_stages", [513, 0, 257], 530, 128, 3, 32, 1),
 ]
 
 
@@ -168,20 +184,39 @@ def test_grouped_split_with_one_stage_is_whole(hkg):
     sizes = [300, 0, 17, 260]
     assert last_round(sizes, 300, 256, 256, 24)[1] == 10
     A, B, offs = workloads.make_grouped_inputs(sizes, 300, 64, seed=12)
-    C2 = run(hkg, A, B, offs, 2, 24, 0, split=2)
-    check(C2, A, B, offs)
-    assert np.array_equal(C2, run(hkg, A, B, offs, 2, 24, 0, split=1))
+    for variant in (2, 3):
+        C2 = run(hkg, A, B, offs, variant, 24, 0, split=2)
+        check(C2, A, B, offs)
+        assert np.array_equal(C2, run(hkg, A, B, offs, variant, 24, 0, split=1))
 
 
+@pytest.mark.parametrize("variant", [2, 3])
 @pytest.mark.parametrize("epi", ["bias", "bias_gelu"])
-def test_grouped_split_epilogue(hkg, epi):
+def test_grouped_split_epilogue(hkg, epi, variant):
     sizes, N, K = [1000, 300, 500, 260], 512, 320
     assert last_round(sizes, N, 256, 256, 8)[1] == 4
     A, B, offs = workloads.make_grouped_inputs(sizes, N, K, seed=31)
     rng = np.random.default_rng(6)
     bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, size=(4, N)).astype(np.float32))
-    C = run(hkg, A, B, offs, 2, 8, 1, bias=bias, epi=epi, split=2)
+    C = run(hkg, A, B, offs, variant, 8, 1, bias=bias, epi=epi, split=2)
     check(C, A, B, offs, bias=bias, epi=epi)
+
+
+# The two 256 x 256 ping-pong variants (one tile at a time, and tiles streamed
+# stage after stage) multiply every tile in the same order and split a last
+# round at the same stage, so their outputs are identical bit for bit.
+@pytest.mark.parametrize("sizes,N,K,grid,xcd", [
+    ([1000, 300, 500, 260], 512, 320, 8, 1),
+    ([700, 3, 0, 513, 90], 300, 320, 12, 0),
+    ([1, 255, 0, 300, 17, 0, 1200], 700, 136, 16, 1),
+])
+def test_grouped_streamed_equals_one_tile(hkg, sizes, N, K, grid, xcd):
+    A, B, offs = workloads.make_grouped_inputs(sizes, N, K, seed=N + K)
+    for split in (1, 2):
+        C2 = run(hkg, A, B, offs, 2, grid, xcd, split=split)
+        C3 = run(hkg, A, B, offs, 3, grid, xcd, split=split)
+        assert np.array_equal(C2, C3), ("split", split)
+    check(C3, A, B, offs)
 
 
 def test_grouped_many_experts(hkg):
@@ -191,7 +226,7 @@ def test_grouped_many_experts(hkg):
     sizes[rng.random(150) < 0.33] = 0
     _say("many experts", int(sizes.sum()))
     A, B, offs = workloads.make_grouped_inputs(sizes, 72, 64, seed=41)
-    for variant, grid in ((1, None), (0, 5), (2, 5)):
+    for variant, grid in ((1, None), (0, 5), (2, 5), (3, 5)):
         C = run(hkg, A, B, offs, variant, grid)
         check(C, A, B, offs)
 
@@ -218,7 +253,7 @@ def test_grouped_epilogue(hkg, epi):
     A, B, offs = workloads.make_grouped_inputs([70, 0, 130, 3], 200, 256, seed=len(epi))
     rng = np.random.default_rng(5)
     bias = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, size=(4, 200)).astype(np.float32))
-    for variant in (0, 1, 2):
+    for variant in (0, 1, 2, 3):
         C = run(hkg, A, B, offs, variant, bias=bias, epi=epi)
         check(C, A, B, offs, bias=bias, epi=epi)
 

@@ -29,9 +29,9 @@ constexpr int MX_TILE_NUM_VARIANTS = 0
     ;
 
 // Grouped-GEMM instantiations (plan.variant for HKG_KERNEL_GROUPED): the
-// rows of HKG_GROUPED_CONFIGS; the planner's two (the 256 x 256 ping-pong and
-// the 128 x 128 tile).
-constexpr int kGroupedPingPong = 2;
+// rows of HKG_GROUPED_CONFIGS; the planner's two (the 256 x 256 ping-pong
+// streaming its tiles' stages, and the 128 x 128 tile).
+constexpr int kGroupedPingPong = 3;
 constexpr int kGroupedSmall = 1;
 constexpr int GROUPED_NUM_VARIANTS = 0
 #define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1

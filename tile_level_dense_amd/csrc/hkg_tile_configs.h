@@ -40,9 +40,12 @@
     X(128, 128, 128, 2, 2, 2, 0)
 
 // Grouped (mixture-of-experts) instantiations on a persistent grid, same
-// fields; bf16 only, no split-K.  Variant 2 (the ping-pong) and 1 are the
-// planner's; 0 is kept as the register-pipelined alternative.
+// fields; bf16 only, K split only in a partial last round.  Variant 3 (the
+// ping-pong whose workgroups stream their tiles' stages; with a fused
+// epilogue it runs as 2) and 1 are the planner's; 0 (register-pipelined) and
+// 2 (the ping-pong one tile at a time) are kept as alternatives.
 #define HKG_GROUPED_CONFIGS(X)     \
     X(256, 256, 64, 2, 2, 4, 2)    \
     X(128, 128, 64, 2, 2, 2, 2)    \
-    X(256, 256, 64, 2, 4, 2, 5)
+    X(256, 256, 64, 2, 4, 2, 5)    \
+    X(256, 256, 64, 2, 4, 2, 6)

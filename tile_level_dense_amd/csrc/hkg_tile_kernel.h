@@ -189,10 +189,11 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     // SCHED 6: the persistent ping-pong (one workgroup per compute unit
-    // walking several tiles, hkg_tile_persistent.h); with a fused epilogue,
-    // which stages through LDS, the one-tile ping-pong below.
-    if constexpr (SCHED == 6 && !EPI && !MX && !GROUPED) {
-        pingpong_persistent<WM, WN>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc, smem);
+    // walking several tiles or grouped items, hkg_tile_persistent.h); with a
+    // fused epilogue, which stages through LDS, the one-tile ping-pong below.
+    if constexpr (SCHED == 6 && !EPI && !MX) {
+        pingpong_persistent<WM, WN, GROUPED>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc,
+                                             smem, offs, G, split_k, ws, counters);
         return;
     }
 

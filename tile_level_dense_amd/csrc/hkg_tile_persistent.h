@@ -20,7 +20,18 @@
 //
 // Waits: every vmcnt wait counts only the buffer->LDS copies issued after
 // the ones it needs (loads complete in order among themselves); the C stores
-// of a finished tile can only make such a wait longer, never shorter.
+// of a finished tile, and the loads of expert offsets in grouped mode, can
+// only make such a wait longer, never shorter.
+//
+// GROUPED: the workgroup's items are tiles of the grouped (mixture-of-
+// experts) list instead, walked as the one-tile grouped loop walks them (the
+// same tiles, order and chiplet parts), the last of them possibly one half
+// of K of a tile of a split last round (its partial summed with the other
+// half's after the stream ends).  Only the position of the B copies, which
+// runs ahead of the others, looks a tile up (a forward scan over the expert
+// offsets); the A-copy position is one stage behind it and the compute
+// position one stage behind that, so when either crosses into a new item
+// the position ahead of it stands on that item's first stage and is copied.
 #pragma once
 
 #include <type_traits>
@@ -31,11 +42,12 @@
 namespace hkg {
 namespace {
 
-template <int WM, int WN>
+template <int WM, int WN, bool GROUPED>
 __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av, const void* __restrict__ Bv,
                                                     uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
                                                     int tiles_n, int win_w, int chunk_c, int lda, int ldb, int ldc,
-                                                    char* smem)
+                                                    char* smem, const int* __restrict__ offs, int G, int split_k,
+                                                    float* __restrict__ ws, int* __restrict__ counters)
 {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -80,37 +92,163 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     const int a_row = wm * WTM - 128 * g + lrow;
     const int b_row = wn * WTN + lrow;
 
-    // The workgroup's tiles and its stream of stages.
-    const int total = tiles_m * tiles_n;
-    const int G = gridDim.x;
-    const int ntiles = ((int)blockIdx.x < total) ? (total - (int)blockIdx.x + G - 1) / G : 0;
+    // The workgroup's items and its stream of stages.
     const int nk = (K + BK - 1) / BK;
-    const int U = ntiles * nk;
+    int n_items = 0;                        // items of this workgroup
+    int n_whole = 0;                        // of which whole tiles (all of K)
+    int unit = -1;                          // grouped: unit of the split last round, if any
+    int64_t first = blockIdx.x, stride = gridDim.x, whole = 0;
+    const int per_split = (nk + 1) / 2;     // stages of a split unit's first half
+
+    // Grouped mode.  Expert g owns rows [offs[g-1], offs[g]) of A and C and
+    // the N x K weight g of B; offsets are clamped into [0, M] and made non-
+    // decreasing per expert, so any offsets keep every access in bounds.
+    auto expert_rows = [&](int e, int& r0, int& r1) {
+        r0 = e > 0 ? min(max(offs[e - 1], 0), M) : 0;
+        r1 = max(r0, min(offs[e], M));
+    };
+    // Lane l: expert gb + l's tile count and the inclusive prefix over the
+    // 64 experts from gb (64-bit: clamped offsets may overlap).
+    auto chunk = [&](int gb, int64_t& tiles_l, int64_t& incl_l) {
+        const int e = gb + lane;
+        tiles_l = 0;
+        if (e < G) {
+            int r0, r1;
+            expert_rows(e, r0, r1);
+            tiles_l = (int64_t)((r1 - r0 + BM - 1) / BM) * tiles_n;
+        }
+        incl_l = tiles_l;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t o = __shfl_up(incl_l, d, 64);
+            if (lane >= d)
+                incl_l += o;
+        }
+    };
+    auto uniform64 = [](int64_t v) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    if constexpr (!GROUPED) {
+        const int total = tiles_m * tiles_n;
+        const int P = gridDim.x;
+        n_items = ((int)blockIdx.x < total) ? (total - (int)blockIdx.x + P - 1) / P : 0;
+        n_whole = n_items;
+    } else {
+        // The tiles of all experts form one list, expert after expert, each
+        // expert's column-first in windows of 8 tile rows.  Whole rounds of P
+        // (grid) tiles: with P a multiple of 8 and chunk_c != 0 the list is
+        // cut into 8 contiguous parts and the workgroups of XCD x (b mod 8
+        // under round-robin dispatch) walk part x; otherwise b, b + P, ...
+        // When the last round's R tiles (total mod P) fill at most half the
+        // grid and split_k is 2, each is split into two halves of K (units
+        // 2r and 2r + 1 of its tile r), cut into 8 contiguous parts the same
+        // way, and a workgroup's unit is its last item.
+        int64_t total = 0;
+        for (int gb = 0; gb < G; gb += 64) {
+            int64_t tl, il;
+            chunk(gb, tl, il);
+            total += uniform64(__shfl(il, 63, 64));
+        }
+        const int64_t P = gridDim.x;
+        const int64_t rem = total % P;
+        const bool tail_split = split_k == 2 && rem > 0 && 2 * rem <= P && nk >= 2;
+        whole = tail_split ? total - rem : total;
+        int64_t limit = whole;
+        if (chunk_c != 0 && P % 8 == 0 && whole >= P) {
+            const int64_t x = blockIdx.x % 8;
+            first = whole * x / 8 + blockIdx.x / 8;
+            stride = P / 8;
+            limit = whole * (x + 1) / 8;
+        }
+        if (tail_split) {
+            const int64_t units = 2 * rem;
+            const int64_t x = blockIdx.x % 8, i = blockIdx.x / 8;
+            const int64_t u0 = units * x / 8, u1 = units * (x + 1) / 8;
+            if (P % 8 == 0) {
+                if (u0 + i < u1)
+                    unit = (int)(u0 + i);
+            } else if ((int64_t)blockIdx.x < units) {
+                unit = (int)blockIdx.x;
+            }
+        }
+        n_whole = first < limit ? (int)((limit - first + stride - 1) / stride) : 0;
+        n_items = n_whole + (unit >= 0 ? 1 : 0);
+    }
+    const int unit_k0 = min(nk, (unit & 1) * per_split);
+    const int U = n_whole * nk + (unit >= 0 ? min(nk, unit_k0 + per_split) - unit_k0 : 0);
     if (U == 0)
         return;
 
-    // A position in the stream: tile j of this workgroup (its m0, n0 and
-    // buffer descriptors) and stage s of that tile.
+    // A position in the stream: item j of this workgroup (its C rows m0 ..
+    // m_lim - 1, columns n0 .., buffer descriptors, stages s_end - 1 at most)
+    // and stage s of it; gb, tb: where the scan over the experts stands.
     struct Pos {
-        int j, s, m0, n0;
+        int j, s, s_end, m0, m_lim, n0;
         __amdgpu_buffer_rsrc_t ra, rb;
+        int gb;
+        int64_t tb;
     };
     auto tile_at = [&](int j, Pos& p) {
         p.j = j;
         p.s = 0;
-        int tm = 0, tn = 0;
-        if (j < ntiles)
-            tile_order((int)blockIdx.x + j * G, tiles_m, tiles_n, win_w, chunk_c, tm, tn);
-        p.m0 = tm * BM;
-        p.n0 = tn * BN;
-        const int rows_a = min(BM, M - p.m0), rows_b = min(BN, N - p.n0);
-        p.ra = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Av + (size_t)p.m0 * a_rb), 0,
-                                                 (int)(rows_a * a_rb), kW3);
-        p.rb = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Bv + (size_t)p.n0 * b_rb), 0,
-                                                 (int)(rows_b * b_rb), kW3);
+        p.s_end = nk;
+        if constexpr (!GROUPED) {
+            int tm = 0, tn = 0;
+            if (j < n_items)
+                tile_order((int)blockIdx.x + j * (int)gridDim.x, tiles_m, tiles_n, win_w, chunk_c, tm, tn);
+            p.m0 = tm * BM;
+            p.n0 = tn * BN;
+            p.m_lim = M;
+            const int rows_a = min(BM, M - p.m0), rows_b = min(BN, N - p.n0);
+            p.ra = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Av + (size_t)p.m0 * a_rb), 0,
+                                                     (int)(rows_a * a_rb), kW3);
+            p.rb = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Bv + (size_t)p.n0 * b_rb), 0,
+                                                     (int)(rows_b * b_rb), kW3);
+        } else {
+            if (j >= n_items)               // past the last item: copies read nothing
+                return;
+            const bool half = j == n_whole;
+            const int64_t t = half ? whole + unit / 2 : first + (int64_t)j * stride;
+            if (half) {
+                p.s = unit_k0;
+                p.s_end = min(nk, unit_k0 + per_split);
+            }
+            // Expert of list tile t: items come in increasing t, so the scan
+            // only moves forward.
+            int64_t tiles_l, incl_l;
+            chunk(p.gb, tiles_l, incl_l);
+            int64_t chunk_total = uniform64(__shfl(incl_l, 63, 64));
+            while (t >= p.tb + chunk_total) {
+                p.tb += chunk_total;
+                p.gb += 64;
+                chunk(p.gb, tiles_l, incl_l);
+                chunk_total = uniform64(__shfl(incl_l, 63, 64));
+            }
+            const uint64_t hit = __ballot(p.tb + incl_l > t);
+            const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+            const int e = p.gb + l;
+            const int64_t t0 = p.tb + uniform64(__shfl(incl_l - tiles_l, l, 64));
+            int r0, r1;
+            expert_rows(e, r0, r1);
+            r0 = __builtin_amdgcn_readfirstlane(r0);
+            r1 = __builtin_amdgcn_readfirstlane(r1);
+            int tm, tn;
+            tile_order((int)(t - t0), (r1 - r0 + BM - 1) / BM, tiles_n, 8, 0, tm, tn);
+            p.m0 = r0 + tm * BM;
+            p.m_lim = r1;
+            p.n0 = tn * BN;
+            const char* bg = (const char*)Bv + (size_t)e * (size_t)N * b_rb;
+            const int rows_a = min(BM, r1 - p.m0), rows_b = min(BN, N - p.n0);
+            p.ra = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)Av + (size_t)p.m0 * a_rb), 0,
+                                                     (int)(rows_a * a_rb), kW3);
+            p.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(bg + (size_t)p.n0 * b_rb), 0, (int)(rows_b * b_rb),
+                                                     kW3);
+        }
     };
     auto advance = [&](Pos& p) {
-        if (++p.s == nk)
+        if (++p.s == p.s_end)
             tile_at(p.j + 1, p);
     };
 
@@ -119,7 +257,7 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     // and the copy writes zeros nobody reads.
     auto copy_half = [&](const Pos& p, bool is_a, char* dst) {
         const int k0 = p.s * BK;
-        const bool k_out = p.j >= ntiles || k0 + p_k >= K;
+        const bool k_out = p.j >= n_items || k0 + p_k >= K;
         const uint32_t rb = is_a ? a_rb : b_rb;
         const uint32_t off0 = k_out ? kOOR : (is_a ? p_off_a : p_off_b) + (uint32_t)k0 * 2u;
         const uint32_t p_step = (uint32_t)(4 * RPW) * rb;
@@ -156,13 +294,13 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = p.m0 + wm * WTM + i * 16 + lrow;
-            uint16_t* crow = C + (size_t)(m < M ? m : 0) * (size_t)ldc;
+            uint16_t* crow = C + (size_t)(m < p.m_lim ? m : 0) * (size_t)ldc;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int n = p.n0 + wn * WTN + j * 16 + lgrp * 4;
                 __builtin_amdgcn_sched_barrier(0);
                 const uint2 h = __builtin_bit_cast(uint2, __builtin_convertvector(acc[i][j], bf16x4));
-                if (m < M) {
+                if (m < p.m_lim) {
                     if (vec_ok && n + 3 < N) {
                         *(uint2*)(crow + n) = h;
                     } else {
@@ -186,6 +324,8 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     // Stream positions: the stage being computed, the next A copy (one
     // stage ahead) and the next B copy (two stages ahead).
     Pos pc, pa, pb;
+    pc.gb = 0;
+    pc.tb = 0;
     tile_at(0, pc);
     pa = pc;
     pb = pc;
@@ -229,16 +369,26 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
                     for (int j = 0; j < FN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[s][j], af[s][i], acc[i][j], 0, 0, 0);
             fence();
-            if (pc.s == nk - 1)
-                store_tile(pc);
+            if (pc.s == pc.s_end - 1 && (!GROUPED || pc.j < n_whole))
+                store_tile(pc);             // (a split unit's partial is summed after the stream)
             fence();
             // all but this phase's B copies
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
             if (!G1 || u + 1 < U)
                 phase_barrier();
-            advance(pc);
-            advance(pa);
-            advance(pb);
+            if constexpr (GROUPED) {
+                // followers take the position ahead of them when they cross
+                // into its item (see the head of this file)
+                if (++pc.s == pc.s_end)
+                    pc = pa;
+                if (++pa.s == pa.s_end)
+                    pa = pb;
+                advance(pb);
+            } else {
+                advance(pc);
+                advance(pa);
+                advance(pb);
+            }
             u3 = u3 == 2 ? 0 : u3 + 1;
             pb3 = pb3 == 2 ? 0 : pb3 + 1;
         }
@@ -248,6 +398,71 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     else
         stream(std::integral_constant<bool, false>{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    if constexpr (GROUPED) if (unit >= 0) {
+        // The last item was half (unit & 1) of K of a tile of the split last
+        // round, and acc holds that partial.  Each half writes its fp32 tile
+        // to its own slot of ws (tile-local, BN floats per row, device-scope
+        // stores); the half that arrives second adds the other's partial to
+        // its own and stores the tile.  fp32 addition is commutative, so the
+        // sum is the same whichever half arrives second.  The ordering
+        // argument is the split-K arrival protocol in hkg_internal.h.
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        constexpr int kDev = 16;            // cache-policy operand: sc1, device scope
+        constexpr int SLOT = BM * BN;
+        Pos pu;
+        pu.gb = 0;
+        pu.tb = 0;
+        tile_at(n_whole, pu);
+        const __amdgpu_buffer_rsrc_t mine =
+            __builtin_amdgcn_make_buffer_rsrc(ws + (size_t)unit * SLOT, 0, SLOT * 4, kW3);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int off = ((wm * WTM + i * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), mine, off, 0, kDev);
+            }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Every wave is past its last read of the stages and its copies have
+        // landed: the first word of LDS carries the arrival result.
+        __syncthreads();
+        int* const arrived = (int*)smem;
+        if (threadIdx.x == 0)
+            *arrived = __hip_atomic_fetch_add(&counters[unit >> 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*arrived != 1)
+            return;
+        const __amdgpu_buffer_rsrc_t other =
+            __builtin_amdgcn_make_buffer_rsrc(ws + (size_t)(unit ^ 1) * SLOT, 0, SLOT * 4, kW3);
+        // RBLK block rows at a time (16 loads in flight beside the
+        // accumulators); the empty asm keeps each sum here rather than sunk
+        // into the store, which would hold every loaded partial until then.
+        constexpr int RBLK = FN >= 16 ? 1 : (16 / FN < FM ? 16 / FN : FM);
+        static_assert(FM % RBLK == 0, "whole groups of block rows");
+#pragma unroll
+        for (int i0 = 0; i0 < FM; i0 += RBLK) {
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 o[RBLK][FN];
+#pragma unroll
+            for (int ii = 0; ii < RBLK; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int off = ((wm * WTM + (i0 + ii) * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                    o[ii][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(other, off, 0, kDev));
+                }
+#pragma unroll
+            for (int ii = 0; ii < RBLK; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    acc[i0 + ii][j] += o[ii][j];
+                    asm volatile("" : "+v"(acc[i0 + ii][j]));
+                }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[unit >> 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_tile(pu);
+    }
 }
 
 }  // namespace
