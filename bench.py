@@ -106,16 +106,25 @@ def graph_warmup(warmup, sets):
 # loaded level, and a 5-launch warm-up timed the ramp, ~10% slow at 8192^3),
 # then WINDOWS windows of K calls each, every window bracketed by device
 # synchronisation and timed with HIP events on the stream the calls are
-# launched on; the leg's figure is the median window.  SCLK / MCLK are
-# sampled during the windows (amdsmi; null where unavailable).
+# launched on; the leg's figure is the median window.  Engine and memory
+# clocks and socket power are sampled from the start of the settle period to
+# the end of the windows (amdsmi's metrics table, refreshed by the firmware
+# about once a second; null where unavailable or not refreshed meanwhile).
+# The 8192^3 legs settle SQUARE_SETTLE x longer (1.2 s by default), so a
+# refresh falls while they run and their clocks are those of the loaded GPU.
 SETTLE_S = 0.5
+SQUARE_SETTLE = 2.4
 WINDOWS = 5
 TIMINGS = {}
 
 
 class ClockSampler:
-    """Background sampling of the GPU's current engine and memory clocks and
-    activity through amdsmi (optional: every failure leaves the figures null)."""
+    """Background sampling of the GPU's engine clock, memory clock, socket
+    power and activity through amdsmi's metrics table (optional: every
+    failure leaves the figures null).  The firmware refreshes that table
+    about once a second, so a leg's figures come only from refreshes made
+    while the leg was running (a reading from before it would show the idle
+    clock); the engine clock is the mean over the XCDs."""
 
     def __init__(self):
         self.handle = None
@@ -135,11 +144,16 @@ class ClockSampler:
         self._stop = None
 
     def read(self):
-        a = self.amdsmi
-        sclk = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"]
-        mclk = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.MEM)["clk"]
-        act = a.amdsmi_get_gpu_activity(self.handle).get("gfx_activity")
-        return sclk, mclk, act
+        """(engine MHz, memory MHz, gfx activity %, socket W, firmware timestamp)."""
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+
+        def num(v):
+            return v if isinstance(v, (int, float)) and v != 0xFFFF else None
+        xcd = [num(v) for v in (m.get("current_gfxclks") or [])]
+        xcd = [v for v in xcd if v is not None]
+        sclk = float(np.mean(xcd)) if xcd else num(m.get("current_gfxclk"))
+        return (sclk, num(m.get("current_uclk")), num(m.get("average_gfx_activity")),
+                num(m.get("current_socket_power")), m.get("firmware_timestamp"))
 
     def activity(self, n=5, gap_s=0.02):
         """gfx activity % over n samples with nothing of ours running (idle check)."""
@@ -178,21 +192,35 @@ class ClockSampler:
             self._thread = None
         if not self.samples:
             return None
-        sc = [x[0] for x in self.samples if x[0] is not None]
-        mc = [x[1] for x in self.samples if x[1] is not None]
-        return dict(samples=len(self.samples),
-                    sclk_mhz_median=float(np.median(sc)) if sc else None,
-                    sclk_mhz_min=float(min(sc)) if sc else None, sclk_mhz_max=float(max(sc)) if sc else None,
-                    mclk_mhz_median=float(np.median(mc)) if mc else None)
+        # keep the refreshes made after sampling began (the first reading's
+        # firmware timestamp marks a table filled before the leg)
+        first_ts = self.samples[0][4]
+        fresh = [x for x in self.samples if x[4] is not None and x[4] != first_ts]
+        refreshes = len(set(x[4] for x in fresh))
+        if not fresh:
+            return dict(samples=len(self.samples), metric_refreshes=0, sclk_mhz_median=None,
+                        note="no metrics refresh while the leg ran")
+        sc = [x[0] for x in fresh if x[0] is not None]
+        mc = [x[1] for x in fresh if x[1] is not None]
+        pw = [x[3] for x in fresh if x[3] is not None]
+        return dict(samples=len(fresh), metric_refreshes=refreshes,
+                    sclk_mhz_median=round(float(np.median(sc)), 1) if sc else None,
+                    sclk_mhz_min=round(float(min(sc)), 1) if sc else None,
+                    sclk_mhz_max=round(float(max(sc)), 1) if sc else None,
+                    mclk_mhz_median=float(np.median(mc)) if mc else None,
+                    socket_power_w_median=float(np.median(pw)) if pw else None)
 
 
 CLOCKS = None
 
 
-def time_launches(torch, fn, steps, warmup, label=None, per_call=1):
+def time_launches(torch, fn, steps, warmup, label=None, per_call=1, settle_s=None):
     """Median ms per fn() over WINDOWS windows of `steps` calls each, after
-    `warmup` calls and SETTLE_S seconds of untimed calls; per_call divides
-    (fn launching that many GEMMs, e.g. a graph over rotating buffers)."""
+    `warmup` calls and settle_s (default SETTLE_S) seconds of untimed calls;
+    per_call divides (fn launching that many GEMMs, e.g. a graph over
+    rotating buffers).  Clocks are sampled from the start of the settle
+    calls to the end of the windows, the load being steady throughout."""
+    settle_s = SETTLE_S if settle_s is None else settle_s
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -204,7 +232,9 @@ def time_launches(torch, fn, steps, warmup, label=None, per_call=1):
     stop.record()
     torch.cuda.synchronize()
     est_ms = max(start.elapsed_time(stop), 1e-3)
-    settle = int(min(200000, max(1, np.ceil(SETTLE_S * 1e3 / est_ms))))
+    settle = int(min(200000, max(1, np.ceil(settle_s * 1e3 / est_ms))))
+    if CLOCKS is not None:
+        CLOCKS.start()
     done = 0
     while done < settle:
         chunk = min(settle - done, max(1, int(20.0 / est_ms)))     # ~20 ms between host syncs
@@ -212,8 +242,6 @@ def time_launches(torch, fn, steps, warmup, label=None, per_call=1):
             fn()
         done += chunk
         torch.cuda.synchronize()
-    if CLOCKS is not None:
-        CLOCKS.start()
     wins = []
     for _ in range(WINDOWS):
         torch.cuda.synchronize()
@@ -245,7 +273,8 @@ def bench_square(torch, hkg, steps, warmup):
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     plan = hkg.plan(M, N, K)
     log("plan", plan.kernel_name.decode(), plan.reason.decode())
-    ms = time_launches(torch, lambda: hkg.gemm(a, b, out=c), steps, warmup, label="square")
+    ms = time_launches(torch, lambda: hkg.gemm(a, b, out=c), steps, warmup, label="square",
+                       settle_s=SQUARE_SETTLE * SETTLE_S)
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     log("square: %.3f ms/step, %.1f TFLOP/s" % (ms, tflops))
@@ -253,10 +282,11 @@ def bench_square(torch, hkg, steps, warmup):
     # inputs: its cost over the plain GEMM.
     bias = torch.linspace(-1.0, 1.0, N, device="cuda").to(torch.bfloat16)
     ms_e = time_launches(torch, lambda: hkg.gemm(a, b, out=c, bias=bias, epilogue="bias_gelu"), steps, warmup,
-                         label="square_bias_gelu")
+                         label="square_bias_gelu", settle_s=SQUARE_SETTLE * SETTLE_S)
     log("square with bias+GELU epilogue: %.3f ms/step, %.1f TFLOP/s" % (ms_e, flops / (ms_e * 1e-3) / 1e12))
     # Context only: the vendor library on the same inputs, same protocol.
-    ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup, label="square_torch_mm")
+    ms_v = time_launches(torch, lambda: torch.mm(a, b.t(), out=c), steps, warmup, label="square_torch_mm",
+                         settle_s=SQUARE_SETTLE * SETTLE_S)
     tflops_v = flops / (ms_v * 1e-3) / 1e12
     log("square, torch.mm (hipBLASLt) for context: %.3f ms/step, %.1f TFLOP/s" % (ms_v, tflops_v))
     # Context: the same kernel on constant operands (every element 0.01147),
@@ -265,7 +295,8 @@ def bench_square(torch, hkg, steps, warmup):
     # power limit, not the schedule.
     ac = torch.full((M, K), 0.01147, dtype=torch.bfloat16, device="cuda")
     bc = torch.full((N, K), 0.01147, dtype=torch.bfloat16, device="cuda")
-    ms_c = time_launches(torch, lambda: hkg.gemm(ac, bc, out=c), steps, warmup, label="square_constant_inputs")
+    ms_c = time_launches(torch, lambda: hkg.gemm(ac, bc, out=c), steps, warmup, label="square_constant_inputs",
+                         settle_s=SQUARE_SETTLE * SETTLE_S)
     del ac, bc
     log("square on constant inputs (power context): %.3f ms/step, %.1f TFLOP/s" % (ms_c, flops / (ms_c * 1e-3) / 1e12))
     return dict(M=M, N=N, K=K, ms=ms, tflops=tflops, flops=flops, plan=plan, vendor_tflops=tflops_v,
@@ -751,7 +782,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(sq["tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": tr, "kernel": tile_kernel,
                      "per_launch": "2 M N K = %.4g flop per launch (one launch per step)" % sq["flops"],
-                     "clocks_during_timing": (TIMINGS.get("square") or {}).get("clocks")},
+                     "clocks_during_timing": (TIMINGS.get("square") or {}).get("clocks"),
+                     "vendor_clocks_during_timing": (TIMINGS.get("square_torch_mm") or {}).get("clocks")},
         "decode": {"workload": "decode_16x4096x4096: M = 16, N = 4096, K = 4096",
                    "value": round(dec["gbps"], 1), "unit": "GB/s",
                    "frac_of_hbm": round(dec["gbps"] / PEAK_HBM_GBPS, 4),
@@ -805,8 +837,10 @@ def main():
         "timing": {"protocol": "per leg: W warm-up calls, then untimed back-to-back calls for %.2f s of device "
                                "time (clock settle), then %d windows of K calls, each bracketed by device "
                                "synchronisation and timed with HIP events on the launch stream; the figure is "
-                               "the median window; clocks sampled with amdsmi during the windows" % (SETTLE_S, WINDOWS),
-                   "settle_s": SETTLE_S, "windows": WINDOWS,
+                               "the median window (8192^3 legs settle %.2f s); engine clock (mean over the XCDs), "
+                               "memory clock and socket power from amdsmi's metrics table, keeping refreshes made "
+                               "while the leg ran" % (SETTLE_S, WINDOWS, SQUARE_SETTLE * SETTLE_S),
+                   "settle_s": SETTLE_S, "square_settle_s": SQUARE_SETTLE * SETTLE_S, "windows": WINDOWS,
                    "idle_gfx_activity_pct_before": idle, "legs": TIMINGS},
         "mxfp8": {
             "square": {"workload": "mx_square_8192: E4M3 A, B N(0,1), E8M0 scale per 32 k, M = N = K = 8192",

@@ -1,6 +1,7 @@
 """Host-side checks of bench.py: the one-GPU contract, the roofline each
-workload is reported against, and that a traffic figure is only reported
-for the kernel and source it was measured on."""
+workload is reported against, that a traffic figure is only reported
+for the kernel and source it was measured on, and that clock figures come
+only from metrics refreshed while a leg ran."""
 import json
 import os
 import subprocess
@@ -40,3 +41,19 @@ def test_traffic_only_for_its_kernel_and_source():
         assert (got == e["bytes_per_launch"]) if current else got is None
         assert bench.measured_traffic(workload, e["kernel"] + "_other") is None
     assert bench.measured_traffic("no_such_workload", "tile_256x256x64_s2_w4x2_p5") is None
+
+
+def test_clock_sampler_keeps_only_refreshes_made_while_the_leg_ran():
+    # (engine MHz, memory MHz, activity %, socket W, firmware timestamp): the
+    # first reading's table predates the leg, so only later refreshes count.
+    cs = bench.ClockSampler.__new__(bench.ClockSampler)
+    cs._thread = None
+    cs.samples = [(2400.0, 2000, 0, 300, 10), (2400.0, 2000, 0, 300, 10), (1800.0, 2000, 100, 1390, 11),
+                  (1800.0, 2000, 100, 1390, 11), (1790.0, 2000, 100, 1395, 12)]
+    r = cs.stop()
+    assert r["metric_refreshes"] == 2 and r["samples"] == 3
+    assert r["sclk_mhz_median"] == 1800.0 and r["sclk_mhz_min"] == 1790.0
+    assert r["socket_power_w_median"] == 1390.0
+    cs.samples = [(2400.0, 2000, 0, 300, 10)] * 3
+    r = cs.stop()
+    assert r["metric_refreshes"] == 0 and r["sclk_mhz_median"] is None
