@@ -162,8 +162,10 @@ def test_plan_boundaries():
     assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (64, 64, 1, 256)
     p = hkg.plan(512, 4096, 4096)        # 128 x 128 needs split 2, 128 x 64 fills unsplit
     assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 64, 1, 256)
-    p = hkg.plan(256, 12288, 4096)       # both unsplit: the larger tile
-    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 128, 1, 192)
+    p = hkg.plan(256, 12288, 4096)       # unsplit: the smallest tile filling one round (128 x 128: 192 tiles)
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 96, 1, 256)
+    p = hkg.plan(256, 16384, 4096)       # 128 x 96 would take two rounds: 128 x 128 fills one
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 128, 1, 256)
     # tile grid under one workgroup per CU: split-K across workgroups,
     # at least 8 k-tiles per split; the 128-row tile is skipped at M = 64
     # (half its rows would be padding)

@@ -294,7 +294,10 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     // tiles) 39.1 us, 128 x 128 split 2 44.8 us; M = 256, N = K = 4096:
     // 64 x 64 unsplit 21.9 us, 128 x 64 split 2 22.6 us; 256^3: 64 x 64 3.8 us,
     // 128 x 128 7.2 us; 512^3: 64 x 64 unsplit 5.1 us, split 2 6.7 us,
-    // 128 x 128 split 2 13.1 us.
+    // 128 x 128 split 2 13.1 us.  128 x 96 where it is the smallest tile
+    // filling one round (M = 256, N = 12288: 256 tiles) against 128 x 128 (192
+    // tiles): 44.7 vs 51.2 us; M = 1024, N = 3072: 41.8 vs 46.9; M = 512,
+    // N = 5120: 38.9 vs 46.7; M = 128, N = 18432: 47.0 vs 53.9 (K = 4096).
     int best = -1;
     int64_t best_split = 0, best_area = 0;
     bool best_fits = false;

@@ -30,7 +30,8 @@
     X(64, 128, 64, 4, 2, 2, 2)    \
     X(128, 64, 64, 4, 2, 2, 2)     \
     X(256, 256, 64, 2, 4, 2, 6)    \
-    X(64, 96, 64, 4, 2, 2, 2)
+    X(64, 96, 64, 4, 2, 2, 2)      \
+    X(128, 96, 64, 4, 2, 2, 2)
 
 // MXFP8 instantiations (E4M3 operands, E8M0 scale per 32 k), same fields;
 // BK = 128 k (128 bytes per row, as the bf16 BK = 64), SCHED 5 or 0 (a
