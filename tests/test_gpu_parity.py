@@ -166,6 +166,18 @@ def test_ragged_shapes(hkg, shape):
     full_check(run(hkg, A, B), A, B)
 
 
+def test_planner_wide_n_streaming_tile(hkg):
+    # Mid-size M, wide N: the planner's 128 x 96 streaming tile (one round of
+    # 256 tiles; 128 x 128 would leave 64 CUs idle), ragged M and K, every
+    # output against the oracle.
+    M, N, K = 200, 12288, 520
+    p = hkg.plan(M, N, K)
+    _say("wide-N streaming tile", (M, N, K), p.kernel_name.decode())
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (128, 96, 1, 256), p
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=96)
+    full_check(run(hkg, A, B), A, B)
+
+
 # ---------------------------------------------------- forced plans
 def forced(hkg, A, B, edit):
     M, K = A.shape
