@@ -182,14 +182,30 @@ def test_plan_boundaries():
         assert (p.tile_m, p.tile_n, p.split_k) == (64, 64, 1), shape
     p = hkg.plan(64, 4096, 128)
     assert p.split_k == 1 and p.workspace_bytes == 0
-    # compute-bound ladder: 256 x 256 from 3/4 of the CUs on, then the
-    # two-stage 128 x 128 tile while its tiles outnumber the CUs
-    for shape, name in [((3072, 4096, 1024), "tile_256x256x64_s2"), ((2048, 2048, 1024), "tile_128x128x64_s4"),
-                        ((4096, 2048, 1024), "tile_128x128x64_s2"), ((1024, 8192, 4096), "tile_128x128x64_s2"),
+    # compute-bound ladder: 256 x 256 from 3/4 of the CUs on; then one round
+    # of k-interleaved 128 x 256 tiles (160 to 256 of them, K >= 1024); the
+    # two-stage 128 x 128 tile while its tiles outnumber the CUs; one round
+    # of k-interleaved 128 x 128 tiles (224 to 256, K >= 1024)
+    for shape, name in [((3072, 4096, 1024), "tile_256x256x64_s2"),
+                        ((2048, 2048, 1024), "tile_128x128x64_s3_w2x2_p7"),
+                        ((4096, 2048, 1024), "tile_128x256x64_s3_w2x2_p7"),
+                        ((1024, 8192, 4096), "tile_128x256x64_s3_w2x2_p7"),
+                        ((1280, 4096, 4096), "tile_128x256x64_s3_w2x2_p7"),     # 160 tiles
+                        ((1152, 4096, 4096), "tile_128x128x64_s2_w2x2_p2"),     # 144 tiles of 128 x 256
+                        ((2560, 4096, 1024), "tile_128x128x64_s2_w2x2_p2"),     # 320 tiles of 128 x 256
+                        ((2048, 4096, 256), "tile_128x128x64_s2_w2x2_p2"),      # K under 1024
+                        ((150, 40960, 4096), "tile_128x128x64_s2_w2x2_p2"),     # rows 41% padding
+                        ((256, 16384, 4096), "tile_128x128x64_s3_w2x2_p7"),
+                        ((1024, 3584, 4096), "tile_128x128x64_s3_w2x2_p7"),     # 224 tiles
                         ((8192, 8192, 8192), "tile_256x256x64_s2")]:
         p = hkg.plan(*shape)
         assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and p.split_k == 1
         assert p.kernel_name.decode().startswith(name), (shape, p)
+    p = hkg.plan(1024, 4096, 4096)
+    assert (p.waves, p.block_x, p.grid_x, p.lds_bytes) == (8, 512, 256, 3 * 256 * 128), p
+    assert "k-interleaved" in p.reason.decode()
+    p = hkg.plan(1024, 3072, 4096)          # 192 tiles of 128 x 128: the streaming 128 x 96 fills a round
+    assert (p.tile_m, p.tile_n, p.grid_x) == (128, 96, 256)
 
 
 @pytest.mark.parametrize("shape", [(-1, 4, 8), (4, -1, 8), (4, 4, -8), (2**31, 4, 8), (4, 4, 2**31),

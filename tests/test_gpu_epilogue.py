@@ -67,12 +67,12 @@ def run_forced(hkg, A, B, bias, epi, edit=None):
 
 def _tile(hkg, variant, split=1):
     from tile_level_dense_amd import build as hkg_build
-    bm, bn, bk, stages, wm, wn, _ = hkg_build.tile_configs()[variant]
+    bm, bn, bk, stages, wm, wn, sc = hkg_build.tile_configs()[variant]
 
     def edit(p):
         p.kernel_id = hkg.HKG_KERNEL_TILE
         p.variant = variant
-        p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn
+        p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn * (2 if sc == 7 else 1)
         p.split_k = split
         p.grid_y = split
         p.workspace_bytes = split * p.M * p.N * 4 if split > 1 else 0
@@ -107,6 +107,8 @@ CASES = [
     ("pipelined_256", (300, 500, 136), lambda h: _tile(h, 4)),
     ("tile_256x128", (129, 300, 264), lambda h: _tile(h, 1)),
     ("tile_128_split3", (200, 333, 1032), lambda h: _tile(h, 2, 3)),
+    ("kinter_128x256", (300, 530, 392), lambda h: _tile(h, 14)),
+    ("kinter_128x128", (129, 270, 136), lambda h: _tile(h, 15)),
     ("planner_skinny", (16, 1000, 2056), None),
     ("skinny_split3", (20, 300, 4096), lambda h: _skinny(h, 1, 3)),
     ("skinny_nb4", (9, 100, 520), lambda h: _skinny(h, 5, 1)),

@@ -166,6 +166,72 @@ def test_ragged_shapes(hkg, shape):
     full_check(run(hkg, A, B), A, B)
 
 
+# One round of k-interleaved tiles (two 4-wave groups over the whole tile,
+# alternate 64-k stages, partials added through LDS), as the planner picks
+# them: ragged M, N and K, an odd number of stages (the last one padded
+# with zeros), every output; a second run is bit-identical.
+KINTER_SHAPES = [((1300, 4000, 1032), "tile_128x256x64_s3_w2x2_p7"),
+                 ((1280, 4096, 1096), "tile_128x256x64_s3_w2x2_p7"),
+                 ((1000, 3600, 1160), "tile_128x128x64_s3_w2x2_p7"),
+                 ((250, 16384, 1032), "tile_128x128x64_s3_w2x2_p7")]
+
+
+@pytest.mark.parametrize("shape,name", KINTER_SHAPES, ids=lambda v: "%dx%dx%d" % v if isinstance(v, tuple) else v)
+def test_kinter_planner_shapes(hkg, shape, name):
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    _say("k-interleaved", shape, p.kernel_name.decode())
+    assert p.kernel_name.decode() == name, p
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=M + N)
+    C1 = run(hkg, A, B)
+    full_check(C1, A, B)
+    assert np.array_equal(C1, run(hkg, A, B))
+
+
+def test_kinter_strided(hkg):
+    """Padded leading dimensions of A, B and C on the k-interleaved tile
+    (through the layout entry point's in-place path); C's padding kept."""
+    M, N, K = 1300, 4000, 1032
+    lda, ldb, ldc = K + 24, K + 8, N + 40
+    assert hkg.plan(M, N, K).kernel_name.decode() == "tile_128x256x64_s3_w2x2_p7"
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=7)
+    As = np.full((M, lda), 0x7FC1, dtype=np.uint16)
+    As[:, :K] = A
+    Bs = np.full((N, ldb), 0xFFC3, dtype=np.uint16)
+    Bs[:, :K] = B
+    a, b = dev(As), dev(Bs)
+    c = dev(np.full((M, ldc), 0x4B80, dtype=np.uint16))
+    _say("k-interleaved strided", (M, N, K))
+    st = hkg.hkg_gemm_bf16_ex(a.data_ptr(), lda, hkg.LAYOUT_ROW, b.data_ptr(), ldb, hkg.LAYOUT_ROW, None,
+                              c.data_ptr(), ldc, M, N, K, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == hkg.HKG_OK
+    torch.cuda.synchronize()
+    Cs = host(c)
+    assert (Cs[:, N:] == 0x4B80).all()
+    full_check(np.ascontiguousarray(Cs[:, :N]), A, B)
+
+
+@pytest.mark.parametrize("shape,name", [((2048, 4096, 4096), "tile_128x256x64_s3_w2x2_p7"),
+                                        ((1024, 4096, 4096), "tile_128x128x64_s3_w2x2_p7")],
+                         ids=lambda v: "%dx%dx%d" % v if isinstance(v, tuple) else v)
+def test_kinter_full_size_sampled(hkg, shape, name):
+    """The compute-bound middle at its real size: rows at every tile
+    boundary and 20000 random outputs against the oracle."""
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    _say("k-interleaved full size", shape, p.kernel_name.decode())
+    assert p.kernel_name.decode() == name, p
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=11)
+    C = run(hkg, A, B)
+    rows = sample_rows(M, tile=128)
+    gates.compare(C[rows], *oracle_rows(A, B, rows))
+    rng = np.random.default_rng(2)
+    ii = rng.integers(0, M, size=20000)
+    jj = rng.integers(0, N, size=20000)
+    Ce, Se, ae = oracle.gemm_entries(A, B, ii, jj)
+    gates.compare(C[ii, jj], Ce, Se, ae)
+
+
 def test_planner_wide_n_streaming_tile(hkg):
     # Mid-size M, wide N: the planner's 128 x 96 streaming tile (one round of
     # 256 tiles; 128 x 128 would leave 64 CUs idle), ragged M and K, every
@@ -192,10 +258,11 @@ def forced(hkg, A, B, edit):
 def force_tile(hkg, p, variant, win_w=None, chunk_c=None, split=1):
     """Edit plan p to run tile-kernel variant `variant` (hkg_tile_configs.h)."""
     from tile_level_dense_amd import build as hkg_build
-    bm, bn, bk, stages, wm, wn, _ = hkg_build.tile_configs()[variant]
+    bm, bn, bk, stages, wm, wn, sc = hkg_build.tile_configs()[variant]
     p.kernel_id = hkg.HKG_KERNEL_TILE
     p.variant = variant
-    p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn
+    # schedule 7: two groups, each a wm x wn grid over the whole tile
+    p.tile_m, p.tile_n, p.tile_k, p.waves = bm, bn, bk, wm * wn * (2 if sc == 7 else 1)
     p.split_k = split
     p.grid_y = split
     p.workspace_bytes = split * p.M * p.N * 4 if split > 1 else 0
@@ -229,7 +296,7 @@ TILE_SPLIT_SHAPES = [(300, 500, 136), (520, 1000, 392), (129, 40, 4104)]
 def _split_variants():
     from tile_level_dense_amd import build as hkg_build
     return [v for v, (bm, bn, bk, st, wm, wn, sc) in enumerate(hkg_build.tile_configs())
-            if (bm // wm // 16) * (bn // wn // 16) <= 16]
+            if (bm // wm // 16) * (bn // wn // 16) <= 16 and sc != 7]
 
 
 @pytest.mark.parametrize("variant", _split_variants())

@@ -272,10 +272,43 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
             fill_tile(p, TILE_LADDER[0], 1, M, N);
             return;
         }
+        // One round of k-interleaved tiles (schedule 7): 128 x 256 tiles
+        // when they fill 160 to 256 compute units, 128 x 128 tiles when they
+        // fill 224 to 256, for K of at least 1024 and rows at most a quarter
+        // padding.  Measured on MI355X (rotating buffers, us, k-interleaved
+        // vs the tile it replaces, torch.mm): 2048 x 4096 x 4096 59.0 vs 63.3
+        // (58.3); 1280 x 4096 x 4096 58.7 vs 65.3 (48.4); 1024 x 8192 x 8192
+        // 110.4 vs 121.3 (109.7); 256 x 32768 x 4096 78.1 vs 93.1 (76.0);
+        // 128 x 40960 x 4096 85.7 vs 94.7 (81.2); under 224 tiles with few
+        // tile rows or K = 1024 it loses 2-3%: 768 x 8192 x 4096 69.8 vs
+        // 68.2 (54.8), 640 x 8192 x 4096 66.9 vs 65.6, 1536 x 4096 x 1024
+        // 19.7 vs 19.3; below K = 1024 it loses more.  128 x 128 tiles:
+        // 1024 x 4096 x 4096 37.3 vs 45.4 (36.5); 512 x 8192 x 4096 44.9 vs
+        // 49.0 (42.6); 1024 x 4096 x 1024 13.8 vs 16.1 (19.6).  With fewer
+        // 128 x 128 tiles the streaming tiles win where they fill a round
+        // (512 x 6144 x 4096, 192 tiles: 55.3 vs 39.5 for 128 x 96 tiles).
+        if (K >= 1024) {
+            const TileShape w = tile_shape(TILE_KINTER[0]);
+            const int64_t tw = cdiv(M, w.bm) * cdiv(N, w.bn);
+            const bool rows_ok = 4 * (cdiv(M, w.bm) * w.bm - M) <= cdiv(M, w.bm) * w.bm;
+            if (rows_ok && 8 * tw >= 5 * kNumCUs && tw <= kNumCUs) {
+                fill_tile(p, TILE_KINTER[0], 1, M, N);
+                return;
+            }
+        }
         const TileShape t = tile_shape(TILE_LADDER[1]);
         if (cdiv(M, t.bm) * cdiv(N, t.bn) > kNumCUs) {
             fill_tile(p, TILE_LADDER[1], 1, M, N);
             return;
+        }
+        if (K >= 1024) {
+            const TileShape w = tile_shape(TILE_KINTER[1]);
+            const int64_t tw = cdiv(M, w.bm) * cdiv(N, w.bn);
+            const bool rows_ok = 4 * (cdiv(M, w.bm) * w.bm - M) <= cdiv(M, w.bm) * w.bm;
+            if (rows_ok && 8 * tw >= 7 * kNumCUs && tw <= kNumCUs) {
+                fill_tile(p, TILE_KINTER[1], 1, M, N);
+                return;
+            }
         }
     }
     // Smaller outputs: the operands are streamed from HBM a few times at most
@@ -309,7 +342,7 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
         if (i + 1 < n_stream && 4 * (tm * s.bm - M) > tm * s.bm)
             continue;
         int64_t split = 1;
-        if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {   // fp32 partials addressed in 32 bits
+        if (tm * tn < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) {   // fp32 partials addressed in 32 bits
             split = std::min<int64_t>(kNumCUs / (tm * tn), cdiv(K, s.bk) / 8);
             split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
         }
@@ -355,7 +388,7 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
                   s.stages, s.wm, s.wn, s.sched);
     std::snprintf(p->reason, sizeof p->reason, "%lldx%lld tiles of %dx%d (%d stages), split-K %lld on %d CUs%s",
                   (long long)tm, (long long)tn, s.bm, s.bn, s.stages, (long long)split, kNumCUs,
-                  s.sched == 6 ? ", persistent" : "");
+                  s.sched == 6 ? ", persistent" : s.sched == 7 ? ", k-interleaved" : "");
 }
 
 // Fill the skinny-kernel fields of p for (variant, split).
@@ -523,7 +556,7 @@ bool plan_matches_library(const hkg_plan_t* p)
         const TileShape s = tile_shape(p->variant);
         return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
                p->split_k >= 1 && p->split_k <= kMaxTileSplit &&
-               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn)) &&
+               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) &&
                (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
                p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
                cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
@@ -831,7 +864,7 @@ hkg_status_t make_mx_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     if (tiles > INT32_MAX)
         return HKG_ERR_UNSUPPORTED;
     int64_t split = 1;
-    if (tiles < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn)) {
+    if (tiles < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) {
         split = std::min<int64_t>(cdiv(kNumCUs, tiles), (K / 128) / 4);
         split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
     }
@@ -860,7 +893,7 @@ bool mx_plan_matches_library(const hkg_plan_t* p)
         const TileShape s = mx_tile_shape(p->variant);
         return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
                p->split_k >= 1 && p->split_k <= kMaxTileSplit &&
-               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn)) &&
+               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) &&
                (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
                p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 128 == 0 && mx_shape_supported(p->M, p->N, p->K) &&
                cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;

@@ -48,6 +48,9 @@ constexpr int GROUPED_NUM_VARIANTS = 0
 // workgroup), 3072 x 4096 x 4096 0.0838 vs 0.0843 ms.
 constexpr int TILE_LADDER[] = {11, 2};
 constexpr int STREAM_TILES[] = {8, 13, 10, 9, 12, 7};
+// The k-interleaved ping-pong tiles (schedule 7), 128 x 256 and 128 x 128,
+// for outputs that fill one round of compute units with them.
+constexpr int TILE_KINTER[] = {14, 15};
 
 // MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
 constexpr int MX_SKINNY_NUM_VARIANTS = 0
@@ -70,8 +73,12 @@ struct TileShape { int bm, bn, bk, stages, waves, wm, wn, sched; };
 // the 8 XCDs, so workgroup b keeps the XCD of the tiles b + k G it walks.
 constexpr int kPersistentGrid = 256;
 // Split-K is built into tile variants whose waves hold at most 16 blocks
-// of 16 x 16 accumulators (the split sums need as many registers again).
-constexpr bool tile_split_capable(int bm, int bn, int wm, int wn) { return (bm / wm / 16) * (bn / wn / 16) <= 16; }
+// of 16 x 16 accumulators (the split sums need as many registers again),
+// other than the k-interleaved schedule 7, whose groups already divide K.
+constexpr bool tile_split_capable(int bm, int bn, int wm, int wn, int sched)
+{
+    return sched != 7 && (bm / wm / 16) * (bn / wn / 16) <= 16;
+}
 TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 

@@ -11,7 +11,7 @@ TileShape tile_shape(int variant)
     int v = 0;
 #define HKG_SHAPE(bm, bn, bk, st, wm, wn, sc) \
     if (v++ == variant)                   \
-        return TileShape{bm, bn, bk, st, (wm) * (wn), wm, wn, sc};
+        return TileShape{bm, bn, bk, st, (wm) * (wn) * ((sc) == 7 ? 2 : 1), wm, wn, sc};
     HKG_TILE_CONFIGS(HKG_SHAPE)
 #undef HKG_SHAPE
     return TileShape{0, 0, 0, 0, 0, 0, 0, 0};

@@ -49,6 +49,7 @@
 #include "hkg_internal.h"
 #include "hkg_lds_copy.h"
 #include "hkg_tile_order.h"
+#include "hkg_tile_kinter.h"
 #include "hkg_tile_persistent.h"
 
 namespace hkg {
@@ -145,8 +146,13 @@ __device__ __forceinline__ void sync_stage(int ahead)
 // E8M0 scales of A and B (mx_pack_kernel layout).
 // GROUPED = true: the persistent grouped (mixture-of-experts) form, B the
 // G x N x K expert weights, offs the G row ends of the experts in A and C.
+// Threads of a workgroup: the WM x WN wave grid, twice for schedule 7 (two
+// groups, each a WM x WN grid over the whole tile).
+template <int WM, int WN, int SCHED>
+constexpr int tile_threads() { return WM * WN * 64 * (SCHED == 7 ? 2 : 1); }
+
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SCHED, bool EPI, bool MX, bool GROUPED>
-__global__ __launch_bounds__(WM * WN * 64, 2)
+__global__ __launch_bounds__(WM * WN * 64 * (SCHED == 7 ? 2 : 1), 2)
 void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                  uint16_t* __restrict__ C, int M, int N, int K,
                  int tiles_m, int tiles_n, int win_w, int chunk_c,
@@ -175,6 +181,8 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     constexpr int L = A_LOADS + B_LOADS;   // copies per wave per stage
     static_assert(MX ? BK == 128 : (BK == 32 || BK == 64), "stage k: 32 or 64 (bf16), 128 (MXFP8)");
     static_assert(!MX || SCHED == 0 || SCHED == 5, "MXFP8: schedules 0 and 5");
+    static_assert(SCHED <= 2 || (SCHED >= 5 && SCHED <= 7), "schedules 0, 1, 2, 5, 6 and 7");
+    static_assert(SCHED != 7 || (!MX && !GROUPED && BK == 64 && STAGES == 3), "schedule 7: bf16 tiles, 3 stages of 64 k");
     static_assert(!MX || (WTM % 64 == 0 && WTN % 64 == 0), "MXFP8: wave tiles of whole 64-row scale groups");
     static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
@@ -194,6 +202,12 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     if constexpr (SCHED == 6 && !EPI && !MX) {
         pingpong_persistent<WM, WN, GROUPED>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc,
                                              smem, offs, G, split_k, ws, counters);
+        return;
+    }
+    // SCHED 7: the k-interleaved ping-pong (hkg_tile_kinter.h), K not split.
+    if constexpr (SCHED == 7) {
+        pingpong_kinter<BM, BN, WM, WN, EPI>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc, smem,
+                                             bias, epi);
         return;
     }
 
@@ -489,7 +503,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             }
             // Leave no copy in flight into LDS that is about to be released.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else {
+        } else if constexpr (PINGPONG) {
             // Ping-pong (HipKittens talk notes, section 2, 8-wave schedule).
             // Waves 0-3 (group 0) and 4-7 (group 1) put one wave on each SIMD
             // and alternate a memory phase (LDS fragment reads of a whole
@@ -520,7 +534,6 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // them) and loading the next stage's ahead of its copies, so no wait
             // for scales ever holds back a copy issued after them; 2 (SWA + SWB)
             // VGPRs.
-            static_assert(PINGPONG, "schedules 0, 1, 2, 5 and 6");
             static_assert(BM == 256 && BN == 256 && RB == 128 && NW == 8 && WM <= 4,
                           "split-buffer ping-pong: 256 x 256 tile of 128-byte rows, 8 waves");
             constexpr int HALF = 128 * RB;                  // 128 rows of one stage
@@ -667,7 +680,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
 
-        if constexpr (!GROUPED && tile_split_capable(BM, BN, WM, WN)) if (split_k > 1) {
+        if constexpr (!GROUPED && tile_split_capable(BM, BN, WM, WN, SCHED)) if (split_k > 1) {
             // Split-K: each workgroup writes its fp32 partial tile; the last one
             // of the tile to arrive adds the partials in split order 0, 1, ...
             // (the same order whichever split arrives last, so results are
@@ -1060,7 +1073,7 @@ hipError_t launch_tile_t(const void* A, const void* B, uint16_t* C, int M, int N
     // the persistent schedule: at most one workgroup per compute unit
     const int grid = (SCHED == 6 && !EPI && !MX) ? min(tiles_m * tiles_n, kPersistentGrid) : tiles_m * tiles_n;
     hipLaunchKernelGGL((tile_kernel<BM, BN, BK, STAGES, WM, WN, SCHED, EPI, MX, false>),
-                       dim3(grid, split_k), dim3(WM * WN * 64), 0, stream, A, B, C, M, N, K, tiles_m,
+                       dim3(grid, split_k), dim3(tile_threads<WM, WN, SCHED>()), 0, stream, A, B, C, M, N, K, tiles_m,
                        tiles_n, win_w, chunk_c, split_k, ws, counters, bias, epi, psa, psb, nullptr, 0, lda, ldb,
                        ldc);
     return hipGetLastError();
