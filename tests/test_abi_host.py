@@ -195,14 +195,15 @@ def test_plan_boundaries():
                         ((2560, 4096, 1024), "tile_128x128x64_s2_w2x2_p2"),     # 320 tiles of 128 x 256
                         ((2048, 4096, 256), "tile_128x128x64_s2_w2x2_p2"),      # K under 1024
                         ((150, 40960, 4096), "tile_128x128x64_s2_w2x2_p2"),     # rows 41% padding
-                        ((256, 16384, 4096), "tile_128x128x64_s3_w2x2_p7"),
-                        ((1024, 3584, 4096), "tile_128x128x64_s3_w2x2_p7"),     # 224 tiles
+                        ((256, 16384, 4096), "tile_128x128x64_s5_w2x2_p7"),     # five stages from K = 4096
+                        ((1024, 3584, 4096), "tile_128x128x64_s5_w2x2_p7"),     # 224 tiles
+                        ((1024, 3584, 2048), "tile_128x128x64_s3_w2x2_p7"),
                         ((8192, 8192, 8192), "tile_256x256x64_s2")]:
         p = hkg.plan(*shape)
         assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and p.split_k == 1
         assert p.kernel_name.decode().startswith(name), (shape, p)
     p = hkg.plan(1024, 4096, 4096)
-    assert (p.waves, p.block_x, p.grid_x, p.lds_bytes) == (8, 512, 256, 3 * 256 * 128), p
+    assert (p.waves, p.block_x, p.grid_x, p.lds_bytes) == (8, 512, 256, 5 * 256 * 128), p
     assert "k-interleaved" in p.reason.decode()
     p = hkg.plan(1024, 3072, 4096)          # 192 tiles of 128 x 128: the streaming 128 x 96 fills a round
     assert (p.tile_m, p.tile_n, p.grid_x) == (128, 96, 256)

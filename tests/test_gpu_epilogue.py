@@ -109,6 +109,7 @@ CASES = [
     ("tile_128_split3", (200, 333, 1032), lambda h: _tile(h, 2, 3)),
     ("kinter_128x256", (300, 530, 392), lambda h: _tile(h, 14)),
     ("kinter_128x128", (129, 270, 136), lambda h: _tile(h, 15)),
+    ("kinter_128x128_s5", (200, 300, 456), lambda h: _tile(h, 16)),
     ("planner_skinny", (16, 1000, 2056), None),
     ("skinny_split3", (20, 300, 4096), lambda h: _skinny(h, 1, 3)),
     ("skinny_nb4", (9, 100, 520), lambda h: _skinny(h, 5, 1)),

@@ -212,7 +212,7 @@ def test_kinter_strided(hkg):
 
 
 @pytest.mark.parametrize("shape,name", [((2048, 4096, 4096), "tile_128x256x64_s3_w2x2_p7"),
-                                        ((1024, 4096, 4096), "tile_128x128x64_s3_w2x2_p7")],
+                                        ((1024, 4096, 4096), "tile_128x128x64_s5_w2x2_p7")],
                          ids=lambda v: "%dx%dx%d" % v if isinstance(v, tuple) else v)
 def test_kinter_full_size_sampled(hkg, shape, name):
     """The compute-bound middle at its real size: rows at every tile

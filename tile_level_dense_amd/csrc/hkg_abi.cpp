@@ -301,12 +301,17 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
             fill_tile(p, TILE_LADDER[1], 1, M, N);
             return;
         }
+        // 128 x 128: five stages in LDS (copies four stages ahead) from
+        // K = 4096, three below: 1024 x 4096 x 4096 40.4 vs 42.7 us,
+        // 1024 x 4096 x 8192 76.0 vs 79.8, 512 x 8192 x 8192 79.0 vs 82.5,
+        // 1024 x 4096 x 1024 14.1 vs 13.6.
         if (K >= 1024) {
-            const TileShape w = tile_shape(TILE_KINTER[1]);
+            const int v = K >= 4096 ? TILE_KINTER[2] : TILE_KINTER[1];
+            const TileShape w = tile_shape(v);
             const int64_t tw = cdiv(M, w.bm) * cdiv(N, w.bn);
             const bool rows_ok = 4 * (cdiv(M, w.bm) * w.bm - M) <= cdiv(M, w.bm) * w.bm;
             if (rows_ok && 8 * tw >= 7 * kNumCUs && tw <= kNumCUs) {
-                fill_tile(p, TILE_KINTER[1], 1, M, N);
+                fill_tile(p, v, 1, M, N);
                 return;
             }
         }

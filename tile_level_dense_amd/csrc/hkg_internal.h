@@ -48,9 +48,10 @@ constexpr int GROUPED_NUM_VARIANTS = 0
 // workgroup), 3072 x 4096 x 4096 0.0838 vs 0.0843 ms.
 constexpr int TILE_LADDER[] = {11, 2};
 constexpr int STREAM_TILES[] = {8, 13, 10, 9, 12, 7};
-// The k-interleaved ping-pong tiles (schedule 7), 128 x 256 and 128 x 128,
-// for outputs that fill one round of compute units with them.
-constexpr int TILE_KINTER[] = {14, 15};
+// The k-interleaved ping-pong tiles (schedule 7), 128 x 256 and 128 x 128
+// (copies 2 and 4 stages ahead), for outputs that fill one round of compute
+// units with them.
+constexpr int TILE_KINTER[] = {14, 15, 16};
 
 // MXFP8 skinny instantiations (plan.variant for HKG_KERNEL_MX_SKINNY).
 constexpr int MX_SKINNY_NUM_VARIANTS = 0

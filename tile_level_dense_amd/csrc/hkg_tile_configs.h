@@ -15,8 +15,9 @@
 //             each walking several tiles as one stream of stages (without a
 //             fused epilogue; with one, it runs as 5); 7: k-interleaved
 //             ping-pong, two groups of WM x WN waves, each group over the
-//             whole tile, taking alternate 64-k stages (3 stages of LDS; the
-//             partial tiles are added through LDS; no split-K)
+//             whole tile, taking alternate 64-k stages (STAGES 3 or 5 in
+//             LDS, copies 2 or 4 stages ahead; the partial tiles are added
+//             through LDS; no split-K)
 // The build script reads this list to map code objects to variants.
 #pragma once
 
@@ -36,7 +37,8 @@
     X(64, 96, 64, 4, 2, 2, 2)      \
     X(128, 96, 64, 4, 2, 2, 2)     \
     X(128, 256, 64, 3, 2, 2, 7)    \
-    X(128, 128, 64, 3, 2, 2, 7)
+    X(128, 128, 64, 3, 2, 2, 7)    \
+    X(128, 128, 64, 5, 2, 2, 7)
 
 // MXFP8 instantiations (E4M3 operands, E8M0 scale per 32 k), same fields;
 // BK = 128 k (128 bytes per row, as the bf16 BK = 64), SCHED 5 or 0 (a

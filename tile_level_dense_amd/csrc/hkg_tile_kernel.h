@@ -182,7 +182,8 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     static_assert(MX ? BK == 128 : (BK == 32 || BK == 64), "stage k: 32 or 64 (bf16), 128 (MXFP8)");
     static_assert(!MX || SCHED == 0 || SCHED == 5, "MXFP8: schedules 0 and 5");
     static_assert(SCHED <= 2 || (SCHED >= 5 && SCHED <= 7), "schedules 0, 1, 2, 5, 6 and 7");
-    static_assert(SCHED != 7 || (!MX && !GROUPED && BK == 64 && STAGES == 3), "schedule 7: bf16 tiles, 3 stages of 64 k");
+    static_assert(SCHED != 7 || (!MX && !GROUPED && BK == 64 && (STAGES == 3 || STAGES == 5)),
+                  "schedule 7: bf16 tiles, 3 or 5 stages of 64 k");
     static_assert(!MX || (WTM % 64 == 0 && WTN % 64 == 0), "MXFP8: wave tiles of whole 64-row scale groups");
     static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
@@ -206,8 +207,8 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     }
     // SCHED 7: the k-interleaved ping-pong (hkg_tile_kinter.h), K not split.
     if constexpr (SCHED == 7) {
-        pingpong_kinter<BM, BN, WM, WN, EPI>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb, ldc, smem,
-                                             bias, epi);
+        pingpong_kinter<BM, BN, WM, WN, STAGES, EPI>(Av, Bv, C, M, N, K, tiles_m, tiles_n, win_w, chunk_c, lda, ldb,
+                                                     ldc, smem, bias, epi);
         return;
     }
 

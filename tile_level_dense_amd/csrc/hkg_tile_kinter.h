@@ -18,25 +18,28 @@
 // every two).
 //
 // Phase p lies between barriers p and p + 1.  In phase p, group p % 2 reads
-// stage p from LDS into registers and copies stage p + 2 into buffer
-// (p + 2) % 3, while the other group multiplies stage p - 1.  Buffer
-// lifetimes (three stages in LDS): stage p + 2 goes into the buffer of stage
-// p - 1, whose reads ended before barrier p (the reading group waited for
-// them, lgkmcnt, before it); its only reader is the copying group itself, in
-// phase p + 2, and every wave of that group waits for its copies (vmcnt) at
-// the end of its compute phase p + 1, before barrier p + 2.  Stages past K
-// (and a last stage that evens out the count) are copied with out-of-range
-// offsets, which write zeros, so both groups run the same number of stages
-// and the loop has no branch around copies or waits.
+// stage p from LDS into registers and copies stage p + D into buffer
+// (p + D) % NB (NB stage buffers, D = NB - 1 = 2 or 4), while the other
+// group multiplies stage p - 1.  Buffer lifetimes: stage p + D goes into
+// the buffer of stage p - 1, whose reads ended before barrier p (the
+// reading group waited for them, lgkmcnt, before it); with D even its only
+// reader is the copying group itself, in phase p + D, and each wave of that
+// group, at the end of its compute phase p + D - 1, waits for all its
+// copies but the D / 2 - 1 batches it issued after them (vmcnt counts its
+// copies in order), before barrier p + D.  Stages past K (and a last stage
+// that evens out the count) are copied with out-of-range offsets, which
+// write zeros, so both groups run the same number of stages and the loop
+// has no branch around copies or waits.
 //
 // Group 0 joins barriers 0 .. nk2 and group 1 barriers 0 .. nk2 - 1 plus
 // one extra at the start (phase 0, in which group 1 has nothing to
-// multiply): nk2 + 1 each.  After the loop all copies have landed and no
-// wave reads a stage, so LDS is reused for the exchange: each wave writes
-// the half of its accumulator blocks that its partner wave (same position
-// in the other group) completes, reads the other half from the partner and
-// adds it to its own, and stores its half of the tile.  fp32 addition is
-// commutative, so both halves form partial(0) + partial(1) identically.
+// multiply): nk2 + 1 each.  After the loop every wave waits for all its
+// copies (vmcnt(0)) and no wave reads a stage, so LDS is reused for the
+// exchange: each wave writes the half of its accumulator blocks that its
+// partner wave (same position in the other group) completes, reads the
+// other half from the partner and adds it to its own, and stores its half
+// of the tile.  fp32 addition is commutative, so both halves form
+// partial(0) + partial(1) identically.
 #pragma once
 
 #include <type_traits>
@@ -48,7 +51,7 @@
 namespace hkg {
 namespace {
 
-template <int BM, int BN, int WM, int WN, bool EPI>
+template <int BM, int BN, int WM, int WN, int NB, bool EPI>
 __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, const void* __restrict__ Bv,
                                                 uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
                                                 int tiles_n, int win_w, int chunk_c, int lda, int ldb, int ldc,
@@ -76,7 +79,10 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "whole 16 x 16 blocks, an even number of block columns");
     static_assert(BM % (4 * RPW) == 0 && BN % (4 * RPW) == 0, "stage rows split over a group's copies");
     static_assert((4 * RPW / RPL) % CPR == 0, "swizzle must repeat across a wave's copies");
-    static_assert(3 * STAGE <= 160 * 1024 && 8 * XCH <= 3 * STAGE, "three stages, and the exchange, in LDS");
+    static_assert(NB == 3 || NB == 5, "stage buffers: copies run NB - 1 (even) stages ahead");
+    static_assert(NB * STAGE <= 160 * 1024 && 8 * XCH <= NB * STAGE, "the stages, and the exchange, in LDS");
+    constexpr int D = NB - 1;               // copy distance in stages (and phases)
+    constexpr int CPS = A_CP + B_CP;        // copies per wave per stage
     constexpr uint32_t kOOR = 0x80000000u;
     constexpr int kW3 = 0x00020000;
 
@@ -108,7 +114,7 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
     const uint32_t p_off_b = (uint32_t)prow * b_rb + (uint32_t)pchunk * 16u;
     const int p_k = pchunk * KPC;
     auto copy_stage = [&](int t) {
-        char* const base = smem + (t % 3) * STAGE;
+        char* const base = smem + (t % NB) * STAGE;
         const int k0 = t * BK;
         const bool k_out = k0 + p_k >= K;   // K % 8 == 0: a chunk is wholly inside or outside
         const uint32_t ko = (uint32_t)k0 * 2u;
@@ -136,7 +142,7 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
     const int b_frag = A_BYTES + (wn * WTN + lrow) * RB;
     bf16x8 af[KS][FM], bf[KS][FN];
     auto read_stage = [&](int t) {
-        const char* const base = smem + (t % 3) * STAGE;
+        const char* const base = smem + (t % NB) * STAGE;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -172,43 +178,57 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
     const int nk = (K + BK - 1) / BK;
     const int pairs = (nk + 1) / 2;         // stages per group
 
-    // Prologue: group g copies stage g.
-    copy_stage(g);
+    // Prologue: group g copies its own first stages g, g + 2, ... below D.
+    // Each wave then waits for all but its newest D / 2 - 1 batches of
+    // copies: the first stage it reads has landed, and the loop's waits (the
+    // same count, at the end of every compute phase) cover the rest.
+#pragma unroll
+    for (int s = 0; s < D; s += 2)
+        copy_stage(s + g);
+    auto wait_copies = [] {                 // all but the newest D / 2 - 1 batches
+        if constexpr (D == 2)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS * (D / 2 - 1)) : "memory");
+    };
     if (g == 0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_copies();
         phase_barrier();                    // barrier 0
         for (int q = 0; q < pairs; ++q) {
             const int t = 2 * q;
             read_stage(t);                  // phase t: memory
             fence();
-            copy_stage(t + 2);
+            copy_stage(t + D);
             fence();
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             phase_barrier();
             mfma_stage();                   // phase t + 1: compute
             fence();
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stage t + 2, read in phase t + 2
+            wait_copies();                  // stage t + 2, read in phase t + 2
             phase_barrier();
         }
     } else {
         phase_barrier();                    // barrier 0; phase 0: group 0 reads stage 0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // stage 1
+        wait_copies();                      // stage 1
         phase_barrier();
         for (int q = 0; q < pairs; ++q) {
             const int t = 2 * q + 1;
             read_stage(t);                  // phase t: memory
             fence();
-            copy_stage(t + 2);
+            copy_stage(t + D);
             fence();
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             phase_barrier();
             mfma_stage();                   // phase t + 1: compute
             fence();
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_copies();
             if (q + 1 < pairs)
                 phase_barrier();
         }
     }
+    // The last copies (stages past K: zeros nobody reads) land before the
+    // exchange reuses LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Exchange and store.  Group 0 completes block columns 0 .. HN - 1 of
     // its wave tile, group 1 columns HN .. FN - 1; the exchange slot of
