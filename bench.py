@@ -25,10 +25,11 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                hkg_gemm_bf16_ex (per-call transpose of the column operands),
                and the transpose pass alone (GB/s); torch.mm on the same views
                for context
-  other_configs  the tiny and MLP-up (128 x 12288 x 4096) workloads (with
-               --only configs also prefill-down, 4096 x 4096 x 12288) in the
-               planner's configuration, per call over rotating buffer sets
-               (graph), torch.mm for context
+  other_configs  the tiny, MLP-up (128 x 12288 x 4096) and prefill-down
+               (4096 x 4096 x 12288) workloads in the planner's configuration,
+               per call over rotating buffer sets (graph), torch.mm for context
+  middle       the compute-bound middle (1024 and 2048 x 4096 x 4096: too few
+               256 x 256 tiles to fill the device), timed as other_configs
   mxfp8        the block-scaled FP8 GEMM (E4M3, E8M0 scale per 32 k) on
                mx_square_8192 (TFLOP/s against the 5.0 PFLOP/s dense fp8
                MFMA peak) and mx_decode_32x4096x4096 (HBM GB/s, rotating
@@ -508,6 +509,7 @@ def bench_mx_decode(torch, hkg, steps, warmup):
 
 
 ALL_CONFIGS = ("tiny_256", "mlp_up_128x12288x4096", "prefill_down_4096x4096x12288")
+MIDDLE_CONFIGS = ("middle_1024x4096x4096", "middle_2048x4096x4096")
 
 
 def bench_configs(torch, hkg, names=ALL_CONFIGS):
@@ -522,7 +524,7 @@ def bench_configs(torch, hkg, names=ALL_CONFIGS):
     out = {}
     stream = torch.cuda.Stream()
     for name in names:
-        w = workloads.WORKLOADS[name]
+        w = workloads.WORKLOADS[name] if name in workloads.WORKLOADS else workloads.MIDDLE_WORKLOADS[name]
         M, N, K = w["M"], w["N"], w["K"]
         A, B = workloads.workload_inputs(name)
         a0, b0 = to_dev(A, torch), to_dev(B, torch)
@@ -701,8 +703,8 @@ def main():
                     help="seconds of untimed calls before each leg's timed windows (clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the tiny / MLP-up / prefill-down leg (counter runs)")
-    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts", "configs"],
+                    help="skip the tiny / MLP-up / prefill-down and compute-bound middle legs (counter runs)")
+    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts", "configs", "middle"],
                     help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -735,8 +737,8 @@ def main():
         grp = bench_grouped(torch, hkg, args.steps, args.warmup)
         print(json.dumps({k: round(v["tflops"], 2) for k, v in grp.items()}), flush=True)
         return 0
-    if args.only == "configs":
-        cfg = bench_configs(torch, hkg, ALL_CONFIGS)
+    if args.only in ("configs", "middle"):
+        cfg = bench_configs(torch, hkg, ALL_CONFIGS if args.only == "configs" else MIDDLE_CONFIGS)
         print(json.dumps({k: round(v["us"], 3) for k, v in cfg.items()}), flush=True)
         return 0
     if args.only == "mx":
@@ -755,6 +757,7 @@ def main():
     grp = bench_grouped(torch, hkg, args.steps, args.warmup)
     lay = bench_layouts(torch, hkg, args.steps, args.warmup)
     cfg = {} if args.no_configs else bench_configs(torch, hkg)
+    mid = {} if args.no_configs else bench_configs(torch, hkg, MIDDLE_CONFIGS)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     tile_kernel = sq["plan"].kernel_name.decode()
@@ -834,6 +837,11 @@ def main():
                                  "vendor_us": round(r["vendor_us"], 3),
                                  "roofline": config_roofline(name, r)}
                           for name, r in cfg.items()},
+        "middle": {name: {"us_per_call": round(r["us"], 3), "tflops": round(r["tflops"], 2),
+                          "kernel": r["kernel"], "rotating_sets": r["sets"],
+                          "launches_per_window": r["launches"], "vendor_us": round(r["vendor_us"], 3),
+                          "roofline": config_roofline(name, r)}
+                   for name, r in mid.items()},
         "timing": {"protocol": "per leg: W warm-up calls, then untimed back-to-back calls for %.2f s of device "
                                "time (clock settle), then %d windows of K calls, each bracketed by device "
                                "synchronisation and timed with HIP events on the launch stream; the figure is "

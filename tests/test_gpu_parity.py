@@ -211,17 +211,18 @@ def test_kinter_strided(hkg):
     full_check(np.ascontiguousarray(Cs[:, :N]), A, B)
 
 
-@pytest.mark.parametrize("shape,name", [((2048, 4096, 4096), "tile_128x256x64_s3_w2x2_p7"),
-                                        ((1024, 4096, 4096), "tile_128x128x64_s5_w2x2_p7")],
-                         ids=lambda v: "%dx%dx%d" % v if isinstance(v, tuple) else v)
-def test_kinter_full_size_sampled(hkg, shape, name):
-    """The compute-bound middle at its real size: rows at every tile
-    boundary and 20000 random outputs against the oracle."""
-    M, N, K = shape
+@pytest.mark.parametrize("workload,name", [("middle_2048x4096x4096", "tile_128x256x64_s3_w2x2_p7"),
+                                           ("middle_1024x4096x4096", "tile_128x128x64_s5_w2x2_p7")])
+def test_kinter_full_size_sampled(hkg, workload, name):
+    """The compute-bound middle workloads the benchmark times, at their
+    size and inputs: rows at every tile boundary and 20000 random outputs
+    against the oracle."""
+    w = workloads.MIDDLE_WORKLOADS[workload]
+    M, N, K = w["M"], w["N"], w["K"]
     p = hkg.plan(M, N, K)
-    _say("k-interleaved full size", shape, p.kernel_name.decode())
+    _say("k-interleaved full size", workload, p.kernel_name.decode())
     assert p.kernel_name.decode() == name, p
-    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=11)
+    A, B = workloads.workload_inputs(workload)
     C = run(hkg, A, B)
     rows = sample_rows(M, tile=128)
     gates.compare(C[rows], *oracle_rows(A, B, rows))

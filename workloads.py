@@ -73,8 +73,20 @@ def make_inputs(M, N, K, a=("uniform", -1.0, 1.0), b=("uniform", -1.0, 1.0), see
     return A, B
 
 
+# The compute-bound middle: prefill chunks of 1024 and 2048 tokens through a
+# 4096-wide projection, where 256 x 256 output tiles are too few to fill the
+# device (64 and 128 tiles for 256 compute units).  Context for the
+# benchmark and the parity tests, beside the workloads above.
+MIDDLE_WORKLOADS = {
+    "middle_1024x4096x4096": dict(M=1024, N=4096, K=4096,
+                                  a=("normal", 0.0, 1.0), b=("normal", 0.0, 0.02)),
+    "middle_2048x4096x4096": dict(M=2048, N=4096, K=4096,
+                                  a=("normal", 0.0, 1.0), b=("normal", 0.0, 0.02)),
+}
+
+
 def workload_inputs(name, seed=0):
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if name in WORKLOADS else MIDDLE_WORKLOADS[name]
     return make_inputs(w["M"], w["N"], w["K"], w["a"], w["b"], seed)
 
 
