@@ -161,3 +161,29 @@ def test_square_8192_with_column_layout_weight(hkg):
     ii, jj = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
     Cr, S, absS = oracle.gemm_entries(A, B, ii, jj)
     gates.compare(Cg[ii, jj], Cr, S, absS)
+
+
+# C's leading dimension picks the store path of the tile kernels: a
+# multiple of 8 elements takes the 16-byte stores of 8 rows x 128 bytes,
+# 4 mod 8 the 8-byte ones, an odd one element stores.  One shape per planner
+# tile family (persistent 256 x 256, two-stage 128 x 128, k-interleaved
+# 128 x 256, streaming 64 x 64), ragged in N so the last 8-column chunks
+# are partial, every output against the oracle and C's padding untouched.
+STORE_SHAPES = [("persistent", 4100, 3004, 64, "tile_256x256x64_s2_w4x2_p6"),
+                ("ring_128", 2600, 4100, 136, "tile_128x128x64_s2_w2x2_p2"),
+                ("kinter", 1300, 4004, 1032, "tile_128x256x64_s3_w2x2_p7"),
+                ("streaming", 300, 500, 136, "tile_64x64x64_s4_w2x2_p2")]
+
+
+@pytest.mark.parametrize("ldc_pad", [8, 4, 1], ids=["wide", "eight_byte", "elements"])
+@pytest.mark.parametrize("name,M,N,K,kernel", STORE_SHAPES, ids=[s[0] for s in STORE_SHAPES])
+def test_store_paths_by_ldc(hkg, name, M, N, K, kernel, ldc_pad):
+    assert hkg.plan(M, N, K).kernel_name.decode() == kernel
+    assert N % 8 == 4                        # the last 8-column chunk of a row is partial
+    ldc = (N + 7) // 8 * 8 + ldc_pad         # 0, 4 or an odd remainder mod 8
+    _say("store path", name, M, N, K, "ldc", ldc)
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.05), seed=N + ldc_pad)
+    C = run_ex(hkg, A, K, False, B, K, False, M, N, K, ldc)
+    assert np.all(C[:, N:] == SENTINEL), "C padding was written"
+    Cr, S, absS = oracle.gemm(A, B)
+    gates.compare(np.ascontiguousarray(C[:, :N]), Cr, S, absS)

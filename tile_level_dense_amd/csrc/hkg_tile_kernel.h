@@ -48,6 +48,7 @@
 
 #include "hkg_internal.h"
 #include "hkg_lds_copy.h"
+#include "hkg_store.h"
 #include "hkg_tile_order.h"
 #include "hkg_tile_kinter.h"
 #include "hkg_tile_persistent.h"
@@ -902,7 +903,17 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             return;
         }
 
-        // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32).
+        // Epilogue: one nearest-even rounding per element (v_cvt_pk_bf16_f32);
+        // 16-byte stores of 8 rows x 128 bytes (or 16 rows x 64 bytes) when
+        // the wave tile has an even number of block columns and C's rows
+        // are 16-byte aligned (hkg_store.h), else masked 8-byte stores.
+        if constexpr (FN % 2 == 0) {
+            if ((ldc & 7) == 0) {
+                store_blocks_wide<FM, FN>([&](int i, int j) { return acc[i][j]; }, C, ldc, m0 + wm * WTM, m_lim,
+                                          n0 + wn * WTN, N);
+                return;
+            }
+        }
     #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + wm * WTM + i * 16 + lrow;

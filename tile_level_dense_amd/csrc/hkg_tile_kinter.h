@@ -46,6 +46,7 @@
 
 #include "hkg_epilogue.h"
 #include "hkg_internal.h"
+#include "hkg_store.h"
 #include "hkg_tile_order.h"
 
 namespace hkg {
@@ -235,6 +236,7 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
     // block (i, jj) of a wave is 1 KiB, lane l at byte 16 l.
     float bv[HN][4];
     const bool vec_ok = ((N | ldc) & 3) == 0;
+    const bool wide_ok = (ldc & 7) == 0;    // 16-byte stores (hkg_store.h)
     auto finish = [&](auto own) {
         constexpr int JO = decltype(own)::value;     // first block column this wave completes
         constexpr int JX = JO == 0 ? HN : 0;         // first block column the partner completes
@@ -257,6 +259,21 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
                 *(f32x4*)(mine + (i * HN + jj) * 1024) = acc[i][JX + jj];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         phase_barrier();
+        // Block (i, jj) of this wave's half: own partial + the partner's,
+        // then the epilogue.
+        auto blk = [&](int i, int jj) {
+            f32x4 v = acc[i][JO + jj] + *(const f32x4*)(theirs + (i * HN + jj) * 1024);
+            if constexpr (EPI) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = epi_activation(v[r] + bv[jj][r], epi);
+            }
+            return v;
+        };
+        if (wide_ok) {
+            store_blocks_wide<FM, HN>(blk, C, ldc, m0 + wm * WTM, M, n0 + wn * WTN + JO * 16, N);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + wm * WTM + i * 16 + lrow;
@@ -264,13 +281,8 @@ __device__ __forceinline__ void pingpong_kinter(const void* __restrict__ Av, con
 #pragma unroll
             for (int jj = 0; jj < HN; ++jj) {
                 __builtin_amdgcn_sched_barrier(0);
-                f32x4 v = acc[i][JO + jj] + *(const f32x4*)(theirs + (i * HN + jj) * 1024);
+                const f32x4 v = blk(i, jj);
                 const int n = n0 + wn * WTN + (JO + jj) * 16 + lgrp * 4;
-                if constexpr (EPI) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[r] = epi_activation(v[r] + bv[jj][r], epi);
-                }
                 const uint2 h = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
                 if (m < M) {
                     if (vec_ok && n + 3 < N) {

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "hkg_internal.h"
+#include "hkg_store.h"
 #include "hkg_tile_order.h"
 
 namespace hkg {
@@ -287,10 +288,23 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
                 bf[s][j] = *(const bf16x8*)(bb + j * 16 * RB + chunk_off[s]);
         }
     };
-    // A finished tile: one nearest-even rounding per element, masked 8-byte
-    // stores, then the accumulators start over for the next tile.
+    // A finished tile: one nearest-even rounding per element, 16-byte stores
+    // of 8 rows x 128 bytes (hkg_store.h) when C's rows are 16-byte aligned,
+    // else masked 8-byte stores; then the accumulators start over for the
+    // next tile.
     const bool vec_ok = ((N | ldc) & 3) == 0;
+    const bool wide_ok = (ldc & 7) == 0;
     auto store_tile = [&](const Pos& p) {
+        if (wide_ok) {
+            store_blocks_wide<FM, FN>([&](int i, int j) { return acc[i][j]; }, C, ldc, p.m0 + wm * WTM, p.m_lim,
+                                      p.n0 + wn * WTN, N);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = p.m0 + wm * WTM + i * 16 + lrow;
