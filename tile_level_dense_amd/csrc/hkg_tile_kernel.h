@@ -777,8 +777,10 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
 
         if constexpr (GROUPED) if (k_parts == 2) {
             // A tile of the last round split in two halves of K: each half
-            // writes its whole fp32 accumulator tile to its own slot (tile-
-            // local, BN floats per row, device-scope stores), and the half that
+            // writes its whole fp32 accumulator tile to its own slot (device-
+            // scope stores, fragment-major: block (i, j) of wave w fills 1 KiB
+            // at ((w FM + i) FN + j) KiB, lane l's four values at 16 l, so each
+            // instruction writes 1 KiB contiguously), and the half that
             // arrives second adds the other's partial to its own and goes on
             // to the store.  fp32 addition is commutative, so the sum is the
             // same whichever half arrives second.  The ordering argument is the
@@ -790,7 +792,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             for (int i = 0; i < FM; ++i)
     #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int off = ((wm * WTM + i * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                    const int off = ((wave * FM + i) * FN + j) * 1024 + lane * 16;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), mine, off, 0,
                                                            kDeviceScope);
                 }
@@ -821,7 +823,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 for (int ii = 0; ii < RBLK; ++ii)
     #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int off = ((wm * WTM + (i0 + ii) * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                        const int off = ((wave * FM + i0 + ii) * FN + j) * 1024 + lane * 16;
                         o[ii][j] = __builtin_bit_cast(
                             f32x4, __builtin_amdgcn_raw_buffer_load_b128(other, off, 0, kDeviceScope));
                     }

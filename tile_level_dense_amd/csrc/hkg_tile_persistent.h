@@ -416,8 +416,11 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     if constexpr (GROUPED) if (unit >= 0) {
         // The last item was half (unit & 1) of K of a tile of the split last
         // round, and acc holds that partial.  Each half writes its fp32 tile
-        // to its own slot of ws (tile-local, BN floats per row, device-scope
-        // stores); the half that arrives second adds the other's partial to
+        // to its own slot of ws (device-scope stores), fragment-major: block
+        // (i, j) of wave w fills 1 KiB at ((w FM + i) FN + j) KiB, lane l's
+        // four values at 16 l, so each store instruction writes 1 KiB
+        // contiguously and the other half reads it back with the same
+        // geometry; the half that arrives second adds the other's partial to
         // its own and stores the tile.  fp32 addition is commutative, so the
         // sum is the same whichever half arrives second.  The ordering
         // argument is the split-K arrival protocol in hkg_internal.h.
@@ -434,7 +437,7 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int off = ((wm * WTM + i * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                const int off = ((wave * FM + i) * FN + j) * 1024 + lane * 16;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), mine, off, 0, kDev);
             }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -462,7 +465,7 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
             for (int ii = 0; ii < RBLK; ++ii)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int off = ((wm * WTM + (i0 + ii) * 16 + lrow) * BN + wn * WTN + j * 16 + lgrp * 4) * 4;
+                    const int off = ((wave * FM + i0 + ii) * FN + j) * 1024 + lane * 16;
                     o[ii][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(other, off, 0, kDev));
                 }
 #pragma unroll
