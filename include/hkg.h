@@ -357,8 +357,13 @@ hkg_status_t hkg_grouped_gemm_bf16_run_plan(const hkg_plan_t* plan, const void* 
  * counters live in a fixed device array of the library (16 MiB of partials
  * and 16384 counters per device, held until the process ends) instead of a
  * workspace the library allocates; the call itself allocates nothing.
- * Every plan the library chooses fits (split plans need at most 256 x 128 x
- * 128 fp32 partials); a plan needing more returns HKG_ERR_WORKSPACE.
+ * Every split-K plan the library chooses fits (at most 256 x 128 x 128 fp32
+ * partials); a plan needing more returns HKG_ERR_WORKSPACE.  One exception
+ * to bit-identity: where hkg_gemm_bf16's plan splits the last round of
+ * 256 x 256 tiles in two halves of K (one 256 KiB partial per workgroup,
+ * 64 MiB), this entry point runs those tiles whole, with the same kernel's
+ * persistent schedule: the output is then within the library's accuracy
+ * bound of the same sum, accumulated in another order.
  * All calls on one device share the array: calls that overlap in time on
  * one device (on different streams, or a captured graph replayed beside
  * another call) race and give wrong results; calls on one stream are

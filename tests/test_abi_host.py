@@ -205,6 +205,16 @@ def test_plan_boundaries():
     p = hkg.plan(1024, 4096, 4096)
     assert (p.waves, p.block_x, p.grid_x, p.lds_bytes) == (8, 512, 256, 5 * 256 * 128), p
     assert "k-interleaved" in p.reason.decode()
+    # more 256 x 256 tiles than CUs with a last round of at most half the
+    # device: that round split in two halves of K (one partial tile of
+    # workspace per workgroup, one grid)
+    for shape, split in [((4352, 4096, 4096), 2), ((6144, 4096, 4096), 2), ((4400, 4200, 136), 2),
+                         ((5120, 5120, 4096), 1), ((8192, 8192, 8192), 1), ((4096, 4096, 12288), 1),
+                         ((4352, 4096, 64), 1)]:
+        p = hkg.plan(*shape)
+        assert p.kernel_name.decode() == "tile_256x256x64_s2_w4x2_p6" and p.split_k == split, (shape, p)
+        assert p.workspace_bytes == (256 * 256 * 256 * 4 if split == 2 else 0) and p.grid_y == 1, (shape, p)
+        assert ("last round split" in p.reason.decode()) == (split == 2)
     p = hkg.plan(1024, 3072, 4096)          # 192 tiles of 128 x 128: the streaming 128 x 96 fills a round
     assert (p.tile_m, p.tile_n, p.grid_x) == (128, 96, 256)
 
@@ -282,10 +292,11 @@ def test_run_plan_errors_precede_device_work():
     q.split_k = 0
     assert hkg.hkg_gemm_bf16_run_plan(q, A, B, C, M, N, K) == hkg.HKG_ERR_UNSUPPORTED
     # split-K exists only in tile variants with at most 16 accumulator
-    # blocks per wave (256 x 256 over 8 waves has 32)
+    # blocks per wave (256 x 256 over 8 waves has 32); the persistent
+    # 256 x 256 tile takes split 2 only, meaning its last round split
     q = hkg.plan(8192, 8192, 8192)
     assert (q.tile_m, q.tile_n, q.waves) == (256, 256, 8)
-    q.split_k = 2
+    q.split_k = 3
     assert hkg.hkg_gemm_bf16_run_plan(q, 1 << 40, 2 << 40, 3 << 40, 8192, 8192, 8192) == hkg.HKG_ERR_UNSUPPORTED
     q = hkg.Plan.from_buffer_copy(p)
     q.abi_version = 7

@@ -110,6 +110,7 @@ CASES = [
     ("kinter_128x256", (300, 530, 392), lambda h: _tile(h, 14)),
     ("kinter_128x128", (129, 270, 136), lambda h: _tile(h, 15)),
     ("kinter_128x128_s5", (200, 300, 456), lambda h: _tile(h, 16)),
+    ("split_tail", (4400, 4200, 136), None),
     ("planner_skinny", (16, 1000, 2056), None),
     ("skinny_split3", (20, 300, 4096), lambda h: _skinny(h, 1, 3)),
     ("skinny_nb4", (9, 100, 520), lambda h: _skinny(h, 5, 1)),

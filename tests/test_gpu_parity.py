@@ -341,6 +341,26 @@ def test_persistent_pingpong_multi_tile(hkg, shape):
     assert np.array_equal(C1, C2)
 
 
+# More 256 x 256 tiles than compute units with a last round of at most half
+# of them: the planner splits that round's tiles into two halves of K (the
+# grouped kernel's streamed schedule with one expert).  Ragged M, N and K,
+# every output; a second run is bit-identical (each split tile's two fp32
+# partials are added once, a commutative sum).
+SPLIT_TAIL_SHAPES = [(4400, 4200, 136), (4352, 4096, 520), (4100, 4608, 72)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_TAIL_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_split_tail_planner_shapes(hkg, shape):
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    _say("split last round", shape, p.reason.decode())
+    assert p.split_k == 2 and "last round split" in p.reason.decode(), p
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=M + N + K)
+    C1 = run(hkg, A, B)
+    full_check(C1, A, B)
+    assert np.array_equal(C1, run(hkg, A, B))
+
+
 def test_persistent_pingpong_strided(hkg):
     """Row-layout operands and C with padded leading dimensions on the
     persistent ping-pong (through the layout entry point's in-place path)."""

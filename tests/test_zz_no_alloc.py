@@ -80,3 +80,21 @@ def test_noalloc_unsplit_and_tiny(hkg):
     for (M, N, K) in ((256, 256, 256), (16, 4096, 512), (3, 5, 24)):
         A, B, c_ref, c_na = both(hkg, M, N, K, seed=7)
         assert np.array_equal(c_na, c_ref), (M, N, K)
+
+
+def test_noalloc_split_last_round_runs_whole(hkg):
+    """Where the plan splits the last round of 256 x 256 tiles (64 MiB of
+    partials, more than the fixed scratch), the no-allocation form runs
+    those tiles whole: every output against the oracle, twice, the second
+    call after a split-K call has left partials and counters behind."""
+    M, N, K = 4352, 4096, 200
+    p = hkg.plan(M, N, K)
+    assert p.split_k == 2 and "last round split" in p.reason.decode(), p
+    for i in range(2):
+        A, B, c_ref, c_na = both(hkg, M, N, K, seed=60 + i)
+        _say("split last round", (M, N, K), "call", i)
+        Cr, S, absS = oracle.gemm(A, B)
+        gates.compare(c_na, Cr, S, absS)
+        gates.compare(c_ref, Cr, S, absS)
+        if i == 0:
+            both(hkg, 64, 512, 4096, seed=5)       # a split-K call on the fixed scratch in between

@@ -268,8 +268,20 @@ void plan_tile(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     // 139 vs 159 us.
     {
         const TileShape s = tile_shape(TILE_LADDER[0]);
-        if (4 * cdiv(M, s.bm) * cdiv(N, s.bn) >= 3 * kNumCUs) {
-            fill_tile(p, TILE_LADDER[0], 1, M, N);
+        const int64_t t256 = cdiv(M, s.bm) * cdiv(N, s.bn);
+        if (4 * t256 >= 3 * kNumCUs) {
+            // More tiles than compute units and a last round filling at most
+            // half of them: that round's tiles are split in two halves of K
+            // (split_k 2; run as the grouped kernel with one expert, whose
+            // streamed schedule does exactly this), so it takes half a tile's
+            // time.  Measured on MI355X (us, split vs whole, torch.mm):
+            // 4352 x 4096 x 4096 (272 tiles) 134.2 vs 153.0 (132.6);
+            // 4096 x 5120 x 4096 (320) 137.3 vs 154.3 (142.0); 4608^2 x 4096
+            // (324) 139.7 vs 153.9 (142.3); 6144 x 4096 x 8192 (384) 287.5 vs
+            // 303.7 (293.0); 6144 x 4096 x 4096 158.1 vs 158.9 (153.2).
+            const int64_t rem = t256 % kNumCUs;
+            const bool split_tail = t256 > kNumCUs && rem > 0 && 2 * rem <= kNumCUs && cdiv(K, s.bk) >= 2;
+            fill_tile(p, TILE_LADDER[0], split_tail ? 2 : 1, M, N);
             return;
         }
         // One round of k-interleaved tiles (schedule 7): 128 x 256 tiles
@@ -382,6 +394,11 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
     p->grid_z = 1;
     p->block_x = s.waves * 64;
     p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    const bool split_tail = s.sched == 6 && split == 2;
+    if (split_tail) {                   // one partial tile per workgroup, one grid
+        p->grid_y = 1;
+        p->workspace_bytes = (int64_t)p->grid_x * s.bm * s.bn * 4;
+    }
     // Chiplet-aware order (talk notes, section 3): 8-tall windows, so one
     // XCD's 32 concurrent workgroups cover an 8 x 4 block of tiles, and 32
     // consecutive tiles per XCD; off when the grid is under one XCD round.
@@ -393,7 +410,8 @@ void fill_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
                   s.stages, s.wm, s.wn, s.sched);
     std::snprintf(p->reason, sizeof p->reason, "%lldx%lld tiles of %dx%d (%d stages), split-K %lld on %d CUs%s",
                   (long long)tm, (long long)tn, s.bm, s.bn, s.stages, (long long)split, kNumCUs,
-                  s.sched == 6 ? ", persistent" : s.sched == 7 ? ", k-interleaved" : "");
+                  split_tail ? ", persistent, last round split in two halves of K"
+                  : s.sched == 6 ? ", persistent" : s.sched == 7 ? ", k-interleaved" : "");
 }
 
 // Fill the skinny-kernel fields of p for (variant, split).
@@ -561,8 +579,9 @@ bool plan_matches_library(const hkg_plan_t* p)
         const TileShape s = tile_shape(p->variant);
         return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
                p->split_k >= 1 && p->split_k <= kMaxTileSplit &&
-               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) &&
-               (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
+               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched) ||
+                (s.sched == 6 && p->split_k == 2)) &&
+               (p->split_k == 1 || s.sched == 6 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
                p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 8 == 0 && p->K <= (INT32_MAX / 2) / 256 &&
                cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
     }
@@ -625,6 +644,39 @@ hkg_status_t run(const hkg_plan_t* p, const void* A, const void* B, void* C, con
     case HKG_KERNEL_TILE: {
         float* ws = nullptr;
         int* counters = nullptr;
+        if (tile_shape(p->variant).sched == 6 && p->split_k == 2) {
+            // The persistent tile with its last round split in two halves of
+            // K runs as the grouped kernel with one expert (a null offset
+            // list), whose streamed schedule splits such a round.  That
+            // kernel reads dense operands and takes one fp32 partial tile per
+            // workgroup; with strided operands, a caller's fixed scratch, or
+            // a capture during which the workspace would have to grow, the
+            // plain persistent kernel runs every tile whole instead.
+            bool split = lda == K && ldb == K && ldc == N && !fixed;
+            if (split) {
+                hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+                e = hipStreamIsCapturing(stream, &cs);
+                if (e != hipSuccess) {
+                    set_hip_error(e, "hipStreamIsCapturing");
+                    return HKG_ERR_HIP;
+                }
+                const std::string before = g_last_hip_error;
+                st = get_workspace(dev, stream, (size_t)p->workspace_bytes, (size_t)p->grid_x, &ws, &counters);
+                if (st == HKG_ERR_WORKSPACE && cs != hipStreamCaptureStatusNone) {
+                    split = false;
+                    g_last_hip_error = before;
+                } else if (st != HKG_OK) {
+                    return st;
+                }
+            }
+            if (split)
+                e = launch_grouped(kGroupedPingPong, a, b, nullptr, 1, c, (int)M, (int)N, (int)K, p->grid_x, 1, 2, ws,
+                                   counters, bias, epi, stream);
+            else
+                e = launch_tile(p->variant, a, b, c, (int)M, (int)N, (int)K, p->xcd_window_w, p->xcd_chunk_c, 1,
+                                nullptr, nullptr, bias, epi, (int)lda, (int)ldb, (int)ldc, stream);
+            break;
+        }
         if (p->split_k > 1) {
             st = split_scratch(dev, stream, fixed, (size_t)p->split_k * (size_t)M * (size_t)N * sizeof(float),
                                (size_t)(cdiv(M, p->tile_m) * cdiv(N, p->tile_n)), &ws, &counters);

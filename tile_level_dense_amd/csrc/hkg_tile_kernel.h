@@ -962,6 +962,11 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         // decreasing per expert, so any offsets keep every access in bounds.
         static_assert(!MX && SCHED != 1, "grouped mode: bf16 tiles");
         auto expert_rows = [&](int g, int& r0, int& r1) {
+            if (offs == nullptr) {          // one expert of M rows (a dense GEMM)
+                r0 = 0;
+                r1 = M;
+                return;
+            }
             r0 = g > 0 ? min(max(offs[g - 1], 0), M) : 0;
             r1 = max(r0, min(offs[g], M));
         };

@@ -105,6 +105,11 @@ __device__ __forceinline__ void pingpong_persistent(const void* __restrict__ Av,
     // the N x K weight g of B; offsets are clamped into [0, M] and made non-
     // decreasing per expert, so any offsets keep every access in bounds.
     auto expert_rows = [&](int e, int& r0, int& r1) {
+        if (offs == nullptr) {              // one expert of M rows (a dense GEMM)
+            r0 = 0;
+            r1 = M;
+            return;
+        }
         r0 = e > 0 ? min(max(offs[e - 1], 0), M) : 0;
         r1 = max(r0, min(offs[e], M));
     };
