@@ -111,6 +111,8 @@ CASES = [
     ("kinter_128x128", (129, 270, 136), lambda h: _tile(h, 15)),
     ("kinter_128x128_s5", (200, 300, 456), lambda h: _tile(h, 16)),
     ("split_tail", (4400, 4200, 136), None),
+    ("tile256_one_round", (700, 900, 200), lambda h: _tile(h, 11)),
+    ("tile256_many_rounds", (4400, 4200, 72), lambda h: _tile(h, 11)),
     ("planner_skinny", (16, 1000, 2056), None),
     ("skinny_split3", (20, 300, 4096), lambda h: _skinny(h, 1, 3)),
     ("skinny_nb4", (9, 100, 520), lambda h: _skinny(h, 5, 1)),
