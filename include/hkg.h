@@ -85,7 +85,8 @@ typedef enum {
     HKG_KERNEL_ZERO = 4,        /* K == 0: C is the empty sum, +0 (then the epilogue) */
     HKG_KERNEL_MX_TILE = 5,     /* MXFP8 large-tile kernel (scaled MFMA) */
     HKG_KERNEL_GROUPED = 6,     /* grouped (mixture-of-experts) tile kernel, persistent grid */
-    HKG_KERNEL_MX_SKINNY = 7    /* MXFP8 small-M kernel: streams B once, split-K */
+    HKG_KERNEL_MX_SKINNY = 7,   /* MXFP8 small-M kernel: streams B once, split-K */
+    HKG_KERNEL_MX4_TILE = 8     /* MXFP4 tile kernel (scaled MFMA, E2M1 operands) */
 } hkg_kernel_t;
 
 /*
@@ -257,6 +258,59 @@ hkg_status_t hkg_gemm_mxfp8_prepacked(const void* A, const void* PA, const void*
  * xcd fields >= 0) on packed scales; other plans give HKG_ERR_UNSUPPORTED.
  */
 hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
+                                     const void* PB, const void* bias, void* C, int64_t M, int64_t N,
+                                     int64_t K, int32_t epilogue, void* stream);
+
+/*
+ * Block-scaled FP4 GEMM (MXFP4), the packed-FP4 form of the same MXFP
+ * section of the FlyDSL-in-PyTorch blog (E2M1 values stored two per byte,
+ * one E8M0 scale per 32 values along K, fp32 accumulation, bf16 output):
+ *
+ *   C[i][j] = bf16( sum over k of  a(i,k) 2^(SA[i][k/32] - 127) * b(j,k) 2^(SB[j][k/32] - 127) )
+ *
+ *   A: M x K/2 bytes, row-major; byte c of row i holds a(i, 2c) in its low
+ *      nibble and a(i, 2c + 1) in its high nibble, each an E2M1 code (OCP
+ *      MX: 1 sign bit, 2 exponent bits with bias 1, 1 fraction bit; values
+ *      0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; no infinities or
+ *      NaNs).  B: N x K/2 bytes likewise.
+ *   SA: M x K/32 bytes, SB: N x K/32 bytes, E8M0 codes as for MXFP8.
+ *   C: M x N bf16, row-major, nearest-even.  K must be a multiple of 128
+ *   (else HKG_ERR_INVALID_ARG); M and N are free.
+ *
+ * Accuracy.  A product of two E2M1 values is a multiple of 1/4 below 37,
+ * and the 32 products of one scale block share one power-of-two scale, so
+ * the matrix cores form every block's partial sums exactly; they combine
+ * them with the running sum in fp32.  So |C - exact| <= 2^-8 |C| + fp32
+ * accumulation (at most 17 roundings of 2^-24 relative per 128 k).
+ *
+ * Scales are consumed in the packed layout of hkg_mx_pack_scales (the same
+ * as MXFP8's); hkg_gemm_mxfp4 packs SA and SB into the stream's
+ * library-owned workspace on every call, hkg_gemm_mxfp4_prepacked takes
+ * packed scales.  Pointers: A, B, C 16-byte aligned, packed scales 4-byte
+ * aligned (else HKG_ERR_MISALIGNED), device memory owned by the caller; C
+ * overlaps no input.  bias / epilogue as in hkg_gemm_bf16_epilogue.  Shapes
+ * whose packed scales reach 2^31 bytes, or K above 16777088, give
+ * HKG_ERR_UNSUPPORTED.
+ */
+
+/* The plan an MXFP4 call of this shape uses (host only, no device). */
+hkg_status_t hkg_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out);
+
+/* C = epilogue(MXFP4 A * B^T + bias) with natural-layout scales SA, SB. */
+hkg_status_t hkg_gemm_mxfp4(const void* A, const void* SA, const void* B, const void* SB, const void* bias,
+                            void* C, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream);
+
+/* hkg_gemm_mxfp4 with packed scales PA (of A, M rows) and PB (of B, N rows). */
+hkg_status_t hkg_gemm_mxfp4_prepacked(const void* A, const void* PA, const void* B, const void* PB,
+                                      const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                                      int32_t epilogue, void* stream);
+
+/*
+ * Runs an MXFP4 plan (from hkg_gemm_mxfp4_plan, possibly edited: variant
+ * with matching tile fields, split_k in [1, 16] for split-capable variants,
+ * xcd fields >= 0) on packed scales; other plans give HKG_ERR_UNSUPPORTED.
+ */
+hkg_status_t hkg_gemm_mxfp4_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
                                      const void* PB, const void* bias, void* C, int64_t M, int64_t N,
                                      int64_t K, int32_t epilogue, void* stream);
 

@@ -70,6 +70,12 @@ def _bind(path):
     lib.hkg_oracle_mx_gemm_entries.argtypes = [u8p, u8p, u8p, u8p, i64, i64, i64, i64p, i64p, i64,
                                                u16p, f64p, f64p, ctypes.c_int]
     lib.hkg_oracle_mx_gemm_entries.restype = None
+    lib.hkg_oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.hkg_oracle_e2m1_value.restype = ctypes.c_double
+    lib.hkg_oracle_mx4_gemm_rows.argtypes = lib.hkg_oracle_mx_gemm_rows.argtypes
+    lib.hkg_oracle_mx4_gemm_rows.restype = None
+    lib.hkg_oracle_mx4_gemm_entries.argtypes = lib.hkg_oracle_mx_gemm_entries.argtypes
+    lib.hkg_oracle_mx4_gemm_entries.restype = None
     lib.hkg_oracle_activation.argtypes = [ctypes.c_double, ctypes.c_int]
     lib.hkg_oracle_activation.restype = ctypes.c_double
     lib.hkg_oracle_epilogue.argtypes = [f64p, u16p, i64, i64, i64p, ctypes.c_int, f64p, u16p]
@@ -276,6 +282,65 @@ class Oracle:
                 int(nthreads))
         return C, S, absS
 
+    def e2m1_value(self, code):
+        """f64 value of one E2M1 code (0..15), from the format definition."""
+        return self.lib.hkg_oracle_e2m1_value(int(code))
+
+    def _mx4_operands(self, A, SA, B, SB):
+        A = np.ascontiguousarray(A, dtype=np.uint8)
+        B = np.ascontiguousarray(B, dtype=np.uint8)
+        SA = np.ascontiguousarray(SA, dtype=np.uint8)
+        SB = np.ascontiguousarray(SB, dtype=np.uint8)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[1] or A.shape[1] % 16:
+            raise ValueError("A must be M x K/2 and B N x K/2 bytes of E2M1 pairs, K a multiple of 32")
+        K = 2 * A.shape[1]
+        if SA.shape != (A.shape[0], K // 32) or SB.shape != (B.shape[0], K // 32):
+            raise ValueError("scales must be M x K/32 and N x K/32 E8M0 codes")
+        return A, SA, B, SB, K
+
+    def mx4_gemm(self, A, SA, B, SB, rows=None, nthreads=0, want_sums=True):
+        """MXFP4 C = (A * 2^SA) (B * 2^SB)^T over rows [r0, r1) (FlyDSL blog, MXFP
+        section; A, B packed two E2M1 codes per byte, k even in the low nibble):
+        (C bits uint16, S, absS) like gemm()."""
+        A, SA, B, SB, K = self._mx4_operands(A, SA, B, SB)
+        M = A.shape[0]
+        N = B.shape[0]
+        r0, r1 = (0, M) if rows is None else rows
+        if not (0 <= r0 <= r1 <= M):
+            raise ValueError("row range out of bounds")
+        C = np.zeros((r1 - r0, N), dtype=np.uint16)
+        S = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        absS = np.zeros((r1 - r0, N), dtype=np.float64) if want_sums else None
+        if r1 > r0 and N > 0:
+            self.lib.hkg_oracle_mx4_gemm_rows(
+                _ptr(A, ctypes.c_uint8), _ptr(SA, ctypes.c_uint8), _ptr(B, ctypes.c_uint8),
+                _ptr(SB, ctypes.c_uint8), M, N, K, r0, r1, _ptr(C, ctypes.c_uint16),
+                _ptr(S, ctypes.c_double), _ptr(absS, ctypes.c_double), int(nthreads))
+        return C, S, absS
+
+    def mx4_gemm_entries(self, A, SA, B, SB, ii, jj, nthreads=0):
+        """Selected elements of the MXFP4 product with their S and absS."""
+        A, SA, B, SB, K = self._mx4_operands(A, SA, B, SB)
+        M = A.shape[0]
+        N = B.shape[0]
+        ii = np.ascontiguousarray(ii, dtype=np.int64)
+        jj = np.ascontiguousarray(jj, dtype=np.int64)
+        if ii.shape != jj.shape:
+            raise ValueError("index arrays differ in shape")
+        if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+            raise ValueError("index out of bounds")
+        n = ii.size
+        C = np.zeros(n, dtype=np.uint16)
+        S = np.zeros(n, dtype=np.float64)
+        absS = np.zeros(n, dtype=np.float64)
+        if n:
+            self.lib.hkg_oracle_mx4_gemm_entries(
+                _ptr(A, ctypes.c_uint8), _ptr(SA, ctypes.c_uint8), _ptr(B, ctypes.c_uint8),
+                _ptr(SB, ctypes.c_uint8), M, N, K, _ptr(ii, ctypes.c_int64), _ptr(jj, ctypes.c_int64), n,
+                _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_double), _ptr(absS, ctypes.c_double),
+                int(nthreads))
+        return C, S, absS
+
     def activation(self, x, epilogue):
         """act(x) in fp64 for one epilogue (x already includes the bias)."""
         return float(self.lib.hkg_oracle_activation(float(x), EPILOGUES[epilogue]))
@@ -364,6 +429,18 @@ def mx_gemm(A, SA, B, SB, rows=None, nthreads=0, want_sums=True):
 
 def mx_gemm_entries(A, SA, B, SB, ii, jj, nthreads=0):
     return default().mx_gemm_entries(A, SA, B, SB, ii, jj, nthreads)
+
+
+def e2m1_value(code):
+    return default().e2m1_value(code)
+
+
+def mx4_gemm(A, SA, B, SB, rows=None, nthreads=0, want_sums=True):
+    return default().mx4_gemm(A, SA, B, SB, rows, nthreads, want_sums)
+
+
+def mx4_gemm_entries(A, SA, B, SB, ii, jj, nthreads=0):
+    return default().mx4_gemm_entries(A, SA, B, SB, ii, jj, nthreads)
 
 
 def epilogue(S, bias, epilogue, cols=None):

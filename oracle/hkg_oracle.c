@@ -37,6 +37,11 @@
  *   MXFP8: every E4M3 and E8M0 code against torch's float8_e4m3fn and
  *   float8_e8m0fnu conversions; all-ones with unit scales (C = K); scale
  *   changes multiply exactly by powers of two; exact rationals on tiny shapes.
+ *   MXFP4: the eight E2M1 magnitudes of the format definition; every E2M1
+ *   code through its E4M3 equivalent and torch's float8_e4m3fn conversion;
+ *   the MXFP4 product equal to the MXFP8 product of the same values (an
+ *   independent decoder); all-ones with unit scales (C = K); scale changes
+ *   multiply exactly by powers of two; exact rationals on tiny shapes.
  *   Layouts: every (A, B) layout with padded leading dimensions equals the
  *   dense oracle on the logical matrices, and padding (filled with NaN
  *   patterns) is never read.
@@ -457,6 +462,102 @@ void hkg_oracle_mx_gemm_entries(const uint8_t* A, const uint8_t* SA, const uint8
     for (int64_t t = 0; t < count; ++t) {
         double s, sa;
         mx_dot_one(A + ii[t] * K, SA + ii[t] * KB, B + jj[t] * K, SB + jj[t] * KB, K, &s, &sa);
+        C[t] = hkg_oracle_bf16_rne(s);
+        if (S)
+            S[t] = s;
+        if (absS)
+            absS[t] = sa;
+    }
+}
+
+
+/* ---- MXFP4 GEMM ----------------------------------------------------------
+ * The same MXFP section of the "FlyDSL in PyTorch" blog page names the
+ * packed-FP4 form: E2M1 operands stored two per byte, one E8M0 scale per 32
+ * values along the reduction axis, fp32 accumulation, bf16 output.  Written
+ * out as for MXFP8:
+ *
+ *   a(i,k) = e2m1(nibble k of row i of A) * e8m0(SA[i][k / 32]),  b likewise
+ *   S[i][j] = sum over k ascending of a(i,k) * b(j,k)   (fp64)
+ *   C[i][j] = bf16 nearest-even rounding of S[i][j], once
+ *
+ * Layouts: A is M x K/2 bytes and B N x K/2 bytes; byte c of a row holds
+ * element 2c in its low nibble and element 2c + 1 in its high nibble.  SA is
+ * M x K/32 and SB N x K/32 bytes.
+ * E2M1 (OCP MX): 1 sign bit, 2 exponent bits (bias 1), 1 fraction bit;
+ * exponent field 0 holds the subnormals 0.f * 2^0 (0 and 0.5), otherwise
+ * 1.f * 2^(e - 1); no infinities or NaNs; the largest value is 6.
+ * Every scaled product is exact in fp64; only the running sums round.
+ */
+double hkg_oracle_e2m1_value(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int f = code & 1;
+    double mag = e == 0 ? (double)f / 2.0                        /* subnormal: 0.f * 2^0 */
+                        : ldexp(1.0 + (double)f / 2.0, e - 1);    /* normal: 1.f * 2^(e-1) */
+    return sign ? -mag : mag;
+}
+
+static double mx4_element(const uint8_t* row, int64_t k)
+{
+    const uint8_t byte = row[k / 2];
+    return hkg_oracle_e2m1_value((uint8_t)((k & 1) ? byte >> 4 : byte & 0xF));
+}
+
+static void mx4_dot_one(const uint8_t* a_row, const uint8_t* sa_row, const uint8_t* b_row,
+                        const uint8_t* sb_row, int64_t K, double* s_out, double* abs_out)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = (mx4_element(a_row, k) * hkg_oracle_e8m0_value(sa_row[k / 32])) *
+                   (mx4_element(b_row, k) * hkg_oracle_e8m0_value(sb_row[k / 32]));
+        s += p;
+        sa += fabs(p);
+    }
+    *s_out = s;
+    *abs_out = sa;
+}
+
+/* Rows [row_begin, row_end) of the MXFP4 product; outputs as in
+ * hkg_oracle_gemm_rows.  K must be a multiple of 32. */
+void hkg_oracle_mx4_gemm_rows(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                              int64_t M, int64_t N, int64_t K, int64_t row_begin, int64_t row_end,
+                              uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    const int64_t KB = K / 32, KH = K / 2;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s, sa;
+            mx4_dot_one(A + i * KH, SA + i * KB, B + j * KH, SB + j * KB, K, &s, &sa);
+            int64_t o = (i - row_begin) * N + j;
+            C[o] = hkg_oracle_bf16_rne(s);
+            if (S)
+                S[o] = s;
+            if (absS)
+                absS[o] = sa;
+        }
+    }
+}
+
+/* Selected elements (ii[t], jj[t]) of the MXFP4 product. */
+void hkg_oracle_mx4_gemm_entries(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                                 int64_t M, int64_t N, int64_t K, const int64_t* ii, const int64_t* jj,
+                                 int64_t count, uint16_t* C, double* S, double* absS, int nthreads)
+{
+    (void)M;
+    (void)N;
+    const int64_t KB = K / 32, KH = K / 2;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
+    for (int64_t t = 0; t < count; ++t) {
+        double s, sa;
+        mx4_dot_one(A + ii[t] * KH, SA + ii[t] * KB, B + jj[t] * KH, SB + jj[t] * KB, K, &s, &sa);
         C[t] = hkg_oracle_bf16_rne(s);
         if (S)
             S[t] = s;

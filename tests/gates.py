@@ -172,3 +172,19 @@ def compare_mx_epilogue(c_bits, c_ref_bits, Y, absS, bias_vals, T, K):
     extra = 1.13 * np.asarray(T, dtype=np.float64) + \
         EPI_REL_EXTRA * (np.abs(Y) + np.abs(np.asarray(bias_vals, dtype=np.float64)))
     return compare(c_bits, c_ref_bits, Y, absS, acc=1.13 * mx_acc(K), extra=extra)
+
+
+# ------------------------------------------------------------------ MXFP4
+# E2M1 x E2M1 products are multiples of 1/4 below 37 (so within a factor
+# 2^8 of one another) and the 32 products of a scale block share one power-
+# of-two scale.  Summed at a fixed point aligned to a group's largest
+# product with the MXFP8 window above (2^13 of that product's power of
+# two), every such product is a whole multiple of the quantum: the block
+# sums are exact, T = 0, and the gate is the bf16 rounding plus the same
+# fp32 accumulation allowance.
+def compare_mx4(c_bits, c_ref_bits, S, absS, K):
+    return compare_mx(c_bits, c_ref_bits, S, absS, 0.0, K)
+
+
+def compare_mx4_epilogue(c_bits, c_ref_bits, Y, absS, bias_vals, K):
+    return compare_mx_epilogue(c_bits, c_ref_bits, Y, absS, bias_vals, 0.0, K)

@@ -433,6 +433,105 @@ def check_layout_index_roles(O):
     assert not np.array_equal(S3, S0)                       # the check above can fail
 
 
+# ------------------------------------------------------------------ MXFP4
+# Block-scaled FP4 GEMM (FlyDSL-in-PyTorch blog, MXFP section): packed E2M1
+# values, one E8M0 scale per 32 along K.
+
+# The E2M1 magnitudes of codes 0-7 as the OCP MX format defines them (sign
+# bit 3, two exponent bits with bias 1, one fraction bit: 0, 0.5 subnormal;
+# then 1.f * 2^(e - 1)).
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e2m1_as_e4m3(code):
+    # The E4M3 code of the same value, by bit fields (an independent route to
+    # the value through torch's float8_e4m3fn decoder).
+    s, e, f = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    if e == 0 and f == 0:
+        return s << 7
+    if e == 0:                                   # 0.5 = 1.0 * 2^-1
+        return (s << 7) | (6 << 3)
+    return (s << 7) | ((e + 6) << 3) | (f << 2)
+
+
+def check_e2m1_magnitudes(O):
+    got = [O.e2m1_value(c) for c in range(16)]
+    assert got[:8] == E2M1_MAGNITUDES
+    assert got[8:] == [-m for m in E2M1_MAGNITUDES]
+    assert np.signbit(got[8]) and not np.signbit(got[0])
+
+
+def check_e2m1_via_e4m3(O):
+    ref = _torch_e4m3(np.array([_e2m1_as_e4m3(c) for c in range(16)], dtype=np.uint8))
+    got = np.array([O.e2m1_value(c) for c in range(16)])
+    assert np.array_equal(got, ref) and np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def check_mx4_equals_mx8_of_same_values(O):
+    # Every E2M1 value is an E4M3 value: the MXFP4 product equals the (pinned)
+    # MXFP8 product of the re-encoded codes with the same scales, bit for bit.
+    to8 = np.array([_e2m1_as_e4m3(c) for c in range(16)], dtype=np.uint8)
+    for (M, N, K, seed) in ((7, 9, 128, 1), (3, 20, 256, 2)):
+        A, SA, B, SB = workloads.make_mx4_inputs(M, N, K, sa=(110, 140), sb=(110, 140), seed=seed)
+        A8, B8 = to8[workloads.unpack_e2m1(A)], to8[workloads.unpack_e2m1(B)]
+        C4, S4, a4 = O.mx4_gemm(A, SA, B, SB)
+        C8, S8, a8 = O.mx_gemm(A8, SA, B8, SB)
+        assert np.array_equal(S4, S8) and np.array_equal(a4, a8) and np.array_equal(C4, C8)
+
+
+def check_mx4_all_ones(O):
+    # E2M1 code 2 is 1.0 (byte 0x22 holds two); unit scales: C = K exactly.
+    for K in (128, 4096):
+        A = np.full((3, K // 2), 0x22, dtype=np.uint8)
+        B = np.full((5, K // 2), 0x22, dtype=np.uint8)
+        C, S, absS = O.mx4_gemm(A, np.full((3, K // 32), 127, np.uint8), B, np.full((5, K // 32), 127, np.uint8))
+        assert np.all(S == K) and np.all(absS == K) and np.all(C == exact.round_exact(K))
+
+
+def check_mx4_blocks_and_pairing(O):
+    # A one-hot at k in both operands gives exactly the product of the two
+    # values times 2^(sa + sb) with the scales of block k / 32, and a one-hot
+    # in the other nibble of the same byte pairs with nothing.  (Which nibble
+    # holds k even changes only the order of the fp64 sum, which the exact
+    # MXFP8 comparison above sees.)
+    K = 128
+    for k in (0, 1, 31, 32, 77, 127):
+        A = np.zeros((1, K // 2), np.uint8)
+        B = np.zeros((1, K // 2), np.uint8)
+        A[0, k // 2] = 0x3 << (4 * (k & 1))                # 1.5 at k
+        B[0, k // 2] = 0x7 << (4 * (k & 1))                # 6.0 at k
+        SA = np.full((1, K // 32), 127, np.uint8); SA[0, k // 32] = 130
+        SB = np.full((1, K // 32), 127, np.uint8); SB[0, k // 32] = 125
+        _, S, _ = O.mx4_gemm(A, SA, B, SB)
+        assert S[0, 0] == 1.5 * 6.0 * 2.0 ** (3 - 2), k
+        B2 = np.zeros_like(B); B2[0, k // 2] = 0x7 << (4 * (1 - (k & 1)))
+        _, S2, _ = O.mx4_gemm(A, SA, B2, SB)
+        assert S2[0, 0] == 0.0, k
+
+
+def check_mx4_brute_force_tiny(O):
+    # Exact rationals from the magnitude list and the scale definition.
+    rng = np.random.default_rng(23)
+    val = [Fraction(m) for m in E2M1_MAGNITUDES] + [-Fraction(m) for m in E2M1_MAGNITUDES]
+    for trial in range(4):
+        M, N = [int(v) for v in rng.integers(1, 5, size=2)]
+        K = 64
+        a = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+        b = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+        SA = rng.integers(100, 150, size=(M, 2)).astype(np.uint8)
+        SB = rng.integers(100, 150, size=(N, 2)).astype(np.uint8)
+        C, S, absS = O.mx4_gemm(workloads.pack_e2m1(a), SA, workloads.pack_e2m1(b), SB)
+        for i in range(M):
+            for j in range(N):
+                s = sum(val[a[i, k]] * val[b[j, k]] * Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254)
+                        for k in range(K))
+                sa = sum(abs(val[a[i, k]] * val[b[j, k]]) * Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254)
+                         for k in range(K))
+                assert abs(Fraction(S[i, j]) - s) <= K * Fraction(2) ** -53 * sa, (trial, i, j)
+                assert Fraction(absS[i, j]) == sa or abs(Fraction(absS[i, j]) - sa) <= K * Fraction(2) ** -53 * sa
+                assert C[i, j] == exact.round_exact(s), (trial, i, j)
+
+
 ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_ties,
               check_rne_vs_float32_bit_rounding, check_all_ones, check_identity,
               check_small_integers, check_brute_force_tiny, check_fp64_bound_workload,
@@ -441,7 +540,9 @@ ALL_CHECKS = [check_value_exhaustive, check_roundtrip_exhaustive, check_golden_t
               check_e8m0_exhaustive, check_mx_all_ones, check_mx_unit_scales_equal_bf16_gemm,
               check_mx_scales_are_powers_of_two, check_mx_brute_force_tiny, check_grouped_one_expert_is_dense,
               check_grouped_expert_identity, check_grouped_permutation, check_grouped_brute_force_tiny,
-              check_layouts_equal_dense, check_layout_index_roles]
+              check_layouts_equal_dense, check_layout_index_roles, check_e2m1_magnitudes, check_e2m1_via_e4m3,
+              check_mx4_equals_mx8_of_same_values, check_mx4_all_ones, check_mx4_blocks_and_pairing,
+              check_mx4_brute_force_tiny]
 
 
 @pytest.fixture(scope="module")
@@ -486,6 +587,25 @@ def test_mx_rows_and_entries_consistent(O):
     assert np.array_equal(ae, absS[ii, jj])
     C1, S1, _ = O.mx_gemm(A, SA, B, SB, nthreads=1)
     assert np.array_equal(C1, C) and np.array_equal(S1, S)
+
+
+def test_mx4_rows_and_entries_consistent(O):
+    A, SA, B, SB = workloads.make_mx4_inputs(40, 33, 256, seed=6)
+    C, S, absS = O.mx4_gemm(A, SA, B, SB)
+    Cr, Sr, _ = O.mx4_gemm(A, SA, B, SB, rows=(7, 29))
+    assert np.array_equal(Cr, C[7:29]) and np.array_equal(Sr, S[7:29])
+    ii = np.array([0, 39, 7, 20]); jj = np.array([32, 0, 5, 17])
+    Ce, Se, ae = O.mx4_gemm_entries(A, SA, B, SB, ii, jj)
+    assert np.array_equal(Ce, C[ii, jj]) and np.array_equal(Se, S[ii, jj])
+    assert np.array_equal(ae, absS[ii, jj])
+
+
+def test_mx4_pack_round_trip():
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, size=(5, 64)).astype(np.uint8)
+    packed = workloads.pack_e2m1(codes)
+    assert packed.shape == (5, 32) and np.array_equal(workloads.unpack_e2m1(packed), codes)
+    assert packed[0, 0] == codes[0, 0] | (codes[0, 1] << 4)
 
 
 def test_mx_quantizer_round_trips(O):

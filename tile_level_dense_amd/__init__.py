@@ -1,5 +1,5 @@
 """Python binding of libhkg.so, the gfx950 dense BF16 GEMM C = A * B^T (and
-its block-scaled FP8 form, MXFP8).
+its block-scaled forms, MXFP8 and MXFP4).
 
 Argument marshalling only: every step of the GEMM runs in the library's HIP
 kernels.  The binding uses ctypes and mirrors the C ABI of include/hkg.h with
@@ -8,12 +8,15 @@ the same names (``hkg_gemm_bf16``, ``hkg_gemm_bf16_epilogue``,
 ``hkg_gemm_bf16_run_plan_epilogue``, ``hkg_status_string``, and the MXFP8
 calls ``hkg_gemm_mxfp8``, ``hkg_gemm_mxfp8_plan``, ``hkg_mx_pack_scales``,
 ``hkg_mx_packed_scales_bytes``, ``hkg_gemm_mxfp8_prepacked``,
-``hkg_gemm_mxfp8_run_plan``, and the grouped calls ``hkg_grouped_gemm_bf16``,
-``hkg_grouped_gemm_bf16_plan``, ``hkg_grouped_gemm_bf16_run_plan``, and the
-layout calls ``hkg_gemm_bf16_ex``, ``hkg_pack_bf16``); ``gemm``, ``gemm_ex``,
-``pack``, ``gemm_mxfp8`` and ``grouped_gemm`` are the torch-facing convenience
-wrappers (with ``bias=`` and ``epilogue=`` for the
-fused epilogues).  torch supplies device memory and streams.
+``hkg_gemm_mxfp8_run_plan``, the MXFP4 calls ``hkg_gemm_mxfp4``,
+``hkg_gemm_mxfp4_plan``, ``hkg_gemm_mxfp4_prepacked``,
+``hkg_gemm_mxfp4_run_plan``, the grouped calls
+``hkg_grouped_gemm_bf16``, ``hkg_grouped_gemm_bf16_plan``,
+``hkg_grouped_gemm_bf16_run_plan``, and the layout calls ``hkg_gemm_bf16_ex``,
+``hkg_pack_bf16``); ``gemm``, ``gemm_ex``, ``pack``, ``gemm_mxfp8``,
+``gemm_mxfp4`` and ``grouped_gemm`` are the torch-facing convenience wrappers
+(with ``bias=`` and ``epilogue=`` for the fused epilogues).  torch supplies
+device memory and streams.
 
 There is no fallback: if the library is not built and cannot be built, or a
 call fails, an exception is raised.
@@ -28,7 +31,9 @@ __all__ = ["HkgError", "Plan", "hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_g
            "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan", "gemm_mxfp8",
            "mx_plan", "mx_pack_scales", "run_mx_plan", "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan",
            "hkg_grouped_gemm_bf16_run_plan", "grouped_gemm", "grouped_plan", "hkg_gemm_bf16_ex", "hkg_pack_bf16",
-           "gemm_ex", "pack", "LAYOUT_ROW", "LAYOUT_COL", "hkg_gemm_bf16_noalloc"]
+           "gemm_ex", "pack", "LAYOUT_ROW", "LAYOUT_COL", "hkg_gemm_bf16_noalloc", "hkg_gemm_mxfp4",
+           "hkg_gemm_mxfp4_plan", "hkg_gemm_mxfp4_prepacked", "hkg_gemm_mxfp4_run_plan", "gemm_mxfp4",
+           "mx4_plan", "run_mx4_plan"]
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libhkg.so")
@@ -45,9 +50,9 @@ HKG_ERR_ARCH = -5
 HKG_ERR_HIP = -6
 HKG_ERR_WORKSPACE = -7
 KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE", 6: "GROUPED",
-                7: "MX_SKINNY"}
+                7: "MX_SKINNY", 8: "MX4_TILE"}
 (HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE,
- HKG_KERNEL_GROUPED, HKG_KERNEL_MX_SKINNY) = range(8)
+ HKG_KERNEL_GROUPED, HKG_KERNEL_MX_SKINNY, HKG_KERNEL_MX4_TILE) = range(9)
 
 LAYOUT_ROW, LAYOUT_COL = 0, 1          # hkg_layout_t
 
@@ -59,7 +64,8 @@ EXPORTED_SYMBOLS = ["hkg_gemm_bf16", "hkg_gemm_bf16_epilogue", "hkg_gemm_bf16_pl
                     "hkg_abi_version", "hkg_gemm_mxfp8", "hkg_gemm_mxfp8_plan", "hkg_mx_pack_scales",
                     "hkg_mx_packed_scales_bytes", "hkg_gemm_mxfp8_prepacked", "hkg_gemm_mxfp8_run_plan",
                     "hkg_grouped_gemm_bf16", "hkg_grouped_gemm_bf16_plan", "hkg_grouped_gemm_bf16_run_plan",
-                    "hkg_gemm_bf16_ex", "hkg_pack_bf16", "hkg_gemm_bf16_noalloc"]
+                    "hkg_gemm_bf16_ex", "hkg_pack_bf16", "hkg_gemm_bf16_noalloc", "hkg_gemm_mxfp4",
+                    "hkg_gemm_mxfp4_plan", "hkg_gemm_mxfp4_prepacked", "hkg_gemm_mxfp4_run_plan"]
 
 
 class Plan(ctypes.Structure):
@@ -151,6 +157,14 @@ def _load():
     lib.hkg_gemm_mxfp8_prepacked.restype = ctypes.c_int
     lib.hkg_gemm_mxfp8_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.hkg_gemm_mxfp8_run_plan.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp4_plan.argtypes = [i64, i64, i64, ctypes.POINTER(Plan)]
+    lib.hkg_gemm_mxfp4_plan.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp4.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp4_prepacked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp4_prepacked.restype = ctypes.c_int
+    lib.hkg_gemm_mxfp4_run_plan.argtypes = [ctypes.POINTER(Plan), vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.hkg_gemm_mxfp4_run_plan.restype = ctypes.c_int
     lib.hkg_grouped_gemm_bf16_plan.argtypes = [i64, i64, i64, i64, ctypes.POINTER(Plan)]
     lib.hkg_grouped_gemm_bf16_plan.restype = ctypes.c_int
     lib.hkg_grouped_gemm_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
@@ -229,6 +243,25 @@ def hkg_gemm_mxfp8_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=
 
 def hkg_gemm_mxfp8_run_plan(plan_, A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
     return _load().hkg_gemm_mxfp8_run_plan(ctypes.byref(plan_), A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_mxfp4(A, SA, B, SB, bias, C, M, N, K, epilogue=0, stream=None):
+    """C-ABI call with raw device addresses (ints); returns the status code."""
+    return _load().hkg_gemm_mxfp4(A, SA, B, SB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_mxfp4_plan(M, N, K):
+    p = Plan()
+    st = _load().hkg_gemm_mxfp4_plan(M, N, K, ctypes.byref(p))
+    return st, p
+
+
+def hkg_gemm_mxfp4_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
+    return _load().hkg_gemm_mxfp4_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
+
+
+def hkg_gemm_mxfp4_run_plan(plan_, A, PA, B, PB, bias, C, M, N, K, epilogue=0, stream=None):
+    return _load().hkg_gemm_mxfp4_run_plan(ctypes.byref(plan_), A, PA, B, PB, bias, C, M, N, K, epilogue, stream)
 
 
 def hkg_gemm_bf16_ex(A, lda, a_layout, B, ldb, b_layout, bias, C, ldc, M, N, K, epilogue=0, stream=None):
@@ -351,9 +384,10 @@ def run_plan(plan_, a, b, out=None, stream=None, bias=None, epilogue="none"):
 
 
 # ------------------------------------------------------------------ MXFP8
-def _check_mx(a, sa, b, sb, out, packed):
-    """Shapes of uint8 device tensors: a M x K and b N x K E4M3 codes; sa, sb the
-    E8M0 scales, M x K/32 and N x K/32 (or, packed, the packed byte counts)."""
+def _check_mx(a, sa, b, sb, out, packed, fp4=False):
+    """Shapes of uint8 device tensors: a M x K and b N x K E4M3 codes (fp4:
+    M x K/2 and N x K/2 bytes of E2M1 pairs); sa, sb the E8M0 scales, M x K/32
+    and N x K/32 (or, packed, the packed byte counts)."""
     import torch
     for t, name in ((a, "A"), (b, "B"), (sa, "SA"), (sb, "SB")):
         if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.device != a.device:
@@ -362,6 +396,8 @@ def _check_mx(a, sa, b, sb, out, packed):
         raise ValueError("A must be M x K and B N x K, got %s and %s" % (tuple(a.shape), tuple(b.shape)))
     M, K = a.shape
     N = b.shape[0]
+    if fp4:
+        K *= 2
     if packed:
         if sa.numel() != max(0, hkg_mx_packed_scales_bytes(M, K)) or \
                 sb.numel() != max(0, hkg_mx_packed_scales_bytes(N, K)):
@@ -389,6 +425,48 @@ def gemm_mxfp8(a, sa, b, sb, out=None, stream=None, bias=None, epilogue="none", 
                 code, _stream_handle(stream, a.device))
     if st != HKG_OK:
         raise HkgError(st, "hkg_gemm_mxfp8_prepacked" if packed else "hkg_gemm_mxfp8")
+    return out
+
+
+def gemm_mxfp4(a, sa, b, sb, out=None, stream=None, bias=None, epilogue="none", packed=False):
+    """C = epilogue(MXFP4 a @ b.T + bias): a (M x K/2) and b (N x K/2) uint8,
+    two E2M1 codes per byte (k even in the low nibble), sa / sb their E8M0
+    scales (M x K/32, N x K/32; or packed by mx_pack_scales when packed=True),
+    K % 128 == 0."""
+    import torch
+    M, N, K = _check_mx(a, sa, b, sb, out, packed, fp4=True)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    fn = _load().hkg_gemm_mxfp4_prepacked if packed else _load().hkg_gemm_mxfp4
+    with torch.cuda.device(a.device):
+        st = fn(a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(), bias_ptr or None, out.data_ptr(), M, N, K,
+                code, _stream_handle(stream, a.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp4_prepacked" if packed else "hkg_gemm_mxfp4")
+    return out
+
+
+def mx4_plan(M, N, K):
+    st, p = hkg_gemm_mxfp4_plan(M, N, K)
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp4_plan")
+    return p
+
+
+def run_mx4_plan(plan_, a, pa, b, pb, out=None, stream=None, bias=None, epilogue="none"):
+    """Runs an MXFP4 plan on packed scales pa, pb (a, b as gemm_mxfp4)."""
+    import torch
+    M, N, K = _check_mx(a, pa, b, pb, out, True, fp4=True)
+    bias_ptr, code = _epilogue_args(a, N, bias, epilogue)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    with torch.cuda.device(a.device):
+        st = _load().hkg_gemm_mxfp4_run_plan(ctypes.byref(plan_), a.data_ptr(), pa.data_ptr(), b.data_ptr(),
+                                             pb.data_ptr(), bias_ptr or None, out.data_ptr(), M, N, K, code,
+                                             _stream_handle(stream, a.device))
+    if st != HKG_OK:
+        raise HkgError(st, "hkg_gemm_mxfp4_run_plan")
     return out
 
 

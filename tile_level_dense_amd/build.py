@@ -30,11 +30,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 
 
-def tile_configs(mx=False, grouped=False):
+def tile_configs(mx=False, grouped=False, mx4=False):
     """(BM, BN, BK, STAGES, WM, WN, SCHED) per tile variant (bf16; MXFP8 with mx=True;
-    grouped with grouped=True), from hkg_tile_configs.h."""
+    MXFP4 with mx4=True; grouped with grouped=True), from hkg_tile_configs.h."""
     text = open(os.path.join(CSRC, "hkg_tile_configs.h")).read()
-    start = text.index("#define HKG_MX_TILE_CONFIGS(X)" if mx else
+    start = text.index("#define HKG_MX_TILE_CONFIGS(X)" if mx else "#define HKG_MX4_TILE_CONFIGS(X)" if mx4 else
                        "#define HKG_GROUPED_CONFIGS(X)" if grouped else "#define HKG_TILE_CONFIGS(X)")
     body = text[start:]
     end = body.find("#define", 10)
@@ -45,6 +45,7 @@ def tile_configs(mx=False, grouped=False):
 
 TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
+MX4_TILE_VARIANTS = tile_configs(mx4=True)
 GROUPED_VARIANTS = tile_configs(grouped=True)
 def skinny_configs(mx=False):
     """(MB, NB, WK, U, CP, AL) per skinny variant (MXFP8 with mx=True), from hkg_skinny_configs.h."""
@@ -111,6 +112,7 @@ def _entry(name, r):
 def _table(resources):
     tile = [None] * len(TILE_VARIANTS)
     mx_tile = [None] * len(MX_TILE_VARIANTS)
+    mx4_tile = [None] * len(MX4_TILE_VARIANTS)
     grouped = [None] * len(GROUPED_VARIANTS)
     skinny = [None] * len(SKINNY_VARIANTS)
     mx_skinny = [None] * len(MX_SKINNY_VARIANTS)
@@ -129,6 +131,8 @@ def _table(resources):
                 tile[TILE_VARIANTS.index(key)] = _entry("tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             elif plain and mx and key in MX_TILE_VARIANTS:
                 mx_tile[MX_TILE_VARIANTS.index(key)] = _entry("mxtile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
+            elif plain and mx and key in MX4_TILE_VARIANTS:
+                mx4_tile[MX4_TILE_VARIANTS.index(key)] = _entry("mx4tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
         m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E",
                       mangled)
@@ -151,10 +155,11 @@ def _table(resources):
               [100 + i for i, e in enumerate(skinny) if e is None] + \
               [200 + i for i, e in enumerate(mx_tile) if e is None] + \
               [300 + i for i, e in enumerate(grouped) if e is None] + \
-              [400 + i for i, e in enumerate(mx_skinny) if e is None] + ([-1] if generic is None else [])
+              [400 + i for i, e in enumerate(mx_skinny) if e is None] + \
+              [500 + i for i, e in enumerate(mx4_tile) if e is None] + ([-1] if generic is None else [])
     if missing:
         raise BuildError("resource report missing kernels: %s" % missing)
-    return tile, mx_tile, grouped, skinny, mx_skinny, generic
+    return tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic
 
 
 def _gate(entries):
@@ -167,7 +172,7 @@ def _gate(entries):
         raise BuildError("kernels use scratch / spill registers (refused): %s" % bad)
 
 
-def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, generic):
+def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic):
     def row(e):
         return '{"%s", %d, %d, %d, %d, %d}' % (e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"])
     text = "// generated by tile_level_dense_amd/build.py -- do not edit\n"
@@ -176,13 +181,14 @@ def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, generic):
     text += "const KernelResources kGroupedResources[] = {\n    " + ",\n    ".join(row(e) for e in grouped) + "};\n"
     text += "const KernelResources kSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in skinny) + "};\n"
     text += "const KernelResources kMxSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in mx_skinny) + "};\n"
+    text += "const KernelResources kMx4TileResources[] = {\n    " + ",\n    ".join(row(e) for e in mx4_tile) + "};\n"
     text += "const KernelResources kGenericResources = " + row(generic) + ";\n"
     path = os.path.join(BUILD, "hkg_resources.inc")
     with open(path, "w") as f:
         f.write(text)
     with open(os.path.join(BUILD, "kernel_resources.json"), "w") as f:
         json.dump(dict(tile=tile, mx_tile=mx_tile, grouped=grouped, skinny=skinny, mx_skinny=mx_skinny,
-                       generic=generic), f, indent=1)
+                       mx4_tile=mx4_tile, generic=generic), f, indent=1)
 
 
 def build(verbose=False):
@@ -195,16 +201,16 @@ def build(verbose=False):
     res = {}
     for _, r in results:
         res.update(r)
-    tile, mx_tile, grouped, skinny, mx_skinny, generic = _table(res)
+    tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic = _table(res)
     _gate([_entry(name, r) for name, r in res.items()])
-    _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, generic)
+    _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic)
     with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
         objs += [f.result()[0] for f in [ex.submit(_compile, s, False) for s in HOST_SOURCES]]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if verbose:
-        for e in tile + mx_tile + grouped + skinny + mx_skinny + [generic]:
+        for e in tile + mx_tile + grouped + skinny + mx_skinny + mx4_tile + [generic]:
             print("%-18s vgpr %3d agpr %3d sgpr %3d scratch %d lds %6d occ %d" % (
                 e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"], e["occupancy"]))
     return LIB

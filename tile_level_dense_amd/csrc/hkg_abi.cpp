@@ -960,12 +960,14 @@ bool mx_plan_matches_library(const hkg_plan_t* p)
     }
 }
 
-// Operand checks of the MXFP8 entry points: data of M x K and N x K bytes,
-// scales of `sa_bytes` and `sb_bytes`, C of M x N bf16; C overlaps nothing.
+// Operand checks of the block-scaled entry points: data of M x K and N x K
+// bytes (MXFP4: K / 2 bytes per row), scales of `sa_bytes` and `sb_bytes`, C
+// of M x N bf16; C overlaps nothing.
 hkg_status_t check_mx_pointers(const void* A, const void* SA, int64_t sa_bytes, const void* B, const void* SB,
-                               int64_t sb_bytes, const void* C, int64_t M, int64_t N, int64_t K)
+                               int64_t sb_bytes, const void* C, int64_t M, int64_t N, int64_t K, bool fp4 = false)
 {
-    const int64_t a_bytes = M * K, b_bytes = N * K, c_bytes = 2 * M * N;
+    const int64_t row = fp4 ? K / 2 : K;
+    const int64_t a_bytes = M * row, b_bytes = N * row, c_bytes = 2 * M * N;
     if ((a_bytes && !A) || (b_bytes && !B) || (c_bytes && !C) || (sa_bytes && !SA) || (sb_bytes && !SB))
         return HKG_ERR_INVALID_ARG;
     if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes) || overlaps(C, c_bytes, SA, sa_bytes) ||
@@ -1001,6 +1003,10 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
         if (p->kernel_id == HKG_KERNEL_MX_SKINNY)
             e = launch_skinny_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
                                  (int)K, p->split_k, ws, counters, bias, epi, PA, PB, natural, stream);
+        else if (p->kernel_id == HKG_KERNEL_MX4_TILE)
+            e = launch_tile_mx4(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
+                                (int)K, p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA,
+                                PB, stream);
         else
             e = launch_tile_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
                                (int)K, p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA, PB,
@@ -1013,7 +1019,10 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
     return HKG_OK;
 }
 
-bool mx_kernel(int id) { return id == HKG_KERNEL_MX_TILE || id == HKG_KERNEL_MX_SKINNY; }
+bool mx_kernel(int id)
+{
+    return id == HKG_KERNEL_MX_TILE || id == HKG_KERNEL_MX_SKINNY || id == HKG_KERNEL_MX4_TILE;
+}
 
 // The MXFP8 kernels read A, B with 16-byte accesses, store C in 8-byte
 // groups and reads packed scales as dwords.
@@ -1063,6 +1072,177 @@ hkg_status_t gemm_mx(const void* A, const void* SA, const void* B, const void* S
     if (p.kernel_id == HKG_KERNEL_MX_SKINNY && ((uintptr_t)SA & 3u) == 0 && ((uintptr_t)SB & 3u) == 0)
         return run_mx(&p, A, (const uint32_t*)SA, B, (const uint32_t*)SB, C, (const uint16_t*)bias, epi,
                       (hipStream_t)stream, true);
+    int dev = 0;
+    st = current_device(&dev);
+    if (st != HKG_OK)
+        return st;
+    const int64_t pa = mx_packed_scale_bytes(M, K), pb = mx_packed_scale_bytes(N, K);
+    uint8_t* ws = nullptr;
+    st = get_mx_workspace(dev, (hipStream_t)stream, (size_t)(pa + pb), &ws);
+    if (st != HKG_OK)
+        return st;
+    hipError_t e = launch_mx_pack((const uint8_t*)SA, (uint32_t*)ws, M, K, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = launch_mx_pack((const uint8_t*)SB, (uint32_t*)(ws + pa), N, K, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, "kernel launch");
+        return HKG_ERR_HIP;
+    }
+    return run_mx(&p, A, (const uint32_t*)ws, B, (const uint32_t*)(ws + pa), C, (const uint16_t*)bias, epi,
+                  (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------- MXFP4
+// Block-scaled FP4 GEMM (the same MXFP section): E2M1 operands two per byte,
+// one E8M0 scale per 32 k, K % 128 == 0; the tile kernel's MXFP4
+// instantiations, scales packed as for MXFP8.
+
+// Largest K whose 256-row tile (K / 2 bytes per row) spans fewer than 2^31
+// bytes.
+constexpr int64_t kMx4MaxK = (int64_t)(INT32_MAX / 256) * 2 / 128 * 128;
+
+bool mx4_shape_supported(int64_t M, int64_t N, int64_t K)
+{
+    return K <= kMx4MaxK && mx_packed_scale_bytes(M, K) <= INT32_MAX && mx_packed_scale_bytes(N, K) <= INT32_MAX;
+}
+
+void fill_mx4_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
+{
+    const TileShape s = mx4_tile_shape(variant);
+    const int64_t tm = cdiv(M, s.bm), tn = cdiv(N, s.bn);
+    p->kernel_id = HKG_KERNEL_MX4_TILE;
+    p->variant = variant;
+    p->tile_m = s.bm;
+    p->tile_n = s.bn;
+    p->tile_k = s.bk;
+    p->waves = s.waves;
+    p->split_k = (int32_t)split;
+    p->grid_x = (int32_t)(tm * tn);
+    p->grid_y = (int32_t)split;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    p->xcd_window_w = tm >= 8 ? 8 : (int32_t)tm;
+    p->xcd_chunk_c = (tm * tn >= 8 * 32) ? 32 : 0;
+    p->lds_bytes = mx4_tile_lds_bytes(variant);
+    fill_resources(p, mx4_tile_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "mx4tile_%dx%dx%d_s%d_w%dx%d_p%d", s.bm, s.bn, s.bk,
+                  s.stages, s.wm, s.wn, s.sched);
+    std::snprintf(p->reason, sizeof p->reason, "MXFP4: %lldx%lld tiles of %dx%d, split-K %lld", (long long)tm,
+                  (long long)tn, s.bm, s.bn, (long long)split);
+}
+
+hkg_status_t make_mx4_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
+{
+    std::memset(p, 0, sizeof *p);
+    p->abi_version = HKG_ABI_VERSION;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->split_k = 1;
+    p->vgprs = p->agprs = p->sgprs = p->scratch_bytes = -1;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (K % 128 != 0)
+        return HKG_ERR_INVALID_ARG;
+    p->flops = 2.0 * (double)M * (double)N * (double)K;
+    p->algorithmic_bytes = ((double)M + (double)N) * (double)(K / 2) + ((double)M + (double)N) * (double)(K / 32) +
+                           2.0 * (double)M * (double)N;
+    if (M == 0 || N == 0) {
+        p->kernel_id = HKG_KERNEL_NONE;
+        copy_str(p->kernel_name, sizeof p->kernel_name, "none");
+        copy_str(p->reason, sizeof p->reason, "empty output");
+        return HKG_OK;
+    }
+    if (K == 0) {
+        p->kernel_id = HKG_KERNEL_ZERO;
+        p->grid_x = 1;
+        p->block_x = 256;
+        copy_str(p->kernel_name, sizeof p->kernel_name, "zero");
+        copy_str(p->reason, sizeof p->reason, "K == 0: C is the empty sum, +0");
+        return HKG_OK;
+    }
+    if (!mx4_shape_supported(M, N, K))
+        return HKG_ERR_UNSUPPORTED;
+    // 256 x 256 ping-pong when its tiles fill the device; otherwise the
+    // 128 x 128 tile, with split-K (at least 2 stages of 256 k per split)
+    // while the grid is under one workgroup per compute unit.
+    const TileShape big = mx4_tile_shape(0);
+    const int variant = cdiv(M, big.bm) * cdiv(N, big.bn) >= kNumCUs ? 0 : 1;
+    const TileShape s = mx4_tile_shape(variant);
+    const int64_t tiles = cdiv(M, s.bm) * cdiv(N, s.bn);
+    if (tiles > INT32_MAX)
+        return HKG_ERR_UNSUPPORTED;
+    int64_t split = 1;
+    if (tiles < kNumCUs && M * N < ((int64_t)1 << 29) && tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) {
+        split = std::min<int64_t>(cdiv(kNumCUs, tiles), (K / 256) / 2);
+        split = std::max<int64_t>(1, std::min<int64_t>(split, kMaxTileSplit));
+    }
+    fill_mx4_tile(p, variant, split, M, N);
+    return HKG_OK;
+}
+
+bool mx4_plan_matches_library(const hkg_plan_t* p)
+{
+    switch (p->kernel_id) {
+    case HKG_KERNEL_NONE:
+        return p->M == 0 || p->N == 0;
+    case HKG_KERNEL_ZERO:
+        return p->K == 0 && p->M > 0 && p->N > 0;
+    case HKG_KERNEL_MX4_TILE: {
+        if (p->variant < 0 || p->variant >= MX4_TILE_NUM_VARIANTS)
+            return false;
+        const TileShape s = mx4_tile_shape(p->variant);
+        return p->tile_m == s.bm && p->tile_n == s.bn && p->tile_k == s.bk && p->waves == s.waves &&
+               p->split_k >= 1 && p->split_k <= kMaxTileSplit &&
+               (p->split_k == 1 || tile_split_capable(s.bm, s.bn, s.wm, s.wn, s.sched)) &&
+               (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->xcd_window_w >= 0 &&
+               p->xcd_chunk_c >= 0 && p->K > 0 && p->K % 128 == 0 && mx4_shape_supported(p->M, p->N, p->K) &&
+               cdiv(p->M, s.bm) * cdiv(p->N, s.bn) <= INT32_MAX;
+    }
+    default:
+        return false;
+    }
+}
+
+hkg_status_t gemm_mx4_prepacked(const void* A, const void* PA, const void* B, const void* PB, const void* bias,
+                                void* C, int64_t M, int64_t N, int64_t K, int32_t epi, void* stream)
+{
+    hkg_plan_t p;
+    hkg_status_t st = make_mx4_plan(M, N, K, &p);
+    if (st != HKG_OK)
+        return st;
+    const int64_t pa = K ? mx_packed_scale_bytes(M, K) : 0, pb = K ? mx_packed_scale_bytes(N, K) : 0;
+    st = check_mx_pointers(A, PA, pa, B, PB, pb, C, M, N, K, true);
+    if (st != HKG_OK)
+        return st;
+    st = check_epilogue(bias, C, M, N, epi);
+    if (st != HKG_OK)
+        return st;
+    if (mx_kernel(p.kernel_id) && !mx_aligned(A, PA, B, PB, C))
+        return HKG_ERR_MISALIGNED;
+    return run_mx(&p, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epi,
+                  (hipStream_t)stream);
+}
+
+hkg_status_t gemm_mx4(const void* A, const void* SA, const void* B, const void* SB, const void* bias, void* C,
+                      int64_t M, int64_t N, int64_t K, int32_t epi, void* stream)
+{
+    hkg_plan_t p;
+    hkg_status_t st = make_mx4_plan(M, N, K, &p);
+    if (st != HKG_OK)
+        return st;
+    st = check_mx_pointers(A, SA, M * (K / 32), B, SB, N * (K / 32), C, M, N, K, true);
+    if (st != HKG_OK)
+        return st;
+    st = check_epilogue(bias, C, M, N, epi);
+    if (st != HKG_OK)
+        return st;
+    if (!mx_kernel(p.kernel_id))
+        return run_mx(&p, A, nullptr, B, nullptr, C, (const uint16_t*)bias, epi, (hipStream_t)stream);
+    if (!(aligned16(A) && aligned16(B) && aligned16(C)))
+        return HKG_ERR_MISALIGNED;
     int dev = 0;
     st = current_device(&dev);
     if (st != HKG_OK)
@@ -1457,6 +1637,26 @@ hkg_status_t hkg_gemm_mxfp8_prepacked(const void* A, const void* PA, const void*
     return gemm_mx_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue, stream);
 }
 
+hkg_status_t hkg_gemm_mxfp4_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* out)
+{
+    if (!out)
+        return HKG_ERR_INVALID_ARG;
+    return make_mx4_plan(M, N, K, out);
+}
+
+hkg_status_t hkg_gemm_mxfp4(const void* A, const void* SA, const void* B, const void* SB, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K, int32_t epilogue, void* stream)
+{
+    return gemm_mx4(A, SA, B, SB, bias, C, M, N, K, epilogue, stream);
+}
+
+hkg_status_t hkg_gemm_mxfp4_prepacked(const void* A, const void* PA, const void* B, const void* PB,
+                                      const void* bias, void* C, int64_t M, int64_t N, int64_t K, int32_t epilogue,
+                                      void* stream)
+{
+    return gemm_mx4_prepacked(A, PA, B, PB, bias, C, M, N, K, epilogue, stream);
+}
+
 hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
                                      const void* PB, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                                      int32_t epilogue, void* stream)
@@ -1476,6 +1676,32 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
     if (st != HKG_OK)
         return st;
     if (!mx_plan_matches_library(plan))
+        return HKG_ERR_UNSUPPORTED;
+    if (mx_kernel(plan->kernel_id) && !mx_aligned(A, PA, B, PB, C))
+        return HKG_ERR_MISALIGNED;
+    return run_mx(plan, A, (const uint32_t*)PA, B, (const uint32_t*)PB, C, (const uint16_t*)bias, epilogue,
+                  (hipStream_t)stream);
+}
+
+hkg_status_t hkg_gemm_mxfp4_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
+                                     const void* PB, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                                     int32_t epilogue, void* stream)
+{
+    if (!plan || plan->abi_version != HKG_ABI_VERSION)
+        return HKG_ERR_INVALID_ARG;
+    hkg_status_t st = check_dims(M, N, K);
+    if (st != HKG_OK)
+        return st;
+    if (plan->M != M || plan->N != N || plan->K != K || K % 128 != 0)
+        return HKG_ERR_INVALID_ARG;
+    const int64_t pa = K ? mx_packed_scale_bytes(M, K) : 0, pb = K ? mx_packed_scale_bytes(N, K) : 0;
+    st = check_mx_pointers(A, PA, pa, B, PB, pb, C, M, N, K, true);
+    if (st != HKG_OK)
+        return st;
+    st = check_epilogue(bias, C, M, N, epilogue);
+    if (st != HKG_OK)
+        return st;
+    if (!mx4_plan_matches_library(plan))
         return HKG_ERR_UNSUPPORTED;
     if (mx_kernel(plan->kernel_id) && !mx_aligned(A, PA, B, PB, C))
         return HKG_ERR_MISALIGNED;

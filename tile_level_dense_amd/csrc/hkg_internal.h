@@ -28,6 +28,14 @@ constexpr int MX_TILE_NUM_VARIANTS = 0
 #undef HKG_COUNT_TILE
     ;
 
+// MXFP4 tile-kernel instantiations (plan.variant for HKG_KERNEL_MX4_TILE):
+// the rows of HKG_MX4_TILE_CONFIGS.
+constexpr int MX4_TILE_NUM_VARIANTS = 0
+#define HKG_COUNT_TILE(bm, bn, bk, st, wm, wn, sc) +1
+    HKG_MX4_TILE_CONFIGS(HKG_COUNT_TILE)
+#undef HKG_COUNT_TILE
+    ;
+
 // Grouped-GEMM instantiations (plan.variant for HKG_KERNEL_GROUPED): the
 // rows of HKG_GROUPED_CONFIGS; the planner's two (the 256 x 256 ping-pong
 // streaming its tiles' stages, and the 128 x 128 tile).
@@ -84,8 +92,10 @@ TileShape tile_shape(int variant);
 int tile_lds_bytes(int variant);
 
 TileShape mx_tile_shape(int variant);
+TileShape mx4_tile_shape(int variant);
 TileShape grouped_shape(int variant);
 int mx_tile_lds_bytes(int variant);
+int mx4_tile_lds_bytes(int variant);
 // Bytes of the packed scales of `rows` rows (rows rounded up to 64).
 int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
 
@@ -131,6 +141,12 @@ hipError_t launch_tile(int variant, const uint16_t* A, const uint16_t* B, uint16
 hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
                           int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
                           int epi, const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
+
+// MXFP4 tile kernel: A, B E2M1 codes two per byte (rows of K / 2 bytes),
+// K % 128 == 0, packed scales as launch_tile_mx; other arguments likewise.
+hipError_t launch_tile_mx4(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                           int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
+                           int epi, const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
 
 // Grouped GEMM: A (M x K), B (G x N x K), offs (G row ends, device int32),
 // C (M x N), bias G x N when epi != EPI_NONE; `grid` persistent workgroups,
@@ -193,6 +209,7 @@ hkg_status_t gemm_fixed_scratch(const void* A, const void* B, void* C, int64_t M
 struct KernelResources { const char* name; int vgprs, agprs, sgprs, scratch, lds; };
 const KernelResources* tile_resources(int variant);
 const KernelResources* mx_tile_resources(int variant);
+const KernelResources* mx4_tile_resources(int variant);
 const KernelResources* grouped_resources(int variant);
 const KernelResources* skinny_resources(int variant);
 const KernelResources* mx_skinny_resources(int variant);

@@ -47,6 +47,13 @@
     X(256, 256, 128, 2, 4, 2, 5)   \
     X(128, 128, 128, 2, 2, 2, 0)
 
+// MXFP4 instantiations (E2M1 operands two per byte, E8M0 scale per 32 k),
+// same fields; BK = 256 k (again 128 bytes per row: two 128-k scaled MFMA
+// steps per stage), SCHED 5 or 0 as for MXFP8.
+#define HKG_MX4_TILE_CONFIGS(X)    \
+    X(256, 256, 256, 2, 4, 2, 5)   \
+    X(128, 128, 256, 2, 2, 2, 0)
+
 // Grouped (mixture-of-experts) instantiations on a persistent grid, same
 // fields; bf16 only, K split only in a partial last round.  Variant 3 (the
 // ping-pong whose workgroups stream their tiles' stages; with a fused

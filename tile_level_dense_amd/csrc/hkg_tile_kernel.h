@@ -37,6 +37,17 @@
 //    scale register chosen by the instruction's op_sel).  Scales come
 //    pre-packed so that one dword per lane holds the bytes of four 16-row
 //    blocks (byte f = block f of a 64-row group); see mx_pack_kernel.
+//  * MXFP4 operand layout of the same instruction with E2M1 operands
+//    (measured on gfx950 with one-hot operands and per-lane scales): lane l
+//    holds in its first four registers the 32 values of row l % 16, 32-k
+//    block g = l / 16 (the last four registers are not read), and that
+//    block's scale comes from lane 16 g + r as for MXFP8.  With two E2M1
+//    codes per byte, a 128-k step of a row is 64 bytes and the lane's
+//    operand is its 16-byte chunk g, so a 256-k stage (128 bytes per row)
+//    has exactly the copies, swizzle and fragment reads of a 64-k bf16
+//    stage: chunk 4 s + g for step s.  Which code of a chunk pairs with
+//    which k inside a block does not matter: A and B are read alike and the
+//    block shares one scale.
 //  * Workgroup -> tile order: chiplet de-interleave with chunk C and a
 //    column-first window of height W (talk notes, section 3, Algorithm 1).
 //  * Ragged M, N and K: rows past the matrix and k past K fall outside the
@@ -95,6 +106,14 @@ __device__ __forceinline__ i32x8 mx_operand(bf16x8 lo, bf16x8 hi)
                                    7);
 }
 
+// The 16 bytes of an MXFP4 operand (32 E2M1 codes) in the first four
+// registers; the instruction does not read the other four.
+__device__ __forceinline__ i32x8 fp4_operand(bf16x8 v)
+{
+    const i32x4 w = __builtin_bit_cast(i32x4, v);
+    return i32x8{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+}
+
 // f(integral_constant<int, I>) for I = B .. E - 1: compile-time indices for
 // the MFMA's op_sel operands.
 template <int B, int E, typename F>
@@ -143,8 +162,10 @@ __device__ __forceinline__ void sync_stage(int ahead)
 }
 
 // MX = false: A, B bf16 (M x K, N x K), BK = 32 or 64.
-// MX = true: A, B E4M3 codes, BK = 128, K % 128 == 0; PSA, PSB the packed
-// E8M0 scales of A and B (mx_pack_kernel layout).
+// MX = true, BK = 128: MXFP8, A, B E4M3 codes, K % 128 == 0; PSA, PSB the
+// packed E8M0 scales of A and B (mx_pack_kernel layout).
+// MX = true, BK = 256: MXFP4, A, B E2M1 codes two per byte (k even in the
+// low nibble; rows of K / 2 bytes), K % 128 == 0, the same packed scales.
 // GROUPED = true: the persistent grouped (mixture-of-experts) form, B the
 // G x N x K expert weights, offs the G row ends of the experts in A and C.
 // Threads of a workgroup: the WM x WN wave grid, twice for schedule 7 (two
@@ -163,13 +184,17 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                  const int* __restrict__ offs, int G, int lda, int ldb, int ldc)
 {
     constexpr int NW = WM * WN;
-    constexpr int EB = MX ? 1 : 2;         // bytes per element
-    constexpr int KPC = 16 / EB;           // k per 16-byte chunk
-    constexpr int RB = BK * EB;            // bytes of one row of a stage
+    constexpr bool FP4 = MX && BK == 256;  // MXFP4 (two E2M1 codes per byte)
+    constexpr int EB = MX ? 1 : 2;         // bytes per element (MXFP4: per two elements)
+    constexpr int KPC = FP4 ? 32 : 16 / EB; // k per 16-byte chunk
+    constexpr int RB = FP4 ? BK / 2 : BK * EB; // bytes of one row of a stage
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
     constexpr int RPW = 1024 / RB;         // rows filled by one wave instruction (1 KB)
     constexpr int RPL = 256 / RB;          // rows sharing one 256-byte sweep of the 64 banks
-    constexpr int KS = MX ? 2 : BK / 32;   // 16-byte reads per fragment per stage (bf16: 32-k MFMA steps)
+    // 16-byte reads per fragment per stage: bf16 one per 32-k MFMA step,
+    // MXFP8 the two halves of one 128-k operand, MXFP4 one per 128-k step.
+    constexpr int KS = FP4 ? 2 : MX ? 2 : BK / 32;
+    constexpr int SPS = FP4 ? 2 : 1;       // 128-k scale steps per stage (block-scaled)
     constexpr int WTM = BM / WM;           // rows of C per wave
     constexpr int WTN = BN / WN;           // columns of C per wave
     constexpr int FM = WTM / 16;
@@ -180,12 +205,13 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     constexpr int A_LOADS = BM / (RPW * NW);
     constexpr int B_LOADS = BN / (RPW * NW);
     constexpr int L = A_LOADS + B_LOADS;   // copies per wave per stage
-    static_assert(MX ? BK == 128 : (BK == 32 || BK == 64), "stage k: 32 or 64 (bf16), 128 (MXFP8)");
-    static_assert(!MX || SCHED == 0 || SCHED == 5, "MXFP8: schedules 0 and 5");
+    static_assert(MX ? (BK == 128 || BK == 256) : (BK == 32 || BK == 64),
+                  "stage k: 32 or 64 (bf16), 128 (MXFP8), 256 (MXFP4)");
+    static_assert(!MX || SCHED == 0 || SCHED == 5, "block-scaled: schedules 0 and 5");
     static_assert(SCHED <= 2 || (SCHED >= 5 && SCHED <= 7), "schedules 0, 1, 2, 5, 6 and 7");
     static_assert(SCHED != 7 || (!MX && !GROUPED && BK == 64 && (STAGES == 3 || STAGES == 5)),
                   "schedule 7: bf16 tiles, 3 or 5 stages of 64 k");
-    static_assert(!MX || (WTM % 64 == 0 && WTN % 64 == 0), "MXFP8: wave tiles of whole 64-row scale groups");
+    static_assert(!MX || (WTM % 64 == 0 && WTN % 64 == 0), "block-scaled: wave tiles of whole 64-row scale groups");
     static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     static_assert(BM % (RPW * NW) == 0 && BN % (RPW * NW) == 0, "tile rows must split over waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
@@ -218,10 +244,12 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
-    // Row strides in bytes (leading dimensions); MXFP8 and grouped launches
-    // use dense operands, so there both operands share one stride.
-    const uint32_t a_rb = (uint32_t)lda * (uint32_t)EB;
-    const uint32_t b_rb = (MX || GROUPED) ? a_rb : (uint32_t)ldb * (uint32_t)EB;
+    // Bytes of k elements of a row.
+    auto kbytes = [](int k) { return FP4 ? (uint32_t)k / 2u : (uint32_t)k * (uint32_t)EB; };
+    // Row strides in bytes (leading dimensions); block-scaled and grouped
+    // launches use dense operands, so there both operands share one stride.
+    const uint32_t a_rb = kbytes(lda);
+    const uint32_t b_rb = (MX || GROUPED) ? a_rb : kbytes(ldb);
     __shared__ int last_flag;               // split-K: this workgroup arrived last
 
     // One output tile: C rows [m0, min(m0 + BM, m_lim)) by columns
@@ -287,7 +315,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             char* base = smem + stage * STAGE;
             const int k0 = kbase + kl;
             const bool k_out = k0 + src_k >= k_lim;  // this lane's chunk past the range
-            const uint32_t koff = (uint32_t)k0 * (uint32_t)EB;
+            const uint32_t koff = kbytes(k0);
     #pragma unroll
             for (int i = 0; i < A_LOADS; ++i)
                 copy_to_lds(words_a, base + (wave + i * NW) * 1024,
@@ -335,11 +363,12 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
         };
 
-        // MXFP8 scales.  Packed layout (mx_pack_kernel): for 64-row group R and
-        // stage kt, dword R * KT * 64 + kt * 64 + lane holds in byte f the scale
-        // of row 64 R + 16 f + lane % 16, block 4 kt + lane / 16: this lane's
-        // scale operand for 16-row block f of the group.  A wave's rows are SWA
-        // (B: SWB) whole groups; one dword load per group per stage.
+        // Block scales.  Packed layout (mx_pack_kernel): for 64-row group R and
+        // 128-k step kt, dword R * KT * 64 + kt * 64 + lane holds in byte f the
+        // scale of row 64 R + 16 f + lane % 16, block 4 kt + lane / 16: this
+        // lane's scale operand for 16-row block f of the group.  A wave's rows
+        // are SWA (B: SWB) whole groups; one dword load per group per 128-k
+        // step (SPS steps per stage).
         constexpr int SWA = MX ? WTM / 64 : 1;
         constexpr int SWB = MX ? WTN / 64 : 1;
         const int KT = K / 128;
@@ -349,29 +378,38 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             (void*)PSB, 0, MX ? ((N + 63) / 64) * KT * 256 : 0, kBufferWord3);
         const uint32_t sa_off0 = (uint32_t)(((m0 + wm * WTM) / 64) * KT) * 256u + (uint32_t)lane * 4u;
         const uint32_t sb_off0 = (uint32_t)(((n0 + wn * WTN) / 64) * KT) * 256u + (uint32_t)lane * 4u;
-        uint32_t sa_cur[SWA], sb_cur[SWB], sa_nxt[SWA], sb_nxt[SWB];
+        uint32_t sa_cur[SPS][SWA], sb_cur[SPS][SWB], sa_nxt[SPS][SWA], sb_nxt[SPS][SWB];
         // Scales of local stage t into the *_nxt registers (t past this
         // workgroup's range reads the next split's or out-of-range zeros; such
-        // values are never used).
+        // values are never used; an MXFP4 step past K reads zeros that scale
+        // zero data).
         auto load_scales = [&](int t) {
             if constexpr (MX) {
-                const uint32_t st = (uint32_t)(kt0 + t) * 256u;
     #pragma unroll
-                for (int r = 0; r < SWA; ++r)
-                    sa_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+                for (int q = 0; q < SPS; ++q) {
+                    const uint32_t st = (uint32_t)((kt0 + t) * SPS + q) * 256u;
     #pragma unroll
-                for (int r = 0; r < SWB; ++r)
-                    sb_nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+                    for (int r = 0; r < SWA; ++r)
+                        sa_nxt[q][r] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+    #pragma unroll
+                    for (int r = 0; r < SWB; ++r)
+                        sb_nxt[q][r] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+                }
             }
         };
         auto take_scales = [&]() {
             if constexpr (MX) {
     #pragma unroll
-                for (int r = 0; r < SWA; ++r)
-                    sa_cur[r] = sa_nxt[r];
+                for (int q = 0; q < SPS; ++q) {
     #pragma unroll
-                for (int r = 0; r < SWB; ++r)
-                    sb_cur[r] = sb_nxt[r];
+                    for (int r = 0; r < SWA; ++r)
+                        sa_cur[q][r] = sa_nxt[q][r];
+    #pragma unroll
+                    for (int r = 0; r < SWB; ++r)
+                        sb_cur[q][r] = sb_nxt[q][r];
+                }
             }
         };
         // One 128-k stage of MXFP8 MFMAs: halves lo (chunk g) and hi (chunk 4 + g).
@@ -383,15 +421,35 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 static_for<0, FN>([&](auto J) {
                     constexpr int j = decltype(J)::value;
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        mx_operand(blo[j], bhi[j]), av, acc[i][j], 0, 0, j % 4, (int)sb_cur[j / 4], i % 4,
-                        (int)sa_cur[i / 4]);
+                        mx_operand(blo[j], bhi[j]), av, acc[i][j], 0, 0, j % 4, (int)sb_cur[0][j / 4], i % 4,
+                        (int)sa_cur[0][i / 4]);
+                });
+            });
+        };
+        // One 128-k MXFP4 step q (format code 4, E2M1, for both operands).
+        auto mfmas_fp4 = [&](auto Q, const bf16x8 (&af)[FM], const bf16x8 (&bf)[FN]) {
+            constexpr int q = decltype(Q)::value;
+            static_for<0, FM>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const i32x8 av = fp4_operand(af[i]);
+                static_for<0, FN>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fp4_operand(bf[j]), av, acc[i][j], 4, 4, j % 4, (int)sb_cur[q][j / 4], i % 4,
+                        (int)sa_cur[q][i / 4]);
                 });
             });
         };
 
         auto compute = [&](int stage) {
             const char* base = smem + stage * STAGE;
-            if constexpr (MX) {
+            if constexpr (FP4) {
+                bf16x8 af[KS][FM], bf[KS][FN];
+    #pragma unroll
+                for (int q = 0; q < KS; ++q)
+                    read_frags(base, q, af[q], bf[q]);
+                static_for<0, KS>([&](auto Q) { mfmas_fp4(Q, af[decltype(Q)::value], bf[decltype(Q)::value]); });
+            } else if constexpr (MX) {
                 bf16x8 alo[FM], blo[FN], ahi[FM], bhi[FN];
                 read_frags(base, 0, alo, blo);
                 read_frags(base, 1, ahi, bhi);
@@ -439,9 +497,10 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // later stages still in flight), all waves finished reading step t - 1
             // (lgkmcnt + barrier), so buffer (t - 1) % STAGES is refilled with step
             // t + STAGES - 1 while step t is computed.
-            // MXFP8 (two stages only): the scales of step t + 1 are loaded just
-            // before its copies, so the wait at the top of step t + 1 covers them.
-            static_assert(!MX || STAGES == 2, "MXFP8 ring: two stages");
+            // Block-scaled (two stages only): the scales of step t + 1 are loaded
+            // just before its copies, so the wait at the top of step t + 1 covers
+            // them.
+            static_assert(!MX || STAGES == 2, "block-scaled ring: two stages");
             load_scales(0);
     #pragma unroll
             for (int s = 0; s < STAGES - 1; ++s)
@@ -531,11 +590,11 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             // next compute phase and for its B copies one memory phase later
             // (group 1) or one compute phase later (group 0): in every case
             // before the first phase that reads them.
-            // MXFP8: each memory phase starts by taking the scales loaded at the
-            // start of the previous one (landed: the waits since then cover
-            // them) and loading the next stage's ahead of its copies, so no wait
-            // for scales ever holds back a copy issued after them; 2 (SWA + SWB)
-            // VGPRs.
+            // Block-scaled: each memory phase starts by taking the scales loaded
+            // at the start of the previous one (landed: the waits since then
+            // cover them) and loading the next stage's ahead of its copies, so no
+            // wait for scales ever holds back a copy issued after them;
+            // 2 SPS (SWA + SWB) VGPRs.
             static_assert(BM == 256 && BN == 256 && RB == 128 && NW == 8 && WM <= 4,
                           "split-buffer ping-pong: 256 x 256 tile of 128-byte rows, 8 waves");
             constexpr int HALF = 128 * RB;                  // 128 rows of one stage
@@ -574,7 +633,7 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 }
                 const int k0 = kbase + t * BK;
                 const bool k_out = k0 + pk >= k_lim;
-                const uint32_t off0 = k_out ? kOutOfRange : p_off + (uint32_t)k0 * (uint32_t)EB;
+                const uint32_t off0 = k_out ? kOutOfRange : p_off + kbytes(k0);
                 const uint32_t p_step = (uint32_t)(4 * RPW) * rb;
     #pragma unroll
                 for (int i = 0; i < CPW; ++i)
@@ -615,7 +674,9 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                 }
             };
             auto mfma_stage = [&]() {
-                if constexpr (MX) {
+                if constexpr (FP4) {
+                    static_for<0, KS>([&](auto Q) { mfmas_fp4(Q, af[decltype(Q)::value], bf[decltype(Q)::value]); });
+                } else if constexpr (MX) {
                     mfmas_mx(af[0], af[1], bf[0], bf[1]);
                 } else {
     #pragma unroll

@@ -1,9 +1,10 @@
-// MXFP8 instantiations of the large-tile MFMA kernel (hkg_tile_kernel.h)
-// and the scale packer that feeds them.
+// MXFP8 and MXFP4 instantiations of the large-tile MFMA kernel
+// (hkg_tile_kernel.h) and the scale packer that feeds them.
 //
-// Block-scaled FP8 as the FlyDSL-in-PyTorch blog describes it (MXFP
-// section): E4M3 elements with one E8M0 power-of-two scale per 32 values
-// along K, consumed by gfx950's scaled MFMA, K a multiple of 128.
+// Block-scaled formats as the FlyDSL-in-PyTorch blog describes them (MXFP
+// section): E4M3 elements (MXFP8) or packed E2M1 elements (MXFP4) with one
+// E8M0 power-of-two scale per 32 values along K, consumed by gfx950's scaled
+// MFMA, K a multiple of 128.
 #include "hkg_tile_kernel.h"
 
 namespace hkg {
@@ -57,6 +58,25 @@ int mx_tile_lds_bytes(int variant)
     return s.stages * (s.bm + s.bn) * s.bk;
 }
 
+TileShape mx4_tile_shape(int variant)
+{
+    int v = 0;
+#define HKG_SHAPE(bm, bn, bk, st, wm, wn, sc) \
+    if (v++ == variant)                   \
+        return TileShape{bm, bn, bk, st, (wm) * (wn), wm, wn, sc};
+    HKG_MX4_TILE_CONFIGS(HKG_SHAPE)
+#undef HKG_SHAPE
+    return TileShape{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+int mx4_tile_lds_bytes(int variant)
+{
+    const TileShape s = mx4_tile_shape(variant);   // rows of bk / 2 bytes
+    if (s.sched == 5)
+        return (4 * (s.bm / 2) + 3 * s.bn) * (s.bk / 2);
+    return s.stages * (s.bm + s.bn) * (s.bk / 2);
+}
+
 int64_t mx_packed_scale_bytes(int64_t rows, int64_t K) { return (rows + 63) / 64 * 64 * (K / 32); }
 
 hipError_t launch_mx_pack(const uint8_t* S, uint32_t* P, int64_t rows, int64_t K, hipStream_t stream)
@@ -85,6 +105,27 @@ hipError_t launch_tile_mx(int variant, const uint8_t* A, const uint8_t* B, uint1
                                                                            split_k, ws, counters, bias, epi,   \
                                                                            psa, psb, K, K, N, stream);
     HKG_MX_TILE_CONFIGS(HKG_LAUNCH)
+#undef HKG_LAUNCH
+    return hipErrorInvalidValue;
+}
+
+// Leading dimensions are passed in elements (K), as for MXFP8; the kernel
+// takes a row of the MXFP4 operands as K / 2 bytes.
+hipError_t launch_tile_mx4(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                           int win_w, int chunk_c, int split_k, float* ws, int* counters, const uint16_t* bias,
+                           int epi, const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
+{
+    int v = 0;
+#define HKG_LAUNCH(bm, bn, bk, st, wm, wn, sc)                                                                    \
+    if (v++ == variant)                                                                                          \
+        return epi == EPI_NONE                                                                                   \
+                   ? launch_tile_t<bm, bn, bk, st, wm, wn, sc, false, true>(A, B, C, M, N, K, win_w, chunk_c,    \
+                                                                            split_k, ws, counters, bias, epi,  \
+                                                                            psa, psb, K, K, N, stream)         \
+                   : launch_tile_t<bm, bn, bk, st, wm, wn, sc, true, true>(A, B, C, M, N, K, win_w, chunk_c,     \
+                                                                           split_k, ws, counters, bias, epi,   \
+                                                                           psa, psb, K, K, N, stream);
+    HKG_MX4_TILE_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
     return hipErrorInvalidValue;
 }

@@ -135,6 +135,53 @@ def mx_workload_inputs(name, seed=0):
     return make_mx_inputs(w["M"], w["N"], w["K"], w["a"], w["b"], seed)
 
 
+# ------------------------------------------------------------------ MXFP4
+# Block-scaled FP4 GEMMs (FlyDSL-in-PyTorch blog, MXFP section: packed E2M1
+# operands, one E8M0 scale per 32 k; its MXFP4 gains peak at 32 x 14336 x
+# 4096, which the decode workload takes).  Recipe: E2M1 codes drawn
+# uniformly from all 16 codes (values 0, +-0.5, ..., +-6; the format has no
+# special codes) and packed two per byte, element 2c in the low nibble of
+# byte c; E8M0 scale codes drawn uniformly from a small range per operand
+# (activations 2^-2 .. 2^1, the decode weights 2^-9 .. 2^-6, the magnitudes
+# quantised N(0, 1) activations and N(0, 0.02) weights carry).  A's codes,
+# A's scales, B's codes, B's scales, in that order, from one seeded stream.
+MX4_WORKLOADS = {
+    "mx4_tiny_256": dict(M=256, N=256, K=256, sa=(125, 129), sb=(125, 129)),
+    "mx4_decode_32x14336x4096": dict(M=32, N=14336, K=4096, sa=(125, 129), sb=(118, 122)),
+    "mx4_square_8192": dict(M=8192, N=8192, K=8192, sa=(125, 129), sb=(125, 129)),
+}
+
+
+def pack_e2m1(codes):
+    """R x K codes (0..15, K even) -> R x K/2 bytes, element 2c in the low nibble of byte c."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_e2m1(packed):
+    """Inverse of pack_e2m1: R x K/2 bytes -> R x K codes."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((packed.shape[0], 2 * packed.shape[1]), dtype=np.uint8)
+    out[:, 0::2] = packed & 0xF
+    out[:, 1::2] = packed >> 4
+    return out
+
+
+def make_mx4_inputs(M, N, K, sa=(125, 129), sb=(125, 129), seed=0):
+    """(A M x K/2, SA M x K/32, B N x K/2, SB N x K/32) uint8; scale codes in [lo, hi)."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 16, size=(M, K), dtype=np.uint8)
+    SA = rng.integers(sa[0], sa[1], size=(M, K // 32)).astype(np.uint8)
+    b = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    SB = rng.integers(sb[0], sb[1], size=(N, K // 32)).astype(np.uint8)
+    return pack_e2m1(a), SA, pack_e2m1(b), SB
+
+
+def mx4_workload_inputs(name, seed=0):
+    w = MX4_WORKLOADS[name]
+    return make_mx4_inputs(w["M"], w["N"], w["K"], w["sa"], w["sb"], seed)
+
+
 # ------------------------------------------------------------ grouped GEMM
 # Mixture-of-experts GEMMs (FlyDSL-in-PyTorch blog, grouped GEMM section):
 # the rows of all experts concatenated in A (sum of M_g rows), one N x K
