@@ -36,6 +36,10 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
                buffers), with scales packed once (the kernel) and per call
                (hkg_gemm_mxfp8 with natural-layout scales); torch._scaled_mm
                with one scale per tensor for context
+  mxfp4        the block-scaled FP4 GEMM (E2M1 two per byte, E8M0 scale per
+               32 k) on mx4_square_8192 (TFLOP/s against the 10.1 PFLOP/s
+               dense fp4 MFMA peak) and mx4_decode_32x14336x4096 (HBM GB/s,
+               rotating buffers), packed scales and per-call packing
 
 Progress and diagnostics go to stderr.  Timing uses HIP events on the stream
 the kernels are launched on (torch's current stream), bracketed by device
@@ -56,6 +60,7 @@ sys.path.insert(0, ROOT)
 METRIC = "BF16 GEMM TFLOP/s @8192³ (% of 2.5 PF) + HBM GB/s @M=16 decode (% of 8 TB/s)"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10100.0          # MI355X dense fp4 MFMA
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 LLC_BYTES = 256 * 2**20
 # HipKittens' best 8192^3 BF16 GEMM on MI355X (talk notes, Table 2).
@@ -427,42 +432,55 @@ def vendor_fp8(torch, a, b, out):
     return lambda: torch._scaled_mm(af, bf.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
 
 
-def bench_mx_square(torch, hkg, steps, warmup):
+def bench_mx_square(torch, hkg, steps, warmup, fmt="fp8"):
+    """The 8192^3 block-scaled workload: MXFP8 (E4M3) or MXFP4 (E2M1, two
+    codes per byte)."""
     import workloads
-    name = "mx_square_8192"
-    w = workloads.MX_WORKLOADS[name]
+    fp4 = fmt == "fp4"
+    name = "mx4_square_8192" if fp4 else "mx_square_8192"
+    w = (workloads.MX4_WORKLOADS if fp4 else workloads.MX_WORKLOADS)[name]
     M, N, K = w["M"], w["N"], w["K"]
     log("generating %s inputs" % name)
-    A, SA, B, SB = workloads.mx_workload_inputs(name)
+    A, SA, B, SB = (workloads.mx4_workload_inputs if fp4 else workloads.mx_workload_inputs)(name)
     a, sa, b, sb = (mx_to_dev(x, torch) for x in (A, SA, B, SB))
     del A, SA, B, SB
     pa, pb = hkg.mx_pack_scales(sa, K), hkg.mx_pack_scales(sb, K)
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    plan = hkg.mx_plan(M, N, K)
-    log("mx plan", plan.kernel_name.decode(), plan.reason.decode())
+    gemm = hkg.gemm_mxfp4 if fp4 else hkg.gemm_mxfp8
+    plan = (hkg.mx4_plan if fp4 else hkg.mx_plan)(M, N, K)
+    tag = "mx4" if fp4 else "mx"
+    log("%s plan" % tag, plan.kernel_name.decode(), plan.reason.decode())
     flops = 2.0 * M * N * K
-    ms = time_launches(torch, lambda: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True), steps, warmup,
-                       label="mx_square")
-    ms_nat = time_launches(torch, lambda: hkg.gemm_mxfp8(a, sa, b, sb, out=c), steps, warmup,
-                           label="mx_square_per_call_packing")
-    log("mx square: %.3f ms/step (%.1f TFLOP/s) packed scales, %.3f ms with per-call packing"
-        % (ms, flops / ms / 1e9, ms_nat))
-    fn = vendor_fp8(torch, a, b, c)
-    ms_v = time_launches(torch, fn, steps, warmup, label="mx_square_scaled_mm") if fn else None
-    if ms_v:
-        log("mx square, torch._scaled_mm per-tensor fp8 for context: %.3f ms (%.1f TFLOP/s)" % (ms_v, flops / ms_v / 1e9))
-    return dict(M=M, N=N, K=K, ms=ms, tflops=flops / ms / 1e9, ms_nat=ms_nat, tflops_nat=flops / ms_nat / 1e9,
-                flops=flops, plan=plan, vendor_tflops=(flops / ms_v / 1e9) if ms_v else None)
+    ms = time_launches(torch, lambda: gemm(a, pa, b, pb, out=c, packed=True), steps, warmup,
+                       label="%s_square" % tag)
+    ms_nat = time_launches(torch, lambda: gemm(a, sa, b, sb, out=c), steps, warmup,
+                           label="%s_square_per_call_packing" % tag)
+    log("%s square: %.3f ms/step (%.1f TFLOP/s) packed scales, %.3f ms with per-call packing"
+        % (tag, ms, flops / ms / 1e9, ms_nat))
+    ms_v = None
+    if not fp4:
+        fn = vendor_fp8(torch, a, b, c)
+        ms_v = time_launches(torch, fn, steps, warmup, label="mx_square_scaled_mm") if fn else None
+        if ms_v:
+            log("mx square, torch._scaled_mm per-tensor fp8 for context: %.3f ms (%.1f TFLOP/s)"
+                % (ms_v, flops / ms_v / 1e9))
+    return dict(name=name, M=M, N=N, K=K, ms=ms, tflops=flops / ms / 1e9, ms_nat=ms_nat,
+                tflops_nat=flops / ms_nat / 1e9, flops=flops, plan=plan,
+                vendor_tflops=(flops / ms_v / 1e9) if ms_v else None)
 
 
-def bench_mx_decode(torch, hkg, steps, warmup):
+def bench_mx_decode(torch, hkg, steps, warmup, fmt="fp8"):
+    """The block-scaled decode workload over rotating buffer sets: MXFP8
+    (32 x 4096 x 4096) or MXFP4 (32 x 14336 x 4096)."""
     import workloads
-    name = "mx_decode_32x4096x4096"
-    w = workloads.MX_WORKLOADS[name]
+    fp4 = fmt == "fp4"
+    name = "mx4_decode_32x14336x4096" if fp4 else "mx_decode_32x4096x4096"
+    w = (workloads.MX4_WORKLOADS if fp4 else workloads.MX_WORKLOADS)[name]
     M, N, K = w["M"], w["N"], w["K"]
-    A, SA, B, SB = workloads.mx_workload_inputs(name)
-    alg_bytes = float(M * K + N * K + (M + N) * (K // 32) + 2 * M * N)
-    per_set = M * K + N * K + (M + N) * (K // 32) * 2 + 2 * M * N
+    A, SA, B, SB = (workloads.mx4_workload_inputs if fp4 else workloads.mx_workload_inputs)(name)
+    eb = 0.5 if fp4 else 1.0            # bytes per element
+    alg_bytes = float(eb * (M * K + N * K) + (M + N) * (K // 32) + 2 * M * N)
+    per_set = int(eb * (M * K + N * K)) + (M + N) * (K // 32) * 2 + 2 * M * N
     sets = int(np.ceil(2 * LLC_BYTES / per_set))
     a0, sa0, b0, sb0 = (mx_to_dev(x, torch) for x in (A, SA, B, SB))
     bufs = []
@@ -470,8 +488,10 @@ def bench_mx_decode(torch, hkg, steps, warmup):
         a, sa, b, sb = a0.clone(), sa0.clone(), b0.clone(), sb0.clone()
         bufs.append((a, sa, hkg.mx_pack_scales(sa, K), b, sb, hkg.mx_pack_scales(sb, K),
                      torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
-    plan = hkg.mx_plan(M, N, K)
-    log("mx decode plan", plan.kernel_name.decode(), plan.reason.decode(), "over %d buffer sets" % sets)
+    plan = (hkg.mx4_plan if fp4 else hkg.mx_plan)(M, N, K)
+    gemm = hkg.gemm_mxfp4 if fp4 else hkg.gemm_mxfp8
+    tag = "mx4" if fp4 else "mx"
+    log("%s decode plan" % tag, plan.kernel_name.decode(), plan.reason.decode(), "over %d buffer sets" % sets)
     stream = torch.cuda.Stream()
     reps = max(1, steps // sets)
 
@@ -487,16 +507,17 @@ def bench_mx_decode(torch, hkg, steps, warmup):
                 call(*buf)
         return g
 
-    g_pk = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, pa, b, pb, out=c, packed=True))
-    ms = time_launches(torch, g_pk.replay, reps, graph_warmup(warmup, sets), label="mx_decode", per_call=sets)
-    g_nat = graph_of(lambda a, sa, pa, b, sb, pb, c: hkg.gemm_mxfp8(a, sa, b, sb, out=c))
-    ms_nat = time_launches(torch, g_nat.replay, reps, graph_warmup(warmup, sets), label="mx_decode_natural_scales",
-                           per_call=sets)
+    g_pk = graph_of(lambda a, sa, pa, b, sb, pb, c: gemm(a, pa, b, pb, out=c, packed=True))
+    ms = time_launches(torch, g_pk.replay, reps, graph_warmup(warmup, sets), label="%s_decode" % tag,
+                       per_call=sets)
+    g_nat = graph_of(lambda a, sa, pa, b, sb, pb, c: gemm(a, sa, b, sb, out=c))
+    ms_nat = time_launches(torch, g_nat.replay, reps, graph_warmup(warmup, sets),
+                           label="%s_decode_natural_scales" % tag, per_call=sets)
     gbps = alg_bytes / (ms * 1e-3) / 1e9
-    log("mx decode: %.2f us/call rotating (%.0f GB/s) packed scales, %.2f us from natural-layout scales"
-        % (ms * 1e3, gbps, ms_nat * 1e3))
+    log("%s decode: %.2f us/call rotating (%.0f GB/s) packed scales, %.2f us from natural-layout scales"
+        % (tag, ms * 1e3, gbps, ms_nat * 1e3))
     ms_v = None
-    if vendor_fp8(torch, bufs[0][0], bufs[0][3], bufs[0][6]):
+    if not fp4 and vendor_fp8(torch, bufs[0][0], bufs[0][3], bufs[0][6]):
         one = torch.ones((), device="cuda")
         g_v = graph_of(lambda a, sa, pa, b, sb, pb, c: torch._scaled_mm(
             a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn).t(), scale_a=one, scale_b=one,
@@ -504,8 +525,8 @@ def bench_mx_decode(torch, hkg, steps, warmup):
         ms_v = time_launches(torch, g_v.replay, reps, graph_warmup(warmup, sets), label="mx_decode_scaled_mm",
                              per_call=sets)
         log("mx decode, torch._scaled_mm per-tensor fp8 for context: %.2f us" % (ms_v * 1e3))
-    return dict(M=M, N=N, K=K, ms=ms, gbps=gbps, ms_nat=ms_nat, alg_bytes=alg_bytes, sets=sets, plan=plan,
-                launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
+    return dict(name=name, M=M, N=N, K=K, ms=ms, gbps=gbps, ms_nat=ms_nat, alg_bytes=alg_bytes, sets=sets,
+                plan=plan, launches=reps * sets, vendor_us=ms_v * 1e3 if ms_v else None)
 
 
 ALL_CONFIGS = ("tiny_256", "mlp_up_128x12288x4096", "prefill_down_4096x4096x12288")
@@ -704,7 +725,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (debug runs)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the tiny / MLP-up / prefill-down and compute-bound middle legs (counter runs)")
-    ap.add_argument("--only", choices=["square", "decode", "mx", "grouped", "layouts", "configs", "middle"],
+    ap.add_argument("--only", choices=["square", "decode", "mx", "mx4", "grouped", "layouts", "configs", "middle"],
                     help="time one leg only (profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -747,6 +768,12 @@ def main():
         print(json.dumps({"mx_square_tflops": round(mxs["tflops"], 2), "mx_decode_gbps": round(mxd["gbps"], 1)}),
               flush=True)
         return 0
+    if args.only == "mx4":
+        m4s = bench_mx_square(torch, hkg, args.steps, args.warmup, fmt="fp4")
+        m4d = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100), fmt="fp4")
+        print(json.dumps({"mx4_square_tflops": round(m4s["tflops"], 2), "mx4_decode_gbps": round(m4d["gbps"], 1)}),
+              flush=True)
+        return 0
     sq = bench_square(torch, hkg, args.steps, args.warmup)
     if args.only == "square":
         print(json.dumps({"square_tflops": round(sq["tflops"], 2), "ms_per_step": round(sq["ms"], 4)}), flush=True)
@@ -754,6 +781,8 @@ def main():
     dec = bench_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
     mxs = bench_mx_square(torch, hkg, args.steps, args.warmup)
     mxd = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100))
+    m4s = bench_mx_square(torch, hkg, args.steps, args.warmup, fmt="fp4")
+    m4d = bench_mx_decode(torch, hkg, args.decode_steps, max(args.warmup * 10, 100), fmt="fp4")
     grp = bench_grouped(torch, hkg, args.steps, args.warmup)
     lay = bench_layouts(torch, hkg, args.steps, args.warmup)
     cfg = {} if args.no_configs else bench_configs(torch, hkg)
@@ -870,6 +899,27 @@ def main():
                                     "per_launch": "M K + N K + (M + N) K / 32 + 2 M N = %d bytes" % mxd["alg_bytes"]},
                        "rotating_sets": mxd["sets"], "launches_timed": mxd["launches"],
                        "vendor_fp8_per_tensor_us": round(mxd["vendor_us"], 3) if mxd["vendor_us"] else None},
+        },
+        "mxfp4": {
+            "square": {"workload": "mx4_square_8192: E2M1 A, B (all 16 codes), E8M0 scale per 32 k, "
+                                   "M = N = K = 8192",
+                       "tflops": round(m4s["tflops"], 2), "ms": round(m4s["ms"], 4),
+                       "per_call_packing_tflops": round(m4s["tflops_nat"], 2),
+                       "roofline": {"bound": "mfma", "achieved": round(m4s["tflops"], 2), "peak": PEAK_FP4_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(m4s["tflops"] / PEAK_FP4_TFLOPS, 4),
+                                    "traffic": measured_traffic(m4s["name"], m4s["plan"].kernel_name.decode()),
+                                    "kernel": m4s["plan"].kernel_name.decode(),
+                                    "per_launch": "2 M N K = %.4g flop per launch" % m4s["flops"]}},
+            "decode": {"workload": "mx4_decode_32x14336x4096: M = 32, N = 14336, K = 4096",
+                       "gbps": round(m4d["gbps"], 1), "us_per_call": round(m4d["ms"] * 1e3, 3),
+                       "natural_scales_us": round(m4d["ms_nat"] * 1e3, 3),
+                       "roofline": {"bound": "hbm", "achieved": round(m4d["gbps"], 1), "peak": PEAK_HBM_GBPS,
+                                    "unit": "GB/s", "frac": round(m4d["gbps"] / PEAK_HBM_GBPS, 4),
+                                    "traffic": measured_traffic(m4d["name"], m4d["plan"].kernel_name.decode()),
+                                    "kernel": m4d["plan"].kernel_name.decode(),
+                                    "per_launch": "(M K + N K) / 2 + (M + N) K / 32 + 2 M N = %d bytes"
+                                                  % m4d["alg_bytes"]},
+                       "rotating_sets": m4d["sets"], "launches_timed": m4d["launches"]},
         },
     }
     print(json.dumps(line), flush=True)

@@ -687,6 +687,18 @@ MUTANTS = {
     "e4m3_bias": ("mag = ldexp(1.0 + (double)f / 8.0, e - 7);", "mag = ldexp(1.0 + (double)f / 8.0, e - 8);"),
     "e4m3_subnormal_scale": ("mag = ldexp((double)f / 8.0, -6);", "mag = ldexp((double)f / 8.0, -7);"),
     "e4m3_ieee_style_nan": ("if (e == 0xF && f == 0x7)", "if (e == 0xF)"),
+    "e2m1_exponent_bias": ("ldexp(1.0 + (double)f / 2.0, e - 1);", "ldexp(1.0 + (double)f / 2.0, e - 2);"),
+    "e2m1_subnormal_scale": ("? (double)f / 2.0 ", "? (double)f "),
+    "e2m1_sign_bit": ("int sign = (code >> 3) & 1;", "int sign = (code >> 2) & 1;"),
+    "mx4_high_nibble_shift": ("(k & 1) ? byte >> 4 : byte & 0xF", "(k & 1) ? byte >> 3 : byte & 0xF"),
+    "mx4_dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double p = (mx4_element",
+                              "for (int64_t k = 0; k < K - 1; ++k) {\n        double p = (mx4_element"),
+    "mx4_one_scale_per_row": ("(mx4_element(a_row, k) * hkg_oracle_e8m0_value(sa_row[k / 32]))",
+                              "(mx4_element(a_row, k) * hkg_oracle_e8m0_value(sa_row[0]))"),
+    "mx4_b_scaled_by_a": ("(mx4_element(b_row, k) * hkg_oracle_e8m0_value(sb_row[k / 32]))",
+                          "(mx4_element(b_row, k) * hkg_oracle_e8m0_value(sa_row[k / 32]))"),
+    "mx4_scale_block_of_16": ("(mx4_element(a_row, k) * hkg_oracle_e8m0_value(sa_row[k / 32]))",
+                              "(mx4_element(a_row, k) * hkg_oracle_e8m0_value(sa_row[k / 16]))"),
     "mx_abs_sum_signed": ("s += p;\n        sa += fabs(p);\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/* Rows [row_begin, row_end) of the MXFP8",
                           "s += p;\n        sa += p;\n    }\n    *s_out = s;\n    *abs_out = sa;\n}\n\n/* Rows [row_begin, row_end) of the MXFP8"),
 }
