@@ -86,7 +86,8 @@ typedef enum {
     HKG_KERNEL_MX_TILE = 5,     /* MXFP8 large-tile kernel (scaled MFMA) */
     HKG_KERNEL_GROUPED = 6,     /* grouped (mixture-of-experts) tile kernel, persistent grid */
     HKG_KERNEL_MX_SKINNY = 7,   /* MXFP8 small-M kernel: streams B once, split-K */
-    HKG_KERNEL_MX4_TILE = 8     /* MXFP4 tile kernel (scaled MFMA, E2M1 operands) */
+    HKG_KERNEL_MX4_TILE = 8,    /* MXFP4 tile kernel (scaled MFMA, E2M1 operands) */
+    HKG_KERNEL_MX4_SKINNY = 9   /* MXFP4 small-M kernel: streams B once, split-K */
 } hkg_kernel_t;
 
 /*
@@ -275,7 +276,9 @@ hkg_status_t hkg_gemm_mxfp8_run_plan(const hkg_plan_t* plan, const void* A, cons
  *      NaNs).  B: N x K/2 bytes likewise.
  *   SA: M x K/32 bytes, SB: N x K/32 bytes, E8M0 codes as for MXFP8.
  *   C: M x N bf16, row-major, nearest-even.  K must be a multiple of 128
- *   (else HKG_ERR_INVALID_ARG); M and N are free.
+ *   (else HKG_ERR_INVALID_ARG); M and N are free.  NaN scale codes give
+ *   unspecified results in the outputs whose sums they enter and leave
+ *   every other output as specified.
  *
  * Accuracy.  A product of two E2M1 values is a multiple of 1/4 below 37,
  * and the 32 products of one scale block share one power-of-two scale, so
@@ -307,8 +310,10 @@ hkg_status_t hkg_gemm_mxfp4_prepacked(const void* A, const void* PA, const void*
 
 /*
  * Runs an MXFP4 plan (from hkg_gemm_mxfp4_plan, possibly edited: variant
- * with matching tile fields, split_k in [1, 16] for split-capable variants,
- * xcd fields >= 0) on packed scales; other plans give HKG_ERR_UNSUPPORTED.
+ * with matching tile fields, split_k in [1, 16] for split-capable tile
+ * variants and in [1, 64] for the small-M kernel, xcd fields >= 0) on packed
+ * scales; other plans give HKG_ERR_UNSUPPORTED.  The planner takes the
+ * small-M kernel (HKG_KERNEL_MX4_SKINNY) for M <= 32.
  */
 hkg_status_t hkg_gemm_mxfp4_run_plan(const hkg_plan_t* plan, const void* A, const void* PA, const void* B,
                                      const void* PB, const void* bias, void* C, int64_t M, int64_t N,

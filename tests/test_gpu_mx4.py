@@ -128,10 +128,90 @@ def test_mx4_parity(hkg, name, shape, variant, split):
 def test_mx4_planner_choices(hkg):
     p = hkg.mx4_plan(8192, 8192, 8192)
     assert p.kernel_id == hkg.HKG_KERNEL_MX4_TILE and p.variant == 0 and p.split_k == 1
-    p = hkg.mx4_plan(32, 14336, 4096)
+    p = hkg.mx4_plan(64, 14336, 4096)
     assert p.kernel_id == hkg.HKG_KERNEL_MX4_TILE and p.variant == 1 and p.split_k == 3
+    p = hkg.mx4_plan(32, 14336, 4096)
+    assert p.kernel_id == hkg.HKG_KERNEL_MX4_SKINNY and p.tile_m == 32 and p.tile_n == 64 and p.split_k == 1
+    p = hkg.mx4_plan(32, 8192, 8192)
+    assert p.kernel_id == hkg.HKG_KERNEL_MX4_SKINNY and p.tile_n == 32 and p.split_k == 1
+    p = hkg.mx4_plan(16, 14336, 4096)
+    assert p.kernel_id == hkg.HKG_KERNEL_MX4_SKINNY and p.tile_m == 32 and p.tile_n == 64
     p = hkg.mx4_plan(32, 1024, 4096)
-    assert p.variant == 1 and p.split_k == 8
+    assert p.kernel_id == hkg.HKG_KERNEL_MX4_SKINNY and p.tile_n == 16 and p.split_k == 2
+    p = hkg.mx4_plan(9, 4096, 4096)
+    assert p.kernel_id == hkg.HKG_KERNEL_MX4_SKINNY and p.tile_m == 16
+
+
+def forced_skinny(hkg, variant, split=1):
+    """Plan edit forcing MXFP4 small-M variant `variant` with `split` K splits."""
+    from tile_level_dense_amd import build as hkg_build
+    mb, nb, wk, u, cp, al = hkg_build.skinny_configs(mx4=True)[variant]
+
+    def edit(p):
+        p.kernel_id = hkg.HKG_KERNEL_MX4_SKINNY
+        p.variant = variant
+        p.tile_m, p.tile_n, p.tile_k, p.waves = 16 * mb, 16 * nb, 256, wk
+        p.split_k = split
+        p.grid_x = -(-p.N // (16 * nb))
+        p.grid_y = split
+        p.workspace_bytes = split * p.M * p.N * 4 if split > 1 else 0
+    return edit
+
+
+# (name, shape, small-M variant, split): ragged N and M, K with a half-empty
+# last 256-k step, splits that leave some workgroups no steps.
+SKINNY_CASES = [
+    ("m16_ragged", (13, 300, 1152), 0, 1),
+    ("m16_one_row_half_step", (1, 50, 128), 0, 1),
+    ("m32_n16", (32, 260, 1024), 1, 1),
+    ("m32_n16_split3_half_step", (17, 200, 1408), 1, 3),
+    ("m32_n32", (30, 333, 2048), 2, 1),
+    ("m32_n32_split5_empty", (32, 96, 768), 2, 5),
+    ("m32_n64", (25, 520, 1536), 3, 1),
+    ("m32_n64_split2_half_step", (32, 700, 640), 3, 2),
+]
+
+
+@pytest.mark.parametrize("name,shape,variant,split", SKINNY_CASES, ids=[c[0] for c in SKINNY_CASES])
+def test_mx4_skinny_parity(hkg, name, shape, variant, split):
+    M, N, K = shape
+    _say("skinny", name, shape, variant, split)
+    A, SA, B, SB = workloads.make_mx4_inputs(M, N, K, sb=(118, 122), seed=len(name) + K)
+    C = run(hkg, A, SA, B, SB, forced_skinny(hkg, variant, split))
+    stats = check(C, A, SA, B, SB)
+    _say(name, stats)
+
+
+@pytest.mark.parametrize("variant,split,shape", [(0, 1, (16, 200, 896)), (1, 1, (32, 136, 512)),
+                                                 (2, 3, (20, 100, 1024)), (3, 1, (32, 300, 384))])
+def test_mx4_skinny_exact_inputs_bit_exact(hkg, variant, split, shape):
+    M, N, K = shape
+    _say("skinny exact", variant, split, shape)
+    A, SA, B, SB = _exact_inputs(M, N, K, seed=M + K)
+    C = run(hkg, A, SA, B, SB, forced_skinny(hkg, variant, split))
+    Cr, S, absS = oracle.mx4_gemm(A, SA, B, SB)
+    assert absS.max() < 2.0 ** 18
+    assert np.array_equal(C, Cr)
+
+
+def test_mx4_skinny_epilogue_and_nan_neighbours(hkg):
+    # bias + SiLU on the small-M kernel; NaN scale codes in columns 64-127 of
+    # B (block 0) leave every other output as specified, with K = 384 (a
+    # half-empty last step).
+    M, N, K = 32, 192, 384
+    A, SA, B, SB = workloads.make_mx4_inputs(M, N, K, seed=43)
+    bias = make_bias(N, 5)
+    for variant in (1, 3):
+        C = run(hkg, A, SA, B, SB, forced_skinny(hkg, variant), bias=bias, epi="bias_silu")
+        stats = check(C, A, SA, B, SB, bias=bias, epi="bias_silu")
+        _say("skinny epilogue", variant, stats)
+    SB[64:128, 0] = 0xFF
+    keep = np.r_[0:64, 128:192]
+    Cr, S, absS = oracle.mx4_gemm(A, SA, B[keep], SB[keep])
+    for variant in (1, 2, 3):
+        C = run(hkg, A, SA, B, SB, forced_skinny(hkg, variant))
+        stats = gates.compare_mx4(C[:, keep], Cr, S, absS, K)
+        _say("skinny NaN neighbours", variant, stats)
 
 
 def _exact_inputs(M, N, K, seed):
@@ -172,6 +252,27 @@ def test_mx4_all_ones_and_one_hot_scales(hkg):
         want[5, :] += 7 * 32
         want[:, 9] -= 0.75 * 32
         assert np.array_equal(exact.widen(C), want), variant
+
+
+def test_mx4_half_stage_ignores_next_groups_scales(hkg):
+    # K = 384 leaves the last 256-k stage half empty; its empty 128-k step
+    # must not pick up the scales the packed layout stores next (the next
+    # 64-row group's first step).  NaN codes (0xFF) in block 0 of rows 64-127
+    # of A and of columns 64-127 of B: the outputs whose sums they enter are
+    # unspecified, every other output is checked.
+    M, N, K = 192, 192, 384
+    A, SA, B, SB = workloads.make_mx4_inputs(M, N, K, seed=41)
+    SA[64:128, 0] = 0xFF
+    SB[64:128, 0] = 0xFF
+    keep_r = np.r_[0:64, 128:192]
+    keep_c = np.r_[0:64, 128:192]
+    Cr, S, absS = oracle.mx4_gemm(A[keep_r], SA[keep_r], B[keep_c], SB[keep_c])
+    for variant in (0, 1):
+        _say("half stage, NaN scales next door, variant", variant)
+        C = run(hkg, A, SA, B, SB, forced(hkg, variant))
+        stats = gates.compare_mx4(C[np.ix_(keep_r, keep_c)], Cr, S, absS, K)
+        _say("variant", variant, stats, "NaN in the rows with NaN codes:",
+             bool(np.isnan(exact.widen(C[64:128, :])).all()))
 
 
 def test_mx4_packed_and_natural_scales_agree(hkg):

@@ -50,9 +50,9 @@ HKG_ERR_ARCH = -5
 HKG_ERR_HIP = -6
 HKG_ERR_WORKSPACE = -7
 KERNEL_NAMES = {0: "NONE", 1: "TILE", 2: "SKINNY", 3: "GENERIC", 4: "ZERO", 5: "MX_TILE", 6: "GROUPED",
-                7: "MX_SKINNY", 8: "MX4_TILE"}
+                7: "MX_SKINNY", 8: "MX4_TILE", 9: "MX4_SKINNY"}
 (HKG_KERNEL_NONE, HKG_KERNEL_TILE, HKG_KERNEL_SKINNY, HKG_KERNEL_GENERIC, HKG_KERNEL_ZERO, HKG_KERNEL_MX_TILE,
- HKG_KERNEL_GROUPED, HKG_KERNEL_MX_SKINNY, HKG_KERNEL_MX4_TILE) = range(9)
+ HKG_KERNEL_GROUPED, HKG_KERNEL_MX_SKINNY, HKG_KERNEL_MX4_TILE, HKG_KERNEL_MX4_SKINNY) = range(10)
 
 LAYOUT_ROW, LAYOUT_COL = 0, 1          # hkg_layout_t
 

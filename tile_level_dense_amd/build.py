@@ -47,10 +47,12 @@ TILE_VARIANTS = tile_configs()
 MX_TILE_VARIANTS = tile_configs(mx=True)
 MX4_TILE_VARIANTS = tile_configs(mx4=True)
 GROUPED_VARIANTS = tile_configs(grouped=True)
-def skinny_configs(mx=False):
-    """(MB, NB, WK, U, CP, AL) per skinny variant (MXFP8 with mx=True), from hkg_skinny_configs.h."""
+def skinny_configs(mx=False, mx4=False):
+    """(MB, NB, WK, U, CP, AL) per skinny variant (MXFP8 with mx=True, MXFP4 with mx4=True), from
+    hkg_skinny_configs.h."""
     text = open(os.path.join(CSRC, "hkg_skinny_configs.h")).read()
-    body = text[text.index("#define HKG_MX_SKINNY_CONFIGS(X)" if mx else "#define HKG_SKINNY_CONFIGS(X)"):]
+    body = text[text.index("#define HKG_MX_SKINNY_CONFIGS(X)" if mx else "#define HKG_MX4_SKINNY_CONFIGS(X)" if mx4
+                           else "#define HKG_SKINNY_CONFIGS(X)"):]
     end = body.find("#define", 10)
     body = body if end < 0 else body[:end]
     fields = r"X\(" + r",\s*".join([r"(\d+)"] * 6) + r"\)"
@@ -59,6 +61,7 @@ def skinny_configs(mx=False):
 
 SKINNY_VARIANTS = skinny_configs()
 MX_SKINNY_VARIANTS = skinny_configs(mx=True)
+MX4_SKINNY_VARIANTS = skinny_configs(mx4=True)
 
 
 class BuildError(RuntimeError):
@@ -116,6 +119,7 @@ def _table(resources):
     grouped = [None] * len(GROUPED_VARIANTS)
     skinny = [None] * len(SKINNY_VARIANTS)
     mx_skinny = [None] * len(MX_SKINNY_VARIANTS)
+    mx4_skinny = [None] * len(MX4_SKINNY_VARIANTS)
     generic = None
     for mangled, r in resources.items():
         # The table holds the plain instantiations (no fused epilogue); the
@@ -134,11 +138,19 @@ def _table(resources):
             elif plain and mx and key in MX4_TILE_VARIANTS:
                 mx4_tile[MX4_TILE_VARIANTS.index(key)] = _entry("mx4tile_%dx%dx%d_s%d_w%dx%d_p%d" % key, r)
             continue
-        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E",
-                      mangled)
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])ELb([01])E"
+                      r"Lb([01])ELb([01])E", mangled)
         if m:
             key = tuple(int(g) for g in m.groups()[:5])
             al, plain, mx = int(m.group(6)), m.group(7) == "0", m.group(8) == "1"
+            nat, f4 = m.group(9) == "1", m.group(10) == "1"
+            if plain and f4 and key + (al,) in MX4_SKINNY_VARIANTS:
+                mx4_skinny[MX4_SKINNY_VARIANTS.index(key + (al,))] = _entry(
+                    "mx4skinny_m%d_n%d_w%d_u%d_c%d" % ((16 * key[0], 16 * key[1]) + key[2:]) + ("_lds" if al else ""),
+                    r)
+                continue
+            if f4 or (mx and nat):
+                continue
             label = (16 * key[0], 16 * key[1]) + key[2:]
             if plain and not mx and key + (al,) in SKINNY_VARIANTS:
                 skinny[SKINNY_VARIANTS.index(key + (al,))] = _entry(
@@ -156,10 +168,11 @@ def _table(resources):
               [200 + i for i, e in enumerate(mx_tile) if e is None] + \
               [300 + i for i, e in enumerate(grouped) if e is None] + \
               [400 + i for i, e in enumerate(mx_skinny) if e is None] + \
-              [500 + i for i, e in enumerate(mx4_tile) if e is None] + ([-1] if generic is None else [])
+              [500 + i for i, e in enumerate(mx4_tile) if e is None] + \
+              [600 + i for i, e in enumerate(mx4_skinny) if e is None] + ([-1] if generic is None else [])
     if missing:
         raise BuildError("resource report missing kernels: %s" % missing)
-    return tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic
+    return tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, mx4_skinny, generic
 
 
 def _gate(entries):
@@ -172,7 +185,7 @@ def _gate(entries):
         raise BuildError("kernels use scratch / spill registers (refused): %s" % bad)
 
 
-def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic):
+def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, mx4_skinny, generic):
     def row(e):
         return '{"%s", %d, %d, %d, %d, %d}' % (e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"])
     text = "// generated by tile_level_dense_amd/build.py -- do not edit\n"
@@ -182,13 +195,14 @@ def _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic):
     text += "const KernelResources kSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in skinny) + "};\n"
     text += "const KernelResources kMxSkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in mx_skinny) + "};\n"
     text += "const KernelResources kMx4TileResources[] = {\n    " + ",\n    ".join(row(e) for e in mx4_tile) + "};\n"
+    text += "const KernelResources kMx4SkinnyResources[] = {\n    " + ",\n    ".join(row(e) for e in mx4_skinny) + "};\n"
     text += "const KernelResources kGenericResources = " + row(generic) + ";\n"
     path = os.path.join(BUILD, "hkg_resources.inc")
     with open(path, "w") as f:
         f.write(text)
     with open(os.path.join(BUILD, "kernel_resources.json"), "w") as f:
         json.dump(dict(tile=tile, mx_tile=mx_tile, grouped=grouped, skinny=skinny, mx_skinny=mx_skinny,
-                       mx4_tile=mx4_tile, generic=generic), f, indent=1)
+                       mx4_tile=mx4_tile, mx4_skinny=mx4_skinny, generic=generic), f, indent=1)
 
 
 def build(verbose=False):
@@ -201,16 +215,16 @@ def build(verbose=False):
     res = {}
     for _, r in results:
         res.update(r)
-    tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic = _table(res)
+    tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, mx4_skinny, generic = _table(res)
     _gate([_entry(name, r) for name, r in res.items()])
-    _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, generic)
+    _write_inc(tile, mx_tile, grouped, skinny, mx_skinny, mx4_tile, mx4_skinny, generic)
     with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
         objs += [f.result()[0] for f in [ex.submit(_compile, s, False) for s in HOST_SOURCES]]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if verbose:
-        for e in tile + mx_tile + grouped + skinny + mx_skinny + mx4_tile + [generic]:
+        for e in tile + mx_tile + grouped + skinny + mx_skinny + mx4_tile + mx4_skinny + [generic]:
             print("%-18s vgpr %3d agpr %3d sgpr %3d scratch %d lds %6d occ %d" % (
                 e["name"], e["vgprs"], e["agprs"], e["sgprs"], e["scratch"], e["lds"], e["occupancy"]))
     return LIB

@@ -1003,6 +1003,9 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
         if (p->kernel_id == HKG_KERNEL_MX_SKINNY)
             e = launch_skinny_mx(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
                                  (int)K, p->split_k, ws, counters, bias, epi, PA, PB, natural, stream);
+        else if (p->kernel_id == HKG_KERNEL_MX4_SKINNY)
+            e = launch_skinny_mx4(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
+                                  (int)K, p->split_k, ws, counters, bias, epi, PA, PB, stream);
         else if (p->kernel_id == HKG_KERNEL_MX4_TILE)
             e = launch_tile_mx4(p->variant, (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, (int)M, (int)N,
                                 (int)K, p->xcd_window_w, p->xcd_chunk_c, p->split_k, ws, counters, bias, epi, PA,
@@ -1021,7 +1024,8 @@ hkg_status_t run_mx(const hkg_plan_t* p, const void* A, const uint32_t* PA, cons
 
 bool mx_kernel(int id)
 {
-    return id == HKG_KERNEL_MX_TILE || id == HKG_KERNEL_MX_SKINNY || id == HKG_KERNEL_MX4_TILE;
+    return id == HKG_KERNEL_MX_TILE || id == HKG_KERNEL_MX_SKINNY || id == HKG_KERNEL_MX4_TILE ||
+           id == HKG_KERNEL_MX4_SKINNY;
 }
 
 // The MXFP8 kernels read A, B with 16-byte accesses, store C in 8-byte
@@ -1132,6 +1136,32 @@ void fill_mx4_tile(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t
                   (long long)tn, s.bm, s.bn, (long long)split);
 }
 
+void fill_mx4_skinny(hkg_plan_t* p, int variant, int64_t split, int64_t M, int64_t N)
+{
+    const SkinnyShape s = mx4_skinny_shape(variant);
+    const int64_t col_blocks = cdiv(N, 16 * s.nblocks);
+    p->kernel_id = HKG_KERNEL_MX4_SKINNY;
+    p->variant = variant;
+    p->tile_m = 16 * s.mblocks;
+    p->tile_n = 16 * s.nblocks;
+    p->tile_k = 256;
+    p->waves = s.waves;
+    p->split_k = (int32_t)split;
+    p->grid_x = (int32_t)col_blocks;
+    p->grid_y = (int32_t)split;
+    p->grid_z = 1;
+    p->block_x = s.waves * 64;
+    p->xcd_window_w = 0;
+    p->xcd_chunk_c = 0;
+    p->workspace_bytes = split > 1 ? (int64_t)(split * M * N * 4) : 0;
+    p->lds_bytes = mx4_skinny_lds_bytes(variant);
+    fill_resources(p, mx4_skinny_resources(variant));
+    std::snprintf(p->kernel_name, sizeof p->kernel_name, "mx4skinny_m%d_n%d_w%d_u%d_c%d%s", 16 * s.mblocks,
+                  16 * s.nblocks, s.waves, s.unroll, s.cache_policy, s.a_lds ? "_lds" : "");
+    std::snprintf(p->reason, sizeof p->reason, "MXFP4, M <= %d: %lld column blocks of %d, split-K %lld",
+                  16 * s.mblocks, (long long)col_blocks, 16 * s.nblocks, (long long)split);
+}
+
 hkg_status_t make_mx4_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
 {
     std::memset(p, 0, sizeof *p);
@@ -1165,6 +1195,49 @@ hkg_status_t make_mx4_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
     }
     if (!mx4_shape_supported(M, N, K))
         return HKG_ERR_UNSUPPORTED;
+    // Decode shapes: the small-M kernel streams B once.  Each workgroup
+    // reads all of A, so the widest column block whose workgroups still
+    // cover 7/8 of the compute units wins (32 x 14336 x 4096: 64 columns on
+    // 224 workgroups 11.5 us, 32 columns on 448 13.4, 16 on 896 15.7; at
+    // N = 8192 32 columns 12.6 vs 64 on 128 workgroups 17.2); among equal
+    // widths the smaller A cover; where no width fills, the narrowest, split
+    // across workgroups (at least one step of 256 k per wave).
+    int mx4_variant = -1;
+    bool mx4_fills = false;
+    for (int v = 0; v < MX4_SKINNY_NUM_VARIANTS; ++v) {
+        const SkinnyShape ss = mx4_skinny_shape(v);
+        if (M > 16 * (int64_t)ss.mblocks)
+            continue;
+        const bool fills = cdiv(N, 16 * ss.nblocks) * 8 >= 7 * (int64_t)kNumCUs;
+        if (mx4_variant < 0) {
+            mx4_variant = v;
+            mx4_fills = fills;
+            continue;
+        }
+        const SkinnyShape cur = mx4_skinny_shape(mx4_variant);
+        bool better;
+        if (fills != mx4_fills)
+            better = fills;
+        else if (ss.nblocks != cur.nblocks)
+            better = fills ? ss.nblocks > cur.nblocks : ss.nblocks < cur.nblocks;
+        else
+            better = ss.mblocks < cur.mblocks;
+        if (better) {
+            mx4_variant = v;
+            mx4_fills = fills;
+        }
+    }
+    if (mx4_variant >= 0) {
+        const SkinnyShape ss = mx4_skinny_shape(mx4_variant);
+        const int64_t col_blocks = cdiv(N, 16 * ss.nblocks);
+        int64_t split = 1;
+        if (!mx4_fills) {
+            split = std::min<int64_t>(cdiv(kNumCUs, col_blocks), (K / 256) / ss.waves);
+            split = std::max<int64_t>(1, std::min<int64_t>(split, 64));
+        }
+        fill_mx4_skinny(p, mx4_variant, split, M, N);
+        return HKG_OK;
+    }
     // 256 x 256 ping-pong when its tiles fill the device; otherwise the
     // 128 x 128 tile, with split-K (at least 2 stages of 256 k per split)
     // while the grid is under one workgroup per compute unit.
@@ -1190,6 +1263,14 @@ bool mx4_plan_matches_library(const hkg_plan_t* p)
         return p->M == 0 || p->N == 0;
     case HKG_KERNEL_ZERO:
         return p->K == 0 && p->M > 0 && p->N > 0;
+    case HKG_KERNEL_MX4_SKINNY: {
+        if (p->variant < 0 || p->variant >= MX4_SKINNY_NUM_VARIANTS)
+            return false;
+        const SkinnyShape s = mx4_skinny_shape(p->variant);
+        return p->M <= 16 * s.mblocks && p->tile_n == 16 * s.nblocks && p->split_k >= 1 && p->split_k <= 64 &&
+               (p->split_k == 1 || p->M * p->N < ((int64_t)1 << 29)) && p->K > 0 && p->K % 128 == 0 &&
+               mx4_shape_supported(p->M, p->N, p->K);
+    }
     case HKG_KERNEL_MX4_TILE: {
         if (p->variant < 0 || p->variant >= MX4_TILE_NUM_VARIANTS)
             return false;

@@ -68,6 +68,13 @@ constexpr int MX_SKINNY_NUM_VARIANTS = 0
 #undef HKG_COUNT_SKINNY
     ;
 
+// MXFP4 skinny instantiations (plan.variant for HKG_KERNEL_MX4_SKINNY).
+constexpr int MX4_SKINNY_NUM_VARIANTS = 0
+#define HKG_COUNT_SKINNY(mb, nb, wk, u, cp, al) +1
+    HKG_MX4_SKINNY_CONFIGS(HKG_COUNT_SKINNY)
+#undef HKG_COUNT_SKINNY
+    ;
+
 // Skinny-kernel instantiations (plan.variant for HKG_KERNEL_SKINNY): the
 // rows of HKG_SKINNY_CONFIGS in hkg_skinny_configs.h, in order.
 constexpr int SKINNY_NUM_VARIANTS = 0
@@ -102,8 +109,10 @@ int64_t mx_packed_scale_bytes(int64_t rows, int64_t K);
 struct SkinnyShape { int mblocks, nblocks, waves, unroll, cache_policy, a_lds; };
 SkinnyShape skinny_shape(int variant);
 SkinnyShape mx_skinny_shape(int variant);
+SkinnyShape mx4_skinny_shape(int variant);
 int skinny_lds_bytes(int variant);
 int mx_skinny_lds_bytes(int variant);
+int mx4_skinny_lds_bytes(int variant);
 
 // Split-K arrival protocol (tile and skinny kernels).  Each workgroup of a
 // split writes its fp32 partials with agent-scope relaxed atomic stores or
@@ -165,6 +174,12 @@ hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uin
                             int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
                             const uint32_t* psa, const uint32_t* psb, bool natural, hipStream_t stream);
 
+// MXFP4 skinny kernel (M <= 16 MB): packed scales only; split-K as
+// launch_skinny.
+hipError_t launch_skinny_mx4(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                             int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
+                             const uint32_t* psa, const uint32_t* psb, hipStream_t stream);
+
 // Packs rows x (K / 32) E8M0 codes S into the tile kernel's layout P
 // (mx_packed_scale_bytes(rows, K) bytes, 4-byte aligned).
 hipError_t launch_mx_pack(const uint8_t* S, uint32_t* P, int64_t rows, int64_t K, hipStream_t stream);
@@ -213,6 +228,7 @@ const KernelResources* mx4_tile_resources(int variant);
 const KernelResources* grouped_resources(int variant);
 const KernelResources* skinny_resources(int variant);
 const KernelResources* mx_skinny_resources(int variant);
+const KernelResources* mx4_skinny_resources(int variant);
 const KernelResources* generic_resources();
 
 }  // namespace hkg

@@ -98,8 +98,11 @@ __device__ __forceinline__ void static_for(F&& f)
 // loads (32 k, MXFP8 128 k).  CP: cache-policy bits of the B loads (B is
 // streamed once).  AL: A staged through LDS (bf16, MB == 1).  MX: E4M3
 // operands with packed E8M0 scales PSA / PSB (NAT: natural-layout scales,
-// row stride K / 32 bytes).
-template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT>
+// row stride K / 32 bytes).  F4 (with MX): MXFP4, E2M1 codes two per byte
+// (rows of K / 2 bytes), steps of 256 k (128 bytes per row, as an MXFP8
+// step): the lane's two 16-byte loads of a step are its operands for the
+// step's two 128-k halves (format code 4), each with its own packed scales.
+template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT, bool F4 = false>
 __global__ __launch_bounds__(WK * 64, 1)
 void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                    uint16_t* __restrict__ C, int M, int N, int K, int split_k,
@@ -107,12 +110,14 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                    const uint16_t* __restrict__ bias, int epi, int lda, int ldb, int ldc,
                    const uint32_t* __restrict__ PSA, const uint32_t* __restrict__ PSB)
 {
-    constexpr int EB = MX ? 1 : 2;           // bytes per element
-    constexpr int SK = MX ? 128 : 32;        // k per step
-    constexpr int SBY = SK * EB;             // bytes of one row per step
+    constexpr int EB = MX ? 1 : 2;           // bytes per element (MXFP4: per two)
+    constexpr int SK = F4 ? 256 : MX ? 128 : 32;   // k per step
+    constexpr int SBY = F4 ? 128 : SK * EB;  // bytes of one row per step
+    constexpr int KPP = F4 ? 32 : 16 / EB;   // k per 16-byte piece
     typedef std::conditional_t<MX, i32x8, i32x4> frag_t;
-    static_assert(!MX || MB <= 4, "MXFP8 skinny: one 64-row scale group of A");
+    static_assert(!MX || MB <= 4, "block-scaled skinny: one 64-row scale group of A");
     static_assert(MX || !NAT, "natural scales are MXFP8 only");
+    static_assert(!F4 || (MX && !NAT), "MXFP4: packed scales");
     constexpr int NBLK = NB * MB;            // 16 x 16 output blocks per wave
     __shared__ f32x4 red[WK][NBLK][64];
     __shared__ int last_flag;
@@ -157,8 +162,9 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
     const int s_begin = min(wg_end, wg_begin + slice * per_wave);
     const int s_end = min(wg_end, s_begin + per_wave);
 
-    const uint32_t a_rb = (uint32_t)lda * (uint32_t)EB;   // row strides in bytes (leading dimensions)
-    const uint32_t b_rb = (uint32_t)ldb * (uint32_t)EB;
+    // row strides in bytes (leading dimensions, in elements)
+    const uint32_t a_rb = F4 ? (uint32_t)lda / 2u : (uint32_t)lda * (uint32_t)EB;
+    const uint32_t b_rb = F4 ? (uint32_t)ldb / 2u : (uint32_t)ldb * (uint32_t)EB;
     const int rows_b = min(16 * NB, N - n0);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)Bv + (size_t)n0 * b_rb), 0, (int)(rows_b * b_rb), kBufferWord3);
@@ -202,12 +208,14 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
 
     // Steps past s_end (or k past K) load from an out-of-range offset and
     // read zero, which the MFMA adds exactly; so chunks need no tail code.
-    // MXFP8 operands are the bytes at k 16 g .. and 64 + 16 g .. of the step.
-    auto load_frag = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok, auto cp) -> frag_t {
+    // MXFP8 operands are the bytes at k 16 g .. and 64 + 16 g .. of the step;
+    // MXFP4 operands of the step's two halves are the bytes at 16 g .. and
+    // 64 + 16 g .. (the second half past K when K % 256 == 128: ok_hi).
+    auto load_frag = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok, bool ok_hi, auto cp) -> frag_t {
         constexpr int P = decltype(cp)::value;
         if constexpr (MX) {
             const i32x4 lo = load16<P>(r, ok ? off : kOutOfRange);
-            const i32x4 hi = load16<P>(r, ok ? off + 64u : kOutOfRange);
+            const i32x4 hi = load16<P>(r, ok_hi ? off + 64u : kOutOfRange);
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
             return load16<P>(r, ok ? off : kOutOfRange);
@@ -226,7 +234,7 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             const int r = q * RPI + lane / ACH;
             const int c = (lane % ACH) ^ a_swz(r);
             const int step = s + c / PPS;
-            const bool ok = step < s_end && step * SK + (c % PPS) * (16 / EB) < K;
+            const bool ok = step < s_end && step * SK + (c % PPS) * KPP < K;
             dma::copy_to_lds(words_a, dst + q * 1024,
                              ok ? (uint32_t)r * a_rb + (uint32_t)step * SBY + (uint32_t)(c % PPS) * 16u
                                 : kOutOfRange);
@@ -249,7 +257,9 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
             }
         }
     };
-    constexpr int SWA = MX ? (NAT ? MB : 1) : 0, SWB = MX ? NB : 0;
+    // Scale dwords per step: MXFP8 one for A and one per B block (natural
+    // layout: one per A row block); MXFP4 the same for each 128-k half.
+    constexpr int SWA = F4 ? 2 : MX ? (NAT ? MB : 1) : 0, SWB = F4 ? 2 * NB : MX ? NB : 0;
     constexpr bool NAT_RUN_CHUNK = NAT && AL && (U == 2 || U == 4);
     auto load_chunk = [&](int s, int abuf, frag_t (&bv)[U][NB], frag_t (&av)[U][MB], uint32_t (&sa)[U][SWA + 1],
                           uint32_t (&sb)[U][SWB + 1]) {
@@ -264,16 +274,17 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int step = s + u;
-            const bool ok = step < s_end && step * SK + lgrp * (16 / EB) < K;
+            const bool ok = step < s_end && step * SK + lgrp * KPP < K;
+            const bool ok_hi = F4 ? ok && step * SK + 128 < K : ok;
             const uint32_t kb = (uint32_t)step * (uint32_t)SBY;
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                bv[u][j] = load_frag(rb, lane_off_b + kb + (uint32_t)j * block16_b, ok,
+                bv[u][j] = load_frag(rb, lane_off_b + kb + (uint32_t)j * block16_b, ok, ok_hi,
                                      std::integral_constant<int, CP>{});
             if constexpr (!ALDS) {
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
-                    av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok,
+                    av[u][i] = load_frag(ra, lane_off_a + kb + (uint32_t)i * block16_a, ok, ok_hi,
                                          std::integral_constant<int, 0>{});
             }
             if constexpr (NAT) {
@@ -288,6 +299,21 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                     for (int j = 0; j < NB; ++j)
                         sb[u][j] = __builtin_amdgcn_raw_buffer_load_b32(
                             rsb, ok ? (uint32_t)((n0 + 16 * j + lrow) * KT + step) * 4u : kOutOfRange, 0, 0);
+                }
+            } else if constexpr (F4) {
+                // 128-k halves 2 step and 2 step + 1 (a half past K reads
+                // zero: the finite scale 2^-127 on zero data)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const bool okq = q == 0 ? ok : ok_hi;
+                    const uint32_t st = (uint32_t)(2 * step + q) * 256u + (uint32_t)lane * 4u;
+                    sa[u][q] = __builtin_amdgcn_raw_buffer_load_b32(rsa, okq ? st : kOutOfRange, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const int row = n0 + 16 * j;
+                        sb[u][2 * j + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rsb, okq ? (uint32_t)((row / 64) * KT) * 256u + st : kOutOfRange, 0, 0);
+                    }
                 }
             } else if constexpr (MX) {
                 const uint32_t st = (uint32_t)step * 256u + (uint32_t)lane * 4u;
@@ -340,6 +366,21 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
                         constexpr int i = decltype(I)::value;
                         acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bv[u][j], av[u][i], acc[j][i], 0, 0, 0, bsc, 0, (int)(sa[u][i] >> (8 * lgrp)));
+                    });
+                } else if constexpr (F4) {
+                    // half q: the first four registers of the operand
+                    static_for<0, 2>([&](auto Q) {
+                        constexpr int q = decltype(Q)::value;
+                        const i32x8 bq = __builtin_shufflevector(bv[u][j], i32x8{}, 4 * q, 4 * q + 1, 4 * q + 2,
+                                                                 4 * q + 3, 8, 9, 10, 11);
+                        const int bsc = (int)(sb[u][2 * j + q] >> (8 * (((n0 + 16 * j) >> 4) & 3)));
+                        static_for<0, MB>([&](auto I) {
+                            constexpr int i = decltype(I)::value;
+                            const i32x8 aq = __builtin_shufflevector(av[u][i], i32x8{}, 4 * q, 4 * q + 1,
+                                                                     4 * q + 2, 4 * q + 3, 8, 9, 10, 11);
+                            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bq, aq, acc[j][i], 4, 4, 0, bsc, i, (int)sa[u][q]);
+                        });
                     });
                 } else if constexpr (MX) {
                     const int bsc = (int)(sb[u][j] >> (8 * (((n0 + 16 * j) >> 4) & 3)));
@@ -498,13 +539,13 @@ void skinny_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT>
+template <int MB, int NB, int WK, int U, int CP, bool AL, bool EPI, bool MX, bool NAT, bool F4 = false>
 hipError_t launch_skinny_t(const void* A, const void* B, uint16_t* C, int M, int N, int K, int split_k, float* ws,
                            int* counters, const uint16_t* bias, int epi, int lda, int ldb, int ldc,
                            const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
 {
     const int col_blocks = (N + 16 * NB - 1) / (16 * NB);
-    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, AL, EPI, MX, NAT>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, WK, U, CP, AL, EPI, MX, NAT, F4>), dim3(col_blocks, split_k), dim3(WK * 64), 0,
                        stream, A, B, C, M, N, K, split_k, ws, counters, bias, epi, lda, ldb, ldc, psa, psb);
     return hipGetLastError();
 }
@@ -585,6 +626,41 @@ hipError_t launch_skinny_mx(int variant, const uint8_t* A, const uint8_t* B, uin
     HKG_MX_SKINNY_CONFIGS(HKG_LAUNCH)
 #undef HKG_LAUNCH
 #undef HKG_LAUNCH_NAT
+    return hipErrorInvalidValue;
+}
+
+SkinnyShape mx4_skinny_shape(int variant)
+{
+    int v = 0;
+#define HKG_SHAPE(mb, nb, wk, u, cp, al) \
+    if (v++ == variant)                  \
+        return SkinnyShape{mb, nb, wk, u, cp, al};
+    HKG_MX4_SKINNY_CONFIGS(HKG_SHAPE)
+#undef HKG_SHAPE
+    return SkinnyShape{0, 0, 0, 0, 0, 0};
+}
+
+int mx4_skinny_lds_bytes(int variant)
+{
+    const SkinnyShape s = mx4_skinny_shape(variant);
+    const int a_bufs = s.a_lds ? s.waves * 2 * 16 * s.mblocks * s.unroll * 128 : 0;   // A through LDS
+    return s.waves * s.mblocks * s.nblocks * 64 * 16 + a_bufs + 4;
+}
+
+// Packed scales only; leading dimensions in elements (K).
+hipError_t launch_skinny_mx4(int variant, const uint8_t* A, const uint8_t* B, uint16_t* C, int M, int N, int K,
+                             int split_k, float* ws, int* counters, const uint16_t* bias, int epi,
+                             const uint32_t* psa, const uint32_t* psb, hipStream_t stream)
+{
+    int v = 0;
+#define HKG_LAUNCH(mb, nb, wk, u, cp, al)                                                                        \
+    if (v++ == variant)                                                                                     \
+        return epi == EPI_NONE ? launch_skinny_t<mb, nb, wk, u, cp, al, false, true, false, true>(            \
+                                     A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream) \
+                               : launch_skinny_t<mb, nb, wk, u, cp, al, true, true, false, true>(             \
+                                     A, B, C, M, N, K, split_k, ws, counters, bias, epi, K, K, N, psa, psb, stream);
+    HKG_MX4_SKINNY_CONFIGS(HKG_LAUNCH)
+#undef HKG_LAUNCH
     return hipErrorInvalidValue;
 }
 

@@ -29,3 +29,11 @@
     X(2, 1, 8, 2, 0, 0)          \
     X(1, 1, 8, 4, 0, 1)          \
     X(2, 1, 8, 2, 0, 1)
+
+// MXFP4 instantiations, same fields; U counts steps of 256 k (128 bytes of a
+// row, two 128-k scaled MFMA halves).
+#define HKG_MX4_SKINNY_CONFIGS(X) \
+    X(1, 1, 8, 2, 0, 1)           \
+    X(2, 1, 8, 2, 0, 1)           \
+    X(2, 2, 8, 1, 0, 1)           \
+    X(2, 4, 8, 1, 0, 1)

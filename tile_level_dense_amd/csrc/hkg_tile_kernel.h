@@ -381,21 +381,28 @@ void tile_kernel(const void* __restrict__ Av, const void* __restrict__ Bv,
         uint32_t sa_cur[SPS][SWA], sb_cur[SPS][SWB], sa_nxt[SPS][SWA], sb_nxt[SPS][SWB];
         // Scales of local stage t into the *_nxt registers (t past this
         // workgroup's range reads the next split's or out-of-range zeros; such
-        // values are never used; an MXFP4 step past K reads zeros that scale
-        // zero data).
+        // values are never used).  An MXFP4 128-k step past K (the empty half
+        // of a last 256-k stage, whose data are zero-filled) reads through an
+        // empty descriptor (the choice is uniform across the wave, so it
+        // costs no vector register), so it gets code 0 (the finite scale
+        // 2^-127) and never the next row group's scales, which may hold NaN
+        // codes.
+        const __amdgpu_buffer_rsrc_t rsrc_none = __builtin_amdgcn_make_buffer_rsrc((void*)PSA, 0, 0, kBufferWord3);
         auto load_scales = [&](int t) {
             if constexpr (MX) {
     #pragma unroll
                 for (int q = 0; q < SPS; ++q) {
-                    const uint32_t st = (uint32_t)((kt0 + t) * SPS + q) * 256u;
+                    const int step = (kt0 + t) * SPS + q;
+                    const uint32_t st = (uint32_t)step * 256u;
+                    const bool past = FP4 && q > 0 && step >= KT;
     #pragma unroll
                     for (int r = 0; r < SWA; ++r)
                         sa_nxt[q][r] = __builtin_amdgcn_raw_buffer_load_b32(
-                            rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+                            past ? rsrc_none : rsrc_sa, sa_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
     #pragma unroll
                     for (int r = 0; r < SWB; ++r)
                         sb_nxt[q][r] = __builtin_amdgcn_raw_buffer_load_b32(
-                            rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
+                            past ? rsrc_none : rsrc_sb, sb_off0 + (uint32_t)(r * KT) * 256u + st, 0, 0);
                 }
             }
         };
