@@ -145,7 +145,9 @@ def test_plan_decode_geometry():
 def test_plan_boundaries():
     assert hkg.KERNEL_NAMES[hkg.plan(16, 4096, 4096).kernel_id] == "SKINNY"
     assert hkg.KERNEL_NAMES[hkg.plan(17, 4096, 4096).kernel_id] == "TILE"
-    assert hkg.KERNEL_NAMES[hkg.plan(16, 4112, 4096).kernel_id] == "TILE"      # 257 column blocks
+    assert hkg.KERNEL_NAMES[hkg.plan(16, 4112, 4096).kernel_id] == "SKINNY"    # 257 column blocks
+    assert hkg.KERNEL_NAMES[hkg.plan(16, 8192, 4096).kernel_id] == "SKINNY"    # 512: two rounds
+    assert hkg.KERNEL_NAMES[hkg.plan(16, 8208, 4096).kernel_id] == "TILE"      # 513 column blocks
     assert hkg.KERNEL_NAMES[hkg.plan(32, 4096, 4096).kernel_id] == "TILE"
     p = hkg.plan(128, 12288, 4096)       # 256 tiles of 64 x 96: one per CU, unsplit
     assert hkg.KERNEL_NAMES[p.kernel_id] == "TILE" and (p.tile_m, p.tile_n, p.split_k, p.grid_x) == (64, 96, 1, 256)

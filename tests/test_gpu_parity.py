@@ -245,6 +245,19 @@ def test_planner_wide_n_streaming_tile(hkg):
     full_check(run(hkg, A, B), A, B)
 
 
+@pytest.mark.parametrize("shape", [(16, 8192, 4096), (13, 6000, 1000), (1, 4112, 256)],
+                         ids=lambda s: "%dx%dx%d" % s)
+def test_planner_skinny_two_rounds(hkg, shape):
+    # M <= 16 with 257 to 512 column blocks of 16: the planner's small-M
+    # kernel over two rounds of workgroups, every output against the oracle.
+    M, N, K = shape
+    p = hkg.plan(M, N, K)
+    _say("skinny, two rounds", shape, p.kernel_name.decode())
+    assert hkg.KERNEL_NAMES[p.kernel_id] == "SKINNY" and p.grid_x == -(-N // 16), p
+    A, B = workloads.make_inputs(M, N, K, ("normal", 0.0, 1.0), ("normal", 0.0, 0.02), seed=N + K)
+    full_check(run(hkg, A, B), A, B)
+
+
 # ---------------------------------------------------- forced plans
 def forced(hkg, A, B, edit):
     M, K = A.shape

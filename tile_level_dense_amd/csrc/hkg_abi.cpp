@@ -28,12 +28,19 @@ namespace {
 constexpr int kNumCUs = 256;
 
 // Skinny path for M up to this many rows (decode shapes) when its column
-// blocks of 16 fit one per compute unit (N <= 16 * 256).  Otherwise the
-// 4-stage 64 x 64 tile (B read once per 64 rows) measured faster on MI355X:
-// M = 16: N = 12288, K = 4096 26 vs 31 us; M = 32: N = K = 4096 12 vs 16 us,
-// N = 12288 27 vs 42 us; at M = 16, N = K = 4096 the skinny kernel leads,
-// 11.1 vs 11.6 us.
+// blocks of 16 fill at most two rounds of compute units (N <= 16 * 512).
+// Beyond that the 4-stage 64 x 64 tile (B read once per 64 rows) keeps up
+// with it on MI355X (A through LDS, rotating buffers, graph timing, the two
+// interleaved): K = 4096, M = 16: N = 5120 15.6 vs 19.5 us for the tile,
+// 6144 15.8 vs 19.9, 8192 17.3 vs 21.3 (K = 8192: 31.0 vs 41.2); N = 8192
+// at M = 12 16.0 vs 21.2 and M = 4 14.8 vs 20.8; and past two rounds,
+// M = 16: N = 12288 24.5 vs 24.2, 14336 30.3 vs 27.8, 28672 55.1 vs 51.9.  (With A loaded
+// straight into registers the tile led from N = 12288, 26 vs 31 us; at
+// M = 32 the tile leads: N = K = 4096 12 vs 16 us.)  Wider column blocks
+// through LDS (32 and 64 columns per workgroup) were slower at every one
+// of those shapes but N = 14336 (27.6 us with 64 columns).
 constexpr int64_t kSkinnyMaxM = 16;
+constexpr int64_t kSkinnyMaxColBlocks = 2 * kNumCUs;
 // Largest split-K factor of the tile kernel.
 constexpr int64_t kMaxTileSplit = 16;
 
@@ -535,7 +542,7 @@ hkg_status_t make_plan(int64_t M, int64_t N, int64_t K, hkg_plan_t* p)
         plan_generic(M, N, p, "K too large for 32-bit buffer offsets of a tile");
         return HKG_OK;
     }
-    if (M <= kSkinnyMaxM && cdiv(N, 16) <= kNumCUs) {
+    if (M <= kSkinnyMaxM && cdiv(N, 16) <= kSkinnyMaxColBlocks) {
         plan_skinny(M, N, K, p);
         return HKG_OK;
     }
